@@ -1,0 +1,186 @@
+"""Seeded synthetic inputs for the gated delta rule workloads.
+
+This module only draws random numbers and shapes them; it holds none of the
+recurrence's arithmetic, so both the GPU library's tests and the CPU oracle can
+consume the same bytes.
+
+Distributions (the workload descriptions; draws on a CPU ``torch.Generator``):
+  * q, k ~ N(0, 1), then L2-normalised per token in fp32, then cast to the input dtype;
+  * v ~ N(0, 1);
+  * beta = sigmoid(N(0, 1));
+  * log alpha = -a_h * softplus(N(0, 1)) with a_h = exp(A_h), A_h = log U(1, 16) drawn once
+    per value head (the "tiny_gdn/fugue.py" page draws A_log = log U(1, 16) per head and
+    direction; the "sparse-delta-memory layer.py" page, ``compute_gates``, has the same
+    -exp(A) * softplus(.) form);
+  * h0 ~ sigma * N(0, 1) in fp32 (sigma read as a standard deviation).
+
+Draw order per case: per-head A, q, k, v, the decay normals, the beta normals, then h0.
+The segment lengths of a packed case are drawn first, with their own seed offset.
+
+Extra gate regimes (for tests that must see the carried state, which the workload
+gates erase within a few tokens):
+  * "zero":  log alpha = 0 (pure delta rule, alpha = 1);
+  * "p5":    alpha ~ U(0.5, 1) (the "Prizma seq/delta.py" page's self-test regime);
+  * "slow":  log alpha = -U(0, 0.05).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+GATE_REGIMES = ("config", "zero", "p5", "slow")
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(g, shape, std=1.0):
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    return x * std if std != 1.0 else x
+
+
+def _l2_normalise(x):
+    return torch.nn.functional.normalize(x, dim=-1, eps=1e-12)
+
+
+def _gates(g, A_head, lead_shape, regime):
+    """log_alpha, beta of shape lead_shape = (..., Hv, T); A_head has shape (Hv,)."""
+    z = _normal(g, lead_shape)
+    zb = _normal(g, lead_shape)
+    beta = torch.sigmoid(zb)
+    if regime == "config":
+        a = torch.exp(A_head).view(*([1] * (len(lead_shape) - 2)), -1, 1)
+        log_alpha = -a * torch.nn.functional.softplus(z)
+    elif regime == "zero":
+        log_alpha = torch.zeros(lead_shape)
+    elif regime == "p5":
+        log_alpha = torch.log(0.5 + 0.5 * torch.rand(tuple(lead_shape), generator=g))
+    elif regime == "slow":
+        log_alpha = -0.05 * torch.rand(tuple(lead_shape), generator=g)
+    else:
+        raise ValueError("unknown gate regime %r (choose from %s)" % (regime, GATE_REGIMES))
+    return log_alpha.contiguous(), beta.contiguous()
+
+
+@dataclass
+class ChunkCase:
+    """Inputs of one chunked-forward call (CPU tensors)."""
+    q: torch.Tensor            # [B, Hk, T, dk]
+    k: torch.Tensor            # [B, Hk, T, dk]
+    v: torch.Tensor            # [B, Hv, T, dv]
+    log_alpha: torch.Tensor    # [B, Hv, T] fp32
+    beta: torch.Tensor         # [B, Hv, T] fp32
+    h0: torch.Tensor | None    # [nseq, Hv, dk, dv] fp32
+    cu_seqlens: torch.Tensor | None   # [nseq + 1] int32
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def tokens(self) -> int:
+        return int(self.q.shape[0] * self.q.shape[2])
+
+
+def chunk_case(*, B=1, T=256, Hk=2, Hv=None, dk=64, dv=64, dtype=torch.float32, seed=0,
+               h0_std=0.0, regime="config", lengths=None) -> ChunkCase:
+    """Draw one chunked-forward case. ``lengths`` (list of ints) packs segments into B=1."""
+    Hv = Hk if Hv is None else Hv
+    g = _gen(seed)
+    cu = None
+    if lengths is not None:
+        B = 1
+        lengths = [int(x) for x in lengths]
+        T = sum(lengths)
+        cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    nseq = B if cu is None else len(lengths)
+    A_head = torch.log(1.0 + 15.0 * torch.rand(Hv, generator=g))
+    q = _l2_normalise(_normal(g, (B, Hk, T, dk))).to(dtype).contiguous()
+    k = _l2_normalise(_normal(g, (B, Hk, T, dk))).to(dtype).contiguous()
+    v = _normal(g, (B, Hv, T, dv)).to(dtype).contiguous()
+    log_alpha, beta = _gates(g, A_head, (B, Hv, T), regime)
+    h0 = _normal(g, (nseq, Hv, dk, dv), h0_std).contiguous() if h0_std > 0 else None
+    return ChunkCase(q, k, v, log_alpha, beta, h0, cu)
+
+
+def segment_lengths(n, lo, hi, seed) -> list[int]:
+    """n integer lengths drawn uniformly from [lo, hi], both ends included."""
+    g = _gen(seed)
+    return torch.randint(lo, hi + 1, (n,), generator=g).tolist()
+
+
+@dataclass
+class DecodeCase:
+    q: torch.Tensor          # [steps, N, Hk, dk]
+    k: torch.Tensor          # [steps, N, Hk, dk]
+    v: torch.Tensor          # [steps, N, Hv, dv]
+    log_alpha: torch.Tensor  # [steps, N, Hv] fp32
+    beta: torch.Tensor       # [steps, N, Hv] fp32
+    state: torch.Tensor      # [N, Hv, dk, dv] fp32
+
+
+def decode_case(*, N=4, Hk=2, Hv=4, dk=128, dv=128, steps=1, dtype=torch.bfloat16, seed=0,
+                state_std=0.05, regime="config") -> DecodeCase:
+    g = _gen(seed)
+    A_head = torch.log(1.0 + 15.0 * torch.rand(Hv, generator=g))
+    q = _l2_normalise(_normal(g, (steps, N, Hk, dk))).to(dtype).contiguous()
+    k = _l2_normalise(_normal(g, (steps, N, Hk, dk))).to(dtype).contiguous()
+    v = _normal(g, (steps, N, Hv, dv)).to(dtype).contiguous()
+    # gates laid out [steps, N, Hv] with the per-head A broadcast along the head axis
+    la, beta = _gates(g, A_head, (steps * N, Hv, 1), regime)
+    log_alpha = la.view(steps, N, Hv).contiguous()
+    beta = beta.view(steps, N, Hv).contiguous()
+    state = _normal(g, (N, Hv, dk, dv), state_std).contiguous()
+    return DecodeCase(q, k, v, log_alpha, beta, state)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads. Seeds are 1000 + workload index.
+
+WORKLOADS = {
+    0: "gdr-fwd-fp32-B1-H2-T256-d64-c64",
+    1: "gdr-chunk-fwd-bf16-B4-H16-T4096-d128-c64",
+    2: "gdr-varlen-bf16-8seg-512..8192-H32-d128-c64",
+    3: "gdr-decode-bf16-N256-Hk16-Hv32-d128-64steps",
+    4: "gdr-bidir-pre-bf16-4x4096-H16-d128-c64",
+}
+
+
+def workload0(regime="config") -> ChunkCase:
+    return chunk_case(B=1, T=256, Hk=2, dk=64, dv=64, dtype=torch.float32, seed=1000,
+                      h0_std=0.0, regime=regime)
+
+
+def workload1(regime="config", T=4096) -> ChunkCase:
+    return chunk_case(B=4, T=T, Hk=16, dk=128, dv=128, dtype=torch.bfloat16, seed=1001,
+                      h0_std=0.1, regime=regime)
+
+
+def workload2(regime="config", lengths=None) -> ChunkCase:
+    if lengths is None:
+        lengths = segment_lengths(8, 512, 8192, seed=1002 + 7919)
+    return chunk_case(Hk=32, dk=128, dv=128, dtype=torch.bfloat16, seed=1002, h0_std=0.1,
+                      regime=regime, lengths=lengths)
+
+
+def workload3(regime="config", N=256, steps=64) -> DecodeCase:
+    return decode_case(N=N, Hk=16, Hv=32, dk=128, dv=128, steps=steps, dtype=torch.bfloat16,
+                       seed=1003, state_std=0.05, regime=regime)
+
+
+def workload4(regime="config", seg_len=4096, nseg=4, H=16):
+    """Bidirectional case: shared q, k, v; one gate set per direction; h0 = 0."""
+    lengths = [seg_len] * nseg
+    g = _gen(1004)
+    T = sum(lengths)
+    cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    A_dir = torch.log(1.0 + 15.0 * torch.rand(2, H, generator=g))
+    q = _l2_normalise(_normal(g, (1, H, T, 128))).to(torch.bfloat16).contiguous()
+    k = _l2_normalise(_normal(g, (1, H, T, 128))).to(torch.bfloat16).contiguous()
+    v = _normal(g, (1, H, T, 128)).to(torch.bfloat16).contiguous()
+    la_f, b_f = _gates(g, A_dir[0], (1, H, T), regime)
+    la_b, b_b = _gates(g, A_dir[1], (1, H, T), regime)
+    case = ChunkCase(q, k, v, la_f, b_f, None, cu)
+    case.extra = {"log_alpha_bwd": la_b, "beta_bwd": b_b}
+    return case
