@@ -1,0 +1,241 @@
+"""Benchmark of the gated delta rule library on one MI355X.
+
+Headline: chunked-forward tokens/s on the B4 H16 T4096 d128 bf16 workload (chunk 64,
+nonzero h0, post-write read); one step is one gdr_chunk_fwd call over the whole batch.
+Also reported: decode-step state GB/s (256 sequences, 16 key / 32 value heads, d128,
+fp32 state, 64 consecutive in-place steps), the packed variable-length and bidirectional
+workloads' tokens/s, roofline fractions, and the fp64 CPU oracle timed on this host.
+
+All inputs are synthetic (seeded generators in gated_delta_rule_70_amd/inputs.py) and
+resident in HBM before timing starts. Kernel times come from HIP events recorded on the
+stream the kernels are launched on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix, published
+
+METRIC = "GDR chunk-fwd tokens/s (B4 H16 T4096 d128); decode-step state GB/s"
+
+
+def chunk_bytes(B, H, T, dk, dv, es, nseq, gates=2, state=True):
+    """Algorithmic HBM bytes of one chunked forward: q, k, v, out once each, the gates,
+    h0 and hT."""
+    tok = B * H * T
+    b = tok * (2 * dk + dv) * es + tok * dv * es + tok * gates * 4
+    if state:
+        b += 2 * nseq * H * dk * dv * 4
+    return b
+
+
+def chunk_flops(B, H, T, dk, dv, C=64):
+    """Algorithmic flops per token-head of the chunk form: 6*dk*dv for K H, Q H and the state
+    update, C*(3*dk + 2*dv) for the triangular Gram products (K K^T, Q K^T), W/U and the
+    intra-chunk read (halved for the triangles), C^2/3 for the solve."""
+    per = 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3
+    return B * H * T * per
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), wall
+
+
+def bench_chunk(binding, inputs, steps, warmup):
+    import torch
+    case = inputs.workload1()
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (case.q, case.k, case.v))
+    la, b, h0 = case.log_alpha.to(dev), case.beta.to(dev), case.h0.to(dev)
+    out = torch.empty_like(v)
+    hT = torch.empty_like(h0)
+    stream = torch.cuda.current_stream(dev)
+    fn = lambda: binding.chunk_fwd(q, k, v, la, b, h0, None, chunk=64, out=out, hT=hT)
+    ms, wall = timed(fn, steps, warmup, stream)
+    B, H, T, dk = case.q.shape
+    dv = case.v.shape[-1]
+    return dict(ms=ms, wall=wall, tokens=B * T, bytes=chunk_bytes(B, H, T, dk, dv, 2, B),
+                flops=chunk_flops(B, H, T, dk, dv), shape=(B, H, T, dk, dv))
+
+
+def bench_decode(binding, inputs, reps):
+    import torch
+    dc = inputs.workload3()
+    dev = torch.device("cuda:0")
+    steps = dc.q.shape[0]
+    q, k, v, la, b = (t.to(dev) for t in (dc.q, dc.k, dc.v, dc.log_alpha, dc.beta))
+    state = dc.state.to(dev)
+    out = torch.empty((steps,) + tuple(dc.v.shape[1:]), dtype=dc.v.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    # one warm pass of the 64 steps, then `reps` timed passes (state keeps evolving in place)
+    for s in range(steps):
+        binding.decode_step(q[s], k[s], v[s], la[s], b[s], state, state_out=state, out=out[s])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * reps)]
+    for r in range(reps):
+        for s in range(steps):
+            e0, e1 = ev[r * steps + s]
+            e0.record(stream)
+            binding.decode_step(q[s], k[s], v[s], la[s], b[s], state, state_out=state, out=out[s])
+            e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(c) for a, c in ev)
+    mean = sum(per) / len(per)
+    N, Hv, dk, dv = dc.state.shape
+    sbytes = 2 * N * Hv * dk * dv * 4
+    io = (dc.q[0].numel() * 2 + dc.v[0].numel()) * 2 + N * Hv * 2 * 4 + N * Hv * dv * 2
+    return dict(ms=mean, median=per[len(per) // 2], state_bytes=sbytes, io_bytes=io,
+                tokens=N, steps=steps * reps)
+
+
+def bench_varlen(binding, inputs, steps):
+    import torch
+    case = inputs.workload2()
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (case.q, case.k, case.v))
+    la, b, h0, cu = case.log_alpha.to(dev), case.beta.to(dev), case.h0.to(dev), case.cu_seqlens.to(dev)
+    out, hT = torch.empty_like(v), torch.empty_like(h0)
+    fn = lambda: binding.chunk_fwd(q, k, v, la, b, h0, cu, chunk=64, out=out, hT=hT)
+    ms, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev))
+    T = case.q.shape[2]
+    H, dk, dv = case.q.shape[1], case.q.shape[3], case.v.shape[3]
+    nseq = case.cu_seqlens.numel() - 1
+    return dict(ms=ms, tokens=T, bytes=chunk_bytes(1, H, T, dk, dv, 2, nseq),
+                lengths=[int(x) for x in (case.cu_seqlens[1:] - case.cu_seqlens[:-1])])
+
+
+def bench_bidir(binding, inputs, steps):
+    import torch
+    case = inputs.workload4()
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (case.q, case.k, case.v))
+    la, b, cu = case.log_alpha.to(dev), case.beta.to(dev), case.cu_seqlens.to(dev)
+    la2, b2 = case.extra["log_alpha_bwd"].to(dev), case.extra["beta_bwd"].to(dev)
+    out = torch.empty_like(v)
+
+    def fn():
+        binding.chunk_fwd(q, k, v, la, b, None, cu, chunk=64, read="pre", out=out, want_state=False)
+        binding.chunk_fwd(q, k, v, la2, b2, None, cu, chunk=64, read="pre", reverse=True, out=out,
+                          accumulate=True, want_state=False)
+
+    ms, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev))
+    return dict(ms=ms, tokens=case.q.shape[2])
+
+
+def cpu_baseline(inputs):
+    """The fp64 oracle, as it is, on this host: the whole B4 H16 T4096 d128 workload."""
+    import oracle
+    case = inputs.workload1()
+    threads = min(len(os.sched_getaffinity(0)), 64)
+    import numpy as np
+    args = [np.ascontiguousarray(t.double().numpy()) for t in
+            (case.q, case.k, case.v, case.log_alpha, case.beta, case.h0)]
+    t0 = time.perf_counter()
+    oracle.scan(*args, threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = case.q.shape[0] * case.q.shape[2]
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole B4 H16 T4096 d128 workload (64 sequence-heads), fp64 per-token "
+                      "recurrence, %.1f s wall; CPU: %s" % (dt, cpu_model)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every workload here runs on a single MI355X "
+              "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_70_amd import binding, inputs
+    binding.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    print("[bench] chunked forward B4 H16 T4096 d128 ...", file=sys.stderr, flush=True)
+    c = bench_chunk(binding, inputs, args.steps, args.warmup)
+    B, H, T, dk, dv = c["shape"]
+    res["value"] = c["tokens"] / (c["ms"] / 1e3)
+    res["unit"] = "tokens/s"
+    res["ms_per_step"] = c["ms"]
+    res["config"] = {"workload": inputs.WORKLOADS[1], "B": B, "H": H, "T": T, "dk": dk, "dv": dv,
+                     "chunk": 64, "read": "post", "h0": "N(0, 0.1)", "inputs": "bf16 q/k/v, fp32 gates/state"}
+    gbs = c["bytes"] / (c["ms"] / 1e3) / 1e9
+    tflops = c["flops"] / (c["ms"] / 1e3) / 1e12
+    res["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                       "kernel": "chunk_fwd_kernel<bf16, 64, 128>", "bytes_per_launch": c["bytes"],
+                       "mfma": {"achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": c["flops"]}}
+    if args.only in ("all", "decode"):
+        print("[bench] decode 64 steps N256 Hv32 d128 ...", file=sys.stderr, flush=True)
+        d = bench_decode(binding, inputs, reps=2)
+        sgbs = d["state_bytes"] / (d["ms"] / 1e3) / 1e9
+        res["decode"] = {"metric": "decode-step state GB/s", "value": sgbs, "unit": "GB/s",
+                         "us_per_step": d["ms"] * 1e3, "median_us": d["median"] * 1e3,
+                         "tokens_per_s": d["tokens"] / (d["ms"] / 1e3),
+                         "workload": inputs.WORKLOADS[3],
+                         "roofline": {"bound": "hbm", "achieved": (d["state_bytes"] + d["io_bytes"]) / (d["ms"] / 1e3) / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": (d["state_bytes"] + d["io_bytes"]) / (d["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                      "kernel": "decode_kernel<bf16, 128, 128>"}}
+    if args.only == "all":
+        print("[bench] packed variable-length and bidirectional workloads ...", file=sys.stderr, flush=True)
+        vl = bench_varlen(binding, inputs, max(3, args.steps // 4))
+        bd = bench_bidir(binding, inputs, max(3, args.steps // 4))
+        res["other_workloads"] = {
+            inputs.WORKLOADS[2]: {"tokens_per_s": vl["tokens"] / (vl["ms"] / 1e3), "ms": vl["ms"],
+                                  "hbm_frac": vl["bytes"] / (vl["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                  "lengths": vl["lengths"]},
+            inputs.WORKLOADS[4]: {"tokens_per_s": bd["tokens"] / (bd["ms"] / 1e3), "ms": bd["ms"],
+                                  "calls": 2},
+        }
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

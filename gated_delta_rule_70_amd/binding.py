@@ -1,0 +1,202 @@
+"""Python binding of ``libgdr.so`` (the C ABI in include/gdr.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape and
+contiguity, their device pointers and the current HIP stream are handed to the C entry
+points, and a non-zero status is raised as ``GdrError``. Every step of the computation
+runs in the library's HIP kernels. There is no fallback: if the library is missing the
+import fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdr.so")
+
+GDR_F32, GDR_BF16 = 0, 1
+GDR_READ_PRE, GDR_REVERSE, GDR_ACCUMULATE = 1, 2, 4
+
+STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE", 4: "GDR_ERR_CHUNK",
+          5: "GDR_ERR_ALIGN", 6: "GDR_ERR_ALIAS", 7: "GDR_ERR_UNSUPPORTED", 8: "GDR_ERR_FLAGS",
+          9: "GDR_ERR_HIP"}
+
+# every symbol include/gdr.h declares
+EXPORTS = ("gdr_chunk_fwd", "gdr_decode_step", "gdr_status_string", "gdr_last_error",
+           "gdr_abi_version", "gdr_selftest_mfma")
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__("%s: %s" % (self.name, detail))
+
+
+class ChunkDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("Hk", ctypes.c_int64),
+                ("Hv", ctypes.c_int64), ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("num_seqs", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("Hk", ctypes.c_int64), ("Hv", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError("%s is missing: build it with `python -m gated_delta_rule_70_amd.build` "
+                          "(there is no fallback path)" % path)
+    lib = ctypes.CDLL(path)
+    p, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.gdr_chunk_fwd.argtypes = [p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_decode_step.argtypes = [p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
+    lib.gdr_decode_step.restype = ctypes.c_int
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_abi_version.argtypes = []
+    lib.gdr_abi_version.restype = ctypes.c_int32
+    lib.gdr_selftest_mfma.argtypes = [p, p, p, p]
+    lib.gdr_selftest_mfma.restype = ctypes.c_int
+    return lib
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdrError(status, lib().gdr_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return GDR_BF16
+    if dt == torch.float32:
+        return GDR_F32
+    raise ValueError("q, k, v must be bfloat16 or float32 (got %s)" % dt)
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk: int = 64,
+              read: str = "post", reverse: bool = False, out=None, accumulate: bool = False,
+              hT=None, want_state: bool = True):
+    """Chunked forward (``gdr_chunk_fwd``).
+
+    q, k [B, Hk, T, dk]; v [B, Hv, T, dv] (bf16 or fp32, same dtype); log_alpha, beta
+    [B, Hv, T] fp32; h0 [S, Hv, dk, dv] fp32 or None; cu_seqlens int32 [S+1] (device) or
+    None. Returns (out [B, Hv, T, dv], hT [S, Hv, dk, dv] or None). ``out`` may be given
+    (required for ``accumulate``); ``hT`` may be given (it may be ``h0`` itself).
+    """
+    _need(q, "q")
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    _need(k, "k", dt, (B, Hk, T, dk), dev)
+    _need(v, "v", dt, (B, Hv, T, dv), dev)
+    _need(log_alpha, "log_alpha", torch.float32, (B, Hv, T), dev)
+    _need(beta, "beta", torch.float32, (B, Hv, T), dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (S, Hv, dk, dv), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, Hv, T, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, Hv, T, dv), dev)
+    if hT is None and want_state:
+        hT = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+    elif hT is not None:
+        _need(hT, "hT", torch.float32, (S, Hv, dk, dv), dev)
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0) | \
+        (GDR_ACCUMULATE if accumulate else 0)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    _check(lib().gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                               _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT),
+                               ctypes.byref(dims), _stream(q)))
+    return out, hT
+
+
+def decode_step(q, k, v, log_alpha, beta, state_in, state_out=None, out=None, *, read: str = "post"):
+    """One decode step (``gdr_decode_step``). q, k [N, Hk, dk]; v [N, Hv, dv]; log_alpha,
+    beta [N, Hv] fp32; state_in [N, Hv, dk, dv] fp32. ``state_out`` defaults to a new
+    tensor; pass ``state_in`` itself to update in place. Returns (out, state_out)."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _need(k, "k", dt, (N, Hk, dk), dev)
+    _need(v, "v", dt, (N, Hv, dv), dev)
+    _need(log_alpha, "log_alpha", torch.float32, (N, Hv), dev)
+    _need(beta, "beta", torch.float32, (N, Hv), dev)
+    _need(state_in, "state_in", torch.float32, (N, Hv, dk, dv), dev)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    else:
+        _need(state_out, "state_out", torch.float32, (N, Hv, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, Hv, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (N, Hv, dv), dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    dims = DecodeDims(N, Hk, Hv, dk, dv, code, GDR_READ_PRE if read == "pre" else 0)
+    _check(lib().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                 _ptr(state_in), _ptr(state_out), _ptr(out), ctypes.byref(dims),
+                                 _stream(q)))
+    return out, state_out
+
+
+def selftest_mfma(a, b):
+    """Diagnostic: the 16x16 product of a [16, 32] and b [32, 16] (fp32 GPU tensors) through
+    the library's matrix-core operand layouts. Returns d [3, 16, 16] (see include/gdr.h)."""
+    _need(a, "a", torch.float32, (16, 32))
+    _need(b, "b", torch.float32, (32, 16), a.device)
+    d = torch.empty((3, 16, 16), dtype=torch.float32, device=a.device)
+    _check(lib().gdr_selftest_mfma(_ptr(a), _ptr(b), _ptr(d), _stream(a)))
+    return d

@@ -1,0 +1,198 @@
+// C ABI of the gated delta rule library: host-side argument validation and dispatch.
+// Every check happens before anything is enqueued; see include/gdr.h for the contract.
+#include "../../include/gdr.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "gdr_kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdr_status_t fail(gdr_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+    bool present() const { return lo != 0 && hi > lo; }
+};
+
+Range rng(const char *name, const void *p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(const Range &a, const Range &b) {
+    return a.present() && b.present() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// product of non-negative sizes, or -1 on overflow past 2^62
+int64_t prod(std::initializer_list<int64_t> xs) {
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x < 0) return -1;
+        if (x != 0 && r > (INT64_C(1) << 62) / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+int64_t elem_size(int32_t dtype) { return dtype == GDR_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdr_abi_version(void) { return 1; }
+
+const char *gdr_last_error(void) { return g_last_error; }
+
+const char *gdr_status_string(gdr_status_t s) {
+    switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL: return "a required pointer is NULL";
+    case GDR_ERR_DIMS: return "invalid or inconsistent sizes";
+    case GDR_ERR_DTYPE: return "unknown dtype";
+    case GDR_ERR_CHUNK: return "chunk must be 16, 32 or 64";
+    case GDR_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GDR_ERR_ALIAS: return "buffers overlap";
+    case GDR_ERR_UNSUPPORTED: return "unsupported head size";
+    case GDR_ERR_FLAGS: return "unknown flag bits";
+    case GDR_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, const float *h0, const int32_t *cu_seqlens,
+                           int32_t chunk, void *out, float *hT, const gdr_chunk_dims_t *dims,
+                           void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    const gdr_chunk_dims_t d = *dims;
+    if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
+    if (d.flags & ~(GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE)) return fail(GDR_ERR_FLAGS, "flags 0x%x has unknown bits", d.flags);
+    if (chunk != 16 && chunk != 32 && chunk != 64) return fail(GDR_ERR_CHUNK, "chunk %d is not 16, 32 or 64", chunk);
+    if (d.B < 0 || d.T < 0) return fail(GDR_ERR_DIMS, "B (%lld) and T (%lld) must be >= 0", (long long)d.B, (long long)d.T);
+    if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
+    if (d.dk != 64 && d.dk != 128) return fail(GDR_ERR_UNSUPPORTED, "dk %lld is not 64 or 128", (long long)d.dk);
+    if (d.dv < 32 || d.dv > 256 || d.dv % 32) return fail(GDR_ERR_UNSUPPORTED, "dv %lld is not a multiple of 32 in [32, 256]", (long long)d.dv);
+    int64_t nseq = d.B;
+    if (cu_seqlens) {
+        if (d.B != 1) return fail(GDR_ERR_DIMS, "cu_seqlens needs B == 1 (got %lld)", (long long)d.B);
+        if (d.num_seqs < 1) return fail(GDR_ERR_DIMS, "num_seqs (%lld) must be >= 1 with cu_seqlens", (long long)d.num_seqs);
+        nseq = d.num_seqs;
+    }
+    const int64_t es = elem_size(d.dtype);
+    const int64_t nq = prod({d.B, d.Hk, d.T, d.dk}), nv = prod({d.B, d.Hv, d.T, d.dv});
+    const int64_t ng = prod({d.B, d.Hv, d.T}), ns = prod({nseq, d.Hv, d.dk, d.dv});
+    if (nq < 0 || nv < 0 || ng < 0 || ns < 0 || nq > (INT64_C(1) << 60) / es)
+        return fail(GDR_ERR_DIMS, "sizes overflow");
+    if (nq > 0 && (!q || !k)) return fail(GDR_ERR_NULL, "q or k is NULL");
+    if (nv > 0 && (!v || !out)) return fail(GDR_ERR_NULL, "v or out is NULL");
+    if (ng > 0 && (!log_alpha || !beta)) return fail(GDR_ERR_NULL, "log_alpha or beta is NULL");
+    const void *al16[] = {q, k, v, out, h0, hT};
+    const char *al16n[] = {"q", "k", "v", "out", "h0", "hT"};
+    for (int i = 0; i < 6; ++i)
+        if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
+    if ((log_alpha && !aligned(log_alpha, 4)) || (beta && !aligned(beta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return fail(GDR_ERR_ALIGN, "log_alpha, beta or cu_seqlens is not 4-byte aligned");
+
+    const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
+    const Range ra = rng("log_alpha", log_alpha, ng * 4), rb = rng("beta", beta, ng * 4);
+    const Range rh0 = rng("h0", h0, ns * 4), rhT = rng("hT", hT, ns * 4);
+    const Range rcu = rng("cu_seqlens", cu_seqlens, cu_seqlens ? (nseq + 1) * 4 : 0);
+    const Range ro = rng("out", out, nv * es);
+    const Range ins[] = {rq, rk, rv, ra, rb, rh0, rcu};
+    for (const Range &r : ins) {
+        if (overlap(ro, r)) return fail(GDR_ERR_ALIAS, "out overlaps %s", r.name);
+        if (&r != &ins[5] && overlap(rhT, r)) return fail(GDR_ERR_ALIAS, "hT overlaps %s", r.name);
+    }
+    if (overlap(ro, rhT)) return fail(GDR_ERR_ALIAS, "out overlaps hT");
+    if (overlap(rhT, rh0) && rhT.lo != rh0.lo) return fail(GDR_ERR_ALIAS, "hT partially overlaps h0");
+
+    gdr::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0;
+    a.cu_seqlens = cu_seqlens;
+    a.out = out; a.hT = hT;
+    a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv; a.dv = d.dv;
+    a.units = nseq * d.Hv;
+    a.ntiles = d.dv / 32;
+    a.flags = d.flags;
+    const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
+    if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
+    const hipError_t e = gdr::launch_chunk_fwd(a, d.dtype, chunk, (int)d.dk, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                             const float *beta, const float *state_in, float *state_out, void *out,
+                             const gdr_decode_dims_t *dims, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    const gdr_decode_dims_t d = *dims;
+    if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
+    if (d.flags & ~GDR_READ_PRE) return fail(GDR_ERR_FLAGS, "flags 0x%x: decode takes GDR_READ_PRE only", d.flags);
+    if (d.N < 0) return fail(GDR_ERR_DIMS, "N (%lld) must be >= 0", (long long)d.N);
+    if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
+    if ((d.dk != 64 && d.dk != 128) || (d.dv != 64 && d.dv != 128))
+        return fail(GDR_ERR_UNSUPPORTED, "dk (%lld) and dv (%lld) must be 64 or 128", (long long)d.dk, (long long)d.dv);
+    const int64_t es = elem_size(d.dtype);
+    const int64_t nq = prod({d.N, d.Hk, d.dk}), nv = prod({d.N, d.Hv, d.dv}), ng = prod({d.N, d.Hv});
+    const int64_t ns = prod({d.N, d.Hv, d.dk, d.dv});
+    if (nq < 0 || nv < 0 || ng < 0 || ns < 0 || ns > (INT64_C(1) << 60)) return fail(GDR_ERR_DIMS, "sizes overflow");
+    if (d.N * d.Hv > INT32_MAX) return fail(GDR_ERR_DIMS, "N * Hv too large");
+    if (d.N > 0 && (!q || !k || !v || !log_alpha || !beta || !state_in || !state_out || !out))
+        return fail(GDR_ERR_NULL, "a tensor pointer is NULL");
+    const void *al16[] = {q, k, v, out, state_in, state_out};
+    const char *al16n[] = {"q", "k", "v", "out", "state_in", "state_out"};
+    for (int i = 0; i < 6; ++i)
+        if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
+    if ((log_alpha && !aligned(log_alpha, 4)) || (beta && !aligned(beta, 4)))
+        return fail(GDR_ERR_ALIGN, "log_alpha or beta is not 4-byte aligned");
+    const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
+    const Range ra = rng("log_alpha", log_alpha, ng * 4), rb = rng("beta", beta, ng * 4);
+    const Range rsi = rng("state_in", state_in, ns * 4), rso = rng("state_out", state_out, ns * 4);
+    const Range ro = rng("out", out, nv * es);
+    const Range ins[] = {rq, rk, rv, ra, rb, rsi};
+    for (const Range &r : ins) {
+        if (overlap(ro, r)) return fail(GDR_ERR_ALIAS, "out overlaps %s", r.name);
+        if (&r != &ins[5] && overlap(rso, r)) return fail(GDR_ERR_ALIAS, "state_out overlaps %s", r.name);
+    }
+    if (overlap(ro, rso)) return fail(GDR_ERR_ALIAS, "out overlaps state_out");
+    if (overlap(rso, rsi) && rso.lo != rsi.lo) return fail(GDR_ERR_ALIAS, "state_out partially overlaps state_in");
+
+    gdr::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.log_alpha = log_alpha; a.beta = beta;
+    a.state_in = state_in; a.state_out = state_out; a.out = out;
+    a.N = d.N; a.Hk = d.Hk; a.Hv = d.Hv;
+    a.flags = d.flags;
+    const hipError_t e = gdr::launch_decode(a, d.dtype, (int)d.dk, (int)d.dv, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status_t gdr_selftest_mfma(const float *a, const float *b, float *d, void *stream) {
+    g_last_error[0] = '\0';
+    if (!a || !b || !d) return fail(GDR_ERR_NULL, "a, b and d must be device pointers");
+    const hipError_t e = gdr::launch_selftest_mfma(a, b, d, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "selftest: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+/*
+ * gdr.h - C ABI of the gated delta rule library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (state H = S^T stored row-major [d_k][d_v] per sequence and value head):
+ *
+ *   H_t = alpha_t * H_{t-1} + k_t u_t^T,     u_t = beta_t * (v_t - alpha_t * H_{t-1}^T k_t)
+ *   post-write read   o_t = H_t^T q_t        pre-write read   o_t = H_{t-1}^T q_t
+ *
+ * with alpha_t = exp(log_alpha_t). This is the update defined in the module docstring
+ * of the "Prizma seq/delta.py" page (which stores S = H^T and reads before the write)
+ * and in the SparseDeltaMemory docstring of the "sparse-delta-memory layer.py" page
+ * (decay by exp(g), then the beta-weighted erase-and-write, read after the write).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory, 16-byte
+ *     aligned; the `dims` structs are HOST pointers. The caller owns all memory: the
+ *     library allocates nothing on the device and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the call
+ *     returns without synchronising. No host read of device data happens, so calls can
+ *     be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is launched. A non-GDR_OK
+ *     status means nothing was enqueued; gdr_last_error() then names the offending
+ *     argument (thread-local text, valid until the next call on that thread).
+ *   - Value head j reads query/key head j / (Hv / Hk) (key heads shared by groups of
+ *     value heads, as in `heads` of BidirectionalGatedDeltaNet2 on the "tiny_gdn/fugue.py"
+ *     page and the head-profile checks on the "flashrt-structures fused_layer.py" page).
+ *   - log_alpha must be <= 0 and finite (a decay); q and k are used as given (callers
+ *     normalise them if they want unit keys).
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdr_status {
+    GDR_OK = 0,
+    GDR_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDR_ERR_DIMS = 2,        /* a size is out of range or sizes disagree */
+    GDR_ERR_DTYPE = 3,       /* unknown dtype code */
+    GDR_ERR_CHUNK = 4,       /* chunk is not 16, 32 or 64 */
+    GDR_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    GDR_ERR_ALIAS = 6,       /* two buffers overlap in a way the operation forbids */
+    GDR_ERR_UNSUPPORTED = 7, /* a head size the kernels do not cover */
+    GDR_ERR_FLAGS = 8,       /* unknown flag bits */
+    GDR_ERR_HIP = 9          /* the HIP runtime reported an error */
+} gdr_status_t;
+
+typedef enum gdr_dtype {
+    GDR_F32 = 0,  /* IEEE binary32 */
+    GDR_BF16 = 1  /* bfloat16 */
+} gdr_dtype_t;
+
+/* flag bits */
+#define GDR_READ_PRE 1u   /* o_t = H_{t-1}^T q_t instead of H_t^T q_t */
+#define GDR_REVERSE 2u    /* scan each sequence from its last token to its first */
+#define GDR_ACCUMULATE 4u /* out += o instead of out = o */
+
+typedef struct gdr_chunk_dims {
+    int64_t B;        /* batch rows; must be 1 when cu_seqlens is given */
+    int64_t T;        /* tokens per row (the packed total when cu_seqlens is given) */
+    int64_t Hk;       /* query/key heads, >= 1 */
+    int64_t Hv;       /* value heads, a positive multiple of Hk */
+    int64_t dk;       /* key size: 64 or 128 */
+    int64_t dv;       /* value size: a multiple of 32, at most 256 */
+    int64_t num_seqs; /* segments described by cu_seqlens (ignored when it is NULL) */
+    int32_t dtype;    /* gdr_dtype_t of q, k, v and out */
+    uint32_t flags;   /* GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE */
+} gdr_chunk_dims_t;
+
+typedef struct gdr_decode_dims {
+    int64_t N;      /* independent sequences */
+    int64_t Hk;     /* query/key heads */
+    int64_t Hv;     /* value heads, a positive multiple of Hk */
+    int64_t dk;     /* 64 or 128 */
+    int64_t dv;     /* 64 or 128 */
+    int32_t dtype;  /* gdr_dtype_t of q, k, v and out */
+    uint32_t flags; /* GDR_READ_PRE only */
+} gdr_decode_dims_t;
+
+/*
+ * gdr_chunk_fwd - the chunk-parallel forward over whole sequences.
+ *
+ * Computes, for every sequence and value head, the outputs o_t of every token and the
+ * final state, exactly as the per-token recurrence above would (up to rounding): the
+ * WY/UT chunk form of `chunked_delta` on the "Prizma seq/delta.py" page, where a unit
+ * lower-triangular solve per chunk makes the intra-chunk recurrence exact, so `chunk`
+ * changes the result only through rounding (the same page and the module docstring of
+ * the "sparse-delta-memory layer.py" page). Packed segments (cu_seqlens) restart the
+ * state at each segment start, and GDR_REVERSE scans each segment from its end, as
+ * `segment_layout` and `BidirectionalGatedDeltaNet2.scan` on the "tiny_gdn/fugue.py"
+ * page do.
+ *
+ *   q, k        [B][Hk][T][dk]  dtype
+ *   v           [B][Hv][T][dv]  dtype
+ *   log_alpha   [B][Hv][T]      fp32, <= 0
+ *   beta        [B][Hv][T]      fp32
+ *   h0          [S][Hv][dk][dv] fp32 initial state per sequence, or NULL for zeros;
+ *               S = B, or num_seqs with cu_seqlens. Read only.
+ *   cu_seqlens  NULL, or DEVICE int32 [num_seqs + 1] segment offsets into row 0 with
+ *               cu[0] = 0, non-decreasing, cu[num_seqs] = T (a precondition: it is not
+ *               read on the host). Empty segments are allowed (their hT is h0).
+ *   chunk       16, 32 or 64 tokens per chunk.
+ *   out         [B][Hv][T][dv]  dtype; written (or accumulated into with GDR_ACCUMULATE).
+ *               Must not overlap any input.
+ *   hT          [S][Hv][dk][dv] fp32 final state, or NULL when not wanted. It may be
+ *               exactly h0 (updated in place); any other overlap is GDR_ERR_ALIAS.
+ *
+ * Errors: GDR_ERR_NULL (q, k, v, log_alpha, beta, out or dims NULL, or num_seqs < 1 with
+ * cu_seqlens), GDR_ERR_DIMS, GDR_ERR_DTYPE, GDR_ERR_CHUNK, GDR_ERR_ALIGN, GDR_ERR_ALIAS,
+ * GDR_ERR_UNSUPPORTED (dk not 64/128, dv not a multiple of 32 up to 256), GDR_ERR_FLAGS,
+ * GDR_ERR_HIP (launch failure). T == 0 is valid: only hT is written.
+ */
+gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const float *h0, const int32_t *cu_seqlens, int32_t chunk,
+                           void *out, float *hT,
+                           const gdr_chunk_dims_t *dims, void *stream);
+
+/*
+ * gdr_decode_step - one token of the recurrence for N independent sequences.
+ *
+ * The one-token recurrent core of `_decode_one` on the "flashrt-structures
+ * fused_layer.py" page: it reads state_in and writes state_out and the read o.
+ *
+ *   q, k        [N][Hk][dk]      dtype
+ *   v           [N][Hv][dv]      dtype
+ *   log_alpha   [N][Hv]          fp32, <= 0
+ *   beta        [N][Hv]          fp32
+ *   state_in    [N][Hv][dk][dv]  fp32
+ *   state_out   [N][Hv][dk][dv]  fp32; may be exactly state_in (in place), any other
+ *               overlap is GDR_ERR_ALIAS.
+ *   out         [N][Hv][dv]      dtype; must not overlap any other argument.
+ *
+ * Each state element is read once and written once.
+ * Errors: as gdr_chunk_fwd (no chunk); dk, dv must be 64 or 128.
+ */
+gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta,
+                             const float *state_in, float *state_out, void *out,
+                             const gdr_decode_dims_t *dims, void *stream);
+
+/* Static text for a status code. */
+const char *gdr_status_string(gdr_status_t status);
+
+/* Thread-local detail of the last non-GDR_OK status returned on this thread ("" if none). */
+const char *gdr_last_error(void);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int32_t gdr_abi_version(void);
+
+/*
+ * gdr_selftest_mfma - diagnostic: multiplies one 16x32 by one 32x16 matrix through the
+ * library's matrix-core operand layouts and writes the 16x16 product.
+ *   a   DEVICE fp32 [16][32], b DEVICE fp32 [32][16], d DEVICE fp32 [3][16][16]:
+ *   d[0] through the bf16 32-deep instruction (inputs rounded to bf16),
+ *   d[1] through the fp32 instruction, d[2] through the bf16 16-deep instruction on the
+ *   first 16 columns of a and rows of b. Synchronous on `stream`.
+ */
+gdr_status_t gdr_selftest_mfma(const float *a, const float *b, float *d, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

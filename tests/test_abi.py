@@ -1,0 +1,124 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/gdr.h declares, and
+its host-side validation rejects bad arguments before touching the GPU (no compute here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_70_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                               reason="libgdr.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert _declared() == sorted(binding.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert binding.load().gdr_abi_version() == 1
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-NULL address that is never dereferenced
+
+
+def _chunk(lib, **over):
+    d = dict(B=1, T=128, Hk=2, Hv=2, dk=64, dv=64, num_seqs=0, dtype=1, flags=0)
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, la=FAKE * 4, beta=FAKE * 5, h0=None, cu=None,
+               out=FAKE * 6, hT=None, chunk=64)
+    for k_, v_ in over.items():
+        (d if k_ in d else ptr)[k_] = v_
+    dims = binding.ChunkDims(d["B"], d["T"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["num_seqs"],
+                             d["dtype"], d["flags"])
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_chunk_fwd(vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["la"]), vp(ptr["beta"]),
+                           vp(ptr["h0"]), vp(ptr["cu"]), ptr["chunk"], vp(ptr["out"]), vp(ptr["hT"]),
+                           ctypes.byref(dims), None)
+    return binding.STATUS[st], lib.gdr_last_error().decode()
+
+
+CHUNK_REJECTS = [
+    (dict(chunk=48), "GDR_ERR_CHUNK", "chunk"),
+    (dict(chunk=128), "GDR_ERR_CHUNK", "chunk"),
+    (dict(dk=96), "GDR_ERR_UNSUPPORTED", "dk"),
+    (dict(dv=48), "GDR_ERR_UNSUPPORTED", "dv"),
+    (dict(dv=512), "GDR_ERR_UNSUPPORTED", "dv"),
+    (dict(dtype=7), "GDR_ERR_DTYPE", "dtype"),
+    (dict(flags=8), "GDR_ERR_FLAGS", "flags"),
+    (dict(Hk=3, Hv=4), "GDR_ERR_DIMS", "Hv"),
+    (dict(T=-1), "GDR_ERR_DIMS", "T"),
+    (dict(B=2, cu=FAKE * 9, num_seqs=1), "GDR_ERR_DIMS", "cu_seqlens"),
+    (dict(cu=FAKE * 9, num_seqs=0), "GDR_ERR_DIMS", "num_seqs"),
+    (dict(q=None), "GDR_ERR_NULL", "q"),
+    (dict(out=None), "GDR_ERR_NULL", "out"),
+    (dict(la=None), "GDR_ERR_NULL", "log_alpha"),
+    (dict(q=FAKE + 8), "GDR_ERR_ALIGN", "q"),
+    (dict(hT=FAKE * 7 + 4), "GDR_ERR_ALIGN", "hT"),
+    (dict(out=FAKE * 3 + 64), "GDR_ERR_ALIAS", "out overlaps v"),
+    (dict(h0=FAKE * 16, hT=FAKE * 16 + 256), "GDR_ERR_ALIAS", "partially overlaps h0"),
+    (dict(hT=FAKE), "GDR_ERR_ALIAS", "hT overlaps q"),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status,text", CHUNK_REJECTS, ids=[c[1] + ":" + c[2] for c in CHUNK_REJECTS])
+def test_chunk_fwd_rejects(over, status, text):
+    st, msg = _chunk(binding.load(), **over)
+    assert st == status and text in msg, (st, msg)
+
+
+@needs_lib
+def test_null_dims_and_status_strings():
+    lib = binding.load()
+    st = lib.gdr_chunk_fwd(None, None, None, None, None, None, None, 64, None, None, None, None)
+    assert binding.STATUS[st] == "GDR_ERR_NULL"
+    for code in range(10):
+        assert lib.gdr_status_string(code)
+    assert lib.gdr_status_string(0) == b"ok"
+
+
+def _decode(lib, **over):
+    d = dict(N=4, Hk=2, Hv=4, dk=128, dv=128, dtype=1, flags=0)
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, la=FAKE * 4, beta=FAKE * 5, si=FAKE * 8,
+               so=FAKE * 16, out=FAKE * 6)
+    for k_, v_ in over.items():
+        (d if k_ in d else ptr)[k_] = v_
+    dims = binding.DecodeDims(d["N"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["dtype"], d["flags"])
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_decode_step(vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["la"]), vp(ptr["beta"]),
+                             vp(ptr["si"]), vp(ptr["so"]), vp(ptr["out"]), ctypes.byref(dims), None)
+    return binding.STATUS[st], lib.gdr_last_error().decode()
+
+
+DECODE_REJECTS = [
+    (dict(dk=96), "GDR_ERR_UNSUPPORTED", "dk"),
+    (dict(dv=256), "GDR_ERR_UNSUPPORTED", "dv"),
+    (dict(flags=2), "GDR_ERR_FLAGS", "GDR_READ_PRE"),
+    (dict(Hk=3), "GDR_ERR_DIMS", "Hv"),
+    (dict(N=-2), "GDR_ERR_DIMS", "N"),
+    (dict(si=None), "GDR_ERR_NULL", "NULL"),
+    (dict(so=FAKE * 16 + 8), "GDR_ERR_ALIGN", "state_out"),
+    (dict(so=FAKE * 8 + 4096), "GDR_ERR_ALIAS", "partially overlaps"),
+    (dict(out=FAKE * 8 + 64), "GDR_ERR_ALIAS", "out overlaps state_in"),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status,text", DECODE_REJECTS, ids=[c[1] + ":" + c[2] for c in DECODE_REJECTS])
+def test_decode_rejects(over, status, text):
+    st, msg = _decode(binding.load(), **over)
+    assert st == status and text in msg, (st, msg)
