@@ -35,6 +35,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream);
+bool chunk_fwd_fast_supported(int dtype, int chunk, int dk);
+hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 hipError_t launch_selftest_mfma(const float *a, const float *b, float *d, hipStream_t stream);
 
