@@ -35,6 +35,9 @@ def _flags():
     return ["-O3", "-std=c++17", "-fPIC", "--offload-arch=%s" % ARCH,
             # packed fp32 instructions are switched off for all device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core accumulators in ordinary VGPRs: the kernels apply VALU ops to
+            # them every chunk, and AGPR accumulators would need a move each way
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
