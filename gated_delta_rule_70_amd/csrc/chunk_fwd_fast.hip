@@ -11,16 +11,17 @@
 //                                              [(q_i . k_j) e^{b'_i - b_j}]_{j<i}  (pre)
 //   H  <- e^{b_C} H + K^T diag(e^{b_C - b}) U
 //
-// One workgroup = 4 waves per (sequence, value head, 32 columns of d_v), walking the chunks:
-//   wave 0  "chain": the state-dependent part for chunk c over all 32 columns. The state
-//           tiles stay in accumulator registers and are the B operands of K H and Q H
-//           directly; each operand fragment read from LDS feeds both 16-column tiles.
-//   wave 1  "diagonal" prep for chunk c+1: gate scalars, diagonal tiles of K K^T and the four
-//           16x16 inverses T_ii by forward substitution; copies K of chunk c+2.
-//   wave 2  "P" prep for chunk c+1: the ten lower tiles of Q K^T with their decay factors;
-//           copies Q of chunk c+2.
-//   wave 3  "A" prep for chunk c+1: the six off-diagonal tiles of K K^T (-> -A_ij); copies V
-//           and the gates of chunk c+2.
+// One workgroup = 8 waves per (sequence, value head, 32 columns of d_v), walking the chunks.
+// Waves w and w + 4 share a SIMD.
+//   waves 0, 1  "chain": the state-dependent part for chunk c, one 16-column tile each. The
+//               state tiles stay in accumulator registers and are the B operands of K H and
+//               Q H directly.
+//   wave 2      diagonal prep for chunk c+1: gate scalars, diagonal tiles of K K^T and the
+//               four 16x16 inverses T_ii by substitution.
+//   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1.
+//   waves 6, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1.
+//   waves 4, 5  copies for chunk c+2 (K; Q, V and gates) and the write-back of the output
+//               of chunk c-1; they issue little and share the chain waves' SIMDs.
 // Raw q/k/v of a chunk are copied once per workgroup, global -> LDS directly (16 bytes per
 // lane, no registers), into a ring of three buffers: while the chain reads chunk c and the
 // prep waves read chunk c+1, the loads for chunk c+2 are in flight. Rows are XOR-swizzled by
@@ -53,6 +54,10 @@ namespace gdr {
 namespace {
 
 constexpr int kC = 64, kDK = 128, kDVT = 32;
+// Wave roles. Waves w and w + 4 share a SIMD: each chain wave (0, 1) shares its SIMD with a
+// copy wave, which issues little; the four prep waves take the other two SIMDs.
+constexpr int kThreads = 512;
+constexpr int kWaveCopyK = 4, kWaveCopyQ = 5, kWaveDiag = 2, kWaveP3 = 6, kWaveA = 3, kWaveP012 = 7;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // raw buffer (one of three): K, Q [64 rows][256 B] and V [64 rows][64 B], swizzled; gates
@@ -66,11 +71,12 @@ constexpr int kDerSc = 11264; // beta, e^b, read scale, e^{bC-b} [64] each, then
 constexpr int kDerBytes = 12320;
 constexpr int kOffRaw = 0;
 constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
-constexpr int kOffAd = kOffDer + 2 * kDerBytes;   // wave 1: A_ii^T blocks fp32 [4][16][16]
-constexpr int kOffG1 = kOffAd + 4096;             // wave 1: b2, beta [64]
-constexpr int kOffG2 = kOffG1 + 512;              // wave 2: rowfP [64], colfP [3][64]
-constexpr int kOffG3 = kOffG2 + 1024;             // wave 3: beta*rowfA [64], colfA [3][64]
-constexpr int kOffStage = kOffG3 + 1024;         // output staging, two of [32 cols][64 rows] bf16
+constexpr int kOffAd = kOffDer + 2 * kDerBytes;   // diagonal prep: A_ii blocks fp32 [4][16][16]
+constexpr int kOffG1 = kOffAd + 4096;             // diagonal prep: b2, beta [64]
+constexpr int kOffG2 = kOffG1 + 512;              // P prep, row tiles 0-2: row factors [64], column factors [3][64]
+constexpr int kOffG3 = kOffG2 + 1024;             // A prep: beta * row factors [64], column factors [3][64]
+constexpr int kOffG4 = kOffG3 + 1024;             // P prep, row tile 3: as G2
+constexpr int kOffStage = kOffG4 + 1024;          // output staging, two of [32 cols][64 rows] bf16
 constexpr int kStageBytes = 4096;
 constexpr int kSmemBytes = kOffStage + 2 * kStageBytes;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
@@ -284,11 +290,18 @@ __device__ __forceinline__ float lane_value(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-__device__ __forceinline__ floatx4 gram_u4(const uint4 (&x)[4], const uint4 (&y)[4]) {
-    floatx4 acc = zero4();
+
+// Gram tiles x_a . y_b for a list of (a, b) pairs, slice-outer so that consecutive products
+// go to different accumulators and none waits for the previous one's result.
+template <int N>
+__device__ __forceinline__ void grams(floatx4 (&acc)[N], const uint4 (*x)[4], const uint4 (*y)[4], const int (&xa)[N],
+                                      const int (&yb)[N]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mma32(acc, u4_frag(x[ks]), u4_frag(y[ks]));
-    return acc;
+    for (int n = 0; n < N; ++n) acc[n] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[n] = mma32(acc[n], u4_frag(x[xa[n]][ks]), u4_frag(y[yb[n]][ks]));
 }
 
 __device__ __forceinline__ uint2 pack4(floatx4 v) { return __builtin_bit_cast(uint2, cvt4<__bf16>(v)); }
@@ -307,7 +320,7 @@ __device__ __forceinline__ Gates read_gates(const char *raw) {
     return gt;
 }
 
-// ------------------------------------------------------------------ wave 1: diagonal prep
+// ------------------------------------------------------------------ diagonal prep
 __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der, bool pre, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     const Gates gt = read_gates(raw);
@@ -330,40 +343,46 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
         for (int ks = 0; ks < 4; ++ks) kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
     wave_lds_sync();
     float *adt = reinterpret_cast<float *>(smem + kOffAd);
+    floatx4 gkk[4];
+    grams<4>(gkk, kf, kf, {0, 1, 2, 3}, {0, 1, 2, 3});
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // A_ii in standard orientation: lane holds rows 16i + 4g + r, column 16i + c
-        const floatx4 gk = gram_u4(kf[i], kf[i]);
-        const floatx4 b4 = *reinterpret_cast<const floatx4 *>(gb + 16 * i + 4 * g);
-        const floatx4 beta4 = *reinterpret_cast<const floatx4 *>(gb + 64 + 16 * i + 4 * g);
-        const float bc = gb[16 * i + c];
-        floatx4 a;
+        // A_ii transposed from the Gram tile: lane holds row 16i + c, columns 16i + 4g + r
+        const floatx4 gk = gkk[i];
+        const floatx4 bcol = *reinterpret_cast<const floatx4 *>(gb + 16 * i + 4 * g);
+        const float brow = gb[16 * i + c], betarow = gb[64 + 16 * i + c];
+        floatx4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = (c < 4 * g + r) ? beta4[r] * gk[r] * ex2(b4[r] - bc) : 0.f;
-        *reinterpret_cast<floatx4 *>(adt + (i * 16 + c) * 16 + 4 * g) = a;
+        for (int r = 0; r < 4; ++r) av[r] = (4 * g + r < c) ? betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
+        *reinterpret_cast<floatx4 *>(adt + (i * 16 + c) * 16 + 4 * g) = av;  // row-major A_ii
     }
     wave_lds_sync();
-    // T_ii = (I + A_ii)^{-1}: lane (i = g, c) computes column c. The column of A it needs is
-    // read into registers first; then each solved t_j is eliminated from every later row.
+    // T_ii = (I + A_ii)^{-1}: lane (i = g, c) computes row c, y (I + A_ii) = e_c, from the
+    // last column down: once y_k is final, row k of A_ii is eliminated from the earlier y_j.
+    // The rows of A_ii are read into registers first (the same address in all 16 lanes).
     const float *ablk = adt + g * 256;
-    floatx4 acol[15][4];
+    floatx4 arow[16][4];
 #pragma unroll
-    for (int j = 0; j < 15; ++j)
+    for (int k = 1; k < 16; ++k)
 #pragma unroll
-        for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) acol[j][q4] = reinterpret_cast<const floatx4 *>(ablk + j * 16)[q4];
-    float acc[16];
+        for (int q4 = 0; q4 < 4; ++q4)
+            if (4 * q4 < k) arow[k][q4] = reinterpret_cast<const floatx4 *>(ablk + k * 16)[q4];
+    float y[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = (r == c) ? 1.f : 0.f;
+    for (int j = 0; j < 16; ++j) y[j] = (j == c) ? 1.f : 0.f;
 #pragma unroll
-    for (int j = 0; j < 15; ++j) {
-        const float tj = acc[j];
+    for (int k = 15; k >= 1; --k) {
+        const float yk = y[k];
 #pragma unroll
-        for (int r = j + 1; r < 16; ++r) acc[r] -= acol[j][r >> 2][r & 3] * tj;
+        for (int j = 0; j < k; ++j) y[j] -= arow[k][j >> 2][j & 3] * yk;
     }
-    // 16-deep A-operand fragment of T_ii: element (r, c) -> lane (c/4, r), slot c%4
-    char *td = der + kDerTd + g * 512 + ((c >> 2) << 7) + 2 * (c & 3);
+    // 16-deep A-operand fragment of T_ii: lane 16 kg + row holds columns 4 kg .. 4 kg + 3
+    char *td = der + kDerTd + g * 512 + c * 8;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) *reinterpret_cast<__bf16 *>(td + 8 * r) = (__bf16)acc[r];
+    for (int kg = 0; kg < 4; ++kg) {
+        const floatx4 y4 = {y[4 * kg], y[4 * kg + 1], y[4 * kg + 2], y[4 * kg + 3]};
+        *reinterpret_cast<uint2 *>(td + kg * 128) = pack4(y4);
+    }
 }
 
 // Decay factors of off-diagonal tiles are split at each 16-row tile: for rows in tile i and
@@ -381,11 +400,13 @@ __device__ __forceinline__ void tile_refs(float b2, float &s0, float &s16, float
     e47 = lane_value(b2, 47);
 }
 
-// ------------------------------------------------------------------ wave 2: P prep
-__device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, bool pre, const RowFragOffsets &ro) {
+// ------------------------------------------------------------------ P prep (row tiles I0 .. I1-1)
+template <int I0, int I1>
+__device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, bool pre, const RowFragOffsets &ro,
+                                       int goff) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     const Gates gt = read_gates(raw);
-    float *gw = reinterpret_cast<float *>(smem + kOffG2);
+    float *gw = reinterpret_cast<float *>(smem + goff);
     float s0, s16, s32, s48, e15, e31, e47;
     tile_refs(gt.b2, s0, s16, s32, s48, e15, e31, e47);
     {
@@ -400,25 +421,41 @@ __device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, b
     }
     // read-side log decay of the row and log decay of the column, for the diagonal tiles
     const float bread = pre ? gt.b2 - gt.la2 : gt.b2;
-    uint4 kf[4][4], qf[4][4];
+    uint4 kf[I1][4], qf[I1][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < I1; ++i) {
             kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
-            qf[i][ks] = row_frag(raw + kRawQ, ro, i, ks);
+            if (i >= I0) qf[i][ks] = row_frag(raw + kRawQ, ro, i, ks);
         }
     wave_lds_sync();
     char *pf = der + kDerP;
+    // tiles (i, j), j <= i, in row order
+    constexpr int NT = (I1 * (I1 + 1) - I0 * (I0 + 1)) / 2;
+    int ti[NT], tj[NT];
+    {
+        int n = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = I0; i < I1; ++i)
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+                ti[n] = i;
+                tj[n] = j;
+                ++n;
+            }
+    }
+    floatx4 gqk[NT];
+    grams<NT>(gqk, kf, qf, tj, ti);
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
         // row 16i + c of this lane: its read decay, from lane 16i + c
         const float br = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * i + c), __builtin_bit_cast(int, bread)));
         const float rowf = gw[16 * i + c];
 #pragma unroll
         for (int j = 0; j <= i; ++j) {
             // transposed tile: lane holds row 16i + c, columns 16j + 4g + r
-            const floatx4 gq = gram_u4(kf[j], qf[i]);
+            const floatx4 gq = gqk[(i * (i + 1) - I0 * (I0 + 1)) / 2 + j];
             floatx4 pv;
             if (j < i) {
                 const floatx4 cf = *reinterpret_cast<const floatx4 *>(gw + 64 * i + 16 * j + 4 * g);
@@ -441,7 +478,7 @@ __device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, b
     }
 }
 
-// ------------------------------------------------------------------ wave 3: A prep
+// ------------------------------------------------------------------ A prep
 __device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     const Gates gt = read_gates(raw);
@@ -463,13 +500,15 @@ __device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, c
         for (int i = 0; i < 4; ++i) kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
     wave_lds_sync();
     char *na = der + kDerNA;
+    floatx4 gkk[6];
+    grams<6>(gkk, kf, kf, {0, 0, 1, 0, 1, 2}, {1, 2, 2, 3, 3, 3});
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
         const float ar = gw[16 * i + c];  // beta * row factor of row 16i + c
 #pragma unroll
         for (int j = 0; j < i; ++j) {
             // transposed tile: lane holds row 16i + c, columns 16j + 4g + r
-            const floatx4 gk = gram_u4(kf[j], kf[i]);
+            const floatx4 gk = gkk[(i * (i - 1)) / 2 + j];
             const floatx4 cf = *reinterpret_cast<const floatx4 *>(gw + 64 * i + 16 * j + 4 * g);
             const floatx4 av = (-ar) * cf * gk;
             int aoff;
@@ -482,36 +521,42 @@ __device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, c
     }
 }
 
-// Write-back of one chunk's output from its staging tile: transpose read r covers rows
-// 16(r/2) .. +15 and columns 16(r%2) .. +15; lane (g, i) gets row 16(r/2) + i, columns
-// 16(r%2) + 4g .. +3 and stores them as 8 bytes.
+// Write-back of one chunk's output from its staging tile. Transpose reads 2r and 2r+1 cover
+// rows 16r .. 16r+15; in 16-lane group g, lane i addresses column 8g + 4h + i/4 (h = read
+// parity) and rows 16r + 4(i%4) .. +3, so that lane i receives row 16r + i, columns 8g + 4h
+// .. +3: the two reads give it 16 contiguous bytes of the output row.
 __device__ __forceinline__ void write_back(const char *stg, __bf16 *obase, const ChunkRows &cr, int64_t dv,
                                            bool acc_out) {
     const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
-    bf16x4 val[8];
+    bf16x8 val[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int col = 16 * (r & 1) + 4 * g + (j >> 2);
-        val[r] = tr16(stg + stage_off(col, 4 * (r >> 1) + (j & 3)));
+    for (int r = 0; r < 4; ++r) {
+        const bf16x4 lo = tr16(stg + stage_off(8 * g + (j >> 2), 4 * r + (j & 3)));
+        const bf16x4 hi = tr16(stg + stage_off(8 * g + 4 + (j >> 2), 4 * r + (j & 3)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            val[r][e] = lo[e];
+            val[r][4 + e] = hi[e];
+        }
     }
     wave_lds_sync();
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int row = 16 * (r >> 1) + j;
+    for (int r = 0; r < 4; ++r) {
+        const int row = 16 * r + j;
         if (row <= cr.rmax) {
-            bf16x4 *dst = reinterpret_cast<bf16x4 *>(obase + (int64_t)cr.off(row) * dv + 16 * (r & 1) + 4 * g);
-            bf16x4 v = val[r];
+            bf16x8 *dst = reinterpret_cast<bf16x8 *>(obase + (int64_t)cr.off(row) * dv + 8 * g);
+            bf16x8 v = val[r];
             if (acc_out) {
-                const bf16x4 prev = *dst;
+                const bf16x8 prev = *dst;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (__bf16)((float)v[e] + (float)prev[e]);
+                for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] + (float)prev[e]);
             }
             *dst = v;
         }
     }
 }
 
-__global__ __launch_bounds__(256) void chunk_fwd_fast_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -543,14 +588,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_fast_kernel(ChunkArgs a) {
     const float *bb = a.beta + (row * a.Hv + head) * a.T;
     __bf16 *ob = reinterpret_cast<__bf16 *>(a.out) + (row * a.Hv + head) * a.T * a.dv;
 
-    // The two roles run separate loops with the same barrier sequence (two barriers in
-    // the prologue, one per chunk), so each role's registers are live only in its own loop.
-    if (wave >= 1) {
+    // The roles run separate loops with the same barrier sequence (two barriers in the
+    // prologue, one per chunk), so each role's registers are live only in its own loop.
+    if (wave >= 2) {
         if (nchunks == 0) return;
         RowFragOffsets ro;
         ro.init();
         // the upper 16x16 tiles inside P fragments 0 and 3 are never written: zero them
-        if (wave == 2) {
+        if (wave == kWaveP012) {
             for (int d = 0; d < 2; ++d) {
                 char *pf = smem + kOffDer + d * kDerBytes + kDerP;
                 *reinterpret_cast<uint2 *>(pf + lane * 16 + 8) = make_uint2(0, 0);
@@ -560,21 +605,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_fast_kernel(ChunkArgs a) {
         // one loop per role, so that each keeps only its own loop-invariant registers
         auto run = [&](auto role) {
             constexpr int R = decltype(role)::value;
-            u32x4 rsrc0, rsrc1;
-            if constexpr (R == 1) {
+            constexpr bool kCopies = R == kWaveCopyK || R == kWaveCopyQ;
+            u32x4 rsrc0, rsrc1, rsrc2, rsrc3;
+            if constexpr (R == kWaveCopyK) {
                 rsrc0 = slab_rsrc(kb, a.T * kDK * 2);
-                rsrc1 = rsrc0;
-            } else if constexpr (R == 2) {
+            } else if constexpr (R == kWaveCopyQ) {
                 rsrc0 = slab_rsrc(qb, a.T * kDK * 2);
-                rsrc1 = rsrc0;
-            } else {
-                rsrc0 = slab_rsrc(vb + dcol0, a.T * a.dv * 2 - dcol0 * 2);
-                rsrc1 = slab_rsrc(ab, (t0 + len) * 4);
+                rsrc1 = slab_rsrc(vb + dcol0, a.T * a.dv * 2 - dcol0 * 2);
+                rsrc2 = slab_rsrc(ab, (t0 + len) * 4);
+                rsrc3 = slab_rsrc(bb, (t0 + len) * 4);
             }
-            const u32x4 rbeta = slab_rsrc(bb, (t0 + len) * 4);
             // lane offsets of a full chunk (rmax = 63) and of the last chunk
             CopyOffsets cfull, clast;
-            {
+            if constexpr (kCopies) {
                 ChunkRows full;
                 full.lo = 0;
                 full.rmax = kC - 1;
@@ -582,25 +625,25 @@ __global__ __launch_bounds__(256) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 cfull.init(full, a.dv);
                 clast.init(chunk_rows(t0, len, fwd, nchunks - 1), a.dv);
             }
-            auto copy = [&](char *rawn, const CopyOffsets &co, int64_t lo) {
-                if constexpr (R == 1) copy_kq(rawn + kRawK, rsrc0, co, lo);
-                else if constexpr (R == 2) copy_kq(rawn + kRawQ, rsrc0, co, lo);
-                else {
-                    copy_v(rawn + kRawV, rsrc0, co, lo, a.dv);
-                    copy_gates(rawn, rsrc1, rbeta, co, lo);
-                }
-            };
             // two explicit paths, so that each copy addresses with one of the fixed sets
             auto issue = [&](int64_t ch, const CopyOffsets &co) {
                 char *rawn = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
-                copy(rawn, co, chunk_rows(t0, len, fwd, ch).lo);
+                const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
+                if constexpr (R == kWaveCopyK) {
+                    copy_kq(rawn + kRawK, rsrc0, co, lo);
+                } else if constexpr (R == kWaveCopyQ) {
+                    copy_kq(rawn + kRawQ, rsrc0, co, lo);
+                    copy_v(rawn + kRawV, rsrc1, co, lo, a.dv);
+                    copy_gates(rawn, rsrc2, rsrc3, co, lo);
+                }
             };
             auto prep = [&](int64_t ch) {
                 const char *rawp = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 char *derp = smem + kOffDer + (int)(ch & 1) * kDerBytes;
-                if constexpr (R == 1) prep_diag(smem, rawp, derp, pre, ro);
-                else if constexpr (R == 2) prep_p(smem, rawp, derp, pre, ro);
-                else prep_a(smem, rawp, derp, ro);
+                if constexpr (R == kWaveDiag) prep_diag(smem, rawp, derp, pre, ro);
+                else if constexpr (R == kWaveA) prep_a(smem, rawp, derp, ro);
+                else if constexpr (R == kWaveP012) prep_p<0, 3>(smem, rawp, derp, pre, ro, kOffG2);
+                else if constexpr (R == kWaveP3) prep_p<3, 4>(smem, rawp, derp, pre, ro, kOffG4);
             };
             auto store = [&](int64_t ch) {
                 const ChunkRows cr = chunk_rows(t0, len, fwd, ch);
@@ -608,19 +651,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_fast_kernel(ChunkArgs a) {
                            acc_out);
             };
             auto step = [&](int64_t ch) {
-                if constexpr (R == 3) {
+                if constexpr (R == kWaveCopyK) {
                     if (ch >= 1) store(ch - 1);
                 }
                 if (ch + 1 < nchunks) prep(ch + 1);
                 wait_vmem();
                 lds_barrier();
             };
-            if (nchunks == 1) issue(0, clast);
-            else issue(0, cfull);
+            if constexpr (kCopies) {
+                if (nchunks == 1) issue(0, clast);
+                else issue(0, cfull);
+            }
             wait_vmem();
             lds_barrier();
-            if (nchunks == 2) issue(1, clast);
-            else if (nchunks > 2) issue(1, cfull);
+            if constexpr (kCopies) {
+                if (nchunks == 2) issue(1, clast);
+                else if (nchunks > 2) issue(1, cfull);
+            }
             prep(0);
             wait_vmem();
             lds_barrier();
@@ -628,214 +675,210 @@ __global__ __launch_bounds__(256) void chunk_fwd_fast_kernel(ChunkArgs a) {
             // separate code, so that no copy's offset register is chosen at run time.
             int64_t ch = 0;
             for (; ch + 3 < nchunks; ++ch) {
-                issue(ch + 2, cfull);
+                if constexpr (kCopies) issue(ch + 2, cfull);
                 step(ch);
             }
             for (; ch < nchunks; ++ch) {
-                if (ch + 2 < nchunks) issue(ch + 2, clast);
+                if constexpr (kCopies) {
+                    if (ch + 2 < nchunks) issue(ch + 2, clast);
+                }
                 step(ch);
             }
-            if constexpr (R == 3) store(nchunks - 1);
+            if constexpr (R == kWaveCopyK) store(nchunks - 1);
         };
-        if (wave == 1) run(std::integral_constant<int, 1>{});
-        else if (wave == 2) run(std::integral_constant<int, 2>{});
-        else run(std::integral_constant<int, 3>{});
+        if (wave == kWaveDiag) run(std::integral_constant<int, kWaveDiag>{});
+        else if (wave == kWaveA) run(std::integral_constant<int, kWaveA>{});
+        else if (wave == kWaveP012) run(std::integral_constant<int, kWaveP012>{});
+        else if (wave == kWaveP3) run(std::integral_constant<int, kWaveP3>{});
+        else if (wave == kWaveCopyK) run(std::integral_constant<int, kWaveCopyK>{});
+        else run(std::integral_constant<int, kWaveCopyQ>{});
         return;
     }
 
-    // chain wave: stored state rows 16t + 4g + r (true row 32(t/2) + 8g + 4(t%2) + r) of
-    // the two 16-column tiles ct, column dcol0 + 16 ct + c
-    floatx4 H[2][8];
+    // chain wave ct: stored state rows 16t + 4g + r (true row 32(t/2) + 8g + 4(t%2) + r) of
+    // the 16-column tile ct, column dcol0 + 16 ct + c
+    const int ct = wave;
+    const int col = dcol0 + 16 * ct + c;
+    floatx4 H[8];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) H[ct][t] = zero4();
+    for (int t = 0; t < 8; ++t) H[t] = zero4();
     if (a.h0) {
-        const float *hb = a.h0 + (seq * a.Hv + head) * kDK * a.dv + dcol0 + c;
+        const float *hb = a.h0 + (seq * a.Hv + head) * kDK * a.dv + col;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) H[ct][t][r] = hb[(32 * (t >> 1) + 8 * g + 4 * (t & 1) + r) * a.dv + 16 * ct];
+            for (int r = 0; r < 4; ++r) H[t][r] = hb[(32 * (t >> 1) + 8 * g + 4 * (t & 1) + r) * a.dv];
     }
     RowFragOffsets ro;
     ro.init();
     KtOffsets ko;
     ko.init();
-    const int voff0 = v_lane_offset(0), voff1 = v_lane_offset(1);
+    const int voff = v_lane_offset(ct);
     const int scoff = 16 * g;  // bytes: rows 4g..4g+3 of a 16-row tile
     if (nchunks > 0) {
         lds_barrier();
         lds_barrier();
     }
 
-    // Each phase issues the LDS reads of the next one before its own arithmetic, and
-    // scheduling fences keep the compiler from sinking them back to their uses.
+    // Per chunk: X_K = K H, then R, then the block substitution for U (a chain of dependent
+    // small products) with the independent X_Q = Q H products interleaved into its gaps,
+    // then the state update with the output products interleaved. Operands of a step are
+    // read from LDS one step ahead, and scheduling fences keep that order.
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const char *raw = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
         const char *der = smem + kOffDer + (int)(ch & 1) * kDerBytes;
         const char *sc = der + kDerSc + scoff;
         const char *na = der + kDerNA;
         const char *td = der + kDerTd;
-        // X_K = K H, X_Q = Q H for both column tiles; each operand fragment feeds two products
-        floatx4 XK[2][4], XQ[2][4];
+        // ---- X_K = K H
+        floatx4 XK[4];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int mi = 0; mi < 4; ++mi) XK[mi] = zero4();
+        uint4 fk[2][4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                XK[ct][mi] = zero4();
-                XQ[ct][mi] = zero4();
-            }
-        uint4 fk[2][4], fq[2][4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            fk[0][mi] = row_frag(raw + kRawK, ro, mi, 0);
-            fq[0][mi] = row_frag(raw + kRawQ, ro, mi, 0);
-        }
-        bf16x4 vv[2][4];
+        for (int mi = 0; mi < 4; ++mi) fk[0][mi] = row_frag(raw + kRawK, ro, mi, 0);
+        Frag<__bf16> hf[4];
+        bf16x4 vv[4];
+        floatx4 be[4], eb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (ks < 3) {
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    fk[(ks + 1) & 1][mi] = row_frag(raw + kRawK, ro, mi, ks + 1);
-                    fq[(ks + 1) & 1][mi] = row_frag(raw + kRawQ, ro, mi, ks + 1);
-                }
+                for (int mi = 0; mi < 4; ++mi) fk[(ks + 1) & 1][mi] = row_frag(raw + kRawK, ro, mi, ks + 1);
             } else {
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
-                    vv[0][mi] = tr16(raw + kRawV + voff0 + 1024 * mi);
-                    vv[1][mi] = tr16(raw + kRawV + voff1 + 1024 * mi);
+                    vv[mi] = tr16(raw + kRawV + voff + 1024 * mi);
+                    be[mi] = *reinterpret_cast<const floatx4 *>(sc + 64 * mi);
+                    eb[mi] = *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * mi);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            const Frag<__bf16> h0f = frag_from_acc<__bf16>(H[0][2 * ks], H[0][2 * ks + 1]);
-            const Frag<__bf16> h1f = frag_from_acc<__bf16>(H[1][2 * ks], H[1][2 * ks + 1]);
+            hf[ks] = frag_from_acc<__bf16>(H[2 * ks], H[2 * ks + 1]);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const Frag<__bf16> kf = u4_frag(fk[ks & 1][mi]);
-                const Frag<__bf16> qf = u4_frag(fq[ks & 1][mi]);
-                XK[0][mi] = mma32(XK[0][mi], kf, h0f);
-                XK[1][mi] = mma32(XK[1][mi], kf, h1f);
-                XQ[0][mi] = mma32(XQ[0][mi], qf, h0f);
-                XQ[1][mi] = mma32(XQ[1][mi], qf, h1f);
-            }
+            for (int mi = 0; mi < 4; ++mi) XK[mi] = mma32(XK[mi], u4_frag(fk[ks & 1][mi]), hf[ks]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // R = beta (V - e^{b} X_K); the substitution's operands are read meanwhile
-        floatx4 be[4], eb[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            be[mi] = *reinterpret_cast<const floatx4 *>(sc + 64 * mi);
-            eb[mi] = *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * mi);
-        }
+        // ---- R = beta (V - e^{b} X_K); operands of the substitution and the first Q slice
         const bf16x4 t0f = der_frag_lo(td, 0), t1f = der_frag_lo(td, 1), t2f = der_frag_lo(td, 2), t3f = der_frag_lo(td, 3);
         const bf16x4 a10 = der_frag_lo(na, 0), a32 = der_frag_lo(na + 2560, 0);
         const Frag<__bf16> a2x = der_frag(na + 512, 0), a3x = der_frag(na + 1536, 0);
+        uint4 fq[2][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) fq[0][mi] = row_frag(raw + kRawQ, ro, mi, 0);
         __builtin_amdgcn_sched_barrier(0);
-        floatx4 U[2][4];
+        floatx4 U[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                U[0][mi][r] = be[mi][r] * ((float)vv[0][mi][r] - eb[mi][r] * XK[0][mi][r]);
-                U[1][mi][r] = be[mi][r] * ((float)vv[1][mi][r] - eb[mi][r] * XK[1][mi][r]);
-            }
-        // U_i = T_ii (R_i - sum_{j<i} A_ij U_j), both column tiles interleaved; the output
-        // operands are read meanwhile
-        const Frag<__bf16> p0 = der_frag(der + kDerP, 0), p1 = der_frag(der + kDerP, 1);
-        const Frag<__bf16> p20 = der_frag(der + kDerP, 2), p21 = der_frag(der + kDerP, 3);
-        const Frag<__bf16> p30 = der_frag(der + kDerP, 4), p31 = der_frag(der + kDerP, 5);
-        floatx4 er[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) er[mi] = *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * mi);
+            for (int r = 0; r < 4; ++r) U[mi][r] = be[mi][r] * ((float)vv[mi][r] - eb[mi][r] * XK[mi][r]);
         __builtin_amdgcn_sched_barrier(0);
+        // ---- U_i = T_ii (R_i - sum_{j<i} A_ij U_j) with X_Q = Q H interleaved: the sixteen
+        // X_Q products (slice ks, row tile mi) fill the latency of each level
+        floatx4 XQ[4];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[ct][0] = mma16(zero4(), t0f, cvt4<__bf16>(U[ct][0]));
+        for (int mi = 0; mi < 4; ++mi) XQ[mi] = zero4();
+        floatx4 er[4], ec[4];
+        Frag<__bf16> kt[3][2];
+        auto xq_items = [&](int first, int last) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[ct][1] = mma16(U[ct][1], a10, cvt4<__bf16>(U[ct][0]));
+            for (int it = first; it < last; ++it) {
+                const int ks = it >> 2, mi = it & 3;
+                if (mi == 0) {
+                    if (ks < 3) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[ct][1] = mma16(zero4(), t1f, cvt4<__bf16>(U[ct][1]));
+                        for (int m = 0; m < 4; ++m) fq[(ks + 1) & 1][m] = row_frag(raw + kRawQ, ro, m, ks + 1);
+                    } else {
+                        // operands of the state update and the output
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const Frag<__bf16> u01 = frag_from_acc<__bf16>(U[ct][0], U[ct][1]);
-            U[ct][2] = mma32(U[ct][2], a2x, u01);
-            U[ct][3] = mma32(U[ct][3], a3x, u01);
-        }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[ct][2] = mma16(zero4(), t2f, cvt4<__bf16>(U[ct][2]));
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[ct][3] = mma16(U[ct][3], a32, cvt4<__bf16>(U[ct][2]));
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[ct][3] = mma16(zero4(), t3f, cvt4<__bf16>(U[ct][3]));
-        // O = e^{b | b'} X_Q + P U into the staging tile; the state-update operands are read
-        // meanwhile
-        floatx4 ec[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) ec[mi] = *reinterpret_cast<const floatx4 *>(sc + 768 + 64 * mi);
-        const float gC = *reinterpret_cast<const float *>(der + kDerSc + 1024);
-        Frag<__bf16> kt[2][2];
-        kt[0][0] = kt_frag(raw + kRawK, ko, 0, 0);
-        kt[0][1] = kt_frag(raw + kRawK, ko, 0, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            char *stg = smem + kOffStage + (int)(ch & 1) * kStageBytes;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const Frag<__bf16> u01 = frag_from_acc<__bf16>(U[ct][0], U[ct][1]);
-                const Frag<__bf16> u23 = frag_from_acc<__bf16>(U[ct][2], U[ct][3]);
-                floatx4 O[4];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) O[mi] = er[mi] * XQ[ct][mi];
-                O[0] = mma32(O[0], p0, u01);
-                O[1] = mma32(O[1], p1, u01);
-                O[2] = mma32(O[2], p20, u01);
-                O[2] = mma32(O[2], p21, u23);
-                O[3] = mma32(O[3], p30, u01);
-                O[3] = mma32(O[3], p31, u23);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    *reinterpret_cast<uint2 *>(stg + stage_off(16 * ct + c, 4 * mi + g)) = pack4(O[mi]);
-            }
-        }
-        // H <- e^{b_C} H + K^T diag(e^{b_C - b}) U
-        {
-            floatx4 W[2][4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                W[0][mi] = ec[mi] * U[0][mi];
-                W[1][mi] = ec[mi] * U[1][mi];
-            }
-            const Frag<__bf16> w001 = frag_from_acc<__bf16>(W[0][0], W[0][1]), w023 = frag_from_acc<__bf16>(W[0][2], W[0][3]);
-            const Frag<__bf16> w101 = frag_from_acc<__bf16>(W[1][0], W[1][1]), w123 = frag_from_acc<__bf16>(W[1][2], W[1][3]);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (t < 7) {
-                    kt[(t + 1) & 1][0] = kt_frag(raw + kRawK, ko, t + 1, 0);
-                    kt[(t + 1) & 1][1] = kt_frag(raw + kRawK, ko, t + 1, 1);
+                        for (int m = 0; m < 4; ++m) {
+                            er[m] = *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * m);
+                            ec[m] = *reinterpret_cast<const floatx4 *>(sc + 768 + 64 * m);
+                        }
+                        kt[0][0] = kt_frag(raw + kRawK, ko, 0, 0);
+                        kt[0][1] = kt_frag(raw + kRawK, ko, 0, 1);
+                        kt[1][0] = kt_frag(raw + kRawK, ko, 1, 0);
+                        kt[1][1] = kt_frag(raw + kRawK, ko, 1, 1);
+                    }
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                H[0][t] = H[0][t] * gC;
-                H[1][t] = H[1][t] * gC;
-                H[0][t] = mma32(H[0][t], kt[t & 1][0], w001);
-                H[1][t] = mma32(H[1][t], kt[t & 1][0], w101);
-                H[0][t] = mma32(H[0][t], kt[t & 1][1], w023);
-                H[1][t] = mma32(H[1][t], kt[t & 1][1], w123);
-                __builtin_amdgcn_sched_barrier(0);
+                XQ[mi] = mma32(XQ[mi], u4_frag(fq[ks & 1][mi]), hf[ks]);
             }
+        };
+        U[0] = mma16(zero4(), t0f, cvt4<__bf16>(U[0]));
+        xq_items(0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        U[1] = mma16(U[1], a10, cvt4<__bf16>(U[0]));
+        xq_items(2, 4);
+        __builtin_amdgcn_sched_barrier(0);
+        U[1] = mma16(zero4(), t1f, cvt4<__bf16>(U[1]));
+        xq_items(4, 6);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const Frag<__bf16> u01 = frag_from_acc<__bf16>(U[0], U[1]);
+            U[2] = mma32(U[2], a2x, u01);
+            U[3] = mma32(U[3], a3x, u01);
+        }
+        xq_items(6, 9);
+        __builtin_amdgcn_sched_barrier(0);
+        U[2] = mma16(zero4(), t2f, cvt4<__bf16>(U[2]));
+        xq_items(9, 11);
+        __builtin_amdgcn_sched_barrier(0);
+        U[3] = mma16(U[3], a32, cvt4<__bf16>(U[2]));
+        xq_items(11, 13);
+        __builtin_amdgcn_sched_barrier(0);
+        U[3] = mma16(zero4(), t3f, cvt4<__bf16>(U[3]));
+        xq_items(13, 16);
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- H <- e^{b_C} H + K^T diag(e^{b_C - b}) U, with O = e^{b | b'} X_Q + P U
+        // interleaved (output row tile t/2 after state tile t, for odd t)
+        const float gC = *reinterpret_cast<const float *>(der + kDerSc + 1024);
+        Frag<__bf16> p[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) p[f] = der_frag(der + kDerP, f);
+        Frag<__bf16> w01, w23, u01, u23;
+        {
+            floatx4 W[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) W[mi] = ec[mi] * U[mi];
+            w01 = frag_from_acc<__bf16>(W[0], W[1]);
+            w23 = frag_from_acc<__bf16>(W[2], W[3]);
+            u01 = frag_from_acc<__bf16>(U[0], U[1]);
+            u23 = frag_from_acc<__bf16>(U[2], U[3]);
+        }
+        char *stg = smem + kOffStage + (int)(ch & 1) * kStageBytes;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t < 6) {
+                kt[(t + 2) % 3][0] = kt_frag(raw + kRawK, ko, t + 2, 0);
+                kt[(t + 2) % 3][1] = kt_frag(raw + kRawK, ko, t + 2, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            H[t] = H[t] * gC;
+            H[t] = mma32(H[t], kt[t % 3][0], w01);
+            H[t] = mma32(H[t], kt[t % 3][1], w23);
+            if (t & 1) {
+                const int mi = t >> 1;
+                floatx4 O = er[mi] * XQ[mi];
+                if (mi < 2) {
+                    O = mma32(O, p[mi], u01);
+                } else {
+                    O = mma32(O, p[2 * mi - 2], u01);
+                    O = mma32(O, p[2 * mi - 1], u23);
+                }
+                *reinterpret_cast<uint2 *>(stg + stage_off(16 * ct + c, 4 * mi + g)) = pack4(O);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
     }
 
     if (a.hT) {
-        float *hb = a.hT + (seq * a.Hv + head) * kDK * a.dv + dcol0 + c;
+        float *hb = a.hT + (seq * a.Hv + head) * kDK * a.dv + col;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) hb[(32 * (t >> 1) + 8 * g + 4 * (t & 1) + r) * a.dv + 16 * ct] = H[ct][t][r];
+            for (int r = 0; r < 4; ++r) hb[(32 * (t >> 1) + 8 * g + 4 * (t & 1) + r) * a.dv] = H[t][r];
     }
 }
 
@@ -854,7 +897,7 @@ hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream) {
         configured = true;
     }
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
-    hipLaunchKernelGGL(chunk_fwd_fast_kernel, dim3((unsigned)blocks), dim3(256), kSmemBytes, stream, a);
+    hipLaunchKernelGGL(chunk_fwd_fast_kernel, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
     return hipGetLastError();
 }
 
