@@ -46,22 +46,67 @@ def chunk_flops(B, H, T, dk, dv, C=64):
     return B * H * T * per
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(summary, source, key):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and WRITE_SIZE runs,
+    scaled by a copy of known size), or None when the summary is missing or was taken on a
+    different kernel source."""
+    try:
+        with open(os.path.join(PROFILES, summary)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    try:
+        if fields["kernel source sha256"] != source_digest(os.path.join(CSRC, source)):
+            return None
+        return float(fields[key])
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+def copy_calibration(mib=1024, reps=3):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: each launch reads and writes `mib` MiB."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": mib * (1 << 20), "launches": reps}), flush=True)
+
+
 def timed(fn, steps, warmup, stream):
+    """Mean time per call in ms: HIP events on the launch stream around `steps` back-to-back
+    calls (after `warmup` untimed ones), bracketed by device synchronisation."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         fn()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return sum(per) / len(per), wall
+    return start.elapsed_time(end) / steps, wall
 
 
 def bench_chunk(binding, inputs, steps, warmup):
@@ -94,22 +139,18 @@ def bench_decode(binding, inputs, reps):
     for s in range(steps):
         binding.decode_step(q[s], k[s], v[s], la[s], b[s], state, state_out=state, out=out[s])
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps * reps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
     for r in range(reps):
         for s in range(steps):
-            e0, e1 = ev[r * steps + s]
-            e0.record(stream)
             binding.decode_step(q[s], k[s], v[s], la[s], b[s], state, state_out=state, out=out[s])
-            e1.record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(c) for a, c in ev)
-    mean = sum(per) / len(per)
+    mean = start.elapsed_time(end) / (steps * reps)
     N, Hv, dk, dv = dc.state.shape
     sbytes = 2 * N * Hv * dk * dv * 4
     io = (dc.q[0].numel() * 2 + dc.v[0].numel()) * 2 + N * Hv * 2 * 4 + N * Hv * dv * 2
-    return dict(ms=mean, median=per[len(per) // 2], state_bytes=sbytes, io_bytes=io,
-                tokens=N, steps=steps * reps)
+    return dict(ms=mean, state_bytes=sbytes, io_bytes=io, tokens=N, steps=steps * reps)
 
 
 def bench_varlen(binding, inputs, steps):
@@ -146,18 +187,24 @@ def bench_bidir(binding, inputs, steps):
     return dict(ms=ms, tokens=case.q.shape[2])
 
 
-def cpu_baseline(inputs):
-    """The fp64 oracle, as it is, on this host: the whole B4 H16 T4096 d128 workload."""
+def cpu_baseline(inputs, min_wall=1.5, max_reps=20):
+    """The fp64 oracle, as it is, on this host's cores: the whole B4 H16 T4096 d128 workload,
+    repeated until at least `min_wall` seconds have passed (a bounded sample)."""
     import oracle
     case = inputs.workload1()
     threads = min(len(os.sched_getaffinity(0)), 64)
     import numpy as np
     args = [np.ascontiguousarray(t.double().numpy()) for t in
             (case.q, case.k, case.v, case.log_alpha, case.beta, case.h0)]
+    reps = 0
     t0 = time.perf_counter()
-    oracle.scan(*args, threads=threads)
-    dt = time.perf_counter() - t0
-    tokens = case.q.shape[0] * case.q.shape[2]
+    while True:
+        oracle.scan(*args, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_wall or reps >= max_reps:
+            break
+    tokens = case.q.shape[0] * case.q.shape[2] * reps
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -168,8 +215,9 @@ def cpu_baseline(inputs):
     except OSError:
         pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "whole B4 H16 T4096 d128 workload (64 sequence-heads), fp64 per-token "
-                      "recurrence, %.1f s wall; CPU: %s" % (dt, cpu_model)}
+            "sample": "the whole B4 H16 T4096 d128 workload (64 sequence-heads) %d times, fp64 "
+                      "per-token recurrence, %.1f s wall on %d threads; CPU: %s"
+                      % (reps, dt, threads, cpu_model)}
 
 
 def main():
@@ -179,12 +227,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every workload here runs on a single MI355X "
               "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from gated_delta_rule_70_amd import binding, inputs
     binding.lib()
@@ -204,8 +257,10 @@ def main():
     gbs = c["bytes"] / (c["ms"] / 1e3) / 1e9
     tflops = c["flops"] / (c["ms"] / 1e3) / 1e12
     res["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                       "kernel": "chunk_fwd_kernel<bf16, 64, 128>", "bytes_per_launch": c["bytes"],
+                       "frac": gbs / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("chunk_fwd_fast_B4_H16_T4096_d128_hbm_traffic.md",
+                                                   "chunk_fwd_fast.hip", "HBM bytes per launch"),
+                       "kernel": "chunk_fwd_fast_kernel", "bytes_per_launch": c["bytes"],
                        "mfma": {"achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                 "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": c["flops"]}}
     if args.only in ("all", "decode"):
@@ -213,13 +268,15 @@ def main():
         d = bench_decode(binding, inputs, reps=2)
         sgbs = d["state_bytes"] / (d["ms"] / 1e3) / 1e9
         res["decode"] = {"metric": "decode-step state GB/s", "value": sgbs, "unit": "GB/s",
-                         "us_per_step": d["ms"] * 1e3, "median_us": d["median"] * 1e3,
+                         "us_per_step": d["ms"] * 1e3,
                          "tokens_per_s": d["tokens"] / (d["ms"] / 1e3),
                          "workload": inputs.WORKLOADS[3],
                          "roofline": {"bound": "hbm", "achieved": (d["state_bytes"] + d["io_bytes"]) / (d["ms"] / 1e3) / 1e9,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": (d["state_bytes"] + d["io_bytes"]) / (d["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                      "kernel": "decode_kernel<bf16, 128, 128>"}}
+                                      "kernel": "decode_kernel<bf16, 128, 128>",
+                                      "traffic": measured_traffic("decode_N256_Hv32_d128_hbm_traffic.md",
+                                                                  "decode.hip", "HBM bytes per step")}}
     if args.only == "all":
         print("[bench] packed variable-length and bidirectional workloads ...", file=sys.stderr, flush=True)
         vl = bench_varlen(binding, inputs, max(3, args.steps // 4))
