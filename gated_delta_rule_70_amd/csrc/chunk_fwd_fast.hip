@@ -72,7 +72,10 @@ constexpr int kDerBytes = 12320;
 constexpr int kOffRaw = 0;
 constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
 constexpr int kOffAd = kOffDer + 2 * kDerBytes;   // diagonal prep: A_ii blocks fp32 [4][16][16]
-constexpr int kOffG1 = kOffAd + 4096;             // diagonal prep: b2, beta [64]
+// Block stride of A_ii: one row (64 B) plus 16 B, so that the four blocks, which the four
+// lane groups read at the same time, start in different banks.
+constexpr int kAdBlock = 16 * 16 + 4;             // floats
+constexpr int kOffG1 = kOffAd + 4 * kAdBlock * 4; // diagonal prep: b2, beta [64]
 constexpr int kOffG2 = kOffG1 + 512;              // P prep, row tiles 0-2: row factors [64], column factors [3][64]
 constexpr int kOffG3 = kOffG2 + 1024;             // A prep: beta * row factors [64], column factors [3][64]
 constexpr int kOffG4 = kOffG3 + 1024;             // P prep, row tile 3: as G2
@@ -341,7 +344,7 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
-    wave_lds_sync();
+    __builtin_amdgcn_sched_barrier(0);
     float *adt = reinterpret_cast<float *>(smem + kOffAd);
     floatx4 gkk[4];
     grams<4>(gkk, kf, kf, {0, 1, 2, 3}, {0, 1, 2, 3});
@@ -353,14 +356,15 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
         const float brow = gb[16 * i + c], betarow = gb[64 + 16 * i + c];
         floatx4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) av[r] = (4 * g + r < c) ? betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
-        *reinterpret_cast<floatx4 *>(adt + (i * 16 + c) * 16 + 4 * g) = av;  // row-major A_ii
+        for (int r = 0; r < 4; ++r) av[r] = (4 * g + r < c) ? -betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
+        *reinterpret_cast<floatx4 *>(adt + i * kAdBlock + c * 16 + 4 * g) = av;  // row-major -A_ii
     }
-    wave_lds_sync();
+    // LDS accesses of one wave complete in order: the row loads below see these stores
+    asm volatile("" ::: "memory");
     // T_ii = (I + A_ii)^{-1}: lane (i = g, c) computes row c, y (I + A_ii) = e_c, from the
     // last column down: once y_k is final, row k of A_ii is eliminated from the earlier y_j.
-    // The rows of A_ii are read into registers first (the same address in all 16 lanes).
-    const float *ablk = adt + g * 256;
+    // The rows of -A_ii are read into registers first (the same address in all 16 lanes).
+    const float *ablk = adt + g * kAdBlock;
     floatx4 arow[16][4];
 #pragma unroll
     for (int k = 1; k < 16; ++k)
@@ -374,7 +378,7 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
     for (int k = 15; k >= 1; --k) {
         const float yk = y[k];
 #pragma unroll
-        for (int j = 0; j < k; ++j) y[j] -= arow[k][j >> 2][j & 3] * yk;
+        for (int j = 0; j < k; ++j) y[j] += arow[k][j >> 2][j & 3] * yk;
     }
     // 16-deep A-operand fragment of T_ii: lane 16 kg + row holds columns 4 kg .. 4 kg + 3
     char *td = der + kDerTd + g * 512 + c * 8;
@@ -429,7 +433,7 @@ __device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, b
             kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
             if (i >= I0) qf[i][ks] = row_frag(raw + kRawQ, ro, i, ks);
         }
-    wave_lds_sync();
+    __builtin_amdgcn_sched_barrier(0);
     char *pf = der + kDerP;
     // tiles (i, j), j <= i, in row order
     constexpr int NT = (I1 * (I1 + 1) - I0 * (I0 + 1)) / 2;
@@ -498,7 +502,7 @@ __device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, c
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
-    wave_lds_sync();
+    __builtin_amdgcn_sched_barrier(0);
     char *na = der + kDerNA;
     floatx4 gkk[6];
     grams<6>(gkk, kf, kf, {0, 0, 1, 0, 1, 2}, {1, 2, 2, 3, 3, 3});

@@ -54,7 +54,14 @@ template <>
 __device__ __forceinline__ floatx4 cvt4<float>(floatx4 x) { return x; }
 template <>
 __device__ __forceinline__ bf16x4 cvt4<__bf16>(floatx4 x) {
-    return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    // two packed converts (round to nearest even), each materialised as one 32-bit word so
+    // that the compiler does not split them into single-element converts and permutes
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 lo = __builtin_convertvector((f2){x[0], x[1]}, b2);
+    const b2 hi = __builtin_convertvector((f2){x[2], x[3]}, b2);
+    const unsigned w[2] = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    return __builtin_bit_cast(bf16x4, w);
 }
 
 template <typename E, typename S>
