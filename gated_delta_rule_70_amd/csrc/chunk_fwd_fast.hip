@@ -19,9 +19,10 @@
 //   wave 2      diagonal prep for chunk c+1: gate scalars, diagonal tiles of K K^T and the
 //               four 16x16 inverses T_ii by substitution.
 //   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1.
-//   waves 6, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1.
-//   waves 4, 5  copies for chunk c+2 (K; Q, V and gates) and the write-back of the output
-//               of chunk c-1; they issue little and share the chain waves' SIMDs.
+//   waves 6, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1;
+//               wave 7 also writes back the output of chunk c-1 from its staging tile.
+//   waves 4, 5  copies for chunk c+2 (K; Q, V and gates); they issue little and share the
+//               chain waves' SIMDs.
 // Raw q/k/v of a chunk are copied once per workgroup, global -> LDS directly (16 bytes per
 // lane, no registers), into a ring of three buffers: while the chain reads chunk c and the
 // prep waves read chunk c+1, the loads for chunk c+2 are in flight. Rows are XOR-swizzled by
@@ -58,6 +59,7 @@ constexpr int kC = 64, kDK = 128, kDVT = 32;
 // copy wave, which issues little; the four prep waves take the other two SIMDs.
 constexpr int kThreads = 512;
 constexpr int kWaveCopyK = 4, kWaveCopyQ = 5, kWaveDiag = 2, kWaveP3 = 6, kWaveA = 3, kWaveP012 = 7;
+constexpr int kWaveStore = kWaveP012;  // the wave that writes the output back
 constexpr float kLog2e = 1.4426950408889634f;
 
 // raw buffer (one of three): K, Q [64 rows][256 B] and V [64 rows][64 B], swizzled; gates
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                            acc_out);
             };
             auto step = [&](int64_t ch) {
-                if constexpr (R == kWaveCopyK) {
+                if constexpr (R == kWaveStore) {
                     if (ch >= 1) store(ch - 1);
                 }
                 if (ch + 1 < nchunks) prep(ch + 1);
@@ -688,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 }
                 step(ch);
             }
-            if constexpr (R == kWaveCopyK) store(nchunks - 1);
+            if constexpr (R == kWaveStore) store(nchunks - 1);
         };
         if (wave == kWaveDiag) run(std::integral_constant<int, kWaveDiag>{});
         else if (wave == kWaveA) run(std::integral_constant<int, kWaveA>{});
