@@ -3,10 +3,11 @@
 // Same chunk algebra as chunk_fwd.hip (the WY/UT form of `chunked_delta` on the "Prizma
 // seq/delta.py" page, with H = S^T), organised for the matrix cores of gfx950:
 //
-//   A   = strict_lower(beta_i (k_i . k_j) e^{b_i - b_j})        T_ii = (I + A_ii)^{-1}
-//   R   = diag(beta) (V - diag(e^{b}) K H)
-//   U   by block forward substitution over the four 16-row blocks:
-//         U_i = T_ii (R_i - sum_{j<i} A_ij U_j)                 (U = (I + A)^{-1} R exactly)
+//   A   = diag(beta) Ah,  Ah = strict_lower((k_i . k_j) e^{b_i - b_j}),  T_ii = (I + A_ii)^{-1}
+//   R   = V - diag(e^{b}) K H
+//   U   by block forward substitution over the four 16-row blocks, with beta folded into the
+//       diagonal inverses (U = (I + A)^{-1} diag(beta) R exactly):
+//         U_i = (T_ii diag(beta_i)) (R_i - sum_{j<i} Ah_ij U_j)
 //   O   = diag(e^{b} | e^{b'}) Q H + P U,   P = [(q_i . k_j) e^{b_i - b_j}]_{j<=i} (post)
 //                                              [(q_i . k_j) e^{b'_i - b_j}]_{j<i}  (pre)
 //   H  <- e^{b_C} H + K^T diag(e^{b_C - b}) U
@@ -19,10 +20,9 @@
 //   wave 2      diagonal prep for chunk c+1: gate scalars, diagonal tiles of K K^T and the
 //               four 16x16 inverses T_ii by substitution.
 //   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1.
-//   waves 6, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1;
+//   waves 5, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1;
 //               wave 7 also writes back the output of chunk c-1 from its staging tile.
-//   waves 4, 5  copies for chunk c+2 (K; Q, V and gates); they issue little and share the
-//               chain waves' SIMDs.
+//   waves 4, 6  copies for chunk c+2 (K; Q, V and gates); they issue little.
 // Raw q/k/v of a chunk are copied once per workgroup, global -> LDS directly (16 bytes per
 // lane, no registers), into a ring of three buffers: while the chain reads chunk c and the
 // prep waves read chunk c+1, the loads for chunk c+2 are in flight. Rows are XOR-swizzled by
@@ -58,7 +58,7 @@ constexpr int kC = 64, kDK = 128, kDVT = 32;
 // Wave roles. Waves w and w + 4 share a SIMD: each chain wave (0, 1) shares its SIMD with a
 // copy wave, which issues little; the four prep waves take the other two SIMDs.
 constexpr int kThreads = 512;
-constexpr int kWaveCopyK = 4, kWaveCopyQ = 5, kWaveDiag = 2, kWaveP3 = 6, kWaveA = 3, kWaveP012 = 7;
+constexpr int kWaveCopyK = 4, kWaveCopyQ = 6, kWaveDiag = 2, kWaveP3 = 5, kWaveA = 3, kWaveP012 = 7;
 constexpr int kWaveStore = kWaveP012;  // the wave that writes the output back
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -69,7 +69,7 @@ constexpr int kRawBytes = 37376;
 constexpr int kDerP = 0;      // 6 P fragments (row tile, 32-deep slice) x 1 KB
 constexpr int kDerNA = 6144;  // -A: A10 (16-deep, 512 B), A2x (1 KB), A3x (1 KB), A32 (16-deep, 512 B)
 constexpr int kDerTd = 9216;  // T_ii: four 16-deep fragments of 512 B
-constexpr int kDerSc = 11264; // beta, e^b, read scale, e^{bC-b} [64] each, then e^{bC}
+constexpr int kDerSc = 11264; // (unused), e^b, read scale, e^{bC-b} [64] each, then e^{bC}
 constexpr int kDerBytes = 12320;
 constexpr int kOffRaw = 0;
 constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
@@ -83,6 +83,7 @@ constexpr int kOffG3 = kOffG2 + 1024;             // A prep: beta * row factors 
 constexpr int kOffG4 = kOffG3 + 1024;             // P prep, row tile 3: as G2
 constexpr int kOffStage = kOffG4 + 1024;          // output staging, two of [32 cols][64 rows] bf16
 constexpr int kStageBytes = 4096;
+constexpr int kSortMax = 2 * kStageBytes / 4 - 2;  // segments ranked by length in the staging area
 constexpr int kSmemBytes = kOffStage + 2 * kStageBytes;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 
@@ -335,7 +336,6 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
     {
         float *sc = reinterpret_cast<float *>(der + kDerSc);
         const float bC = lane_value(gt.b2, 63);
-        sc[lane] = gt.beta;
         sc[64 + lane] = ex2(gt.b2);
         sc[128 + lane] = ex2(pre ? gt.b2 - gt.la2 : gt.b2);
         sc[192 + lane] = ex2(bC - gt.b2);
@@ -382,11 +382,13 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
 #pragma unroll
         for (int j = 0; j < k; ++j) y[j] += arow[k][j >> 2][j & 3] * yk;
     }
-    // 16-deep A-operand fragment of T_ii: lane 16 kg + row holds columns 4 kg .. 4 kg + 3
+    // 16-deep A-operand fragment of T_ii diag(beta_i): lane 16 kg + row holds columns 4 kg ..
+    // 4 kg + 3, each scaled by the beta of its token
     char *td = der + kDerTd + g * 512 + c * 8;
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
-        const floatx4 y4 = {y[4 * kg], y[4 * kg + 1], y[4 * kg + 2], y[4 * kg + 3]};
+        const floatx4 b4 = *reinterpret_cast<const floatx4 *>(gb + 64 + 16 * g + 4 * kg);
+        const floatx4 y4 = {y[4 * kg] * b4[0], y[4 * kg + 1] * b4[1], y[4 * kg + 2] * b4[2], y[4 * kg + 3] * b4[3]};
         *reinterpret_cast<uint2 *>(td + kg * 128) = pack4(y4);
     }
 }
@@ -494,7 +496,7 @@ __device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, c
     {
         const int tile = lane >> 4;
         const float ref = tile == 0 ? s0 : tile == 1 ? s16 : tile == 2 ? s32 : s48;
-        gw[lane] = gt.beta * ex2(fminf(gt.b2 - ref, 0.f));
+        gw[lane] = ex2(fminf(gt.b2 - ref, 0.f));
         gw[64 + lane] = lane < 16 ? ex2(s16 - gt.b2) : 0.f;
         gw[128 + lane] = lane < 32 ? ex2(s32 - gt.b2) : 0.f;
         gw[192 + lane] = lane < 48 ? ex2(s48 - gt.b2) : 0.f;
@@ -573,8 +575,33 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     const int64_t unit = (slot / a.ntiles) * 8 + xcd;
     const int tile = (int)(slot % a.ntiles);
     if (unit >= a.units) return;
-    const int64_t seq = unit / a.Hv, head = unit % a.Hv;
+    int64_t seq = unit / a.Hv;
+    const int64_t head = unit % a.Hv;
     const int64_t kh = head / (a.Hv / a.Hk);
+    // Packed segments are taken longest first: unit ranks are dispatched in order, so the
+    // workgroups of long segments start early and short ones fill in at the end. Rank r
+    // goes to the segment with r longer segments before it (ties by index).
+    if (a.cu_seqlens) {
+        const int nseq = (int)(a.units / a.Hv);
+        if (nseq <= kSortMax) {
+            int *cu = reinterpret_cast<int *>(smem + kOffStage);  // unused until the first chunk
+            for (int i = tid; i <= nseq; i += kThreads) cu[i] = a.cu_seqlens[i];
+            __syncthreads();
+            const int rank = (int)seq;
+            for (int s0 = tid; s0 < nseq; s0 += kThreads) {
+                const int l0 = cu[s0 + 1] - cu[s0];
+                int r = 0;
+                for (int s1 = 0; s1 < nseq; ++s1) {
+                    const int l1 = cu[s1 + 1] - cu[s1];
+                    r += (l1 > l0) || (l1 == l0 && s1 < s0);
+                }
+                if (r == rank) cu[nseq + 1] = s0;
+            }
+            __syncthreads();
+            seq = cu[nseq + 1];
+            __syncthreads();
+        }
+    }
     const int64_t row = a.cu_seqlens ? 0 : seq;
     int64_t t0 = 0, len = a.T;
     if (a.cu_seqlens) {
@@ -725,14 +752,22 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         lds_barrier();
         lds_barrier();
     }
+    // the first slice of K for X_K of the next chunk is read before each barrier (the raw
+    // buffer of chunk c+1 is complete while chunk c runs)
+    uint4 fk_next[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) fk_next[mi] = row_frag(smem + kOffRaw + kRawK, ro, mi, 0);
 
     // Per chunk: X_K = K H, then R, then the block substitution for U (a chain of dependent
     // small products) with the independent X_Q = Q H products interleaved into its gaps,
     // then the state update with the output products interleaved. Operands of a step are
     // read from LDS one step ahead, and scheduling fences keep that order.
-    for (int64_t ch = 0; ch < nchunks; ++ch) {
-        const char *raw = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
-        const char *der = smem + kOffDer + (int)(ch & 1) * kDerBytes;
+    // The step is instantiated for the six phases of (ring slot, derived buffer) so that every
+    // LDS address is a per-lane register plus a constant.
+    auto step = [&](int64_t ch, auto phase) {
+        constexpr int P = decltype(phase)::value;
+        const char *raw = smem + kOffRaw + (P % 3) * kRawBytes;
+        const char *der = smem + kOffDer + (P & 1) * kDerBytes;
         const char *sc = der + kDerSc + scoff;
         const char *na = der + kDerNA;
         const char *td = der + kDerTd;
@@ -742,10 +777,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         for (int mi = 0; mi < 4; ++mi) XK[mi] = zero4();
         uint4 fk[2][4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) fk[0][mi] = row_frag(raw + kRawK, ro, mi, 0);
+        for (int mi = 0; mi < 4; ++mi) fk[0][mi] = fk_next[mi];
         Frag<__bf16> hf[4];
         bf16x4 vv[4];
-        floatx4 be[4], eb[4];
+        floatx4 eb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (ks < 3) {
@@ -755,7 +790,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
                     vv[mi] = tr16(raw + kRawV + voff + 1024 * mi);
-                    be[mi] = *reinterpret_cast<const floatx4 *>(sc + 64 * mi);
                     eb[mi] = *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * mi);
                 }
             }
@@ -777,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) U[mi][r] = be[mi][r] * ((float)vv[mi][r] - eb[mi][r] * XK[mi][r]);
+            for (int r = 0; r < 4; ++r) U[mi][r] = (float)vv[mi][r] - eb[mi][r] * XK[mi][r];
         __builtin_amdgcn_sched_barrier(0);
         // ---- U_i = T_ii (R_i - sum_{j<i} A_ij U_j) with X_Q = Q H interleaved: the sixteen
         // X_Q products (slice ks, row tile mi) fill the latency of each level
@@ -798,7 +832,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                         // operands of the state update and the output
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            er[m] = *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * m);
+                            // the post-write read scale e^{b} is eb itself
+                            er[m] = pre ? *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * m) : eb[m];
                             ec[m] = *reinterpret_cast<const floatx4 *>(sc + 768 + 64 * m);
                         }
                         kt[0][0] = kt_frag(raw + kRawK, ko, 0, 0);
@@ -851,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             u01 = frag_from_acc<__bf16>(U[0], U[1]);
             u23 = frag_from_acc<__bf16>(U[2], U[3]);
         }
-        char *stg = smem + kOffStage + (int)(ch & 1) * kStageBytes;
+        char *stg = smem + kOffStage + (P & 1) * kStageBytes;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -876,7 +911,25 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (ch + 1 < nchunks) {
+            const char *raw_next = smem + kOffRaw + ((P + 1) % 3) * kRawBytes;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) fk_next[mi] = row_frag(raw_next + kRawK, ro, mi, 0);
+        }
         lds_barrier();
+    };
+    for (int64_t ch = 0; ch < nchunks; ch += 6) {
+        step(ch, std::integral_constant<int, 0>{});
+        if (ch + 1 >= nchunks) break;
+        step(ch + 1, std::integral_constant<int, 1>{});
+        if (ch + 2 >= nchunks) break;
+        step(ch + 2, std::integral_constant<int, 2>{});
+        if (ch + 3 >= nchunks) break;
+        step(ch + 3, std::integral_constant<int, 3>{});
+        if (ch + 4 >= nchunks) break;
+        step(ch + 4, std::integral_constant<int, 4>{});
+        if (ch + 5 >= nchunks) break;
+        step(ch + 5, std::integral_constant<int, 5>{});
     }
 
     if (a.hT) {
