@@ -148,6 +148,7 @@ SMALL = [
     (torch.bfloat16, 64, 128, 2, 2, 1, 150, 16),
     (torch.bfloat16, 128, 64, 2, 2, 1, 129, 64),
     (torch.bfloat16, 128, 256, 1, 1, 1, 100, 64),
+    (torch.bfloat16, 128, 96, 1, 1, 1, 77, 64),
 ]
 
 
@@ -182,6 +183,22 @@ def test_chunk_fwd_reverse_and_varlen(gdr, dtype, read):
         ro, rh = oracle_chunk(case, read=read, reverse=rev)
         check(o, ro, dtype, "varlen o")
         check(hT, rh, dtype, "varlen hT")
+
+
+@pytest.mark.parametrize("nseg", [40, 2100])
+def test_chunk_fwd_many_segments(gdr, nseg):
+    """Many packed segments of mixed lengths (the fast kernel ranks up to a few thousand of
+    them by length; beyond that it keeps their order)."""
+    g = torch.Generator().manual_seed(nseg)
+    hi = 200 if nseg < 100 else 4
+    lengths = torch.randint(0, hi, (nseg,), generator=g).tolist()
+    case = inputs.chunk_case(Hk=1, Hv=2, dk=128, dv=64, dtype=torch.bfloat16, seed=15, h0_std=0.1,
+                             regime="slow", lengths=lengths)
+    _say("many segments: %d, T=%d" % (nseg, case.q.shape[2]))
+    o, hT = run_chunk(gdr, case, 64)
+    ro, rh = oracle_chunk(case)
+    check(o, ro, torch.bfloat16, "many segments o")
+    check(hT, rh, torch.bfloat16, "many segments hT")
 
 
 def test_chunk_sizes_agree(gdr):
