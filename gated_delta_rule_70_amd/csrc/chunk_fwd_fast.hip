@@ -3,7 +3,8 @@
 // Same chunk algebra as chunk_fwd.hip (the WY/UT form of `chunked_delta` on the "Prizma
 // seq/delta.py" page, with H = S^T), organised for the matrix cores of gfx950:
 //
-//   A   = diag(beta) Ah,  Ah = strict_lower((k_i . k_j) e^{b_i - b_j}),  T_ii = (I + A_ii)^{-1}
+//   A   = diag(beta) Ah,  Ah = strict_lower((k_i . k_j) e^{b_i - b_j}),
+//   T_ii = (I + A_ii)^{-1} = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8)   (A_ii^16 = 0)
 //   R   = V - diag(e^{b}) K H
 //   U   by block forward substitution over the four 16-row blocks, with beta folded into the
 //       diagonal inverses (U = (I + A)^{-1} diag(beta) R exactly):
@@ -18,7 +19,7 @@
 //               state tiles stay in accumulator registers and are the B operands of K H and
 //               Q H directly.
 //   wave 2      diagonal prep for chunk c+1: gate scalars, diagonal tiles of K K^T and the
-//               four 16x16 inverses T_ii by substitution.
+//               four 16x16 inverses T_ii as products of matrix-core squarings.
 //   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1.
 //   waves 5, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1;
 //               wave 7 also writes back the output of chunk c-1 from its staging tile.
@@ -73,11 +74,7 @@ constexpr int kDerSc = 11264; // (unused), e^b, read scale, e^{bC-b} [64] each, 
 constexpr int kDerBytes = 12320;
 constexpr int kOffRaw = 0;
 constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
-constexpr int kOffAd = kOffDer + 2 * kDerBytes;   // diagonal prep: A_ii blocks fp32 [4][16][16]
-// Block stride of A_ii: one row (64 B) plus 16 B, so that the four blocks, which the four
-// lane groups read at the same time, start in different banks.
-constexpr int kAdBlock = 16 * 16 + 4;             // floats
-constexpr int kOffG1 = kOffAd + 4 * kAdBlock * 4; // diagonal prep: b2, beta [64]
+constexpr int kOffG1 = kOffDer + 2 * kDerBytes;   // diagonal prep: b2, beta [64]
 constexpr int kOffG2 = kOffG1 + 512;              // P prep, row tiles 0-2: row factors [64], column factors [3][64]
 constexpr int kOffG3 = kOffG2 + 1024;             // A prep: beta * row factors [64], column factors [3][64]
 constexpr int kOffG4 = kOffG3 + 1024;             // P prep, row tile 3: as G2
@@ -347,49 +344,56 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kf[i][ks] = row_frag(raw + kRawK, ro, i, ks);
     __builtin_amdgcn_sched_barrier(0);
-    float *adt = reinterpret_cast<float *>(smem + kOffAd);
     floatx4 gkk[4];
     grams<4>(gkk, kf, kf, {0, 1, 2, 3}, {0, 1, 2, 3});
+    // B_i = A_ii^T in accumulator layout: lane (g, c) holds A_ii[c][4g + r] (row 16i + c of
+    // the chunk, column 16i + 4g + r), from the symmetric Gram tile.
+    floatx4 bt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // A_ii transposed from the Gram tile: lane holds row 16i + c, columns 16i + 4g + r
         const floatx4 gk = gkk[i];
         const floatx4 bcol = *reinterpret_cast<const floatx4 *>(gb + 16 * i + 4 * g);
         const float brow = gb[16 * i + c], betarow = gb[64 + 16 * i + c];
-        floatx4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) av[r] = (4 * g + r < c) ? -betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
-        *reinterpret_cast<floatx4 *>(adt + i * kAdBlock + c * 16 + 4 * g) = av;  // row-major -A_ii
+        for (int r = 0; r < 4; ++r) bt[i][r] = (4 * g + r < c) ? betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
     }
-    // LDS accesses of one wave complete in order: the row loads below see these stores
-    asm volatile("" ::: "memory");
-    // T_ii = (I + A_ii)^{-1}: lane (i = g, c) computes row c, y (I + A_ii) = e_c, from the
-    // last column down: once y_k is final, row k of A_ii is eliminated from the earlier y_j.
-    // The rows of -A_ii are read into registers first (the same address in all 16 lanes).
-    const float *ablk = adt + g * kAdBlock;
-    floatx4 arow[16][4];
+    // T_ii = (I + A_ii)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8), exact because the strictly
+    // lower 16x16 A has A^16 = 0; all factors are polynomials in A, so they commute. On the
+    // matrix cores: an accumulator-layout tile D(M) serves as the B operand M or as the A
+    // operand M^T, and D(M^T) is D(M) multiplied by I with the operands swapped. Products
+    // accumulate in fp32; operands are rounded to bf16. The four blocks run interleaved.
+    floatx4 eye;
 #pragma unroll
-    for (int k = 1; k < 16; ++k)
+    for (int r = 0; r < 4; ++r) eye[r] = (4 * g + r == c) ? 1.f : 0.f;
+    const bf16x4 eyeb = cvt4<__bf16>(eye);
+    floatx4 da[4], a2[4], a2t[4], a4[4], a4t[4], a8[4], p1t[4], p2t[4], tt[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            if (4 * q4 < k) arow[k][q4] = reinterpret_cast<const floatx4 *>(ablk + k * 16)[q4];
-    float y[16];
+    for (int i = 0; i < 4; ++i) da[i] = mma16(zero4(), cvt4<__bf16>(bt[i]), eyeb);              // D(A)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) y[j] = (j == c) ? 1.f : 0.f;
+    for (int i = 0; i < 4; ++i) a2[i] = mma16(zero4(), cvt4<__bf16>(bt[i]), cvt4<__bf16>(da[i])); // D(A^2)
 #pragma unroll
-    for (int k = 15; k >= 1; --k) {
-        const float yk = y[k];
-#pragma unroll
-        for (int j = 0; j < k; ++j) y[j] += arow[k][j >> 2][j & 3] * yk;
+    for (int i = 0; i < 4; ++i) {
+        a2t[i] = mma16(zero4(), cvt4<__bf16>(a2[i]), eyeb);                                    // D(A^2T)
+        const floatx4 imb = eye - bt[i];                                                       // D(I - A^T)
+        p1t[i] = mma16(imb, cvt4<__bf16>(a2[i]), cvt4<__bf16>(imb));                           // (I + A^2T)(I - A^T)
     }
-    // 16-deep A-operand fragment of T_ii diag(beta_i): lane 16 kg + row holds columns 4 kg ..
-    // 4 kg + 3, each scaled by the beta of its token
-    char *td = der + kDerTd + g * 512 + c * 8;
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-        const floatx4 b4 = *reinterpret_cast<const floatx4 *>(gb + 64 + 16 * g + 4 * kg);
-        const floatx4 y4 = {y[4 * kg] * b4[0], y[4 * kg + 1] * b4[1], y[4 * kg + 2] * b4[2], y[4 * kg + 3] * b4[3]};
-        *reinterpret_cast<uint2 *>(td + kg * 128) = pack4(y4);
+    for (int i = 0; i < 4; ++i) a4[i] = mma16(zero4(), cvt4<__bf16>(a2t[i]), cvt4<__bf16>(a2[i])); // D(A^4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a4t[i] = mma16(zero4(), cvt4<__bf16>(a4[i]), eyeb);                                    // D(A^4T)
+        p2t[i] = mma16(p1t[i], cvt4<__bf16>(a4[i]), cvt4<__bf16>(p1t[i]));                     // (I + A^4T) P1^T
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a8[i] = mma16(zero4(), cvt4<__bf16>(a4t[i]), cvt4<__bf16>(a4[i])); // D(A^8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tt[i] = mma16(p2t[i], cvt4<__bf16>(a8[i]), cvt4<__bf16>(p2t[i]));  // D(T^T)
+    // 16-deep A-operand fragment of T_ii diag(beta_i): lane (g, c) holds T[c][4g + r] (from
+    // D(T^T)), scaled by the beta of column token 16i + 4g + r
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const floatx4 b4 = *reinterpret_cast<const floatx4 *>(gb + 64 + 16 * i + 4 * g);
+        *reinterpret_cast<uint2 *>(der + kDerTd + i * 512 + lane * 8) = pack4(tt[i] * b4);
     }
 }
 
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             }
         }
         // one loop per role, so that each keeps only its own loop-invariant registers
-        auto run = [&](auto role) {
+        auto run = [&](auto role) __attribute__((always_inline)) {
             constexpr int R = decltype(role)::value;
             constexpr bool kCopies = R == kWaveCopyK || R == kWaveCopyQ;
             u32x4 rsrc0, rsrc1, rsrc2, rsrc3;
@@ -659,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 clast.init(chunk_rows(t0, len, fwd, nchunks - 1), a.dv);
             }
             // two explicit paths, so that each copy addresses with one of the fixed sets
-            auto issue = [&](int64_t ch, const CopyOffsets &co) {
+            auto issue = [&](int64_t ch, const CopyOffsets &co) __attribute__((always_inline)) {
                 char *rawn = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
                 if constexpr (R == kWaveCopyK) {
@@ -670,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                     copy_gates(rawn, rsrc2, rsrc3, co, lo);
                 }
             };
-            auto prep = [&](int64_t ch) {
+            auto prep = [&](int64_t ch) __attribute__((always_inline)) {
                 const char *rawp = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 char *derp = smem + kOffDer + (int)(ch & 1) * kDerBytes;
                 if constexpr (R == kWaveDiag) prep_diag(smem, rawp, derp, pre, ro);
@@ -678,12 +682,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 else if constexpr (R == kWaveP012) prep_p<0, 3>(smem, rawp, derp, pre, ro, kOffG2);
                 else if constexpr (R == kWaveP3) prep_p<3, 4>(smem, rawp, derp, pre, ro, kOffG4);
             };
-            auto store = [&](int64_t ch) {
+            auto store = [&](int64_t ch) __attribute__((always_inline)) {
                 const ChunkRows cr = chunk_rows(t0, len, fwd, ch);
                 write_back(smem + kOffStage + (int)(ch & 1) * kStageBytes, ob + cr.lo * a.dv + dcol0, cr, a.dv,
                            acc_out);
             };
-            auto step = [&](int64_t ch) {
+            auto step = [&](int64_t ch) __attribute__((always_inline)) {
                 if constexpr (R == kWaveStore) {
                     if (ch >= 1) store(ch - 1);
                 }
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     // read from LDS one step ahead, and scheduling fences keep that order.
     // The step is instantiated for the six phases of (ring slot, derived buffer) so that every
     // LDS address is a per-lane register plus a constant.
-    auto step = [&](int64_t ch, auto phase) {
+    auto step = [&](int64_t ch, auto phase) __attribute__((always_inline)) {
         constexpr int P = decltype(phase)::value;
         const char *raw = smem + kOffRaw + (P % 3) * kRawBytes;
         const char *der = smem + kOffDer + (P & 1) * kDerBytes;
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         for (int mi = 0; mi < 4; ++mi) XQ[mi] = zero4();
         floatx4 er[4], ec[4];
         Frag<__bf16> kt[3][2];
-        auto xq_items = [&](int first, int last) {
+        auto xq_items = [&](int first, int last) __attribute__((always_inline)) {
 #pragma unroll
             for (int it = first; it < last; ++it) {
                 const int ks = it >> 2, mi = it & 3;
