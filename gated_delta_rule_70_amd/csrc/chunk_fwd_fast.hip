@@ -20,9 +20,9 @@
 //               Q H directly.
 //   wave 2      diagonal prep for chunk c+1: gate scalars, diagonal tiles of K K^T and the
 //               four 16x16 inverses T_ii as products of matrix-core squarings.
-//   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1.
-//   waves 5, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1;
-//               wave 7 also writes back the output of chunk c-1 from its staging tile.
+//   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1, and the write-back of
+//               the output of chunk c-1 from its staging tile.
+//   waves 5, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1.
 //   waves 4, 6  copies for chunk c+2 (K; Q, V and gates); they issue little.
 // Raw q/k/v of a chunk are copied once per workgroup, global -> LDS directly (16 bytes per
 // lane, no registers), into a ring of three buffers: while the chain reads chunk c and the
@@ -60,7 +60,7 @@ constexpr int kC = 64, kDK = 128, kDVT = 32;
 // copy wave, which issues little; the four prep waves take the other two SIMDs.
 constexpr int kThreads = 512;
 constexpr int kWaveCopyK = 4, kWaveCopyQ = 6, kWaveDiag = 2, kWaveP3 = 5, kWaveA = 3, kWaveP012 = 7;
-constexpr int kWaveStore = kWaveP012;  // the wave that writes the output back
+constexpr int kWaveStore = kWaveA;  // the wave that writes the output back
 constexpr float kLog2e = 1.4426950408889634f;
 
 // raw buffer (one of three): K, Q [64 rows][256 B] and V [64 rows][64 B], swizzled; gates
