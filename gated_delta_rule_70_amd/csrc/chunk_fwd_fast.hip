@@ -563,7 +563,9 @@ __device__ __forceinline__ void write_back(const char *stg, __bf16 *obase, const
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] + (float)prev[e]);
             }
-            *dst = v;
+            // streaming store: nothing in this kernel reads the output back, and with
+            // ordinary stores the concurrent copies into LDS run measurably slower
+            __builtin_nontemporal_store(v, dst);
         }
     }
 }
