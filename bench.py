@@ -223,9 +223,11 @@ def cpu_baseline(inputs, min_wall=1.5, max_reps=20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # enough untimed calls (about 7 ms of work) for the GPU to reach its steady clock
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
+    # untimed calls before the timed ones: the GPU takes tens of milliseconds of sustained work
+    # to reach its steady clock (with 50 warmup calls, about 5 ms, the chunked forward still
+    # timed 16% slower than with 300); 500 calls are about 50 ms
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
