@@ -66,20 +66,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // raw buffer (one of three): K, Q [64 rows][256 B] and V [64 rows][64 B], swizzled; gates
 constexpr int kRawK = 0, kRawQ = 16384, kRawV = 32768, kRawLa = 36864, kRawBeta = 37120;
-constexpr int kRawBytes = 37376;
+// gate tables of the chunk, written into its raw buffer by the copy wave once the gates have
+// arrived: inclusive log2 cumsum b [64]; read-side log decay [64]; P and -A decay factors
+// (row factors [64], column factors [3][64] each); e^b, read scale, e^{bC-b} [64] each; e^{bC}
+constexpr int kTabB2 = 37376, kTabBread = 37632, kTabGP = 37888, kTabGA = 38912;
+constexpr int kTabEb = 39936, kTabEr = 40192, kTabEc = 40448, kTabGC = 40704;
+constexpr int kRawBytes = 40720;
 // derived buffer (one of two)
 constexpr int kDerP = 0;      // 6 P fragments (row tile, 32-deep slice) x 1 KB
 constexpr int kDerNA = 6144;  // -A: A10 (16-deep, 512 B), A2x (1 KB), A3x (1 KB), A32 (16-deep, 512 B)
 constexpr int kDerTd = 9216;  // T_ii: four 16-deep fragments of 512 B
-constexpr int kDerSc = 11264; // (unused), e^b, read scale, e^{bC-b} [64] each, then e^{bC}
-constexpr int kDerBytes = 12320;
+constexpr int kDerBytes = 11264;
 constexpr int kOffRaw = 0;
 constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
-constexpr int kOffG1 = kOffDer + 2 * kDerBytes;   // diagonal prep: b2, beta [64]
-constexpr int kOffG2 = kOffG1 + 512;              // P prep, row tiles 0-2: row factors [64], column factors [3][64]
-constexpr int kOffG3 = kOffG2 + 1024;             // A prep: beta * row factors [64], column factors [3][64]
-constexpr int kOffG4 = kOffG3 + 1024;             // P prep, row tile 3: as G2
-constexpr int kOffStage = kOffG4 + 1024;          // output staging, two of [32 cols][64 rows] bf16
+constexpr int kOffStage = kOffDer + 2 * kDerBytes;  // output staging, two of [32 cols][64 rows] bf16
 constexpr int kStageBytes = 4096;
 constexpr int kSortMax = 2 * kStageBytes / 4 - 2;  // segments ranked by length in the staging area
 constexpr int kSmemBytes = kOffStage + 2 * kStageBytes;
@@ -340,18 +340,10 @@ __device__ __forceinline__ Gates read_gates(const char *raw) {
 // ------------------------------------------------------------------ diagonal prep
 __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der, bool pre, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const Gates gt = read_gates(raw);
-    float *gb = reinterpret_cast<float *>(smem + kOffG1);
-    gb[lane] = gt.b2;
-    gb[64 + lane] = gt.beta;
-    {
-        float *sc = reinterpret_cast<float *>(der + kDerSc);
-        const float bC = lane_value(gt.b2, 63);
-        sc[64 + lane] = ex2(gt.b2);
-        sc[128 + lane] = ex2(pre ? gt.b2 - gt.la2 : gt.b2);
-        sc[192 + lane] = ex2(bC - gt.b2);
-        if (lane == 0) sc[256] = ex2(bC);
-    }
+    (void)smem;
+    (void)pre;
+    const float *tb = reinterpret_cast<const float *>(raw + kTabB2);
+    const float *rb = reinterpret_cast<const float *>(raw + kRawBeta);
     uint4 kf[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -366,8 +358,8 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const floatx4 gk = gkk[i];
-        const floatx4 bcol = *reinterpret_cast<const floatx4 *>(gb + 16 * i + 4 * g);
-        const float brow = gb[16 * i + c], betarow = gb[64 + 16 * i + c];
+        const floatx4 bcol = *reinterpret_cast<const floatx4 *>(tb + 16 * i + 4 * g);
+        const float brow = tb[16 * i + c], betarow = rb[16 * i + c];
 #pragma unroll
         for (int r = 0; r < 4; ++r) bt[i][r] = (4 * g + r < c) ? betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
     }
@@ -406,7 +398,7 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
     // D(T^T)), scaled by the beta of column token 16i + 4g + r
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const floatx4 b4 = *reinterpret_cast<const floatx4 *>(gb + 64 + 16 * i + 4 * g);
+        const floatx4 b4 = *reinterpret_cast<const floatx4 *>(rb + 16 * i + 4 * g);
         *reinterpret_cast<uint2 *>(der + kDerTd + i * 512 + lane * 8) = pack4(tt[i] * b4);
     }
 }
@@ -426,27 +418,50 @@ __device__ __forceinline__ void tile_refs(float b2, float &s0, float &s16, float
     e47 = lane_value(b2, 47);
 }
 
-// ------------------------------------------------------------------ P prep (row tiles I0 .. I1-1)
-template <int I0, int I1>
-__device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, bool pre, const RowFragOffsets &ro,
-                                       int goff) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+// Gate tables of one chunk (raw buffer raw, gates already in LDS), for the prep waves and
+// the chain: b = inclusive cumsum of log2 alpha over the chunk, the read-side log decay, the
+// decay factors of the P and -A tiles split at 16-row references (no exponent is positive),
+// and the chain's scalars.
+__device__ __forceinline__ void gate_tables(char *raw, bool pre) {
+    const int lane = threadIdx.x & 63;
     const Gates gt = read_gates(raw);
-    float *gw = reinterpret_cast<float *>(smem + goff);
+    float *tb = reinterpret_cast<float *>(raw + kTabB2);
+    float *tr = reinterpret_cast<float *>(raw + kTabBread);
+    float *gp = reinterpret_cast<float *>(raw + kTabGP);
+    float *ga = reinterpret_cast<float *>(raw + kTabGA);
     float s0, s16, s32, s48, e15, e31, e47;
     tile_refs(gt.b2, s0, s16, s32, s48, e15, e31, e47);
-    {
-        const int tile = lane >> 4;
-        const float ref = tile == 0 ? s0 : tile == 1 ? s16 : tile == 2 ? s32 : s48;
-        const float refp = tile == 1 ? e15 : tile == 2 ? e31 : e47;
-        // row factor of row = lane, for tiles i >= 1
-        gw[lane] = pre ? ex2(fminf(gt.b2 - gt.la2 - refp, 0.f)) : ex2(fminf(gt.b2 - ref, 0.f));
-        gw[64 + lane] = lane < 16 ? ex2((pre ? e15 : s16) - gt.b2) : 0.f;
-        gw[128 + lane] = lane < 32 ? ex2((pre ? e31 : s32) - gt.b2) : 0.f;
-        gw[192 + lane] = lane < 48 ? ex2((pre ? e47 : s48) - gt.b2) : 0.f;
-    }
-    // read-side log decay of the row and log decay of the column, for the diagonal tiles
-    const float bread = pre ? gt.b2 - gt.la2 : gt.b2;
+    tb[lane] = gt.b2;
+    tr[lane] = pre ? gt.b2 - gt.la2 : gt.b2;
+    const int tile = lane >> 4;
+    const float ref = tile == 0 ? s0 : tile == 1 ? s16 : tile == 2 ? s32 : s48;
+    const float refp = tile == 1 ? e15 : tile == 2 ? e31 : e47;
+    // P: row factor of row = lane (used for row tiles >= 1), column factors against the
+    // reference of row tiles 1, 2, 3
+    gp[lane] = pre ? ex2(fminf(gt.b2 - gt.la2 - refp, 0.f)) : ex2(fminf(gt.b2 - ref, 0.f));
+    gp[64 + lane] = lane < 16 ? ex2((pre ? e15 : s16) - gt.b2) : 0.f;
+    gp[128 + lane] = lane < 32 ? ex2((pre ? e31 : s32) - gt.b2) : 0.f;
+    gp[192 + lane] = lane < 48 ? ex2((pre ? e47 : s48) - gt.b2) : 0.f;
+    // -A: the same split for the write-side decays
+    ga[lane] = ex2(fminf(gt.b2 - ref, 0.f));
+    ga[64 + lane] = lane < 16 ? ex2(s16 - gt.b2) : 0.f;
+    ga[128 + lane] = lane < 32 ? ex2(s32 - gt.b2) : 0.f;
+    ga[192 + lane] = lane < 48 ? ex2(s48 - gt.b2) : 0.f;
+    const float bC = lane_value(gt.b2, 63);
+    reinterpret_cast<float *>(raw + kTabEb)[lane] = ex2(gt.b2);
+    reinterpret_cast<float *>(raw + kTabEr)[lane] = ex2(pre ? gt.b2 - gt.la2 : gt.b2);
+    reinterpret_cast<float *>(raw + kTabEc)[lane] = ex2(bC - gt.b2);
+    if (lane == 0) reinterpret_cast<float *>(raw + kTabGC)[0] = ex2(bC);
+}
+
+// ------------------------------------------------------------------ P prep (row tiles I0 .. I1-1)
+template <int I0, int I1>
+__device__ __forceinline__ void prep_p(const char *raw, char *der, bool pre, const RowFragOffsets &ro) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const float *gw = reinterpret_cast<const float *>(raw + kTabGP);
+    // log decay of the columns and read-side log decay of the rows, for the diagonal tiles
+    const float *tb = reinterpret_cast<const float *>(raw + kTabB2);
+    const float *tr = reinterpret_cast<const float *>(raw + kTabBread);
     uint4 kf[I1][4], qf[I1][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -475,8 +490,8 @@ __device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, b
     grams<NT>(gqk, kf, qf, tj, ti);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-        // row 16i + c of this lane: its read decay, from lane 16i + c
-        const float br = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * i + c), __builtin_bit_cast(int, bread)));
+        // row 16i + c of this lane: its read decay and its row factor
+        const float br = tr[16 * i + c];
         const float rowf = gw[16 * i + c];
 #pragma unroll
         for (int j = 0; j <= i; ++j) {
@@ -488,10 +503,7 @@ __device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, b
                 pv = rowf * cf * gq;
             } else {
                 // diagonal tile: columns 16i + 4g + r against row 16i + c
-                const floatx4 bcol = {__builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * i + 4 * g + 0), __builtin_bit_cast(int, gt.b2))),
-                                      __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * i + 4 * g + 1), __builtin_bit_cast(int, gt.b2))),
-                                      __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * i + 4 * g + 2), __builtin_bit_cast(int, gt.b2))),
-                                      __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * i + 4 * g + 3), __builtin_bit_cast(int, gt.b2)))};
+                const floatx4 bcol = *reinterpret_cast<const floatx4 *>(tb + 16 * i + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int cc = 4 * g + r;
@@ -505,20 +517,9 @@ __device__ __forceinline__ void prep_p(char *smem, const char *raw, char *der, b
 }
 
 // ------------------------------------------------------------------ A prep
-__device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, const RowFragOffsets &ro) {
+__device__ __forceinline__ void prep_a(const char *raw, char *der, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const Gates gt = read_gates(raw);
-    float *gw = reinterpret_cast<float *>(smem + kOffG3);
-    float s0, s16, s32, s48, e15, e31, e47;
-    tile_refs(gt.b2, s0, s16, s32, s48, e15, e31, e47);
-    {
-        const int tile = lane >> 4;
-        const float ref = tile == 0 ? s0 : tile == 1 ? s16 : tile == 2 ? s32 : s48;
-        gw[lane] = ex2(fminf(gt.b2 - ref, 0.f));
-        gw[64 + lane] = lane < 16 ? ex2(s16 - gt.b2) : 0.f;
-        gw[128 + lane] = lane < 32 ? ex2(s32 - gt.b2) : 0.f;
-        gw[192 + lane] = lane < 48 ? ex2(s48 - gt.b2) : 0.f;
-    }
+    const float *gw = reinterpret_cast<const float *>(raw + kTabGA);
     uint4 kf[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -530,7 +531,7 @@ __device__ __forceinline__ void prep_a(char *smem, const char *raw, char *der, c
     grams<6>(gkk, kf, kf, {0, 0, 1, 0, 1, 2}, {1, 2, 2, 3, 3, 3});
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
-        const float ar = gw[16 * i + c];  // beta * row factor of row 16i + c
+        const float ar = gw[16 * i + c];  // row factor of row 16i + c
 #pragma unroll
         for (int j = 0; j < i; ++j) {
             // transposed tile: lane holds row 16i + c, columns 16j + 4g + r
@@ -694,14 +695,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 const char *rawp = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 char *derp = smem + kOffDer + (int)(ch & 1) * kDerBytes;
                 if constexpr (R == kWaveDiag) prep_diag(smem, rawp, derp, pre, ro);
-                else if constexpr (R == kWaveA) prep_a(smem, rawp, derp, ro);
-                else if constexpr (R == kWaveP012) prep_p<0, 3>(smem, rawp, derp, pre, ro, kOffG2);
-                else if constexpr (R == kWaveP3) prep_p<3, 4>(smem, rawp, derp, pre, ro, kOffG4);
+                else if constexpr (R == kWaveA) prep_a(rawp, derp, ro);
+                else if constexpr (R == kWaveP012) prep_p<0, 3>(rawp, derp, pre, ro);
+                else if constexpr (R == kWaveP3) prep_p<3, 4>(rawp, derp, pre, ro);
             };
             auto store = [&](int64_t ch) __attribute__((always_inline)) {
                 const ChunkRows cr = chunk_rows(t0, len, fwd, ch);
                 write_back(smem + kOffStage + (int)(ch & 1) * kStageBytes, ob + cr.lo * a.dv + dcol0, cr, a.dv,
                            acc_out);
+            };
+            // the wave that copies the gates builds the chunk's gate tables as soon as its copies
+            // have landed, one chunk ahead of the prep waves that read them
+            auto tables = [&](int64_t ch) __attribute__((always_inline)) {
+                if constexpr (R == kWaveCopyQ) gate_tables(smem + kOffRaw + (int)(ch % 3) * kRawBytes, pre);
             };
             auto step = [&](int64_t ch) __attribute__((always_inline)) {
                 if constexpr (R == kWaveStore) {
@@ -709,6 +715,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 }
                 if (ch + 1 < nchunks) prep(ch + 1);
                 wait_vmem();
+                if (ch + 2 < nchunks) tables(ch + 2);
                 lds_barrier();
             };
             if constexpr (kCopies) {
@@ -716,6 +723,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 else issue(0, cfull);
             }
             wait_vmem();
+            tables(0);
             lds_barrier();
             if constexpr (kCopies) {
                 if (nchunks == 2) issue(1, clast);
@@ -723,6 +731,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             }
             prep(0);
             wait_vmem();
+            if (nchunks > 1) tables(1);
             lds_barrier();
             // The loop that copies full chunks and the tail that copies the last chunk are
             // separate code, so that no copy's offset register is chosen at run time.
@@ -788,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         constexpr int P = decltype(phase)::value;
         const char *raw = smem + kOffRaw + (P % 3) * kRawBytes;
         const char *der = smem + kOffDer + (P & 1) * kDerBytes;
-        const char *sc = der + kDerSc + scoff;
+        const char *sc = raw + kTabEb + scoff;  // e^b, then read scale and e^{bC-b} 256 B apart
         const char *na = der + kDerNA;
         const char *td = der + kDerTd;
         // ---- X_K = K H
@@ -810,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
                     vv[mi] = tr16(raw + kRawV + voff + 1024 * mi);
-                    eb[mi] = *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * mi);
+                    eb[mi] = *reinterpret_cast<const floatx4 *>(sc + 64 * mi);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -853,8 +862,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
                             // the post-write read scale e^{b} is eb itself
-                            er[m] = pre ? *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * m) : eb[m];
-                            ec[m] = *reinterpret_cast<const floatx4 *>(sc + 768 + 64 * m);
+                            er[m] = pre ? *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * m) : eb[m];
+                            ec[m] = *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * m);
                         }
                         kt[0][0] = kt_frag(raw + kRawK, ko, 0, 0);
                         kt[0][1] = kt_frag(raw + kRawK, ko, 0, 1);
@@ -892,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         // ---- H <- e^{b_C} H + K^T diag(e^{b_C - b}) U, with O = e^{b | b'} X_Q + P U
         // interleaved (output row tile t/2 after state tile t, for odd t)
-        const float gC = *reinterpret_cast<const float *>(der + kDerSc + 1024);
+        const float gC = *reinterpret_cast<const float *>(raw + kTabGC);
         Frag<__bf16> p[6];
 #pragma unroll
         for (int f = 0; f < 6; ++f) p[f] = der_frag(der + kDerP, f);
