@@ -82,7 +82,10 @@ constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
 constexpr int kOffStage = kOffDer + 2 * kDerBytes;  // output staging, two of [32 cols][64 rows] bf16
 constexpr int kStageBytes = 4096;
 constexpr int kSortMax = 2 * kStageBytes / 4 - 2;  // segments ranked by length in the staging area
-constexpr int kSmemBytes = kOffStage + 2 * kStageBytes;
+// with accumulation, the output's previous values of a chunk, copied in like the V slice
+constexpr int kOffPrev = kOffStage + 2 * kStageBytes;
+constexpr int kPrevBytes = 4096;
+constexpr int kSmemBytes = kOffPrev + 2 * kPrevBytes;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
@@ -552,10 +555,12 @@ __device__ __forceinline__ void prep_a(const char *raw, char *der, const RowFrag
 // rows 16r .. 16r+15; in 16-lane group g, lane i addresses column 8g + 4h + i/4 (h = read
 // parity) and rows 16r + 4(i%4) .. +3, so that lane i receives row 16r + i, columns 8g + 4h
 // .. +3: the two reads give it 16 contiguous bytes of the output row.
-__device__ __forceinline__ void write_back(const char *stg, __bf16 *obase, const ChunkRows &cr, int64_t dv,
-                                           bool acc_out) {
+// With acc_out, prv holds the output's previous values of the chunk in the V-slice layout
+// (row R at 64 R bytes, 16-byte piece p at p ^ ((R % 16) / 4)).
+__device__ __forceinline__ void write_back(const char *stg, const char *prv, __bf16 *obase, const ChunkRows &cr,
+                                           int64_t dv, bool acc_out) {
     const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
-    bf16x8 val[4];
+    bf16x8 val[4], prev[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const bf16x4 lo = tr16(stg + stage_off(8 * g + (j >> 2), 4 * r + (j & 3)));
@@ -565,6 +570,7 @@ __device__ __forceinline__ void write_back(const char *stg, __bf16 *obase, const
             val[r][e] = lo[e];
             val[r][4 + e] = hi[e];
         }
+        if (acc_out) prev[r] = *reinterpret_cast<const bf16x8 *>(prv + (16 * r + j) * 64 + ((g ^ (j >> 2)) << 4));
     }
     wave_lds_sync();
 #pragma unroll
@@ -574,9 +580,8 @@ __device__ __forceinline__ void write_back(const char *stg, __bf16 *obase, const
             bf16x8 *dst = reinterpret_cast<bf16x8 *>(obase + (int64_t)cr.off(row) * dv + 8 * g);
             bf16x8 v = val[r];
             if (acc_out) {
-                const bf16x8 prev = *dst;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] + (float)prev[e]);
+                for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] + (float)prev[r][e]);
             }
             // streaming store: nothing in this kernel reads the output back, and with
             // ordinary stores the concurrent copies into LDS run measurably slower
@@ -660,12 +665,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         auto run = [&](auto role) __attribute__((always_inline)) {
             constexpr int R = decltype(role)::value;
             constexpr bool kCopies = R == kWaveCopyK || R == kWaveCopyQ;
-            u32x4 rsrc0, rsrc1, rsrc2, rsrc3;
+            u32x4 rsrc0, rsrc1, rsrc2, rsrc3, rsrc4;
             if constexpr (R == kWaveCopyK) {
                 rsrc0 = slab_rsrc(kb, a.T * kDK * 2);
             } else if constexpr (R == kWaveCopyQ) {
                 rsrc0 = slab_rsrc(qb, a.T * kDK * 2);
                 rsrc1 = slab_rsrc(vb + dcol0, a.T * a.dv * 2 - dcol0 * 2);
+                rsrc4 = slab_rsrc(ob + dcol0, a.T * a.dv * 2 - dcol0 * 2);
                 rsrc2 = slab_rsrc(ab, (t0 + len) * 4);
                 rsrc3 = slab_rsrc(bb, (t0 + len) * 4);
             }
@@ -701,8 +707,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             };
             auto store = [&](int64_t ch) __attribute__((always_inline)) {
                 const ChunkRows cr = chunk_rows(t0, len, fwd, ch);
-                write_back(smem + kOffStage + (int)(ch & 1) * kStageBytes, ob + cr.lo * a.dv + dcol0, cr, a.dv,
-                           acc_out);
+                write_back(smem + kOffStage + (int)(ch & 1) * kStageBytes, smem + kOffPrev + (int)(ch & 1) * kPrevBytes,
+                           ob + cr.lo * a.dv + dcol0, cr, a.dv, acc_out);
             };
             // the wave that copies the gates builds the chunk's gate tables as soon as its copies
             // have landed, one chunk ahead of the prep waves that read them
@@ -710,6 +716,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 if constexpr (R == kWaveCopyQ) gate_tables(smem + kOffRaw + (int)(ch % 3) * kRawBytes, pre);
             };
             auto step = [&](int64_t ch) __attribute__((always_inline)) {
+                if constexpr (R == kWaveCopyQ) {
+                    // with accumulation, the output's previous values of chunk ch, which the
+                    // write-back adds in the next step
+                    if (acc_out) {
+                        char *prv = smem + kOffPrev + (int)(ch & 1) * kPrevBytes;
+                        const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
+                        if (ch == nchunks - 1) copy_v(prv, rsrc4, clast, lo, a.dv);
+                        else copy_v(prv, rsrc4, cfull, lo, a.dv);
+                    }
+                }
                 if constexpr (R == kWaveStore) {
                     if (ch >= 1) store(ch - 1);
                 }
