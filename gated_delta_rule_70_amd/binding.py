@@ -17,15 +17,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdr.so")
 
 GDR_F32, GDR_BF16 = 0, 1
-GDR_READ_PRE, GDR_REVERSE, GDR_ACCUMULATE = 1, 2, 4
+GDR_READ_PRE, GDR_REVERSE, GDR_ACCUMULATE, GDR_QK_L2NORM = 1, 2, 4, 8
 
 STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE", 4: "GDR_ERR_CHUNK",
           5: "GDR_ERR_ALIGN", 6: "GDR_ERR_ALIAS", 7: "GDR_ERR_UNSUPPORTED", 8: "GDR_ERR_FLAGS",
           9: "GDR_ERR_HIP"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_decode_step", "gdr_status_string", "gdr_last_error",
-           "gdr_abi_version", "gdr_selftest_mfma")
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
+           "gdr_status_string", "gdr_last_error", "gdr_abi_version", "gdr_selftest_mfma")
 
 
 class GdrError(RuntimeError):
@@ -55,8 +55,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     p, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.gdr_chunk_fwd.argtypes = [p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_gated.argtypes = [p, p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
     lib.gdr_decode_step.restype = ctypes.c_int
+    lib.gdr_decode_step_gated.argtypes = [p, p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
+    lib.gdr_decode_step_gated.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
@@ -116,14 +120,32 @@ def _dtype_code(dt):
 
 def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk: int = 64,
               read: str = "post", reverse: bool = False, out=None, accumulate: bool = False,
-              hT=None, want_state: bool = True):
+              hT=None, want_state: bool = True, l2norm: bool = False):
     """Chunked forward (``gdr_chunk_fwd``).
 
     q, k [B, Hk, T, dk]; v [B, Hv, T, dv] (bf16 or fp32, same dtype); log_alpha, beta
     [B, Hv, T] fp32; h0 [S, Hv, dk, dv] fp32 or None; cu_seqlens int32 [S+1] (device) or
     None. Returns (out [B, Hv, T, dv], hT [S, Hv, dk, dv] or None). ``out`` may be given
     (required for ``accumulate``); ``hT`` may be given (it may be ``h0`` itself).
+    ``l2norm`` normalises each row of q and k in the kernel (``GDR_QK_L2NORM``).
     """
+    return _chunk(q, k, v, log_alpha, beta, None, None, h0, cu_seqlens, chunk, read, reverse, out,
+                  accumulate, hT, want_state, l2norm)
+
+
+def chunk_fwd_gated(q, k, v, a, b, A_log, dt_bias, h0=None, cu_seqlens=None, *, chunk: int = 64,
+                    read: str = "post", reverse: bool = False, out=None, accumulate: bool = False,
+                    hT=None, want_state: bool = True, l2norm: bool = True):
+    """Chunked forward with the gates formed in the kernel (``gdr_chunk_fwd_gated``): a, b
+    [B, Hv, T] fp32 raw inputs, A_log, dt_bias [Hv] fp32; the rest as ``chunk_fwd``."""
+    return _chunk(q, k, v, a, b, A_log, dt_bias, h0, cu_seqlens, chunk, read, reverse, out,
+                  accumulate, hT, want_state, l2norm)
+
+
+def _chunk(q, k, v, ga, gb, A_log, dt_bias, h0, cu_seqlens, chunk, read, reverse, out, accumulate,
+           hT, want_state, l2norm):
+    gated = A_log is not None or dt_bias is not None
+    na, nb = ("a", "b") if gated else ("log_alpha", "beta")
     _need(q, "q")
     dev = q.device
     dt = q.dtype
@@ -132,8 +154,11 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk: int 
     Hv, dv = v.shape[1], v.shape[3]
     _need(k, "k", dt, (B, Hk, T, dk), dev)
     _need(v, "v", dt, (B, Hv, T, dv), dev)
-    _need(log_alpha, "log_alpha", torch.float32, (B, Hv, T), dev)
-    _need(beta, "beta", torch.float32, (B, Hv, T), dev)
+    _need(ga, na, torch.float32, (B, Hv, T), dev)
+    _need(gb, nb, torch.float32, (B, Hv, T), dev)
+    if gated:
+        _need(A_log, "A_log", torch.float32, (Hv,), dev)
+        _need(dt_bias, "dt_bias", torch.float32, (Hv,), dev)
     S = B
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
@@ -150,21 +175,41 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk: int 
         hT = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
     elif hT is not None:
         _need(hT, "hT", torch.float32, (S, Hv, dk, dv), dev)
-    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0) | \
-        (GDR_ACCUMULATE if accumulate else 0)
     if read not in ("pre", "post"):
         raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0) | \
+        (GDR_ACCUMULATE if accumulate else 0) | (GDR_QK_L2NORM if l2norm else 0)
     dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
-    _check(lib().gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
-                               _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT),
-                               ctypes.byref(dims), _stream(q)))
+    if gated:
+        _check(lib().gdr_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(A_log),
+                                         _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), int(chunk), _ptr(out),
+                                         _ptr(hT), ctypes.byref(dims), _stream(q)))
+    else:
+        _check(lib().gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(h0),
+                                   _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT),
+                                   ctypes.byref(dims), _stream(q)))
     return out, hT
 
 
-def decode_step(q, k, v, log_alpha, beta, state_in, state_out=None, out=None, *, read: str = "post"):
+def decode_step(q, k, v, log_alpha, beta, state_in, state_out=None, out=None, *, read: str = "post",
+                l2norm: bool = False):
     """One decode step (``gdr_decode_step``). q, k [N, Hk, dk]; v [N, Hv, dv]; log_alpha,
     beta [N, Hv] fp32; state_in [N, Hv, dk, dv] fp32. ``state_out`` defaults to a new
-    tensor; pass ``state_in`` itself to update in place. Returns (out, state_out)."""
+    tensor; pass ``state_in`` itself to update in place. Returns (out, state_out).
+    ``l2norm`` normalises q and k in the kernel (``GDR_QK_L2NORM``)."""
+    return _decode(q, k, v, log_alpha, beta, None, None, state_in, state_out, out, read, l2norm)
+
+
+def decode_step_gated(q, k, v, a, b, A_log, dt_bias, state_in, state_out=None, out=None, *,
+                      read: str = "post", l2norm: bool = True):
+    """One decode step with the gates formed in the kernel (``gdr_decode_step_gated``): a, b
+    [N, Hv] fp32 raw inputs, A_log, dt_bias [Hv] fp32; the rest as ``decode_step``."""
+    return _decode(q, k, v, a, b, A_log, dt_bias, state_in, state_out, out, read, l2norm)
+
+
+def _decode(q, k, v, ga, gb, A_log, dt_bias, state_in, state_out, out, read, l2norm):
+    gated = A_log is not None or dt_bias is not None
+    na, nb = ("a", "b") if gated else ("log_alpha", "beta")
     _need(q, "q")
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
@@ -172,8 +217,11 @@ def decode_step(q, k, v, log_alpha, beta, state_in, state_out=None, out=None, *,
     Hv, dv = v.shape[1], v.shape[2]
     _need(k, "k", dt, (N, Hk, dk), dev)
     _need(v, "v", dt, (N, Hv, dv), dev)
-    _need(log_alpha, "log_alpha", torch.float32, (N, Hv), dev)
-    _need(beta, "beta", torch.float32, (N, Hv), dev)
+    _need(ga, na, torch.float32, (N, Hv), dev)
+    _need(gb, nb, torch.float32, (N, Hv), dev)
+    if gated:
+        _need(A_log, "A_log", torch.float32, (Hv,), dev)
+        _need(dt_bias, "dt_bias", torch.float32, (Hv,), dev)
     _need(state_in, "state_in", torch.float32, (N, Hv, dk, dv), dev)
     if state_out is None:
         state_out = torch.empty_like(state_in)
@@ -185,10 +233,15 @@ def decode_step(q, k, v, log_alpha, beta, state_in, state_out=None, out=None, *,
         _need(out, "out", dt, (N, Hv, dv), dev)
     if read not in ("pre", "post"):
         raise ValueError("read must be 'pre' or 'post'")
-    dims = DecodeDims(N, Hk, Hv, dk, dv, code, GDR_READ_PRE if read == "pre" else 0)
-    _check(lib().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                 _ptr(state_in), _ptr(state_out), _ptr(out), ctypes.byref(dims),
-                                 _stream(q)))
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_QK_L2NORM if l2norm else 0)
+    dims = DecodeDims(N, Hk, Hv, dk, dv, code, flags)
+    if gated:
+        _check(lib().gdr_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(A_log),
+                                           _ptr(dt_bias), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                           ctypes.byref(dims), _stream(q)))
+    else:
+        _check(lib().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(state_in),
+                                     _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q)))
     return out, state_out
 
 

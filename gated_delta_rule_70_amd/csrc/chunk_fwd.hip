@@ -88,7 +88,8 @@ struct SeqView {
 template <typename E, int C, int DK>
 __device__ __forceinline__ void prefetch_chunk(Prefetch<E, C, DK> &pf, const SeqView &sv, int64_t c,
                                                const char *kb, const char *qb, const char *vb,
-                                               const float *ab, const float *bb, int64_t dv, int dcol0) {
+                                               const float *ab, const float *bb, int64_t dv, int dcol0,
+                                               const float *A_log, const float *dt_bias, int64_t head) {
     typedef Prefetch<E, C, DK> PF;
     const int tid = threadIdx.x;
     const uint4 z = make_uint4(0, 0, 0, 0);
@@ -126,8 +127,9 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<E, C, DK> &pf, const Seq
         const int64_t pos = c * C + tid;
         if (pos < sv.len) {
             const int64_t t = sv.token(pos);
-            pf.la = ab[t];
-            pf.beta = bb[t];
+            // raw gate inputs become log alpha and beta here when A_log is given
+            pf.la = A_log ? gate_log_alpha(ab[t], A_log, dt_bias, head) : ab[t];
+            pf.beta = A_log ? gate_beta(bb[t]) : bb[t];
         }
     }
 }
@@ -157,6 +159,29 @@ __device__ __forceinline__ void store_chunk(const Prefetch<E, C, DK> &pf, Smem<E
     if (tid < C) {
         sm.la[tid] = pf.la;
         sm.beta[tid] = pf.beta;
+    }
+}
+
+// Unit-norm rows: every row of K and Q in LDS divided by max(||row||, eps) (rows past the
+// end are zero and stay zero). One wave per row at a time; each lane holds DK / 64 elements.
+template <typename E, int C, int DK>
+__device__ __forceinline__ void normalize_rows(Smem<E, C, DK> &sm) {
+    typedef Smem<E, C, DK> SM;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int PER = DK / 64;
+    for (int row = wave; row < 2 * C; row += kThreads / 64) {
+        E *p = (row < C ? sm.K : sm.Q) + (row % C) * SM::KP;
+        float x[PER], s = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            x[e] = to_f(p[lane + 64 * e]);
+            s += x[e] * x[e];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+        const float r = 1.f / fmaxf(sqrtf(s), kL2Eps);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) p[lane + 64 * e] = from_f<E>(x[e] * r);
     }
 }
 
@@ -298,6 +323,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
     sv.rev = (a.flags & kFlagReverse) != 0;
     const bool pre = (a.flags & kFlagReadPre) != 0;
     const bool acc_out = (a.flags & kFlagAccumulate) != 0;
+    const bool l2 = (a.flags & kFlagL2Norm) != 0;
     const int64_t nchunks = (sv.len + C - 1) / C;
     const int dcol0 = tile * kDvTile;
 
@@ -331,13 +357,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 
     Prefetch<E, C, DK> pf;
     if (nchunks > 0) {
-        prefetch_chunk<E, C, DK>(pf, sv, 0, kb, qb, vb, ab, bb, a.dv, dcol0);
+        prefetch_chunk<E, C, DK>(pf, sv, 0, kb, qb, vb, ab, bb, a.dv, dcol0, a.A_log, a.dt_bias, head);
         store_chunk<E, C, DK>(pf, sm);
     }
     __syncthreads();
+    if (l2 && nchunks > 0) {
+        normalize_rows<E, C, DK>(sm);
+        __syncthreads();
+    }
 
     for (int64_t c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) prefetch_chunk<E, C, DK>(pf, sv, c + 1, kb, qb, vb, ab, bb, a.dv, dcol0);
+        if (c + 1 < nchunks) prefetch_chunk<E, C, DK>(pf, sv, c + 1, kb, qb, vb, ab, bb, a.dv, dcol0, a.A_log, a.dt_bias, head);
 
         if (wave == 0) gate_cumsum<E, C, DK>(sm);
         __syncthreads();
@@ -437,6 +467,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
         if (c + 1 < nchunks) {
             store_chunk<E, C, DK>(pf, sm);
             __syncthreads();
+            if (l2) {
+                normalize_rows<E, C, DK>(sm);
+                __syncthreads();
+            }
         }
     }
 
@@ -473,7 +507,8 @@ hipError_t launch_dk(const ChunkArgs &a, int chunk, int dk, hipStream_t s) {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream) {
     if (a.units == 0 || a.ntiles == 0) return hipSuccess;
-    if (chunk_fwd_fast_supported(dtype, chunk, dk)) return launch_chunk_fwd_fast(a, stream);
+    if (chunk_fwd_fast_supported(dtype, chunk, dk) && !a.A_log && !(a.flags & kFlagL2Norm))
+        return launch_chunk_fwd_fast(a, stream);
     if (dtype == kDtypeBf16) return launch_dk<__bf16>(a, chunk, dk, stream);
     return launch_dk<float>(a, chunk, dk, stream);
 }

@@ -11,6 +11,10 @@
 // registers between the read and the write, so state_out may equal state_in. The
 // state is streamed once in and once out with 16-byte non-temporal accesses: the
 // kernel is bound by HBM bandwidth, and the reductions over d_k go through LDS.
+//
+// With unit-norm rows requested, q and k enter as r_q q and r_k k (r = 1 / max(||row||,
+// eps)); the scales are applied to the reduced x, y and k.q and to u in the update, so the
+// raw vectors are never rewritten. With raw gates, log alpha and beta are formed here.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     __shared__ float sk[DK], sq[DK], sv[DV];
     __shared__ f4 px[RG][CG], py[RG][CG];
-    __shared__ float skq;
+    __shared__ float skq, srk, srq;
 
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
@@ -62,16 +66,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         sq[i] = ld_f(qp, i);
     }
     for (int i = tid; i < DV; i += kThreads) sv[i] = ld_f(vp, i);
-    const float alpha = __expf(a.log_alpha[w]);
-    const float beta = a.beta[w];
+    const float alpha = __expf(a.A_log ? gate_log_alpha(a.log_alpha[w], a.A_log, a.dt_bias, head) : a.log_alpha[w]);
+    const float beta = a.A_log ? gate_beta(a.beta[w]) : a.beta[w];
+    const bool l2 = (a.flags & kFlagL2Norm) != 0;
     __syncthreads();
 
-    if (tid < 64) {  // k . q by wave 0
-        float s = 0.f;
-        for (int i = tid; i < DK; i += 64) s += sk[i] * sq[i];
+    if (tid < 64) {  // k . q, and the row norms, by wave 0
+        float s = 0.f, skk = 0.f, sqq = 0.f;
+        for (int i = tid; i < DK; i += 64) {
+            s += sk[i] * sq[i];
+            skk += sk[i] * sk[i];
+            sqq += sq[i] * sq[i];
+        }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-        if (tid == 0) skq = s;
+        for (int off = 32; off > 0; off >>= 1) {
+            s += __shfl_xor(s, off, 64);
+            skk += __shfl_xor(skk, off, 64);
+            sqq += __shfl_xor(sqq, off, 64);
+        }
+        if (tid == 0) {
+            const float rk = l2 ? 1.f / fmaxf(sqrtf(skk), kL2Eps) : 1.f;
+            const float rq = l2 ? 1.f / fmaxf(sqrtf(sqq), kL2Eps) : 1.f;
+            skq = s * rk * rq;
+            srk = rk;
+            srq = rq;
+        }
     }
 
     f4 x = {0.f, 0.f, 0.f, 0.f}, y = x;
@@ -90,12 +109,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         x += px[j][cg];
         y += py[j][cg];
     }
+    const float rk = srk, rq = srq;
+    x *= rk;  // x = H^T k with the normalised k
+    y *= rq;
     const f4 v4 = {sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]};
     const f4 u = beta * (v4 - alpha * x);
+    const f4 uk = rk * u;  // the normalised k's scale, moved onto u for the update
 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const f4 r = alpha * h[i] + sk[rg * RPT + i] * u;
+        const f4 r = alpha * h[i] + sk[rg * RPT + i] * uk;
         __builtin_nontemporal_store(r, sout + (rg * RPT + i) * CG + cg);
     }
     if (rg == 0) {

@@ -51,6 +51,20 @@ int64_t prod(std::initializer_list<int64_t> xs) {
 
 int64_t elem_size(int32_t dtype) { return dtype == GDR_BF16 ? 2 : 4; }
 
+// The names the two gate arguments carry in messages.
+struct GateNames {
+    const char *a, *b;
+};
+
+gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                        const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
+                        const gdr_chunk_dims_t *dims, void *stream);
+gdr_status_t decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                         const float *state_in, float *state_out, void *out, const gdr_decode_dims_t *dims,
+                         void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -79,11 +93,44 @@ gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v, const fl
                            const float *beta, const float *h0, const int32_t *cu_seqlens,
                            int32_t chunk, void *out, float *hT, const gdr_chunk_dims_t *dims,
                            void *stream) {
+    return chunk_impl(q, k, v, log_alpha, beta, nullptr, nullptr, false, h0, cu_seqlens, chunk, out, hT, dims,
+                      stream);
+}
+
+gdr_status_t gdr_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *a, const float *b,
+                                 const float *A_log, const float *dt_bias, const float *h0,
+                                 const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
+                                 const gdr_chunk_dims_t *dims, void *stream) {
+    return chunk_impl(q, k, v, a, b, A_log, dt_bias, true, h0, cu_seqlens, chunk, out, hT, dims, stream);
+}
+
+gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                             const float *beta, const float *state_in, float *state_out, void *out,
+                             const gdr_decode_dims_t *dims, void *stream) {
+    return decode_impl(q, k, v, log_alpha, beta, nullptr, nullptr, false, state_in, state_out, out, dims, stream);
+}
+
+gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v, const float *a, const float *b,
+                                   const float *A_log, const float *dt_bias, const float *state_in,
+                                   float *state_out, void *out, const gdr_decode_dims_t *dims, void *stream) {
+    return decode_impl(q, k, v, a, b, A_log, dt_bias, true, state_in, state_out, out, dims, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                        const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
+                        const gdr_chunk_dims_t *dims, void *stream) {
     g_last_error[0] = '\0';
+    const GateNames gn = gated ? GateNames{"a", "b"} : GateNames{"log_alpha", "beta"};
     if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
     const gdr_chunk_dims_t d = *dims;
     if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
-    if (d.flags & ~(GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE)) return fail(GDR_ERR_FLAGS, "flags 0x%x has unknown bits", d.flags);
+    if (d.flags & ~(GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE | GDR_QK_L2NORM))
+        return fail(GDR_ERR_FLAGS, "flags 0x%x has unknown bits", d.flags);
     if (chunk != 16 && chunk != 32 && chunk != 64) return fail(GDR_ERR_CHUNK, "chunk %d is not 16, 32 or 64", chunk);
     if (d.B < 0 || d.T < 0) return fail(GDR_ERR_DIMS, "B (%lld) and T (%lld) must be >= 0", (long long)d.B, (long long)d.T);
     if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
@@ -102,20 +149,24 @@ gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v, const fl
         return fail(GDR_ERR_DIMS, "sizes overflow");
     if (nq > 0 && (!q || !k)) return fail(GDR_ERR_NULL, "q or k is NULL");
     if (nv > 0 && (!v || !out)) return fail(GDR_ERR_NULL, "v or out is NULL");
-    if (ng > 0 && (!log_alpha || !beta)) return fail(GDR_ERR_NULL, "log_alpha or beta is NULL");
+    if (ng > 0 && (!log_alpha || !beta)) return fail(GDR_ERR_NULL, "%s or %s is NULL", gn.a, gn.b);
+    if (gated && (!A_log || !dt_bias)) return fail(GDR_ERR_NULL, "A_log or dt_bias is NULL");
+    if ((A_log && !aligned(A_log, 4)) || (dt_bias && !aligned(dt_bias, 4)))
+        return fail(GDR_ERR_ALIGN, "A_log or dt_bias is not 4-byte aligned");
     const void *al16[] = {q, k, v, out, h0, hT};
     const char *al16n[] = {"q", "k", "v", "out", "h0", "hT"};
     for (int i = 0; i < 6; ++i)
         if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
     if ((log_alpha && !aligned(log_alpha, 4)) || (beta && !aligned(beta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
-        return fail(GDR_ERR_ALIGN, "log_alpha, beta or cu_seqlens is not 4-byte aligned");
+        return fail(GDR_ERR_ALIGN, "%s, %s or cu_seqlens is not 4-byte aligned", gn.a, gn.b);
 
     const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
-    const Range ra = rng("log_alpha", log_alpha, ng * 4), rb = rng("beta", beta, ng * 4);
+    const Range ra = rng(gn.a, log_alpha, ng * 4), rb = rng(gn.b, beta, ng * 4);
     const Range rh0 = rng("h0", h0, ns * 4), rhT = rng("hT", hT, ns * 4);
     const Range rcu = rng("cu_seqlens", cu_seqlens, cu_seqlens ? (nseq + 1) * 4 : 0);
     const Range ro = rng("out", out, nv * es);
-    const Range ins[] = {rq, rk, rv, ra, rb, rh0, rcu};
+    const Range rA = rng("A_log", A_log, gated ? d.Hv * 4 : 0), rdt = rng("dt_bias", dt_bias, gated ? d.Hv * 4 : 0);
+    const Range ins[] = {rq, rk, rv, ra, rb, rh0, rcu, rA, rdt};
     for (const Range &r : ins) {
         if (overlap(ro, r)) return fail(GDR_ERR_ALIAS, "out overlaps %s", r.name);
         if (&r != &ins[5] && overlap(rhT, r)) return fail(GDR_ERR_ALIAS, "hT overlaps %s", r.name);
@@ -126,6 +177,8 @@ gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v, const fl
     gdr::ChunkArgs a;
     a.q = q; a.k = k; a.v = v;
     a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0;
+    a.A_log = gated ? A_log : nullptr;
+    a.dt_bias = gated ? dt_bias : nullptr;
     a.cu_seqlens = cu_seqlens;
     a.out = out; a.hT = hT;
     a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv; a.dv = d.dv;
@@ -139,14 +192,17 @@ gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v, const fl
     return GDR_OK;
 }
 
-gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
-                             const float *beta, const float *state_in, float *state_out, void *out,
-                             const gdr_decode_dims_t *dims, void *stream) {
+gdr_status_t decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                         const float *state_in, float *state_out, void *out, const gdr_decode_dims_t *dims,
+                         void *stream) {
     g_last_error[0] = '\0';
+    const GateNames gn = gated ? GateNames{"a", "b"} : GateNames{"log_alpha", "beta"};
     if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
     const gdr_decode_dims_t d = *dims;
     if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
-    if (d.flags & ~GDR_READ_PRE) return fail(GDR_ERR_FLAGS, "flags 0x%x: decode takes GDR_READ_PRE only", d.flags);
+    if (d.flags & ~(GDR_READ_PRE | GDR_QK_L2NORM))
+        return fail(GDR_ERR_FLAGS, "flags 0x%x: decode takes GDR_READ_PRE and GDR_QK_L2NORM only", d.flags);
     if (d.N < 0) return fail(GDR_ERR_DIMS, "N (%lld) must be >= 0", (long long)d.N);
     if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
     if ((d.dk != 64 && d.dk != 128) || (d.dv != 64 && d.dv != 128))
@@ -158,17 +214,21 @@ gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const 
     if (d.N * d.Hv > INT32_MAX) return fail(GDR_ERR_DIMS, "N * Hv too large");
     if (d.N > 0 && (!q || !k || !v || !log_alpha || !beta || !state_in || !state_out || !out))
         return fail(GDR_ERR_NULL, "a tensor pointer is NULL");
+    if (gated && (!A_log || !dt_bias)) return fail(GDR_ERR_NULL, "A_log or dt_bias is NULL");
+    if ((A_log && !aligned(A_log, 4)) || (dt_bias && !aligned(dt_bias, 4)))
+        return fail(GDR_ERR_ALIGN, "A_log or dt_bias is not 4-byte aligned");
     const void *al16[] = {q, k, v, out, state_in, state_out};
     const char *al16n[] = {"q", "k", "v", "out", "state_in", "state_out"};
     for (int i = 0; i < 6; ++i)
         if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
     if ((log_alpha && !aligned(log_alpha, 4)) || (beta && !aligned(beta, 4)))
-        return fail(GDR_ERR_ALIGN, "log_alpha or beta is not 4-byte aligned");
+        return fail(GDR_ERR_ALIGN, "%s or %s is not 4-byte aligned", gn.a, gn.b);
     const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
-    const Range ra = rng("log_alpha", log_alpha, ng * 4), rb = rng("beta", beta, ng * 4);
+    const Range ra = rng(gn.a, log_alpha, ng * 4), rb = rng(gn.b, beta, ng * 4);
     const Range rsi = rng("state_in", state_in, ns * 4), rso = rng("state_out", state_out, ns * 4);
     const Range ro = rng("out", out, nv * es);
-    const Range ins[] = {rq, rk, rv, ra, rb, rsi};
+    const Range rA = rng("A_log", A_log, gated ? d.Hv * 4 : 0), rdt = rng("dt_bias", dt_bias, gated ? d.Hv * 4 : 0);
+    const Range ins[] = {rq, rk, rv, ra, rb, rsi, rA, rdt};
     for (const Range &r : ins) {
         if (overlap(ro, r)) return fail(GDR_ERR_ALIAS, "out overlaps %s", r.name);
         if (&r != &ins[5] && overlap(rso, r)) return fail(GDR_ERR_ALIAS, "state_out overlaps %s", r.name);
@@ -179,6 +239,8 @@ gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const 
     gdr::DecodeArgs a;
     a.q = q; a.k = k; a.v = v;
     a.log_alpha = log_alpha; a.beta = beta;
+    a.A_log = gated ? A_log : nullptr;
+    a.dt_bias = gated ? dt_bias : nullptr;
     a.state_in = state_in; a.state_out = state_out; a.out = out;
     a.N = d.N; a.Hk = d.Hk; a.Hv = d.Hv;
     a.flags = d.flags;
@@ -186,6 +248,10 @@ gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const 
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return GDR_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 gdr_status_t gdr_selftest_mfma(const float *a, const float *b, float *d, void *stream) {
     g_last_error[0] = '\0';

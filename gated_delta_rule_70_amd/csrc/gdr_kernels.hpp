@@ -9,12 +9,17 @@ namespace gdr {
 constexpr uint32_t kFlagReadPre = 1u;
 constexpr uint32_t kFlagReverse = 2u;
 constexpr uint32_t kFlagAccumulate = 4u;
+constexpr uint32_t kFlagL2Norm = 8u;  // q and k rows divided by max(||row||, kL2Eps) first
+constexpr float kL2Eps = 1e-6f;
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBf16 = 1;
 
+// With A_log (and dt_bias) set, log_alpha and beta hold the raw gate inputs a and b and the
+// kernels form log alpha = -exp(A_log[h]) softplus(a + dt_bias[h]) and beta = sigmoid(b).
 struct ChunkArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta, *h0;
+    const float *A_log, *dt_bias;
     const int32_t *cu_seqlens;
     void *out;
     float *hT;
@@ -27,6 +32,7 @@ struct ChunkArgs {
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta;
+    const float *A_log, *dt_bias;  // as in ChunkArgs
     const float *state_in;
     float *state_out;
     void *out;
@@ -38,6 +44,15 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hi
 bool chunk_fwd_fast_supported(int dtype, int chunk, int dk);
 hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
+// the gates of one token of value head h from their raw inputs (see ChunkArgs)
+__device__ __forceinline__ float gate_log_alpha(float a, const float *A_log, const float *dt_bias, int64_t h) {
+    const float x = a + dt_bias[h];
+    // softplus without overflow: max(x, 0) + log1p(exp(-|x|))
+    const float sp = fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+    return -__expf(A_log[h]) * sp;
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.f / (1.f + __expf(-b)); }
+
 hipError_t launch_selftest_mfma(const float *a, const float *b, float *d, hipStream_t stream);
 
 }  // namespace gdr

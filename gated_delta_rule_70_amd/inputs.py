@@ -138,6 +138,45 @@ def decode_case(*, N=4, Hk=2, Hv=4, dk=128, dv=128, steps=1, dtype=torch.bfloat1
 # ---------------------------------------------------------------------------
 # The five workloads. Seeds are 1000 + workload index.
 
+@dataclass
+class RawCase:
+    """Inputs of the fused prologue: raw q, k (rows of varied length), raw gate inputs a, b
+    and per-value-head gate parameters A_log, dt_bias."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    a: torch.Tensor
+    b: torch.Tensor
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    h0: torch.Tensor | None
+    cu_seqlens: torch.Tensor | None
+
+
+def raw_case(*, B=1, T=256, Hk=2, Hv=None, dk=64, dv=64, dtype=torch.float32, seed=0,
+             h0_std=0.0, lengths=None) -> RawCase:
+    """q, k ~ N(0, 1) times a per-row length factor U(0.25, 4) (not normalised); v ~ N(0, 1);
+    a, b ~ N(0, 1); A_log = log U(1, 16) and dt_bias ~ U(-4, 1) per value head (the range
+    softplus(a + dt_bias) takes at the pages' dt_bias initialisation, 0.001..0.1, and above)."""
+    Hv = Hk if Hv is None else Hv
+    g = _gen(seed + 50000)
+    cu = None
+    if lengths is not None:
+        assert B == 1
+        T = int(sum(lengths))
+        cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    nseq = B if cu is None else len(lengths)
+    A_log = torch.log(torch.rand(Hv, generator=g) * 15.0 + 1.0)
+    dt_bias = torch.rand(Hv, generator=g) * 5.0 - 4.0
+    q = (_normal(g, (B, Hk, T, dk)) * (torch.rand(B, Hk, T, 1, generator=g) * 3.75 + 0.25)).to(dtype).contiguous()
+    k = (_normal(g, (B, Hk, T, dk)) * (torch.rand(B, Hk, T, 1, generator=g) * 3.75 + 0.25)).to(dtype).contiguous()
+    v = _normal(g, (B, Hv, T, dv)).to(dtype).contiguous()
+    a = _normal(g, (B, Hv, T)).contiguous()
+    b = _normal(g, (B, Hv, T)).contiguous()
+    h0 = _normal(g, (nseq, Hv, dk, dv), h0_std).contiguous() if h0_std > 0 else None
+    return RawCase(q, k, v, a, b, A_log.contiguous(), dt_bias.contiguous(), h0, cu)
+
+
 WORKLOADS = {
     0: "gdr-fwd-fp32-B1-H2-T256-d64-c64",
     1: "gdr-chunk-fwd-bf16-B4-H16-T4096-d128-c64",

@@ -24,8 +24,20 @@
  *   - Value head j reads query/key head j / (Hv / Hk) (key heads shared by groups of
  *     value heads, as in `heads` of BidirectionalGatedDeltaNet2 on the "tiny_gdn/fugue.py"
  *     page and the head-profile checks on the "flashrt-structures fused_layer.py" page).
- *   - log_alpha must be <= 0 and finite (a decay); q and k are used as given (callers
- *     normalise them if they want unit keys).
+ *   - log_alpha must be <= 0 and finite (a decay); q and k are used as given unless
+ *     GDR_QK_L2NORM is set.
+ *
+ * The fused prologue (the steps the pages run just before the recurrence):
+ *   - GDR_QK_L2NORM: each row of q and of k (one token of one key head) is first divided by
+ *     max(||row||_2, 1e-6), as F.normalize(x, dim=-1, eps=1e-6) does on the
+ *     "nested-learning self_modifying.py" page, and as the kernels of the "flashrt-structures
+ *     fused_layer.py" page (use_qk_l2norm) and the "tiny_gdn/fugue.py" page
+ *     (use_qk_l2norm_in_kernel) do inside the core.
+ *   - the *_gated entry points take the raw gate inputs a, b [..][Hv] and per-value-head
+ *     parameters A_log, dt_bias [Hv] and form
+ *         log_alpha = -exp(A_log[h]) * softplus(a + dt_bias[h]),   beta = sigmoid(b)
+ *     (compute_gates on the "sparse-delta-memory layer.py" page; the gating step before the
+ *     core on the "flashrt-structures fused_layer.py" page).
  */
 #ifndef GDR_H_
 #define GDR_H_
@@ -58,6 +70,7 @@ typedef enum gdr_dtype {
 #define GDR_READ_PRE 1u   /* o_t = H_{t-1}^T q_t instead of H_t^T q_t */
 #define GDR_REVERSE 2u    /* scan each sequence from its last token to its first */
 #define GDR_ACCUMULATE 4u /* out += o instead of out = o */
+#define GDR_QK_L2NORM 8u  /* normalise each row of q and k to unit L2 norm first */
 
 typedef struct gdr_chunk_dims {
     int64_t B;        /* batch rows; must be 1 when cu_seqlens is given */
@@ -68,7 +81,7 @@ typedef struct gdr_chunk_dims {
     int64_t dv;       /* value size: a multiple of 32, at most 256 */
     int64_t num_seqs; /* segments described by cu_seqlens (ignored when it is NULL) */
     int32_t dtype;    /* gdr_dtype_t of q, k, v and out */
-    uint32_t flags;   /* GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE */
+    uint32_t flags;   /* GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE | GDR_QK_L2NORM */
 } gdr_chunk_dims_t;
 
 typedef struct gdr_decode_dims {
@@ -78,7 +91,7 @@ typedef struct gdr_decode_dims {
     int64_t dk;     /* 64 or 128 */
     int64_t dv;     /* 64 or 128 */
     int32_t dtype;  /* gdr_dtype_t of q, k, v and out */
-    uint32_t flags; /* GDR_READ_PRE only */
+    uint32_t flags; /* GDR_READ_PRE | GDR_QK_L2NORM */
 } gdr_decode_dims_t;
 
 /*
@@ -121,6 +134,23 @@ gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v,
                            const gdr_chunk_dims_t *dims, void *stream);
 
 /*
+ * gdr_chunk_fwd_gated - gdr_chunk_fwd with the gates formed from their raw inputs in the
+ * kernel (see the fused prologue above), typically together with GDR_QK_L2NORM:
+ *
+ *   a, b        [B][Hv][T] fp32 raw decay input and raw write-gate logit (any sign)
+ *   A_log       [Hv] fp32, dt_bias [Hv] fp32: per value head
+ *
+ * Every other argument, flag and error as gdr_chunk_fwd; GDR_ERR_NULL also when A_log or
+ * dt_bias is NULL.
+ */
+gdr_status_t gdr_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                                 const float *a, const float *b,
+                                 const float *A_log, const float *dt_bias,
+                                 const float *h0, const int32_t *cu_seqlens, int32_t chunk,
+                                 void *out, float *hT,
+                                 const gdr_chunk_dims_t *dims, void *stream);
+
+/*
  * gdr_decode_step - one token of the recurrence for N independent sequences.
  *
  * The one-token recurrent core of `_decode_one` on the "flashrt-structures
@@ -142,6 +172,22 @@ gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v,
                              const float *log_alpha, const float *beta,
                              const float *state_in, float *state_out, void *out,
                              const gdr_decode_dims_t *dims, void *stream);
+
+/*
+ * gdr_decode_step_gated - gdr_decode_step with the gates formed from their raw inputs
+ * (see the fused prologue above):
+ *
+ *   a, b        [N][Hv] fp32 raw decay input and raw write-gate logit
+ *   A_log       [Hv] fp32, dt_bias [Hv] fp32: per value head
+ *
+ * Every other argument, flag and error as gdr_decode_step; GDR_ERR_NULL also when A_log or
+ * dt_bias is NULL.
+ */
+gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
+                                   const float *a, const float *b,
+                                   const float *A_log, const float *dt_bias,
+                                   const float *state_in, float *state_out, void *out,
+                                   const gdr_decode_dims_t *dims, void *stream);
 
 /* Static text for a status code. */
 const char *gdr_status_string(gdr_status_t status);

@@ -58,7 +58,7 @@ CHUNK_REJECTS = [
     (dict(dv=48), "GDR_ERR_UNSUPPORTED", "dv"),
     (dict(dv=512), "GDR_ERR_UNSUPPORTED", "dv"),
     (dict(dtype=7), "GDR_ERR_DTYPE", "dtype"),
-    (dict(flags=8), "GDR_ERR_FLAGS", "flags"),
+    (dict(flags=16), "GDR_ERR_FLAGS", "flags"),
     (dict(Hk=3, Hv=4), "GDR_ERR_DIMS", "Hv"),
     (dict(T=-1), "GDR_ERR_DIMS", "T"),
     (dict(B=2, cu=FAKE * 9, num_seqs=1), "GDR_ERR_DIMS", "cu_seqlens"),
@@ -108,6 +108,7 @@ DECODE_REJECTS = [
     (dict(dk=96), "GDR_ERR_UNSUPPORTED", "dk"),
     (dict(dv=256), "GDR_ERR_UNSUPPORTED", "dv"),
     (dict(flags=2), "GDR_ERR_FLAGS", "GDR_READ_PRE"),
+    (dict(flags=16), "GDR_ERR_FLAGS", "GDR_QK_L2NORM"),
     (dict(Hk=3), "GDR_ERR_DIMS", "Hv"),
     (dict(N=-2), "GDR_ERR_DIMS", "N"),
     (dict(si=None), "GDR_ERR_NULL", "NULL"),
@@ -122,3 +123,51 @@ DECODE_REJECTS = [
 def test_decode_rejects(over, status, text):
     st, msg = _decode(binding.load(), **over)
     assert st == status and text in msg, (st, msg)
+
+
+def _chunk_gated(lib, **over):
+    d = dict(B=1, T=128, Hk=2, Hv=2, dk=64, dv=64, num_seqs=0, dtype=1, flags=8)
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, a=FAKE * 4, b=FAKE * 5, A_log=FAKE * 10,
+               dt_bias=FAKE * 11, h0=None, cu=None, out=FAKE * 6, hT=None, chunk=64)
+    for k_, v_ in over.items():
+        (d if k_ in d else ptr)[k_] = v_
+    dims = binding.ChunkDims(d["B"], d["T"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["num_seqs"],
+                             d["dtype"], d["flags"])
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_chunk_fwd_gated(vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["a"]), vp(ptr["b"]),
+                                 vp(ptr["A_log"]), vp(ptr["dt_bias"]), vp(ptr["h0"]), vp(ptr["cu"]),
+                                 ptr["chunk"], vp(ptr["out"]), vp(ptr["hT"]), ctypes.byref(dims), None)
+    return binding.STATUS[st], lib.gdr_last_error().decode()
+
+
+GATED_REJECTS = [
+    (dict(A_log=None), "GDR_ERR_NULL", "A_log"),
+    (dict(dt_bias=None), "GDR_ERR_NULL", "dt_bias"),
+    (dict(a=None), "GDR_ERR_NULL", "a or b"),
+    (dict(A_log=FAKE * 10 + 2), "GDR_ERR_ALIGN", "A_log"),
+    (dict(out=FAKE * 10 - 64), "GDR_ERR_ALIAS", "out overlaps A_log"),
+    (dict(flags=16), "GDR_ERR_FLAGS", "flags"),
+    (dict(chunk=8), "GDR_ERR_CHUNK", "chunk"),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status,text", GATED_REJECTS, ids=[c[1] + ":" + c[2] for c in GATED_REJECTS])
+def test_chunk_fwd_gated_rejects(over, status, text):
+    st, msg = _chunk_gated(binding.load(), **over)
+    assert st == status and text in msg, (st, msg)
+
+
+@needs_lib
+def test_decode_gated_rejects():
+    lib = binding.load()
+    dims = binding.DecodeDims(4, 2, 4, 128, 128, 1, 8)
+    vp = ctypes.c_void_p
+    st = lib.gdr_decode_step_gated(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5), None,
+                                   vp(FAKE * 11), vp(FAKE * 8), vp(FAKE * 16), vp(FAKE * 6), ctypes.byref(dims),
+                                   None)
+    assert binding.STATUS[st] == "GDR_ERR_NULL" and "A_log" in lib.gdr_last_error().decode()
+    st = lib.gdr_decode_step_gated(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5), vp(FAKE * 10),
+                                   vp(FAKE * 11), vp(FAKE * 8), vp(FAKE * 16), vp(FAKE * 10 - 16),
+                                   ctypes.byref(dims), None)
+    assert binding.STATUS[st] == "GDR_ERR_ALIAS", lib.gdr_last_error().decode()

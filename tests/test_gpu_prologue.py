@@ -1,0 +1,168 @@
+"""Parity of the fused prologue (in-kernel q/k L2 normalisation, gates from raw inputs)
+with the fp64 oracle: ``oracle.prologue`` normalises and forms the gates in fp64, then
+runs the plain recurrence. Tolerances as in test_gpu_parity.py."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_70_amd import inputs
+from oracle import prologue
+
+pytestmark = pytest.mark.gpu
+
+FP32_ABS = 2e-4
+BF16_REL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def gdr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_70_amd import binding
+    binding.lib()
+    return binding
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(x, ref, dtype, what):
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == torch.float32:
+        e = float(np.max(np.abs(x - ref))) if x.size else 0.0
+        assert e <= FP32_ABS, "%s: max abs err %.3e > %.1e" % (what, e, FP32_ABS)
+    else:
+        e = float(np.linalg.norm(x - ref)) / max(float(np.linalg.norm(ref)), 1e-30)
+        assert e <= BF16_REL, "%s: rel Frobenius err %.3e > %.1e" % (what, e, BF16_REL)
+    return e
+
+
+def gpu_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+CHUNK = [
+    dict(B=2, T=200, Hk=2, Hv=2, dk=64, dv=64, dtype=torch.float32, chunk=64),
+    dict(B=1, T=333, Hk=2, Hv=4, dk=128, dv=64, dtype=torch.bfloat16, chunk=64),
+    dict(B=2, T=257, Hk=1, Hv=2, dk=128, dv=128, dtype=torch.bfloat16, chunk=64),
+    dict(B=1, T=150, Hk=2, Hv=2, dk=64, dv=32, dtype=torch.bfloat16, chunk=32),
+    dict(B=1, T=96, Hk=1, Hv=1, dk=128, dv=96, dtype=torch.float32, chunk=16),
+]
+
+
+def _ids(c):
+    return "B%d-T%d-Hk%d-Hv%d-dk%d-dv%d-%s-c%d" % (c["B"], c["T"], c["Hk"], c["Hv"], c["dk"], c["dv"],
+                                                 str(c["dtype"]).split(".")[-1], c["chunk"])
+
+
+def _unit_rows(c, dtype):
+    # gates alone: rows made unit length on the host (then rounded), so that the raw row
+    # lengths do not make the recurrence unstable; both sides get these same bytes
+    c.q = torch.from_numpy(prologue.l2_normalize(c.q)).float().to(dtype).contiguous()
+    c.k = torch.from_numpy(prologue.l2_normalize(c.k)).float().to(dtype).contiguous()
+    return c
+
+
+def _dev(c):
+    d = lambda t: None if t is None else t.cuda()
+    return [d(t) for t in (c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, c.h0, c.cu_seqlens)]
+
+
+@pytest.mark.parametrize("cfg", CHUNK, ids=_ids)
+@pytest.mark.parametrize("mode", ["l2", "gated", "gated+l2"])
+@pytest.mark.parametrize("read", ["post", "pre"])
+def test_chunk_prologue(gdr, cfg, mode, read):
+    cfg = dict(cfg)
+    chunk = cfg.pop("chunk")
+    c = inputs.raw_case(seed=3, h0_std=0.1, **cfg)
+    _say("prologue chunk %s %s %s" % (_ids(dict(cfg, chunk=chunk)), mode, read))
+    l2 = "l2" in mode
+    if not l2:
+        c = _unit_rows(c, cfg["dtype"])
+    q, k, v, a, b, A_log, dtb, h0, cu = _dev(c)
+    if "gated" in mode:
+        out, hT = gdr.chunk_fwd_gated(q, k, v, a, b, A_log, dtb, h0, cu, chunk=chunk, read=read, l2norm=l2)
+        ref_o, ref_h = prologue.scan_fused(c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, c.h0, read=read, l2norm=l2)
+    else:
+        # plain gates from the generator, raw rows normalised in the kernel
+        la = -torch.nn.functional.softplus(c.a) * 0.5
+        beta = torch.sigmoid(c.b)
+        out, hT = gdr.chunk_fwd(q, k, v, la.cuda(), beta.cuda(), h0, cu, chunk=chunk, read=read, l2norm=True)
+        ref_o, ref_h = prologue.scan_fused(c.q, c.k, c.v, la, beta, None, None, c.h0, read=read, l2norm=True)
+    torch.cuda.synchronize()
+    check(gpu_np(out), ref_o, cfg["dtype"], "o")
+    check(gpu_np(hT), ref_h, cfg["dtype"], "hT")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_chunk_prologue_varlen_reverse_accumulate(gdr, dtype):
+    lengths = [77, 1, 130, 0, 64, 200]
+    c = inputs.raw_case(B=1, Hk=2, Hv=4, dk=128, dv=64, dtype=dtype, seed=9, lengths=lengths)
+    _say("prologue varlen reverse accumulate %s" % dtype)
+    q, k, v, a, b, A_log, dtb, h0, cu = _dev(c)
+    base = torch.randn(v.shape, generator=torch.Generator().manual_seed(4)).to(dtype)
+    out = base.cuda()
+    gdr.chunk_fwd_gated(q, k, v, a, b, A_log, dtb, None, cu, chunk=64, read="pre", reverse=True,
+                        out=out, accumulate=True, want_state=False, l2norm=True)
+    acc = base.double().numpy().copy()
+    prologue.scan_fused(c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, None, c.cu_seqlens, read="pre",
+                        reverse=True, out=acc, want_state=False)
+    torch.cuda.synchronize()
+    check(gpu_np(out), acc, dtype, "o")
+
+
+def test_chunk_prologue_row_scale_invariance(gdr):
+    # the normalised path does not see a positive per-row rescaling of the raw q and k
+    c = inputs.raw_case(B=1, T=300, Hk=2, Hv=2, dk=128, dv=64, dtype=torch.float32, seed=5, h0_std=0.1)
+    q, k, v, a, b, A_log, dtb, h0, cu = _dev(c)
+    s = torch.rand(q.shape[:-1] + (1,), generator=torch.Generator().manual_seed(6)).cuda() * 20 + 0.05
+    o1, h1 = gdr.chunk_fwd_gated(q, k, v, a, b, A_log, dtb, h0, chunk=64)
+    o2, h2 = gdr.chunk_fwd_gated((q * s).contiguous(), (k / s).contiguous(), v, a, b, A_log, dtb, h0, chunk=64)
+    torch.cuda.synchronize()
+    assert float((o1 - o2).abs().max()) <= 2e-5 and float((h1 - h2).abs().max()) <= 2e-5
+
+
+DECODE = [
+    dict(N=3, Hk=2, Hv=4, dk=128, dv=128, dtype=torch.bfloat16),
+    dict(N=2, Hk=1, Hv=3, dk=64, dv=128, dtype=torch.float32),
+    dict(N=4, Hk=4, Hv=4, dk=128, dv=64, dtype=torch.float32),
+]
+
+
+@pytest.mark.parametrize("cfg", DECODE, ids=lambda c: "N%d-Hk%d-Hv%d-dk%d-dv%d-%s" % (
+    c["N"], c["Hk"], c["Hv"], c["dk"], c["dv"], str(c["dtype"]).split(".")[-1]))
+@pytest.mark.parametrize("mode", ["l2", "gated+l2", "gated"])
+@pytest.mark.parametrize("read", ["post", "pre"])
+def test_decode_prologue(gdr, cfg, mode, read):
+    cfg = dict(cfg)
+    N, Hk, Hv, dk, dv, dtype = (cfg[x] for x in ("N", "Hk", "Hv", "dk", "dv", "dtype"))
+    c = inputs.raw_case(B=N, T=3, Hk=Hk, Hv=Hv, dk=dk, dv=dv, dtype=dtype, seed=8, h0_std=0.3)
+    _say("prologue decode %s %s %s" % (cfg, mode, read))
+    l2 = "l2" in mode
+    if not l2:
+        c = _unit_rows(c, dtype)
+    state = c.h0.cuda()
+    ref_state = c.h0.double().numpy()
+    for t in range(3):
+        q, k, v = (x[:, :, t].contiguous() for x in (c.q, c.k, c.v))
+        a, b = c.a[:, :, t].contiguous(), c.b[:, :, t].contiguous()
+        if "gated" in mode:
+            o, state = gdr.decode_step_gated(q.cuda(), k.cuda(), v.cuda(), a.cuda(), b.cuda(), c.A_log.cuda(),
+                                             c.dt_bias.cuda(), state, state_out=state, read=read, l2norm=l2)
+            ref_o, ref_state = prologue.decode_fused(q, k, v, a, b, c.A_log, c.dt_bias, ref_state, read=read,
+                                                     l2norm=l2)
+        else:
+            la = -torch.nn.functional.softplus(a) * 0.5
+            beta = torch.sigmoid(b)
+            o, state = gdr.decode_step(q.cuda(), k.cuda(), v.cuda(), la.cuda(), beta.cuda(), state,
+                                       state_out=state, read=read, l2norm=True)
+            ref_o, ref_state = prologue.decode_fused(q, k, v, la, beta, None, None, ref_state, read=read)
+        torch.cuda.synchronize()
+        check(gpu_np(o), ref_o, dtype, "decode o step %d" % t)
+        check(gpu_np(state), ref_state, dtype, "decode state step %d" % t)
