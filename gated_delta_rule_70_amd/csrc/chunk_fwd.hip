@@ -507,8 +507,7 @@ hipError_t launch_dk(const ChunkArgs &a, int chunk, int dk, hipStream_t s) {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream) {
     if (a.units == 0 || a.ntiles == 0) return hipSuccess;
-    if (chunk_fwd_fast_supported(dtype, chunk, dk) && !a.A_log && !(a.flags & kFlagL2Norm))
-        return launch_chunk_fwd_fast(a, stream);
+    if (chunk_fwd_fast_supported(dtype, chunk, dk)) return launch_chunk_fwd_fast(a, stream);
     if (dtype == kDtypeBf16) return launch_dk<__bf16>(a, chunk, dk, stream);
     return launch_dk<float>(a, chunk, dk, stream);
 }

@@ -66,12 +66,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // raw buffer (one of three): K, Q [64 rows][256 B] and V [64 rows][64 B], swizzled; gates
 constexpr int kRawK = 0, kRawQ = 16384, kRawV = 32768, kRawLa = 36864, kRawBeta = 37120;
-// gate tables of the chunk, written into its raw buffer by the copy wave once the gates have
-// arrived: inclusive log2 cumsum b [64]; read-side log decay [64]; P and -A decay factors
-// (row factors [64], column factors [3][64] each); e^b, read scale, e^{bC-b} [64] each; e^{bC}
+// gate tables of the chunk, written into its raw buffer by the copy waves once their copies
+// have arrived: inclusive log2 cumsum b [64]; read-side log decay [64]; P and -A decay
+// factors (row factors [64], column factors [3][64] each); e^b, read scale, e^{bC-b} [64]
+// each; e^{bC}; beta [64]; the row scales of k and q (1 / max(||row||, eps), or 1 without
+// normalisation) [64] each
 constexpr int kTabB2 = 37376, kTabBread = 37632, kTabGP = 37888, kTabGA = 38912;
 constexpr int kTabEb = 39936, kTabEr = 40192, kTabEc = 40448, kTabGC = 40704;
-constexpr int kRawBytes = 40720;
+constexpr int kTabBeta = 40720, kTabRk = 40976, kTabRq = 41232;
+constexpr int kRawBytes = 41488;
 // derived buffer (one of two)
 constexpr int kDerP = 0;      // 6 P fragments (row tile, 32-deep slice) x 1 KB
 constexpr int kDerNA = 6144;  // -A: A10 (16-deep, 512 B), A2x (1 KB), A3x (1 KB), A32 (16-deep, 512 B)
@@ -341,12 +344,16 @@ __device__ __forceinline__ Gates read_gates(const char *raw) {
 }
 
 // ------------------------------------------------------------------ diagonal prep
+// kL2: the k rows are scaled to unit length (their scales are in the chunk's table)
+template <bool kL2, bool kPro>
 __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der, bool pre, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     (void)smem;
     (void)pre;
     const float *tb = reinterpret_cast<const float *>(raw + kTabB2);
-    const float *rb = reinterpret_cast<const float *>(raw + kRawBeta);
+    // beta: the table's (formed from a raw input) in the prologue form, else the copied input
+    const float *rb = reinterpret_cast<const float *>(raw + (kPro ? kTabBeta : kRawBeta));
+    const float *rk = reinterpret_cast<const float *>(raw + kTabRk);
     uint4 kf[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -356,15 +363,23 @@ __device__ __forceinline__ void prep_diag(char *smem, const char *raw, char *der
     floatx4 gkk[4];
     grams<4>(gkk, kf, kf, {0, 1, 2, 3}, {0, 1, 2, 3});
     // B_i = A_ii^T in accumulator layout: lane (g, c) holds A_ii[c][4g + r] (row 16i + c of
-    // the chunk, column 16i + 4g + r), from the symmetric Gram tile.
+    // the chunk, column 16i + 4g + r), from the symmetric Gram tile; the k row scales (1
+    // without normalisation) multiply row and column.
     floatx4 bt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const floatx4 gk = gkk[i];
         const floatx4 bcol = *reinterpret_cast<const floatx4 *>(tb + 16 * i + 4 * g);
-        const float brow = tb[16 * i + c], betarow = rb[16 * i + c];
+        floatx4 rcol = {1.f, 1.f, 1.f, 1.f};
+        float betarow = rb[16 * i + c];
+        if constexpr (kL2) {
+            rcol = *reinterpret_cast<const floatx4 *>(rk + 16 * i + 4 * g);
+            betarow *= rk[16 * i + c];
+        }
+        const float brow = tb[16 * i + c];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bt[i][r] = (4 * g + r < c) ? betarow * gk[r] * ex2(brow - bcol[r]) : 0.f;
+        for (int r = 0; r < 4; ++r)
+            bt[i][r] = (4 * g + r < c) ? betarow * rcol[r] * gk[r] * ex2(brow - bcol[r]) : 0.f;
     }
     // T_ii = (I + A_ii)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8), exact because the strictly
     // lower 16x16 A has A^16 = 0; all factors are polynomials in A, so they commute. On the
@@ -425,9 +440,75 @@ __device__ __forceinline__ void tile_refs(float b2, float &s0, float &s16, float
 // the chain: b = inclusive cumsum of log2 alpha over the chunk, the read-side log decay, the
 // decay factors of the P and -A tiles split at 16-row references (no exponent is positive),
 // and the chain's scalars.
-__device__ __forceinline__ void gate_tables(char *raw, bool pre) {
+// Row scales of a K or Q buffer ([64 rows][256 B], pieces swizzled within each row, which
+// does not matter for a sum of squares): lane = row, 1 / max(||row||, eps), or 1 when the
+// rows are used as given. Lane l reads the pieces of its row starting at piece l % 16, so
+// that the sixteen lanes of each LDS pass address sixteen different pieces.
+__device__ __forceinline__ float row_scales(const char *buf, float *dst, bool l2) {
     const int lane = threadIdx.x & 63;
-    const Gates gt = read_gates(raw);
+    float r = 1.f;
+    if (l2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const char *row = buf + lane * 256;
+        // all sixteen reads issued before the first use, so that their latencies overlap
+        uint4 w[16];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) w[p] = *reinterpret_cast<const uint4 *>(row + (((p + lane) & 15) << 4));
+        __builtin_amdgcn_sched_barrier(0);
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const unsigned u[4] = {w[p].x, w[p].y, w[p].z, w[p].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // two squares per instruction, accumulated in fp32 (four independent sums)
+                const bf16x2 x = __builtin_bit_cast(bf16x2, u[e]);
+                s[e] = __builtin_amdgcn_fdot2_f32_bf16(x, x, s[e], false);
+            }
+        }
+        const float ss = (s[0] + s[1]) + (s[2] + s[3]);
+        r = 1.f / fmaxf(sqrtf(ss), kL2Eps);
+    }
+    dst[lane] = r;
+    return r;
+}
+// With row scales, the chain's scalars of the chunk take them (the chain then needs no extra
+// product): e^b and e^{bC-b} those of k, the read scale those of q. The prep waves apply
+// them where they read K and to the rows of P.
+__device__ __forceinline__ void fold_row_scales(char *raw) {
+    const int lane = threadIdx.x & 63;
+    const float rk = reinterpret_cast<const float *>(raw + kTabRk)[lane];
+    const float rq = reinterpret_cast<const float *>(raw + kTabRq)[lane];
+    reinterpret_cast<float *>(raw + kTabEb)[lane] *= rk;
+    reinterpret_cast<float *>(raw + kTabEc)[lane] *= rk;
+    reinterpret_cast<float *>(raw + kTabEr)[lane] *= rq;
+}
+
+// Raw gate inputs of a gated call: the per-head parameters and the chunk's last valid row
+// (rows past it are padding, with no decay and no write).
+struct RawGates {
+    bool raw;        // false: the gates arrive as log alpha and beta
+    float nea, dtb;  // -exp(A_log[h]) and dt_bias[h] of the workgroup's value head
+    int rmax;
+};
+template <bool kPro>
+__device__ __forceinline__ void gate_tables(char *raw, bool pre, const RawGates &rg) {
+    const int lane = threadIdx.x & 63;
+    Gates gt;
+    {
+        const float x = reinterpret_cast<const float *>(raw + kRawLa)[lane];
+        const float y = reinterpret_cast<const float *>(raw + kRawBeta)[lane];
+        const bool valid = lane <= rg.rmax;
+        float la = x, beta = y;
+        if (rg.raw) {
+            la = valid ? rg.nea * softplus_f(x + rg.dtb) : 0.f;
+            beta = valid ? gate_beta(y) : 0.f;
+        }
+        gt.la2 = la * kLog2e;
+        gt.beta = beta;
+        gt.b2 = wave_cumsum(gt.la2);
+    }
+    if constexpr (kPro) reinterpret_cast<float *>(raw + kTabBeta)[lane] = gt.beta;
     float *tb = reinterpret_cast<float *>(raw + kTabB2);
     float *tr = reinterpret_cast<float *>(raw + kTabBread);
     float *gp = reinterpret_cast<float *>(raw + kTabGP);
@@ -458,13 +539,16 @@ __device__ __forceinline__ void gate_tables(char *raw, bool pre) {
 }
 
 // ------------------------------------------------------------------ P prep (row tiles I0 .. I1-1)
-template <int I0, int I1>
+template <int I0, int I1, bool kL2>
 __device__ __forceinline__ void prep_p(const char *raw, char *der, bool pre, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     const float *gw = reinterpret_cast<const float *>(raw + kTabGP);
     // log decay of the columns and read-side log decay of the rows, for the diagonal tiles
     const float *tb = reinterpret_cast<const float *>(raw + kTabB2);
     const float *tr = reinterpret_cast<const float *>(raw + kTabBread);
+    // with unit-norm rows, the k row scales multiply the columns and the q row scales the rows
+    const float *rk = reinterpret_cast<const float *>(raw + kTabRk);
+    const float *rq = reinterpret_cast<const float *>(raw + kTabRq);
     uint4 kf[I1][4], qf[I1][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -495,15 +579,18 @@ __device__ __forceinline__ void prep_p(const char *raw, char *der, bool pre, con
     for (int i = I0; i < I1; ++i) {
         // row 16i + c of this lane: its read decay and its row factor
         const float br = tr[16 * i + c];
-        const float rowf = gw[16 * i + c];
+        const float rqrow = kL2 ? rq[16 * i + c] : 1.f;
+        const float rowf = gw[16 * i + c] * rqrow;
 #pragma unroll
         for (int j = 0; j <= i; ++j) {
             // transposed tile: lane holds row 16i + c, columns 16j + 4g + r
             const floatx4 gq = gqk[(i * (i + 1) - I0 * (I0 + 1)) / 2 + j];
             floatx4 pv;
+            floatx4 rcol = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (kL2) rcol = *reinterpret_cast<const floatx4 *>(rk + 16 * j + 4 * g);
             if (j < i) {
                 const floatx4 cf = *reinterpret_cast<const floatx4 *>(gw + 64 * i + 16 * j + 4 * g);
-                pv = rowf * cf * gq;
+                pv = rowf * cf * rcol * gq;
             } else {
                 // diagonal tile: columns 16i + 4g + r against row 16i + c
                 const floatx4 bcol = *reinterpret_cast<const floatx4 *>(tb + 16 * i + 4 * g);
@@ -511,7 +598,7 @@ __device__ __forceinline__ void prep_p(const char *raw, char *der, bool pre, con
                 for (int r = 0; r < 4; ++r) {
                     const int cc = 4 * g + r;
                     const bool keep = pre ? (cc < c) : (cc <= c);
-                    pv[r] = keep ? gq[r] * ex2(br - bcol[r]) : 0.f;
+                    pv[r] = keep ? rqrow * rcol[r] * gq[r] * ex2(br - bcol[r]) : 0.f;
                 }
             }
             *reinterpret_cast<uint2 *>(pf + pf_index(i, j >> 1) * 1024 + lane * 16 + 8 * (j & 1)) = pack4(pv);
@@ -520,9 +607,11 @@ __device__ __forceinline__ void prep_p(const char *raw, char *der, bool pre, con
 }
 
 // ------------------------------------------------------------------ A prep
+template <bool kL2>
 __device__ __forceinline__ void prep_a(const char *raw, char *der, const RowFragOffsets &ro) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     const float *gw = reinterpret_cast<const float *>(raw + kTabGA);
+    const float *rk = reinterpret_cast<const float *>(raw + kTabRk);  // k row scales (1 without normalisation)
     uint4 kf[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -534,13 +623,14 @@ __device__ __forceinline__ void prep_a(const char *raw, char *der, const RowFrag
     grams<6>(gkk, kf, kf, {0, 0, 1, 0, 1, 2}, {1, 2, 2, 3, 3, 3});
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
-        const float ar = gw[16 * i + c];  // row factor of row 16i + c
+        const float ar = kL2 ? gw[16 * i + c] * rk[16 * i + c] : gw[16 * i + c];  // row factor of row 16i + c
 #pragma unroll
         for (int j = 0; j < i; ++j) {
             // transposed tile: lane holds row 16i + c, columns 16j + 4g + r
             const floatx4 gk = gkk[(i * (i - 1)) / 2 + j];
             const floatx4 cf = *reinterpret_cast<const floatx4 *>(gw + 64 * i + 16 * j + 4 * g);
-            const floatx4 av = (-ar) * cf * gk;
+            floatx4 av = (-ar) * cf * gk;
+            if constexpr (kL2) av *= *reinterpret_cast<const floatx4 *>(rk + 16 * j + 4 * g);
             int aoff;
             if (i == 1) aoff = lane * 8;                           // A10, 16-deep
             else if (i == 2) aoff = 512 + lane * 16 + 8 * j;       // A20 | A21
@@ -590,6 +680,9 @@ __device__ __forceinline__ void write_back(const char *stg, const char *prv, __b
     }
 }
 
+// kPro: the form that takes the fused prologue (unit-norm q/k rows, gates from raw inputs);
+// the plain form carries none of its code.
+template <bool kPro>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -637,6 +730,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     const bool fwd = (a.flags & kFlagReverse) == 0;
     const bool pre = (a.flags & kFlagReadPre) != 0;
     const bool acc_out = (a.flags & kFlagAccumulate) != 0;
+    const bool l2 = kPro && (a.flags & kFlagL2Norm) != 0;
     const int64_t nchunks = (len + kC - 1) / kC;
     const int dcol0 = tile * kDVT;
 
@@ -665,10 +759,29 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         auto run = [&](auto role) __attribute__((always_inline)) {
             constexpr int R = decltype(role)::value;
             constexpr bool kCopies = R == kWaveCopyK || R == kWaveCopyQ;
+            // The K wave copies K (and Q in the prologue form) and computes the row norms; the G
+            // wave copies the gates and V (and Q in the plain form), builds the gate tables and
+            // folds the norms into them. The prologue form puts the norms on the wave that shares
+            // its SIMD with the diagonal prep rather than with a chain wave.
+            constexpr int kKW = kPro ? kWaveCopyQ : kWaveCopyK;
+            constexpr int kGW = kPro ? kWaveCopyK : kWaveCopyQ;
+            // the value head's gate parameters, read once (raw gate inputs only)
+            bool raw_gates = false;
+            float nea = 0.f, dtb = 0.f;
+            if constexpr (kPro && R == kGW) {
+                if (a.A_log) {
+                    raw_gates = true;
+                    nea = -__expf(a.A_log[head]);
+                    dtb = a.dt_bias[head];
+                }
+            }
             u32x4 rsrc0, rsrc1, rsrc2, rsrc3, rsrc4;
-            if constexpr (R == kWaveCopyK) {
+            if constexpr (R == kKW) {
                 rsrc0 = slab_rsrc(kb, a.T * kDK * 2);
-            } else if constexpr (R == kWaveCopyQ) {
+                // the prologue form copies Q here too: this wave then owns both operands whose
+                // row norms it computes
+                if constexpr (kPro) rsrc1 = slab_rsrc(qb, a.T * kDK * 2);
+            } else if constexpr (R == kGW) {
                 rsrc0 = slab_rsrc(qb, a.T * kDK * 2);
                 rsrc1 = slab_rsrc(vb + dcol0, a.T * a.dv * 2 - dcol0 * 2);
                 rsrc4 = slab_rsrc(ob + dcol0, a.T * a.dv * 2 - dcol0 * 2);
@@ -689,10 +802,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             auto issue = [&](int64_t ch, const CopyOffsets &co) __attribute__((always_inline)) {
                 char *rawn = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
-                if constexpr (R == kWaveCopyK) {
+                if constexpr (R == kKW) {
                     copy_kq(rawn + kRawK, rsrc0, co, lo);
-                } else if constexpr (R == kWaveCopyQ) {
-                    copy_kq(rawn + kRawQ, rsrc0, co, lo);
+                    if constexpr (kPro) copy_kq(rawn + kRawQ, rsrc1, co, lo);
+                } else if constexpr (R == kGW) {
+                    if constexpr (!kPro) copy_kq(rawn + kRawQ, rsrc0, co, lo);
                     copy_v(rawn + kRawV, rsrc1, co, lo, a.dv);
                     copy_gates(rawn, rsrc2, rsrc3, co, lo);
                 }
@@ -700,10 +814,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             auto prep = [&](int64_t ch) __attribute__((always_inline)) {
                 const char *rawp = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 char *derp = smem + kOffDer + (int)(ch & 1) * kDerBytes;
-                if constexpr (R == kWaveDiag) prep_diag(smem, rawp, derp, pre, ro);
-                else if constexpr (R == kWaveA) prep_a(rawp, derp, ro);
-                else if constexpr (R == kWaveP012) prep_p<0, 3>(rawp, derp, pre, ro);
-                else if constexpr (R == kWaveP3) prep_p<3, 4>(rawp, derp, pre, ro);
+                // the two forms of each prep, with and without the k row scales
+                if constexpr (R == kWaveDiag) {
+                    if (l2) prep_diag<true, kPro>(smem, rawp, derp, pre, ro);
+                    else prep_diag<false, kPro>(smem, rawp, derp, pre, ro);
+                } else if constexpr (R == kWaveA) {
+                    if (l2) prep_a<true>(rawp, derp, ro);
+                    else prep_a<false>(rawp, derp, ro);
+                } else if constexpr (R == kWaveP012) {
+                    if (l2) prep_p<0, 3, true>(rawp, derp, pre, ro);
+                    else prep_p<0, 3, false>(rawp, derp, pre, ro);
+                } else if constexpr (R == kWaveP3) {
+                    if (l2) prep_p<3, 4, true>(rawp, derp, pre, ro);
+                    else prep_p<3, 4, false>(rawp, derp, pre, ro);
+                }
             };
             auto store = [&](int64_t ch) __attribute__((always_inline)) {
                 const ChunkRows cr = chunk_rows(t0, len, fwd, ch);
@@ -713,10 +837,29 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             // the wave that copies the gates builds the chunk's gate tables as soon as its copies
             // have landed, one chunk ahead of the prep waves that read them
             auto tables = [&](int64_t ch) __attribute__((always_inline)) {
-                if constexpr (R == kWaveCopyQ) gate_tables(smem + kOffRaw + (int)(ch % 3) * kRawBytes, pre);
+                char *rawc = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
+                if constexpr (R == kGW) {
+                    const RawGates rg{raw_gates, nea, dtb, chunk_rows(t0, len, fwd, ch).rmax};
+                    gate_tables<kPro>(rawc, pre, rg);
+                }
+                // the k and q row scales, by the wave that copies K and Q in the prologue form
+                if constexpr (R == kKW && kPro) {
+                    if (l2) {
+                        row_scales(rawc + kRawK, reinterpret_cast<float *>(rawc + kTabRk), true);
+                        row_scales(rawc + kRawQ, reinterpret_cast<float *>(rawc + kTabRq), true);
+                    }
+                }
+            };
+            // One step later (the tables and the row scales of the chunk are complete then): the
+            // row scales folded into the chain's scalars.
+            auto qstage = [&](int64_t ch) __attribute__((always_inline)) {
+                if constexpr (R == kGW) {
+                    if (l2) fold_row_scales(smem + kOffRaw + (int)(ch % 3) * kRawBytes);
+                }
             };
             auto step = [&](int64_t ch) __attribute__((always_inline)) {
-                if constexpr (R == kWaveCopyQ) {
+                if (ch + 1 < nchunks) qstage(ch + 1);
+                if constexpr (R == kGW) {
                     // with accumulation, the output's previous values of chunk ch, which the
                     // write-back adds in the next step
                     if (acc_out) {
@@ -745,6 +888,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 if (nchunks == 2) issue(1, clast);
                 else if (nchunks > 2) issue(1, cfull);
             }
+            qstage(0);
             prep(0);
             wait_vmem();
             if (nchunks > 1) tables(1);
@@ -877,8 +1021,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                         // operands of the state update and the output
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            // the post-write read scale e^{b} is eb itself
-                            er[m] = pre ? *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * m) : eb[m];
+                            // the post-write read scale e^{b} is eb itself, unless eb carries the
+                            // k row scales
+                            er[m] = (pre || l2) ? *reinterpret_cast<const floatx4 *>(sc + 256 + 64 * m) : eb[m];
                             ec[m] = *reinterpret_cast<const floatx4 *>(sc + 512 + 64 * m);
                         }
                         kt[0][0] = kt_frag(raw + kRawK, ko, 0, 0);
@@ -992,17 +1137,23 @@ bool chunk_fwd_fast_supported(int dtype, int chunk, int dk) {
     return dtype == kDtypeBf16 && chunk == kC && dk == kDK;
 }
 
-hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream) {
+template <bool kPro>
+hipError_t launch_form(const ChunkArgs &a, hipStream_t stream) {
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_fwd_fast_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_fwd_fast_kernel<kPro>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
         if (e != hipSuccess) return e;
         configured = true;
     }
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
-    hipLaunchKernelGGL(chunk_fwd_fast_kernel, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
+    hipLaunchKernelGGL(chunk_fwd_fast_kernel<kPro>, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream) {
+    if (a.A_log || (a.flags & kFlagL2Norm)) return launch_form<true>(a, stream);
+    return launch_form<false>(a, stream);
 }
 
 }  // namespace gdr

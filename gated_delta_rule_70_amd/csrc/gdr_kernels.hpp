@@ -44,14 +44,15 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hi
 bool chunk_fwd_fast_supported(int dtype, int chunk, int dk);
 hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
+// softplus without overflow: max(x, 0) + log(1 + e^{-|x|}); the second term is below 2^-24
+// (and lost next to 1) only where it is negligible against the first or is itself < 6e-8
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))); }
 // the gates of one token of value head h from their raw inputs (see ChunkArgs)
 __device__ __forceinline__ float gate_log_alpha(float a, const float *A_log, const float *dt_bias, int64_t h) {
     const float x = a + dt_bias[h];
-    // softplus without overflow: max(x, 0) + log1p(exp(-|x|))
-    const float sp = fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
-    return -__expf(A_log[h]) * sp;
+    return -__expf(A_log[h]) * softplus_f(x);
 }
-__device__ __forceinline__ float gate_beta(float b) { return 1.f / (1.f + __expf(-b)); }
+__device__ __forceinline__ float gate_beta(float b) { return __builtin_amdgcn_rcpf(1.f + __expf(-b)); }
 
 hipError_t launch_selftest_mfma(const float *a, const float *b, float *d, hipStream_t stream);
 
