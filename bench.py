@@ -169,6 +169,21 @@ def bench_varlen(binding, inputs, steps):
                 lengths=[int(x) for x in (case.cu_seqlens[1:] - case.cu_seqlens[:-1])])
 
 
+def bench_fused(binding, inputs, steps):
+    """The fused prologue on the workload-1 shapes: raw q/k rows (normalised in the kernel) and
+    raw gate inputs a, b with per-head A_log, dt_bias (``gdr_chunk_fwd_gated`` with
+    GDR_QK_L2NORM)."""
+    import torch
+    c = inputs.raw_case(B=4, T=4096, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16, seed=1001,
+                        h0_std=0.1)
+    dev = torch.device("cuda:0")
+    q, k, v, a, b, A_log, dtb, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, c.h0))
+    out, hT = torch.empty_like(v), torch.empty_like(h0)
+    fn = lambda: binding.chunk_fwd_gated(q, k, v, a, b, A_log, dtb, h0, chunk=64, out=out, hT=hT, l2norm=True)
+    ms, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
+    return dict(ms=ms, tokens=4 * 4096)
+
+
 def bench_bidir(binding, inputs, steps):
     import torch
     case = inputs.workload4()
@@ -284,10 +299,14 @@ def main():
         print("[bench] packed variable-length and bidirectional workloads ...", file=sys.stderr, flush=True)
         vl = bench_varlen(binding, inputs, max(3, args.steps // 4))
         bd = bench_bidir(binding, inputs, max(3, args.steps // 4))
+        fu = bench_fused(binding, inputs, max(3, args.steps // 4))
         res["other_workloads"] = {
             inputs.WORKLOADS[2]: {"tokens_per_s": vl["tokens"] / (vl["ms"] / 1e3), "ms": vl["ms"],
                                   "hbm_frac": vl["bytes"] / (vl["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                                   "lengths": vl["lengths"]},
+            "gdr-chunk-fwd-fused-prologue-bf16-B4-H16-T4096-d128-c64": {
+                "tokens_per_s": fu["tokens"] / (fu["ms"] / 1e3), "ms": fu["ms"],
+                "prologue": "q/k rows normalised and gates formed from raw inputs in the kernel"},
             inputs.WORKLOADS[4]: {"tokens_per_s": bd["tokens"] / (bd["ms"] / 1e3), "ms": bd["ms"],
                                   "calls": 2},
         }

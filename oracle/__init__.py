@@ -11,6 +11,8 @@ Two parts:
 * ``chunked`` (module ``oracle.chunked``): the exact chunk-parallel (WY/UT) form
   written out in numpy from the "Prizma seq/delta.py" page, ``chunked_delta``;
   it is checked against the recurrence, never against the GPU.
+* ``prologue`` (module ``oracle.prologue``): the steps before the recurrence (q/k
+  row normalisation, gates from raw inputs) in fp64 numpy, then the recurrence.
 
 Arrays are converted to contiguous float64 numpy before the call, so bf16 or
 fp32 inputs are upcast exactly.
