@@ -161,7 +161,7 @@ def bench_varlen(binding, inputs, steps):
     la, b, h0, cu = case.log_alpha.to(dev), case.beta.to(dev), case.h0.to(dev), case.cu_seqlens.to(dev)
     out, hT = torch.empty_like(v), torch.empty_like(h0)
     fn = lambda: binding.chunk_fwd(q, k, v, la, b, h0, cu, chunk=64, out=out, hT=hT)
-    ms, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev))
+    ms, _ = timed(fn, steps, 200, torch.cuda.current_stream(dev))
     T = case.q.shape[2]
     H, dk, dv = case.q.shape[1], case.q.shape[3], case.v.shape[3]
     nseq = case.cu_seqlens.numel() - 1
@@ -180,7 +180,7 @@ def bench_fused(binding, inputs, steps):
     q, k, v, a, b, A_log, dtb, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, c.h0))
     out, hT = torch.empty_like(v), torch.empty_like(h0)
     fn = lambda: binding.chunk_fwd_gated(q, k, v, a, b, A_log, dtb, h0, chunk=64, out=out, hT=hT, l2norm=True)
-    ms, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
+    ms, _ = timed(fn, steps, 300, torch.cuda.current_stream(dev))
     return dict(ms=ms, tokens=4 * 4096)
 
 
@@ -198,7 +198,7 @@ def bench_bidir(binding, inputs, steps):
         binding.chunk_fwd(q, k, v, la2, b2, None, cu, chunk=64, read="pre", reverse=True, out=out,
                           accumulate=True, want_state=False)
 
-    ms, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev))
+    ms, _ = timed(fn, steps, 200, torch.cuda.current_stream(dev))
     return dict(ms=ms, tokens=case.q.shape[2])
 
 
