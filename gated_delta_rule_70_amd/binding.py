@@ -25,6 +25,7 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
 
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
+           "gdr_gdn2_chunk_fwd", "gdr_gdn2_decode_step",
            "gdr_status_string", "gdr_last_error", "gdr_abi_version", "gdr_selftest_mfma")
 
 
@@ -61,6 +62,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step_gated.argtypes = [p, p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
     lib.gdr_decode_step_gated.restype = ctypes.c_int
+    lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_gdn2_decode_step.argtypes = [p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
+    lib.gdr_gdn2_decode_step.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
@@ -242,6 +247,84 @@ def _decode(q, k, v, ga, gb, A_log, dt_bias, state_in, state_out, out, read, l2n
     else:
         _check(lib().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(state_in),
                                      _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q)))
+    return out, state_out
+
+
+def gdn2_chunk_fwd(q, k, v, g, b, w, h0=None, cu_seqlens=None, *, chunk: int = 64, read: str = "post",
+                   reverse: bool = False, out=None, accumulate: bool = False, hT=None, want_state: bool = True,
+                   l2norm: bool = False):
+    """GDN-2 chunked forward (``gdr_gdn2_chunk_fwd``).
+
+    q, k [B, Hk, T, dk] and v [B, Hv, T, dv] (bf16 or fp32, one dtype); g [B, Hk, T, dk] fp32 log
+    decay per key channel; b [B, Hk, T, dk] erase gate and w [B, Hv, T, dv] write gate in the
+    dtype of q. The rest as ``chunk_fwd``.
+    """
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    _need(k, "k", dt, (B, Hk, T, dk), dev)
+    _need(v, "v", dt, (B, Hv, T, dv), dev)
+    _need(g, "g", torch.float32, (B, Hk, T, dk), dev)
+    _need(b, "b", dt, (B, Hk, T, dk), dev)
+    _need(w, "w", dt, (B, Hv, T, dv), dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (S, Hv, dk, dv), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, Hv, T, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, Hv, T, dv), dev)
+    if hT is None and want_state:
+        hT = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+    elif hT is not None:
+        _need(hT, "hT", torch.float32, (S, Hv, dk, dv), dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0) | \
+        (GDR_ACCUMULATE if accumulate else 0) | (GDR_QK_L2NORM if l2norm else 0)
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    _check(lib().gdr_gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0),
+                                    _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT), ctypes.byref(dims),
+                                    _stream(q)))
+    return out, hT
+
+
+def gdn2_decode_step(q, k, v, g, b, w, state_in, state_out=None, out=None, *, read: str = "post",
+                     l2norm: bool = False):
+    """One GDN-2 decode step (``gdr_gdn2_decode_step``). q, k, b [N, Hk, dk] and v, w [N, Hv, dv]
+    in one dtype; g [N, Hk, dk] fp32; state_in [N, Hv, dk, dv] fp32. Returns (out, state_out)."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _need(k, "k", dt, (N, Hk, dk), dev)
+    _need(b, "b", dt, (N, Hk, dk), dev)
+    _need(g, "g", torch.float32, (N, Hk, dk), dev)
+    _need(v, "v", dt, (N, Hv, dv), dev)
+    _need(w, "w", dt, (N, Hv, dv), dev)
+    _need(state_in, "state_in", torch.float32, (N, Hv, dk, dv), dev)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    else:
+        _need(state_out, "state_out", torch.float32, (N, Hv, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, Hv, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (N, Hv, dv), dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_QK_L2NORM if l2norm else 0)
+    dims = DecodeDims(N, Hk, Hv, dk, dv, code, flags)
+    _check(lib().gdr_gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(state_in),
+                                      _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q)))
     return out, state_out
 
 

@@ -31,6 +31,7 @@
 
 #include "gdr_kernels.hpp"
 #include "gdr_mfma.hpp"
+#include "gdr_solve.hpp"
 
 namespace gdr {
 
@@ -238,61 +239,6 @@ __device__ __forceinline__ void gram_tiles(Smem<E, C, DK> &sm, bool pre) {
     }
 }
 
-// T = (I + A)^{-1}, by wave 0. Diagonal 16x16 blocks by forward substitution, then
-// T_10 = -T_11 A_10 T_00 (and T_32 for C = 64), then the lower-left 32x32 block
-// T_BA = -T_BB A_BA T_AA (C = 64). Writes the lower triangle of sm.T; the strictly upper
-// blocks were zeroed once and are never written.
-template <typename E, int C, int DK>
-__device__ __forceinline__ void solve_inverse(Smem<E, C, DK> &sm) {
-    typedef Smem<E, C, DK> SM;
-    constexpr int NT = C / 16;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, cc = lane & 15;
-    // diagonal blocks: lane (blk = g, column cc); rows i of column cc
-    if (g < NT) {
-        const int base = 16 * g;
-        float t[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == cc) ? 1.f : 0.f;
-            const float *arow = sm.A + (base + i) * SM::AP + base;
-#pragma unroll
-            for (int j = 0; j < i; ++j) s -= arow[j] * t[j];
-            t[i] = s;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sm.T[(base + i) * SM::TP + base + cc] = from_f<E>(t[i]);
-    }
-    if (NT == 1) return;
-    wave_lds_sync();
-    // T_{2p+1, 2p} = -T_{2p+1,2p+1} A_{2p+1,2p} T_{2p,2p}
-#pragma unroll
-    for (int p = 0; p < NT / 2; ++p) {
-        const int r1 = 2 * p + 1, c0 = 2 * p;
-        floatx4 z = mma16(zero4(), frag_rows_lo_f32<E>(sm.A, SM::AP, 16 * r1, 16 * c0),
-                          frag_cols_lo<E>(sm.T, SM::TP, 16 * c0, 16 * c0));
-        floatx4 w = mma16(zero4(), frag_rows_lo<E>(sm.T, SM::TP, 16 * r1, 16 * r1), cvt4<E>(z));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.T[(16 * r1 + 4 * g + r) * SM::TP + 16 * c0 + cc] = from_f<E>(-w[r]);
-    }
-    if (NT == 2) return;
-    wave_lds_sync();
-    // lower-left 32x32 block: M = A_BA T_AA, T_BA = -T_BB M, one 16-column slice at a time
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        floatx4 m0 = mma32(zero4(), frag_rows_f32<E>(sm.A, SM::AP, 32, 0), frag_cols<E>(sm.T, SM::TP, 16 * ct, 0));
-        floatx4 m1 = mma32(zero4(), frag_rows_f32<E>(sm.A, SM::AP, 48, 0), frag_cols<E>(sm.T, SM::TP, 16 * ct, 0));
-        const Frag<E> mb = frag_from_acc<E>(m0, m1);
-        floatx4 l0 = mma32(zero4(), frag_rows<E>(sm.T, SM::TP, 32, 32), mb);
-        floatx4 l1 = mma32(zero4(), frag_rows<E>(sm.T, SM::TP, 48, 32), mb);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            sm.T[(32 + 4 * g + r) * SM::TP + 16 * ct + cc] = from_f<E>(-l0[r]);
-            sm.T[(48 + 4 * g + r) * SM::TP + 16 * ct + cc] = from_f<E>(-l1[r]);
-        }
-    }
-}
-
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
     typedef Smem<E, C, DK> SM;
@@ -373,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
         __syncthreads();
         gram_tiles<E, C, DK>(sm, pre);
         __syncthreads();
-        if (wave == 0) solve_inverse<E, C, DK>(sm);
+        if (wave == 0) solve_unit_lower_inverse<E, C>(sm);
         __syncthreads();
 
         if (chain) {

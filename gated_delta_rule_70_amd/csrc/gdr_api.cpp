@@ -251,6 +251,138 @@ gdr_status_t decode_impl(const void *q, const void *k, const void *v, const floa
 
 }  // namespace
 
+namespace {
+
+gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
+                             const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out,
+                             float *hT, const gdr_chunk_dims_t *dims, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    const gdr_chunk_dims_t d = *dims;
+    if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
+    if (d.flags & ~(GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE | GDR_QK_L2NORM))
+        return fail(GDR_ERR_FLAGS, "flags 0x%x has unknown bits", d.flags);
+    if (chunk != 16 && chunk != 32 && chunk != 64) return fail(GDR_ERR_CHUNK, "chunk %d is not 16, 32 or 64", chunk);
+    if (d.B < 0 || d.T < 0) return fail(GDR_ERR_DIMS, "B (%lld) and T (%lld) must be >= 0", (long long)d.B, (long long)d.T);
+    if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
+    if (d.dk != 64 && d.dk != 128) return fail(GDR_ERR_UNSUPPORTED, "dk %lld is not 64 or 128", (long long)d.dk);
+    if (d.dv < 32 || d.dv > 256 || d.dv % 32) return fail(GDR_ERR_UNSUPPORTED, "dv %lld is not a multiple of 32 in [32, 256]", (long long)d.dv);
+    if (!gdr::gdn2_chunk_supported(d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32, chunk, (int)d.dk))
+        return fail(GDR_ERR_CHUNK, "chunk 64 with fp32 and dk 128 does not fit in shared memory (use 16 or 32)");
+    int64_t nseq = d.B;
+    if (cu_seqlens) {
+        if (d.B != 1) return fail(GDR_ERR_DIMS, "cu_seqlens needs B == 1 (got %lld)", (long long)d.B);
+        if (d.num_seqs < 1) return fail(GDR_ERR_DIMS, "num_seqs (%lld) must be >= 1 with cu_seqlens", (long long)d.num_seqs);
+        nseq = d.num_seqs;
+    }
+    const int64_t es = elem_size(d.dtype);
+    const int64_t nq = prod({d.B, d.Hk, d.T, d.dk}), nv = prod({d.B, d.Hv, d.T, d.dv});
+    const int64_t ns = prod({nseq, d.Hv, d.dk, d.dv});
+    if (nq < 0 || nv < 0 || ns < 0 || nq > (INT64_C(1) << 59)) return fail(GDR_ERR_DIMS, "sizes overflow");
+    if (nq > 0 && (!q || !k || !g || !b)) return fail(GDR_ERR_NULL, "q, k, g or b is NULL");
+    if (nv > 0 && (!v || !w || !out)) return fail(GDR_ERR_NULL, "v, w or out is NULL");
+    const void *al16[] = {q, k, v, g, b, w, out, h0, hT};
+    const char *al16n[] = {"q", "k", "v", "g", "b", "w", "out", "h0", "hT"};
+    for (int i = 0; i < 9; ++i)
+        if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDR_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+
+    const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
+    const Range rg = rng("g", g, nq * 4), rb = rng("b", b, nq * es), rw = rng("w", w, nv * es);
+    const Range rh0 = rng("h0", h0, ns * 4), rhT = rng("hT", hT, ns * 4);
+    const Range rcu = rng("cu_seqlens", cu_seqlens, cu_seqlens ? (nseq + 1) * 4 : 0);
+    const Range ro = rng("out", out, nv * es);
+    const Range ins[] = {rq, rk, rv, rg, rb, rw, rh0, rcu};
+    for (const Range &r : ins) {
+        if (overlap(ro, r)) return fail(GDR_ERR_ALIAS, "out overlaps %s", r.name);
+        if (&r != &ins[6] && overlap(rhT, r)) return fail(GDR_ERR_ALIAS, "hT overlaps %s", r.name);
+    }
+    if (overlap(ro, rhT)) return fail(GDR_ERR_ALIAS, "out overlaps hT");
+    if (overlap(rhT, rh0) && rhT.lo != rh0.lo) return fail(GDR_ERR_ALIAS, "hT partially overlaps h0");
+
+    gdr::Gdn2Args a;
+    a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
+    a.g = g; a.h0 = h0;
+    a.cu_seqlens = cu_seqlens;
+    a.out = out; a.hT = hT;
+    a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv; a.dv = d.dv;
+    a.units = nseq * d.Hv;
+    a.ntiles = d.dv / 32;
+    a.flags = d.flags;
+    const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
+    if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
+    const hipError_t e = gdr::launch_gdn2_chunk_fwd(a, d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32, chunk,
+                                                    (int)d.dk, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "GDN-2 chunk forward launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status_t gdn2_decode_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
+                              const void *w, const float *state_in, float *state_out, void *out,
+                              const gdr_decode_dims_t *dims, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    const gdr_decode_dims_t d = *dims;
+    if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
+    if (d.flags & ~(GDR_READ_PRE | GDR_QK_L2NORM))
+        return fail(GDR_ERR_FLAGS, "flags 0x%x: decode takes GDR_READ_PRE and GDR_QK_L2NORM only", d.flags);
+    if (d.N < 0) return fail(GDR_ERR_DIMS, "N (%lld) must be >= 0", (long long)d.N);
+    if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
+    if ((d.dk != 64 && d.dk != 128) || (d.dv != 64 && d.dv != 128))
+        return fail(GDR_ERR_UNSUPPORTED, "dk (%lld) and dv (%lld) must be 64 or 128", (long long)d.dk, (long long)d.dv);
+    const int64_t es = elem_size(d.dtype);
+    const int64_t nq = prod({d.N, d.Hk, d.dk}), nv = prod({d.N, d.Hv, d.dv});
+    const int64_t ns = prod({d.N, d.Hv, d.dk, d.dv});
+    if (nq < 0 || nv < 0 || ns < 0 || ns > (INT64_C(1) << 60)) return fail(GDR_ERR_DIMS, "sizes overflow");
+    if (d.N * d.Hv > INT32_MAX) return fail(GDR_ERR_DIMS, "N * Hv too large");
+    if (d.N > 0 && (!q || !k || !v || !g || !b || !w || !state_in || !state_out || !out))
+        return fail(GDR_ERR_NULL, "a tensor pointer is NULL");
+    const void *al16[] = {q, k, v, g, b, w, out, state_in, state_out};
+    const char *al16n[] = {"q", "k", "v", "g", "b", "w", "out", "state_in", "state_out"};
+    for (int i = 0; i < 9; ++i)
+        if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
+    const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
+    const Range rg = rng("g", g, nq * 4), rb = rng("b", b, nq * es), rw = rng("w", w, nv * es);
+    const Range rsi = rng("state_in", state_in, ns * 4), rso = rng("state_out", state_out, ns * 4);
+    const Range ro = rng("out", out, nv * es);
+    const Range ins[] = {rq, rk, rv, rg, rb, rw, rsi};
+    for (const Range &r : ins) {
+        if (overlap(ro, r)) return fail(GDR_ERR_ALIAS, "out overlaps %s", r.name);
+        if (&r != &ins[6] && overlap(rso, r)) return fail(GDR_ERR_ALIAS, "state_out overlaps %s", r.name);
+    }
+    if (overlap(ro, rso)) return fail(GDR_ERR_ALIAS, "out overlaps state_out");
+    if (overlap(rso, rsi) && rso.lo != rsi.lo) return fail(GDR_ERR_ALIAS, "state_out partially overlaps state_in");
+
+    gdr::Gdn2DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
+    a.g = g;
+    a.state_in = state_in; a.state_out = state_out; a.out = out;
+    a.N = d.N; a.Hk = d.Hk; a.Hv = d.Hv;
+    a.flags = d.flags;
+    const hipError_t e = gdr::launch_gdn2_decode(a, d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32, (int)d.dk,
+                                                 (int)d.dv, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "GDN-2 decode launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *b,
+                                const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk,
+                                void *out, float *hT, const gdr_chunk_dims_t *dims, void *stream) {
+    return gdn2_chunk_impl(q, k, v, g, b, w, h0, cu_seqlens, chunk, out, hT, dims, stream);
+}
+
+gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v, const float *g, const void *b,
+                                  const void *w, const float *state_in, float *state_out, void *out,
+                                  const gdr_decode_dims_t *dims, void *stream) {
+    return gdn2_decode_impl(q, k, v, g, b, w, state_in, state_out, out, dims, stream);
+}
+
+}  // extern "C"
+
 extern "C" {
 
 gdr_status_t gdr_selftest_mfma(const float *a, const float *b, float *d, void *stream) {

@@ -40,9 +40,37 @@ struct DecodeArgs {
     uint32_t flags;
 };
 
+// GDN-2: g [B][Hk][T][dk] fp32 log decay per key channel, b [B][Hk][T][dk] erase gate and
+// w [B][Hv][T][dv] write gate in the element type of q, k, v.
+struct Gdn2Args {
+    const void *q, *k, *v, *b, *w;
+    const float *g, *h0;
+    const int32_t *cu_seqlens;
+    void *out;
+    float *hT;
+    int64_t B, T, Hk, Hv, dv;
+    int64_t units;   // sequences x value heads
+    int64_t ntiles;  // dv / 32
+    uint32_t flags;
+};
+
+// GDN-2 decode: g, b [N][Hk][dk] (g fp32), w [N][Hv][dv].
+struct Gdn2DecodeArgs {
+    const void *q, *k, *v, *b, *w;
+    const float *g;
+    const float *state_in;
+    float *state_out;
+    void *out;
+    int64_t N, Hk, Hv;
+    uint32_t flags;
+};
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream);
 bool chunk_fwd_fast_supported(int dtype, int chunk, int dk);
 hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream);
+bool gdn2_chunk_supported(int dtype, int chunk, int dk);
+hipError_t launch_gdn2_chunk_fwd(const Gdn2Args &a, int dtype, int chunk, int dk, hipStream_t stream);
+hipError_t launch_gdn2_decode(const Gdn2DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 // softplus without overflow: max(x, 0) + log(1 + e^{-|x|}); the second term is below 2^-24
 // (and lost next to 1) only where it is negligible against the first or is itself < 6e-8

@@ -25,6 +25,7 @@ gates erase within a few tokens):
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
 
 import torch
@@ -175,6 +176,73 @@ def raw_case(*, B=1, T=256, Hk=2, Hv=None, dk=64, dv=64, dtype=torch.float32, se
     b = _normal(g, (B, Hv, T)).contiguous()
     h0 = _normal(g, (nseq, Hv, dk, dv), h0_std).contiguous() if h0_std > 0 else None
     return RawCase(q, k, v, a, b, A_log.contiguous(), dt_bias.contiguous(), h0, cu)
+
+
+@dataclass
+class Gdn2Case:
+    q: torch.Tensor          # [B, Hk, T, dk]
+    k: torch.Tensor          # [B, Hk, T, dk]
+    v: torch.Tensor          # [B, Hv, T, dv]
+    g: torch.Tensor          # [B, Hk, T, dk] fp32 log decay per key channel
+    b: torch.Tensor          # [B, Hk, T, dk] erase gate
+    w: torch.Tensor          # [B, Hv, T, dv] write gate
+    h0: torch.Tensor | None  # [S, Hv, dk, dv] fp32
+    cu_seqlens: torch.Tensor | None = None
+
+
+GDN2_REGIMES = ("page", "weak", "strong", "mixed")
+
+
+def gdn2_case(*, B=1, T=256, Hk=2, Hv=None, dk=64, dv=64, dtype=torch.float32, seed=0, h0_std=0.0,
+              lengths=None, regime="page", unit_rows=True) -> Gdn2Case:
+    """GDN-2 inputs with the distributions of the BidirectionalGatedDeltaNet2 layer on the
+    "tiny_gdn/fugue.py" page at its initialisation:
+      * "page": g = -A_h softplus(f + dt_bias_c), A_h ~ U(1, 16) per key head, dt_bias_c the
+        inverse softplus of dt ~ logU(0.001, 0.1) per key channel, f ~ N(0, 1) per token and channel;
+      * "weak": g = -U(0, 0.05) (long memory); "strong": g = -U(2, 10) (every 16-token block decays
+        by more than e^-60 on some channel); "mixed": "page", with g = -U(2, 10) on every fourth
+        key channel of the tokens t with (t // 16) % 3 == 0 (strong and weak blocks side by side);
+      * b = 2 sigmoid(N(0, 1)) (the allow_neg_eigval range (0, 2)), w = sigmoid(N(0, 1));
+      * q, k ~ N(0, 1), L2-normalised per row in fp32 when ``unit_rows``, otherwise times a
+        per-row length factor U(0.25, 4); v ~ N(0, 1); h0 ~ h0_std N(0, 1).
+    Draw order: A, dt, q, k, v, f (or the uniform g), b, w, row factors, h0."""
+    assert regime in GDN2_REGIMES, regime
+    Hv = Hk if Hv is None else Hv
+    g = _gen(seed + 70000)
+    cu = None
+    if lengths is not None:
+        assert B == 1
+        T = int(sum(lengths))
+        cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    nseq = B if cu is None else len(lengths)
+    A = torch.rand(Hk, generator=g) * 15.0 + 1.0
+    dt = torch.exp(torch.rand(dk, generator=g) * (math.log(0.1) - math.log(0.001)) + math.log(0.001))
+    dt_bias = dt + torch.log(-torch.expm1(-dt))
+    q = _normal(g, (B, Hk, T, dk))
+    k = _normal(g, (B, Hk, T, dk))
+    v = _normal(g, (B, Hv, T, dv)).to(dtype).contiguous()
+    if regime == "page":
+        f = _normal(g, (B, Hk, T, dk))
+        gate = -A[None, :, None, None] * torch.nn.functional.softplus(f + dt_bias)
+    elif regime == "mixed":
+        f = _normal(g, (B, Hk, T, dk))
+        gate = -A[None, :, None, None] * torch.nn.functional.softplus(f + dt_bias)
+        strong = -(torch.rand(B, Hk, T, dk, generator=g) * 8.0 + 2.0)
+        sel = ((torch.arange(T) // 16) % 3 == 0)[:, None] & (torch.arange(dk) % 4 == 0)[None, :]
+        gate = torch.where(sel, strong, gate)
+    elif regime == "weak":
+        gate = -torch.rand(B, Hk, T, dk, generator=g) * 0.05
+    else:
+        gate = -(torch.rand(B, Hk, T, dk, generator=g) * 8.0 + 2.0)
+    b = (2.0 * torch.sigmoid(_normal(g, (B, Hk, T, dk)))).to(dtype).contiguous()
+    w = torch.sigmoid(_normal(g, (B, Hv, T, dv))).to(dtype).contiguous()
+    if unit_rows:
+        q, k = _l2_normalise(q), _l2_normalise(k)
+    else:
+        q = q * (torch.rand(B, Hk, T, 1, generator=g) * 3.75 + 0.25)
+        k = k * (torch.rand(B, Hk, T, 1, generator=g) * 3.75 + 0.25)
+    h0 = _normal(g, (nseq, Hv, dk, dv), h0_std).contiguous() if h0_std > 0 else None
+    return Gdn2Case(q.to(dtype).contiguous(), k.to(dtype).contiguous(), v, gate.float().contiguous(), b, w, h0, cu)
 
 
 WORKLOADS = {

@@ -189,6 +189,60 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
                                    const float *state_in, float *state_out, void *out,
                                    const gdr_decode_dims_t *dims, void *stream);
 
+/*
+ * GDN-2: the delta rule with a decay per key channel and separate erase and write gates, the
+ * update stated in the BidirectionalGatedDeltaNet2 docstring on the "tiny_gdn/fugue.py" page
+ * (which also forms g = -exp(A_log) softplus(f + dt_bias) per key channel, b = sigmoid(.) or
+ * twice that with negative eigenvalues allowed, w = sigmoid(.), in its `heads` and `project`):
+ *
+ *   H_t = (I - k_t (b_t * k_t)^T) Diag(exp g_t) H_{t-1} + k_t (w_t * v_t)^T
+ *       = Diag(e^{g_t}) H_{t-1} + k_t u_t^T,   u_t = w_t * v_t - (Diag(e^{g_t}) H_{t-1})^T (b_t * k_t)
+ *
+ * (* is the element-wise product). g and b belong to the key head (one value per key channel),
+ * w to the value head (one value per value channel); the reads are those of the scalar rule.
+ * With g_t = log(alpha_t), b_t = w_t = beta_t on every channel this is gdr_chunk_fwd's update.
+ * g must be finite and <= 0; b and w may take any finite value (b in (0, 2) allows the negative
+ * eigenvalues of the page's allow_neg_eigval option).
+ *
+ * gdr_gdn2_chunk_fwd - the chunk-parallel forward of GDN-2 over whole sequences (the per-channel
+ * form of the chunk algebra of gdr_chunk_fwd; `chunk_gdn2` as the page calls it).
+ *
+ *   q, k        [B][Hk][T][dk]  dtype
+ *   v           [B][Hv][T][dv]  dtype
+ *   g           [B][Hk][T][dk]  fp32 log decay per key channel, <= 0
+ *   b           [B][Hk][T][dk]  dtype erase gate per key channel
+ *   w           [B][Hv][T][dv]  dtype write gate per value channel
+ *   h0, cu_seqlens, out, hT, dims, stream: as gdr_chunk_fwd (all four flags apply).
+ *
+ * Every tensor pointer 16-byte aligned. chunk 16, 32 or 64, except that fp32 with dk = 128
+ * takes 16 or 32 only (GDR_ERR_CHUNK): the fp32 operands of a 64-token chunk do not fit in the
+ * 160 KB of shared memory of a compute unit. A 16-token block whose decay summed over the block
+ * is below -60 on some channel is computed exactly on a slower path (see gdn2_fwd.hip);
+ * results do not depend on which path a block takes beyond rounding.
+ * Errors: as gdr_chunk_fwd; GDR_ERR_NULL also when g, b or w is NULL with T > 0.
+ */
+gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v,
+                                const float *g, const void *b, const void *w,
+                                const float *h0, const int32_t *cu_seqlens, int32_t chunk,
+                                void *out, float *hT,
+                                const gdr_chunk_dims_t *dims, void *stream);
+
+/*
+ * gdr_gdn2_decode_step - one GDN-2 token for N independent sequences.
+ *
+ *   q, k, b     [N][Hk][dk]      dtype (b: erase gate)
+ *   g           [N][Hk][dk]      fp32 log decay, <= 0
+ *   v, w        [N][Hv][dv]      dtype (w: write gate)
+ *   state_in, state_out, out, dims, stream: as gdr_decode_step (GDR_READ_PRE, GDR_QK_L2NORM).
+ *
+ * Every tensor pointer 16-byte aligned. Each state element is read once and written once.
+ * Errors: as gdr_decode_step.
+ */
+gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v,
+                                  const float *g, const void *b, const void *w,
+                                  const float *state_in, float *state_out, void *out,
+                                  const gdr_decode_dims_t *dims, void *stream);
+
 /* Static text for a status code. */
 const char *gdr_status_string(gdr_status_t status);
 

@@ -18,7 +18,7 @@ needs_lib = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_binding_exports():
@@ -171,3 +171,68 @@ def test_decode_gated_rejects():
                                    vp(FAKE * 11), vp(FAKE * 8), vp(FAKE * 16), vp(FAKE * 10 - 16),
                                    ctypes.byref(dims), None)
     assert binding.STATUS[st] == "GDR_ERR_ALIAS", lib.gdr_last_error().decode()
+
+
+def _gdn2_chunk(lib, **over):
+    d = dict(B=1, T=128, Hk=2, Hv=2, dk=64, dv=64, num_seqs=0, dtype=1, flags=8)
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, b=FAKE * 5, w=FAKE * 7, h0=None, cu=None,
+               out=FAKE * 6, hT=None, chunk=64)
+    for k_, v_ in over.items():
+        (d if k_ in d else ptr)[k_] = v_
+    dims = binding.ChunkDims(d["B"], d["T"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["num_seqs"],
+                             d["dtype"], d["flags"])
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_gdn2_chunk_fwd(vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["g"]), vp(ptr["b"]),
+                                vp(ptr["w"]), vp(ptr["h0"]), vp(ptr["cu"]), ptr["chunk"], vp(ptr["out"]),
+                                vp(ptr["hT"]), ctypes.byref(dims), None)
+    return binding.STATUS[st], lib.gdr_last_error().decode()
+
+
+GDN2_REJECTS = [
+    (dict(g=None), "GDR_ERR_NULL", "g"),
+    (dict(w=None), "GDR_ERR_NULL", "w"),
+    (dict(b=FAKE * 5 + 4), "GDR_ERR_ALIGN", "b"),
+    (dict(g=FAKE * 4 + 8), "GDR_ERR_ALIGN", "g"),
+    (dict(out=FAKE * 7 + 64), "GDR_ERR_ALIAS", "out overlaps w"),
+    (dict(hT=FAKE * 4 + 4096), "GDR_ERR_ALIAS", "hT overlaps g"),
+    (dict(dtype=0, dk=128), "GDR_ERR_CHUNK", "shared memory"),
+    (dict(chunk=8), "GDR_ERR_CHUNK", "chunk"),
+    (dict(flags=16), "GDR_ERR_FLAGS", "flags"),
+    (dict(dv=40), "GDR_ERR_UNSUPPORTED", "dv"),
+    (dict(Hk=4, Hv=2), "GDR_ERR_DIMS", "Hv"),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status,text", GDN2_REJECTS, ids=[c[1] + ":" + c[2] for c in GDN2_REJECTS])
+def test_gdn2_chunk_rejects(over, status, text):
+    st, msg = _gdn2_chunk(binding.load(), **over)
+    assert st == status and text in msg, (st, msg)
+
+
+@needs_lib
+def test_gdn2_fp32_d128_takes_chunk_32():
+    # the same call with chunk 32 passes validation; with no sequences nothing is launched
+    st, msg = _gdn2_chunk(binding.load(), dtype=0, dk=128, chunk=32, B=0)
+    assert st == "GDR_OK", msg
+
+
+@needs_lib
+def test_gdn2_decode_rejects():
+    lib = binding.load()
+    vp = ctypes.c_void_p
+
+    def call(dims, g=FAKE * 4, w=FAKE * 7, out=FAKE * 6):
+        st = lib.gdr_gdn2_decode_step(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), None if g is None else vp(g),
+                                      vp(FAKE * 5), vp(w), vp(FAKE * 8), vp(FAKE * 16), vp(out),
+                                      ctypes.byref(dims), None)
+        return binding.STATUS[st], lib.gdr_last_error().decode()
+
+    ok = binding.DecodeDims(4, 2, 4, 128, 128, 1, 8)
+    assert call(ok, g=None)[0] == "GDR_ERR_NULL"
+    assert call(ok, g=FAKE * 4 + 4)[0] == "GDR_ERR_ALIGN"
+    st, msg = call(ok, out=FAKE * 7 + 16)
+    assert st == "GDR_ERR_ALIAS" and "out overlaps w" in msg, msg
+    assert call(binding.DecodeDims(4, 2, 4, 128, 128, 1, 4))[0] == "GDR_ERR_FLAGS"
+    assert call(binding.DecodeDims(4, 2, 4, 96, 128, 1, 0))[0] == "GDR_ERR_UNSUPPORTED"
+    assert call(binding.DecodeDims(0, 2, 4, 128, 128, 1, 0))[0] == "GDR_OK"
