@@ -202,6 +202,39 @@ def bench_bidir(binding, inputs, steps):
     return dict(ms=ms, tokens=case.q.shape[2])
 
 
+def gdn2_bytes(B, Hk, Hv, T, dk, dv, es, nseq):
+    """Algorithmic HBM bytes of one GDN-2 chunked forward: q, k, b (erase gate) and the fp32
+    decay g per key head; v, w (write gate) and out per value head; h0 and hT."""
+    return B * Hk * T * dk * (3 * es + 4) + B * Hv * T * dv * 3 * es + 2 * nseq * Hv * dk * dv * 4
+
+
+def bench_gdn2(binding, inputs, steps):
+    """GDN-2 (per-key-channel decay, separate erase and write gates) on the workload-1 shapes,
+    chunk 32, gates drawn as at the layer's initialisation; and its one-token decode step on the
+    decode workload's shapes."""
+    import torch
+    dev = torch.device("cuda:0")
+    c = inputs.gdn2_case(B=4, T=4096, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16, seed=1001,
+                         h0_std=0.1)
+    q, k, v, g, b, w, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.g, c.b, c.w, c.h0))
+    out, hT = torch.empty_like(v), torch.empty_like(h0)
+    fn = lambda: binding.gdn2_chunk_fwd(q, k, v, g, b, w, h0, chunk=32, out=out, hT=hT)
+    ms, _ = timed(fn, steps, 50, torch.cuda.current_stream(dev))
+    chunk = dict(ms=ms, tokens=4 * 4096, bytes=gdn2_bytes(4, 16, 16, 4096, 128, 128, 2, 4))
+    del q, k, v, g, b, w, h0, out, hT
+    N, Hk, Hv = 256, 16, 32
+    dc = inputs.gdn2_case(B=N, T=1, Hk=Hk, Hv=Hv, dk=128, dv=128, dtype=torch.bfloat16, seed=1003, h0_std=0.1)
+    one = lambda t: t[:, :, 0].contiguous().to(dev)
+    dq, dk_, dv_, dg, db, dw = (one(t) for t in (dc.q, dc.k, dc.v, dc.g, dc.b, dc.w))
+    state = dc.h0.to(dev)
+    dout = torch.empty((N, Hv, 128), dtype=torch.bfloat16, device=dev)
+    fn = lambda: binding.gdn2_decode_step(dq, dk_, dv_, dg, db, dw, state, state_out=state, out=dout)
+    dms, _ = timed(fn, max(steps, 64), 300, torch.cuda.current_stream(dev))
+    sbytes = 2 * N * Hv * 128 * 128 * 4
+    io = N * Hk * 128 * (3 * 2 + 4) + N * Hv * 128 * 3 * 2
+    return chunk, dict(ms=dms, state_bytes=sbytes, io_bytes=io, tokens=N)
+
+
 def cpu_baseline(inputs, min_wall=1.5, max_reps=20):
     """The fp64 oracle, as it is, on this host's cores: the whole B4 H16 T4096 d128 workload,
     repeated until at least `min_wall` seconds have passed (a bounded sample)."""
@@ -244,7 +277,8 @@ def main():
     # timed 16% slower than with 300); 500 calls are about 50 ms
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
+    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "all"], default="all",
+                    help="gdn2: only the GDN-2 workloads (for profiling them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -261,6 +295,11 @@ def main():
     binding.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.only == "gdn2":
+        g2, g2d = bench_gdn2(binding, inputs, args.steps)
+        print(json.dumps({"gdn2_chunk_ms": g2["ms"], "gdn2_chunk_bytes": g2["bytes"], "steps": args.steps,
+                          "gdn2_decode_us": g2d["ms"] * 1e3}), flush=True)
+        return
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
@@ -300,6 +339,7 @@ def main():
         vl = bench_varlen(binding, inputs, max(3, args.steps // 4))
         bd = bench_bidir(binding, inputs, max(3, args.steps // 4))
         fu = bench_fused(binding, inputs, max(3, args.steps // 4))
+        g2, g2d = bench_gdn2(binding, inputs, max(3, args.steps // 8))
         res["other_workloads"] = {
             inputs.WORKLOADS[2]: {"tokens_per_s": vl["tokens"] / (vl["ms"] / 1e3), "ms": vl["ms"],
                                   "hbm_frac": vl["bytes"] / (vl["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -309,6 +349,20 @@ def main():
                 "prologue": "q/k rows normalised and gates formed from raw inputs in the kernel"},
             inputs.WORKLOADS[4]: {"tokens_per_s": bd["tokens"] / (bd["ms"] / 1e3), "ms": bd["ms"],
                                   "calls": 2},
+            "gdn2-chunk-fwd-bf16-B4-H16-T4096-d128-c32": {
+                "tokens_per_s": g2["tokens"] / (g2["ms"] / 1e3), "ms": g2["ms"],
+                "roofline": {"bound": "hbm", "achieved": g2["bytes"] / (g2["ms"] / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": g2["bytes"] / (g2["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                             "bytes_per_launch": g2["bytes"], "kernel": "gdn2_chunk_kernel<bf16, 32, 128>",
+                             "traffic": measured_traffic("gdn2_chunk_B4_H16_T4096_d128_hbm_traffic.md",
+                                                         "gdn2_fwd.hip", "HBM bytes per launch")}},
+            "gdn2-decode-bf16-N256-Hk16-Hv32-d128": {
+                "state_GB_per_s": g2d["state_bytes"] / (g2d["ms"] / 1e3) / 1e9, "us_per_step": g2d["ms"] * 1e3,
+                "roofline": {"bound": "hbm",
+                             "achieved": (g2d["state_bytes"] + g2d["io_bytes"]) / (g2d["ms"] / 1e3) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": (g2d["state_bytes"] + g2d["io_bytes"]) / (g2d["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                             "kernel": "gdn2_decode_kernel<bf16, 128, 128>"}},
         }
     if not args.no_cpu:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
