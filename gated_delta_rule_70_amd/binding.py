@@ -25,7 +25,7 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
 
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
-           "gdr_gdn2_chunk_fwd", "gdr_gdn2_decode_step",
+           "gdr_gdn2_chunk_fwd", "gdr_gdn2_decode_step", "gdr_delta_product_fwd",
            "gdr_status_string", "gdr_last_error", "gdr_abi_version", "gdr_selftest_mfma")
 
 
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step_gated.argtypes = [p, p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
     lib.gdr_decode_step_gated.restype = ctypes.c_int
+    lib.gdr_delta_product_fwd.argtypes = [p, p, p, p, p, p, p, i32, i32, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_delta_product_fwd.restype = ctypes.c_int
     lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
     lib.gdr_gdn2_chunk_fwd.restype = ctypes.c_int
     lib.gdr_gdn2_decode_step.argtypes = [p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
@@ -248,6 +250,49 @@ def _decode(q, k, v, ga, gb, A_log, dt_bias, state_in, state_out, out, read, l2n
         _check(lib().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(state_in),
                                      _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q)))
     return out, state_out
+
+
+def delta_product_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk: int = 64,
+                      read: str = "pre", out=None, accumulate: bool = False, hT=None, want_state: bool = True,
+                      l2norm: bool = False):
+    """DeltaProduct forward (``gdr_delta_product_fwd``): q [B, Hk, T, dk]; k [B, Hk, T, n, dk];
+    v [B, Hv, T, n, dv]; log_alpha [B, Hv, T] fp32; beta [B, Hv, T, n] fp32. ``read`` defaults
+    to the pre-write read of the page this variant comes from. Returns (out, hT)."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    B, Hk, T, dk = q.shape
+    n = k.shape[3]
+    Hv, dv = v.shape[1], v.shape[4]
+    _need(k, "k", dt, (B, Hk, T, n, dk), dev)
+    _need(v, "v", dt, (B, Hv, T, n, dv), dev)
+    _need(log_alpha, "log_alpha", torch.float32, (B, Hv, T), dev)
+    _need(beta, "beta", torch.float32, (B, Hv, T, n), dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (S, Hv, dk, dv), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, Hv, T, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, Hv, T, dv), dev)
+    if hT is None and want_state:
+        hT = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+    elif hT is not None:
+        _need(hT, "hT", torch.float32, (S, Hv, dk, dv), dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_ACCUMULATE if accumulate else 0) | \
+        (GDR_QK_L2NORM if l2norm else 0)
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    _check(lib().gdr_delta_product_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                       _ptr(cu_seqlens), int(n), int(chunk), _ptr(out), _ptr(hT),
+                                       ctypes.byref(dims), _stream(q)))
+    return out, hT
 
 
 def gdn2_chunk_fwd(q, k, v, g, b, w, h0=None, cu_seqlens=None, *, chunk: int = 64, read: str = "post",

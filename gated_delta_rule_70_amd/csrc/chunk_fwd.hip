@@ -80,10 +80,27 @@ struct Prefetch {
     float la, beta;
 };
 
+// One sequence as the kernel walks it. With ns delta sub-steps per token (DeltaProduct) the
+// walk is over the ns * tokens sub-steps of the sequence in order; k, v and beta are stored per
+// sub-step, q, the decay and the output per token: sub-step pos belongs to token tok0 + pos / ns,
+// the decay enters on its first sub-step and the read happens on sub-step jread of each token.
 struct SeqView {
-    int64_t t0, len;  // first token and length of the sequence in its row
-    bool rev;
+    int64_t t0, len;  // first step (token, or sub-step) and length of the sequence in its row
+    int64_t tok0;     // first token of the sequence (= t0 when ns == 1)
+    bool rev;         // only with ns == 1
+    int ns, jread;
     __device__ __forceinline__ int64_t token(int64_t pos) const { return rev ? t0 + len - 1 - pos : t0 + pos; }
+    // token of step pos and whether that step is the one its token reads at / decays at
+    __device__ __forceinline__ int64_t owner(int64_t pos, bool &read_step, bool &first_step) const {
+        if (ns == 1) {
+            read_step = first_step = true;
+            return token(pos);
+        }
+        const int p = (int)pos, j = p % ns;
+        read_step = j == jread;
+        first_step = j == 0;
+        return tok0 + p / ns;
+    }
 };
 
 template <typename E, int C, int DK>
@@ -105,7 +122,9 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<E, C, DK> &pf, const Seq
             if (pos < sv.len) {
                 const int64_t off = sv.token(pos) * (int64_t)(DK * sizeof(E)) + cp * 16;
                 pf.k[i] = *reinterpret_cast<const uint4 *>(kb + off);
-                pf.q[i] = *reinterpret_cast<const uint4 *>(qb + off);
+                bool rd, first;
+                const int64_t t = sv.owner(pos, rd, first);
+                if (rd) pf.q[i] = *reinterpret_cast<const uint4 *>(qb + t * (int64_t)(DK * sizeof(E)) + cp * 16);
             }
         }
     }
@@ -127,10 +146,12 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<E, C, DK> &pf, const Seq
     if (tid < C) {
         const int64_t pos = c * C + tid;
         if (pos < sv.len) {
-            const int64_t t = sv.token(pos);
+            const int64_t e = sv.token(pos);
+            bool rd, first;
+            const int64_t t = sv.owner(pos, rd, first);
             // raw gate inputs become log alpha and beta here when A_log is given
-            pf.la = A_log ? gate_log_alpha(ab[t], A_log, dt_bias, head) : ab[t];
-            pf.beta = A_log ? gate_beta(bb[t]) : bb[t];
+            if (first) pf.la = A_log ? gate_log_alpha(ab[t], A_log, dt_bias, head) : ab[t];
+            pf.beta = A_log ? gate_beta(bb[e]) : bb[e];
         }
     }
 }
@@ -260,12 +281,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
     const int64_t kh = head / (a.Hv / a.Hk);
     const int64_t row = a.cu_seqlens ? 0 : seq;
     SeqView sv;
-    sv.t0 = 0;
-    sv.len = a.T;
+    const int ns = a.n_sub;
+    sv.ns = ns;
+    sv.jread = (a.flags & kFlagReadPre) ? 0 : ns - 1;
+    sv.tok0 = 0;
+    int64_t ntok = a.T;
     if (a.cu_seqlens) {
-        sv.t0 = a.cu_seqlens[seq];
-        sv.len = a.cu_seqlens[seq + 1] - sv.t0;
+        sv.tok0 = a.cu_seqlens[seq];
+        ntok = a.cu_seqlens[seq + 1] - sv.tok0;
     }
+    sv.t0 = sv.tok0 * ns;
+    sv.len = ntok * ns;
     sv.rev = (a.flags & kFlagReverse) != 0;
     const bool pre = (a.flags & kFlagReadPre) != 0;
     const bool acc_out = (a.flags & kFlagAccumulate) != 0;
@@ -273,11 +299,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
     const int64_t nchunks = (sv.len + C - 1) / C;
     const int dcol0 = tile * kDvTile;
 
-    const char *kb = reinterpret_cast<const char *>(a.k) + (row * a.Hk + kh) * a.T * DK * (int64_t)sizeof(E);
+    const int64_t Ts = a.T * ns;  // steps per row
+    const char *kb = reinterpret_cast<const char *>(a.k) + (row * a.Hk + kh) * Ts * DK * (int64_t)sizeof(E);
     const char *qb = reinterpret_cast<const char *>(a.q) + (row * a.Hk + kh) * a.T * DK * (int64_t)sizeof(E);
-    const char *vb = reinterpret_cast<const char *>(a.v) + (row * a.Hv + head) * a.T * a.dv * (int64_t)sizeof(E);
+    const char *vb = reinterpret_cast<const char *>(a.v) + (row * a.Hv + head) * Ts * a.dv * (int64_t)sizeof(E);
     const float *ab = a.log_alpha + (row * a.Hv + head) * a.T;
-    const float *bb = a.beta + (row * a.Hv + head) * a.T;
+    const float *bb = a.beta + (row * a.Hv + head) * Ts;
     E *ob = reinterpret_cast<E *>(a.out) + (row * a.Hv + head) * a.T * a.dv;
 
     // zero T and P once: their strictly upper blocks are never written again
@@ -383,8 +410,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int64_t pos = c * C + 16 * mi + 4 * g + r;
-                    if (pos < sv.len) {
-                        E *dst = ob + sv.token(pos) * a.dv + dcol;
+                    bool rd, first;
+                    const int64_t t = pos < sv.len ? sv.owner(pos, rd, first) : 0;
+                    if (pos < sv.len && rd) {
+                        E *dst = ob + t * a.dv + dcol;
                         const float prev = acc_out ? to_f(*dst) : 0.f;
                         *dst = from_f<E>(prev + o[r]);
                     }
@@ -453,7 +482,7 @@ hipError_t launch_dk(const ChunkArgs &a, int chunk, int dk, hipStream_t s) {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream) {
     if (a.units == 0 || a.ntiles == 0) return hipSuccess;
-    if (chunk_fwd_fast_supported(dtype, chunk, dk)) return launch_chunk_fwd_fast(a, stream);
+    if (a.n_sub == 1 && chunk_fwd_fast_supported(dtype, chunk, dk)) return launch_chunk_fwd_fast(a, stream);
     if (dtype == kDtypeBf16) return launch_dk<__bf16>(a, chunk, dk, stream);
     return launch_dk<float>(a, chunk, dk, stream);
 }

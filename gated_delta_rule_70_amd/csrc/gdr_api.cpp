@@ -59,7 +59,7 @@ struct GateNames {
 gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                         const float *beta, const float *A_log, const float *dt_bias, bool gated,
                         const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
-                        const gdr_chunk_dims_t *dims, void *stream);
+                        const gdr_chunk_dims_t *dims, void *stream, int32_t n_sub = 1);
 gdr_status_t decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                          const float *beta, const float *A_log, const float *dt_bias, bool gated,
                          const float *state_in, float *state_out, void *out, const gdr_decode_dims_t *dims,
@@ -104,6 +104,13 @@ gdr_status_t gdr_chunk_fwd_gated(const void *q, const void *k, const void *v, co
     return chunk_impl(q, k, v, a, b, A_log, dt_bias, true, h0, cu_seqlens, chunk, out, hT, dims, stream);
 }
 
+gdr_status_t gdr_delta_product_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                                   const float *beta, const float *h0, const int32_t *cu_seqlens, int32_t n_delta,
+                                   int32_t chunk, void *out, float *hT, const gdr_chunk_dims_t *dims, void *stream) {
+    return chunk_impl(q, k, v, log_alpha, beta, nullptr, nullptr, false, h0, cu_seqlens, chunk, out, hT, dims,
+                      stream, n_delta);
+}
+
 gdr_status_t gdr_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                              const float *beta, const float *state_in, float *state_out, void *out,
                              const gdr_decode_dims_t *dims, void *stream) {
@@ -123,7 +130,7 @@ namespace {
 gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                         const float *beta, const float *A_log, const float *dt_bias, bool gated,
                         const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
-                        const gdr_chunk_dims_t *dims, void *stream) {
+                        const gdr_chunk_dims_t *dims, void *stream, int32_t n_sub) {
     g_last_error[0] = '\0';
     const GateNames gn = gated ? GateNames{"a", "b"} : GateNames{"log_alpha", "beta"};
     if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
@@ -136,6 +143,10 @@ gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float
     if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
     if (d.dk != 64 && d.dk != 128) return fail(GDR_ERR_UNSUPPORTED, "dk %lld is not 64 or 128", (long long)d.dk);
     if (d.dv < 32 || d.dv > 256 || d.dv % 32) return fail(GDR_ERR_UNSUPPORTED, "dv %lld is not a multiple of 32 in [32, 256]", (long long)d.dv);
+    if (n_sub < 1 || n_sub > 16) return fail(GDR_ERR_DIMS, "n_delta %d is not in [1, 16]", n_sub);
+    if (n_sub > 1 && (d.flags & GDR_REVERSE))
+        return fail(GDR_ERR_FLAGS, "GDR_REVERSE is not supported with n_delta > 1");
+    if (d.T > INT32_MAX / n_sub) return fail(GDR_ERR_DIMS, "T * n_delta must be below 2^31");
     int64_t nseq = d.B;
     if (cu_seqlens) {
         if (d.B != 1) return fail(GDR_ERR_DIMS, "cu_seqlens needs B == 1 (got %lld)", (long long)d.B);
@@ -145,7 +156,9 @@ gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float
     const int64_t es = elem_size(d.dtype);
     const int64_t nq = prod({d.B, d.Hk, d.T, d.dk}), nv = prod({d.B, d.Hv, d.T, d.dv});
     const int64_t ng = prod({d.B, d.Hv, d.T}), ns = prod({nseq, d.Hv, d.dk, d.dv});
-    if (nq < 0 || nv < 0 || ng < 0 || ns < 0 || nq > (INT64_C(1) << 60) / es)
+    // k, v and beta carry n_sub rows per token
+    const int64_t nk = prod({nq, n_sub}), nvs = prod({nv, n_sub}), ngs = prod({ng, n_sub});
+    if (nq < 0 || nv < 0 || ng < 0 || ns < 0 || nk < 0 || nvs < 0 || ngs < 0 || nk > (INT64_C(1) << 60) / es)
         return fail(GDR_ERR_DIMS, "sizes overflow");
     if (nq > 0 && (!q || !k)) return fail(GDR_ERR_NULL, "q or k is NULL");
     if (nv > 0 && (!v || !out)) return fail(GDR_ERR_NULL, "v or out is NULL");
@@ -160,8 +173,8 @@ gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float
     if ((log_alpha && !aligned(log_alpha, 4)) || (beta && !aligned(beta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
         return fail(GDR_ERR_ALIGN, "%s, %s or cu_seqlens is not 4-byte aligned", gn.a, gn.b);
 
-    const Range rq = rng("q", q, nq * es), rk = rng("k", k, nq * es), rv = rng("v", v, nv * es);
-    const Range ra = rng(gn.a, log_alpha, ng * 4), rb = rng(gn.b, beta, ng * 4);
+    const Range rq = rng("q", q, nq * es), rk = rng("k", k, nk * es), rv = rng("v", v, nvs * es);
+    const Range ra = rng(gn.a, log_alpha, ng * 4), rb = rng(gn.b, beta, ngs * 4);
     const Range rh0 = rng("h0", h0, ns * 4), rhT = rng("hT", hT, ns * 4);
     const Range rcu = rng("cu_seqlens", cu_seqlens, cu_seqlens ? (nseq + 1) * 4 : 0);
     const Range ro = rng("out", out, nv * es);
@@ -185,6 +198,7 @@ gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float
     a.units = nseq * d.Hv;
     a.ntiles = d.dv / 32;
     a.flags = d.flags;
+    a.n_sub = n_sub;
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
     if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
     const hipError_t e = gdr::launch_chunk_fwd(a, d.dtype, chunk, (int)d.dk, reinterpret_cast<hipStream_t>(stream));

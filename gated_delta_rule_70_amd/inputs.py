@@ -245,6 +245,40 @@ def gdn2_case(*, B=1, T=256, Hk=2, Hv=None, dk=64, dv=64, dtype=torch.float32, s
     return Gdn2Case(q.to(dtype).contiguous(), k.to(dtype).contiguous(), v, gate.float().contiguous(), b, w, h0, cu)
 
 
+@dataclass
+class DeltaProductCase:
+    q: torch.Tensor          # [B, Hk, T, dk]
+    k: torch.Tensor          # [B, Hk, T, n, dk]
+    v: torch.Tensor          # [B, Hv, T, n, dv]
+    log_alpha: torch.Tensor  # [B, Hv, T] fp32
+    beta: torch.Tensor       # [B, Hv, T, n] fp32
+    h0: torch.Tensor | None  # [S, Hv, dk, dv] fp32
+    cu_seqlens: torch.Tensor | None = None
+
+
+def delta_product_case(*, B=1, T=256, n=2, Hk=2, Hv=None, dk=64, dv=64, dtype=torch.float32, seed=0,
+                       h0_std=0.0, lengths=None, regime="config") -> DeltaProductCase:
+    """DeltaProduct inputs: the distributions of ``chunk_case`` with n keys, values and betas per
+    token (every sub-step's key L2-normalised in fp32) and one decay per token. Draw order: A, q,
+    k, v, the decay normals (or uniforms), the beta normals, h0."""
+    Hv = Hk if Hv is None else Hv
+    g = _gen(seed + 90000)
+    cu = None
+    if lengths is not None:
+        assert B == 1
+        T = int(sum(lengths))
+        cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    nseq = B if cu is None else len(lengths)
+    A = torch.log(torch.rand(Hv, generator=g) * 15.0 + 1.0)
+    q = _l2_normalise(_normal(g, (B, Hk, T, dk))).to(dtype).contiguous()
+    k = _l2_normalise(_normal(g, (B, Hk, T, n, dk))).to(dtype).contiguous()
+    v = _normal(g, (B, Hv, T, n, dv)).to(dtype).contiguous()
+    log_alpha, _ = _gates(g, A, (B, Hv, T), regime)
+    beta = torch.sigmoid(_normal(g, (B, Hv, T, n))).contiguous()
+    h0 = _normal(g, (nseq, Hv, dk, dv), h0_std).contiguous() if h0_std > 0 else None
+    return DeltaProductCase(q, k, v, log_alpha, beta, h0, cu)
+
+
 WORKLOADS = {
     0: "gdr-fwd-fp32-B1-H2-T256-d64-c64",
     1: "gdr-chunk-fwd-bf16-B4-H16-T4096-d128-c64",

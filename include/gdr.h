@@ -190,6 +190,36 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
                                    const gdr_decode_dims_t *dims, void *stream);
 
 /*
+ * gdr_delta_product_fwd - DeltaProduct: n_delta delta sub-steps per token (the n_delta branch of
+ * `_delta_reference` and `chunked_delta` on the "Prizma seq/delta.py" page). For token t and
+ * sub-step j = 0 .. n_delta-1, with alpha_tj = exp(log_alpha_t) for j = 0 and 1 otherwise (the
+ * decay applies once per token, on its first sub-step):
+ *
+ *   u_tj = beta_tj (v_tj - alpha_tj H^T k_tj),   H <- alpha_tj H + k_tj u_tj^T
+ *
+ * GDR_READ_PRE reads o_t = H^T q_t before the token's first sub-step (the page's read); without
+ * it the read comes after the token's last sub-step. This is gdr_chunk_fwd over the sequence of
+ * T * n_delta sub-steps, and is computed that way (chunks of sub-steps).
+ *
+ *   q           [B][Hk][T][dk]           dtype
+ *   k           [B][Hk][T][n_delta][dk]  dtype
+ *   v           [B][Hv][T][n_delta][dv]  dtype
+ *   log_alpha   [B][Hv][T]               fp32, <= 0 (one decay per token)
+ *   beta        [B][Hv][T][n_delta]      fp32
+ *   h0, cu_seqlens (in tokens), chunk (in sub-steps), out [B][Hv][T][dv], hT, dims, stream:
+ *   as gdr_chunk_fwd.
+ *
+ * n_delta in [1, 16] (GDR_ERR_DIMS otherwise, and when T * n_delta >= 2^31); GDR_REVERSE with
+ * n_delta > 1 is GDR_ERR_FLAGS; GDR_QK_L2NORM normalises q and every sub-step's key.
+ * Errors otherwise as gdr_chunk_fwd.
+ */
+gdr_status_t gdr_delta_product_fwd(const void *q, const void *k, const void *v,
+                                   const float *log_alpha, const float *beta,
+                                   const float *h0, const int32_t *cu_seqlens, int32_t n_delta,
+                                   int32_t chunk, void *out, float *hT,
+                                   const gdr_chunk_dims_t *dims, void *stream);
+
+/*
  * GDN-2: the delta rule with a decay per key channel and separate erase and write gates, the
  * update stated in the BidirectionalGatedDeltaNet2 docstring on the "tiny_gdn/fugue.py" page
  * (which also forms g = -exp(A_log) softplus(f + dt_bias) per key channel, b = sigmoid(.) or

@@ -236,3 +236,24 @@ def test_gdn2_decode_rejects():
     assert call(binding.DecodeDims(4, 2, 4, 128, 128, 1, 4))[0] == "GDR_ERR_FLAGS"
     assert call(binding.DecodeDims(4, 2, 4, 96, 128, 1, 0))[0] == "GDR_ERR_UNSUPPORTED"
     assert call(binding.DecodeDims(0, 2, 4, 128, 128, 1, 0))[0] == "GDR_OK"
+
+
+@needs_lib
+def test_delta_product_rejects():
+    lib = binding.load()
+    vp = ctypes.c_void_p
+
+    def call(n=2, flags=0, T=128, out=FAKE * 6):
+        dims = binding.ChunkDims(1, T, 2, 2, 64, 64, 0, 1, flags)
+        st = lib.gdr_delta_product_fwd(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5), None, None,
+                                       n, 64, vp(out), None, ctypes.byref(dims), None)
+        return binding.STATUS[st], lib.gdr_last_error().decode()
+
+    assert call(n=0) == ("GDR_ERR_DIMS", "n_delta 0 is not in [1, 16]")
+    assert call(n=17)[0] == "GDR_ERR_DIMS"
+    st, msg = call(flags=2)
+    assert st == "GDR_ERR_FLAGS" and "GDR_REVERSE" in msg, msg
+    assert call(T=(1 << 30))[0] == "GDR_ERR_DIMS"
+    # k holds n rows per token: an output placed after a one-row-per-token k still overlaps it
+    st, msg = call(n=4, out=FAKE * 2 + 2 * 128 * 64 * 2 + 64)
+    assert st == "GDR_ERR_ALIAS" and "out overlaps k" in msg, msg

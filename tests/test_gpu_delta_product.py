@@ -1,0 +1,130 @@
+"""Parity of the DeltaProduct forward (``gdr_delta_product_fwd``, n delta sub-steps per token) with
+the fp64 oracle ``oracle.delta_product`` (the n_delta branch of the "Prizma seq/delta.py" page).
+Tolerances as in test_gpu_parity.py: fp32 max abs <= 2e-4, bf16 relative Frobenius <= 2e-2."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_70_amd import inputs
+from oracle import delta_product as dp
+
+pytestmark = pytest.mark.gpu
+
+FP32_ABS = 2e-4
+BF16_REL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def gdr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_70_amd import binding
+    binding.lib()
+    return binding
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(x, ref, dtype, what):
+    x = np.asarray(x, dtype=np.float64)
+    assert np.all(np.isfinite(x)), "%s: non-finite values" % what
+    if dtype == torch.float32:
+        e = float(np.max(np.abs(x - ref))) if x.size else 0.0
+        assert e <= FP32_ABS, "%s: max abs err %.3e > %.1e" % (what, e, FP32_ABS)
+    else:
+        e = float(np.linalg.norm(x - ref)) / max(float(np.linalg.norm(ref)), 1e-30)
+        assert e <= BF16_REL, "%s: rel Frobenius err %.3e > %.1e" % (what, e, BF16_REL)
+    return e
+
+
+def gpu_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _run(gdr, c, chunk, read, l2norm=False, accumulate=None):
+    d = lambda t: None if t is None else t.cuda()
+    out = None if accumulate is None else accumulate.cuda().clone()
+    o, hT = gdr.delta_product_fwd(d(c.q), d(c.k), d(c.v), d(c.log_alpha), d(c.beta), d(c.h0), d(c.cu_seqlens),
+                                  chunk=chunk, read=read, l2norm=l2norm, out=out, accumulate=accumulate is not None)
+    torch.cuda.synchronize()
+    return gpu_np(o), gpu_np(hT)
+
+
+CASES = [
+    dict(B=2, T=100, n=2, Hk=2, Hv=2, dk=64, dv=64, dtype=torch.float32, chunk=64),
+    dict(B=1, T=77, n=3, Hk=1, Hv=2, dk=128, dv=64, dtype=torch.float32, chunk=32),
+    dict(B=1, T=150, n=2, Hk=2, Hv=4, dk=128, dv=128, dtype=torch.bfloat16, chunk=64),
+    dict(B=2, T=61, n=4, Hk=1, Hv=1, dk=64, dv=96, dtype=torch.bfloat16, chunk=16),
+]
+
+
+def _ids(c):
+    return "B%d-T%d-n%d-Hk%d-Hv%d-dk%d-dv%d-%s-c%d" % (c["B"], c["T"], c["n"], c["Hk"], c["Hv"], c["dk"], c["dv"],
+                                                      str(c["dtype"]).split(".")[-1], c["chunk"])
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=_ids)
+@pytest.mark.parametrize("regime", ["config", "slow"])
+@pytest.mark.parametrize("read", ["pre", "post"])
+def test_parity(gdr, cfg, regime, read):
+    cfg = dict(cfg)
+    chunk, dtype = cfg.pop("chunk"), cfg["dtype"]
+    _say("delta product %s %s %s" % (_ids(dict(cfg, chunk=chunk)), regime, read))
+    c = inputs.delta_product_case(**cfg, seed=7, h0_std=0.5, regime=regime)
+    o, hT = _run(gdr, c, chunk, read)
+    ro, rh = dp.scan(c.q, c.k, c.v, c.log_alpha, c.beta, c.h0, read=read)
+    check(o, ro, dtype, "out")
+    check(hT, rh, dtype, "hT")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_varlen_accumulate_l2norm(gdr, dtype):
+    lengths = [0, 1, 9, 32, 33, 70]
+    _say("delta product varlen %s" % dtype)
+    c = inputs.delta_product_case(B=1, n=3, Hk=2, Hv=2, dk=64, dv=64, dtype=dtype, seed=17, h0_std=0.5,
+                                  lengths=lengths, regime="slow")
+    # raw rows of any length: the kernel normalises q and every sub-step's key
+    g = torch.Generator().manual_seed(18)
+    c.q = (c.q.float() * (torch.rand(c.q.shape[:-1] + (1,), generator=g) * 3 + 0.5)).to(dtype).contiguous()
+    c.k = (c.k.float() * (torch.rand(c.k.shape[:-1] + (1,), generator=g) * 3 + 0.5)).to(dtype).contiguous()
+    base = torch.randn(1, 2, sum(lengths), 64, generator=g).to(dtype)
+    for read in ("pre", "post"):
+        o, hT = _run(gdr, c, 32, read, l2norm=True, accumulate=base)
+        ref = base.double().numpy().copy()
+        _, rh = dp.scan(c.q, c.k, c.v, c.log_alpha, c.beta, c.h0, c.cu_seqlens, read=read, out=ref, l2norm=True)
+        check(o, ref, dtype, "out %s" % read)
+        check(hT, rh, dtype, "hT %s" % read)
+
+
+def test_one_substep_is_the_plain_rule(gdr):
+    # n = 1 through this entry point equals gdr_chunk_fwd on the same inputs
+    _say("delta product n=1")
+    c = inputs.delta_product_case(B=2, T=90, n=1, Hk=2, Hv=2, dk=64, dv=64, dtype=torch.float32, seed=27, h0_std=0.5)
+    d = lambda t: t.cuda()
+    o1, h1 = gdr.delta_product_fwd(d(c.q), d(c.k), d(c.v), d(c.log_alpha), d(c.beta), d(c.h0), read="post")
+    o2, h2 = gdr.chunk_fwd(d(c.q), d(c.k[:, :, :, 0].contiguous()), d(c.v[:, :, :, 0].contiguous()),
+                           d(c.log_alpha), d(c.beta[..., 0].contiguous()), d(c.h0))
+    torch.cuda.synchronize()
+    check(gpu_np(o1), gpu_np(o2), torch.float32, "out")
+    check(gpu_np(h1), gpu_np(h2), torch.float32, "hT")
+
+
+def test_full_size_sampled(gdr):
+    # B4 H16 T4096 d128 bf16 with two sub-steps per token, chunk 64: four (sequence, head) pairs
+    # against the oracle, pre-write read (the page's)
+    _say("delta product full size B4 H16 T4096 n2")
+    c = inputs.delta_product_case(B=4, T=4096, n=2, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16, seed=37,
+                                  h0_std=0.1)
+    o, hT = _run(gdr, c, 64, "pre")
+    for (bi, h) in ((0, 0), (1, 5), (2, 10), (3, 15)):
+        sl = lambda t: t[bi:bi + 1, h:h + 1]
+        ro, rh = dp.scan(sl(c.q), sl(c.k), sl(c.v), sl(c.log_alpha), sl(c.beta), sl(c.h0), read="pre")
+        check(o[bi:bi + 1, h:h + 1], ro, torch.bfloat16, "out (%d, %d)" % (bi, h))
+        check(hT[bi:bi + 1, h:h + 1], rh, torch.bfloat16, "hT (%d, %d)" % (bi, h))
