@@ -26,6 +26,7 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
            "gdr_gdn2_chunk_fwd", "gdr_gdn2_decode_step", "gdr_delta_product_fwd",
+           "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_bytes",
            "gdr_status_string", "gdr_last_error", "gdr_abi_version", "gdr_selftest_mfma")
 
 
@@ -62,6 +63,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step_gated.argtypes = [p, p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
     lib.gdr_decode_step_gated.restype = ctypes.c_int
+    lib.gdr_chunk_bwd.argtypes = [p] * 15 + [p, ctypes.c_int64, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDims), i32]
+    lib.gdr_chunk_bwd_workspace_bytes.restype = ctypes.c_int64
     lib.gdr_delta_product_fwd.argtypes = [p, p, p, p, p, p, p, i32, i32, p, p, ctypes.POINTER(ChunkDims), p]
     lib.gdr_delta_product_fwd.restype = ctypes.c_int
     lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
@@ -250,6 +255,57 @@ def _decode(q, k, v, ga, gb, A_log, dt_bias, state_in, state_out, out, read, l2n
         _check(lib().gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(gb), _ptr(state_in),
                                      _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q)))
     return out, state_out
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, dout, h0=None, cu_seqlens=None, dhT=None, *, read: str = "post",
+              reverse: bool = False, want_dh0: bool = True, workspace=None):
+    """Gradients of ``chunk_fwd`` (``gdr_chunk_bwd``): the inputs as given to the forward, dout
+    [B, Hv, T, dv] in their dtype, dhT [S, Hv, dk, dv] fp32 or None. Returns fp32 tensors
+    (dq, dk, dv, dlog_alpha, dbeta, dh0 or None). ``workspace`` (a uint8 GPU tensor of at least
+    ``chunk_bwd_workspace_bytes`` bytes) is allocated here when not given."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    _need(k, "k", dt, (B, Hk, T, dk), dev)
+    _need(v, "v", dt, (B, Hv, T, dv), dev)
+    _need(dout, "dout", dt, (B, Hv, T, dv), dev)
+    _need(log_alpha, "log_alpha", torch.float32, (B, Hv, T), dev)
+    _need(beta, "beta", torch.float32, (B, Hv, T), dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    for name, t in (("h0", h0), ("dhT", dhT)):
+        if t is not None:
+            _need(t, name, torch.float32, (S, Hv, dk, dv), dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0)
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    need = lib().gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), int(cu_seqlens is not None))
+    if need < 0:
+        raise ValueError("invalid sizes for the backward workspace")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError("workspace holds %d bytes, %d needed" % (workspace.numel(), need))
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk_ = torch.empty((B, Hk, T, dk), **f32), torch.empty((B, Hk, T, dk), **f32)
+    dv_ = torch.empty((B, Hv, T, dv), **f32)
+    dla, dbe = torch.empty((B, Hv, T), **f32), torch.empty((B, Hv, T), **f32)
+    dh0 = torch.empty((S, Hv, dk, dv), **f32) if want_dh0 else None
+    _check(lib().gdr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+                               _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbe), _ptr(dh0),
+                               _ptr(workspace), ctypes.c_int64(workspace.numel()), ctypes.byref(dims), _stream(q)))
+    return dq, dk_, dv_, dla, dbe, dh0
+
+
+def chunk_bwd_workspace_bytes(B, T, Hk, Hv, dk, dv, num_seqs=0, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace ``gdr_chunk_bwd`` needs (num_seqs > 0: packed sequences)."""
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, num_seqs, _dtype_code(dtype), 0)
+    return int(lib().gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), int(num_seqs > 0)))
 
 
 def delta_product_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk: int = 64,

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 
-SOURCES = ["gdr_api.cpp", "chunk_fwd.hip", "chunk_fwd_fast.hip", "decode.hip", "gdn2_fwd.hip", "gdn2_decode.hip"]
+SOURCES = ["gdr_api.cpp", "chunk_fwd.hip", "chunk_fwd_fast.hip", "decode.hip", "gdn2_fwd.hip", "gdn2_decode.hip", "bwd.hip"]
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 

@@ -397,6 +397,110 @@ gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v, c
 
 }  // extern "C"
 
+namespace {
+
+// block-start states per value head: one slot per 32-token block of every sequence
+int64_t bwd_slots(const gdr_chunk_dims_t &d, bool packed) {
+    const int64_t CB = gdr::kBwdBlock;
+    if (packed) return d.T / CB + d.num_seqs + 1;
+    return d.B * ((d.T + CB - 1) / CB);
+}
+
+int64_t bwd_workspace_bytes(const gdr_chunk_dims_t &d, bool packed) {
+    const int64_t nseq = packed ? d.num_seqs : d.B;
+    const int64_t states = d.Hv * bwd_slots(d, packed) + nseq * d.Hv * gdr::kBwdBlock;
+    const int64_t b = prod({states, d.dk, d.dv, 4});
+    return b;
+}
+
+gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
+                      const float *h0, const int32_t *cu_seqlens, const void *dout, const float *dhT, float *dq,
+                      float *dk, float *dv, float *dlog_alpha, float *dbeta, float *dh0, void *workspace,
+                      int64_t workspace_bytes, const gdr_chunk_dims_t *dims, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    const gdr_chunk_dims_t d = *dims;
+    if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
+    if (d.flags & ~(GDR_READ_PRE | GDR_REVERSE | GDR_ACCUMULATE))
+        return fail(GDR_ERR_FLAGS, "flags 0x%x: the backward takes GDR_READ_PRE, GDR_REVERSE and GDR_ACCUMULATE", d.flags);
+    if (d.B < 0 || d.T < 0) return fail(GDR_ERR_DIMS, "B (%lld) and T (%lld) must be >= 0", (long long)d.B, (long long)d.T);
+    if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
+    if ((d.dk != 64 && d.dk != 128) || (d.dv != 64 && d.dv != 128))
+        return fail(GDR_ERR_UNSUPPORTED, "the backward takes dk and dv of 64 or 128 (got %lld, %lld)", (long long)d.dk, (long long)d.dv);
+    int64_t nseq = d.B;
+    if (cu_seqlens) {
+        if (d.B != 1) return fail(GDR_ERR_DIMS, "cu_seqlens needs B == 1 (got %lld)", (long long)d.B);
+        if (d.num_seqs < 1) return fail(GDR_ERR_DIMS, "num_seqs (%lld) must be >= 1 with cu_seqlens", (long long)d.num_seqs);
+        nseq = d.num_seqs;
+    }
+    const int64_t es = elem_size(d.dtype);
+    const int64_t nq = prod({d.B, d.Hk, d.T, d.dk}), nv = prod({d.B, d.Hv, d.T, d.dv});
+    const int64_t ng = prod({d.B, d.Hv, d.T}), ns = prod({nseq, d.Hv, d.dk, d.dv});
+    const int64_t need = bwd_workspace_bytes(d, cu_seqlens != nullptr);
+    if (nq < 0 || nv < 0 || ng < 0 || ns < 0 || need < 0 || nq > (INT64_C(1) << 59))
+        return fail(GDR_ERR_DIMS, "sizes overflow");
+    if (nq > 0 && (!q || !k || !dq || !dk)) return fail(GDR_ERR_NULL, "q, k, dq or dk is NULL");
+    if (nv > 0 && (!v || !dout || !dv)) return fail(GDR_ERR_NULL, "v, dout or dv is NULL");
+    if (ng > 0 && (!log_alpha || !beta || !dlog_alpha || !dbeta))
+        return fail(GDR_ERR_NULL, "log_alpha, beta, dlog_alpha or dbeta is NULL");
+    if (nseq * d.Hv > 0 && !workspace) return fail(GDR_ERR_NULL, "workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(GDR_ERR_DIMS, "workspace_bytes %lld is below the %lld bytes this call needs", (long long)workspace_bytes, (long long)need);
+    const void *al16[] = {q, k, v, dout, h0, dhT, dq, dk, dv, dh0, workspace};
+    const char *al16n[] = {"q", "k", "v", "dout", "h0", "dhT", "dq", "dk", "dv", "dh0", "workspace"};
+    for (int i = 0; i < 11; ++i)
+        if (al16[i] && !aligned(al16[i], 16)) return fail(GDR_ERR_ALIGN, "%s is not 16-byte aligned", al16n[i]);
+    if ((log_alpha && !aligned(log_alpha, 4)) || (beta && !aligned(beta, 4)) || (dlog_alpha && !aligned(dlog_alpha, 4)) ||
+        (dbeta && !aligned(dbeta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return fail(GDR_ERR_ALIGN, "a gate, gate gradient or cu_seqlens pointer is not 4-byte aligned");
+    const Range ins[] = {rng("q", q, nq * es), rng("k", k, nq * es), rng("v", v, nv * es),
+                         rng("log_alpha", log_alpha, ng * 4), rng("beta", beta, ng * 4), rng("h0", h0, ns * 4),
+                         rng("cu_seqlens", cu_seqlens, cu_seqlens ? (nseq + 1) * 4 : 0), rng("dout", dout, nv * es),
+                         rng("dhT", dhT, ns * 4)};
+    const Range outs[] = {rng("dq", dq, nq * 4), rng("dk", dk, nq * 4), rng("dv", dv, nv * 4),
+                          rng("dlog_alpha", dlog_alpha, ng * 4), rng("dbeta", dbeta, ng * 4), rng("dh0", dh0, ns * 4),
+                          rng("workspace", workspace, need)};
+    for (const Range &o : outs) {
+        for (const Range &r : ins)
+            if (overlap(o, r)) return fail(GDR_ERR_ALIAS, "%s overlaps %s", o.name, r.name);
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlap(o, o2)) return fail(GDR_ERR_ALIAS, "%s overlaps %s", o.name, o2.name);
+    }
+    gdr::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.dout = dout;
+    a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0; a.dhT = dhT;
+    a.cu_seqlens = cu_seqlens;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
+    a.ws = static_cast<float *>(workspace);
+    a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv;
+    a.units = nseq * d.Hv;
+    a.nslots = bwd_slots(d, cu_seqlens != nullptr);
+    a.flags = d.flags;
+    if (a.units > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units");
+    const hipError_t e = gdr::launch_bwd(a, d.dtype, (int)d.dk, (int)d.dv, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t gdr_chunk_bwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t packed) {
+    if (!dims || dims->T < 0 || dims->B < 0 || dims->Hv < 1 || (packed && dims->num_seqs < 1)) return -1;
+    return bwd_workspace_bytes(*dims, packed != 0);
+}
+
+gdr_status_t gdr_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
+                           const float *h0, const int32_t *cu_seqlens, const void *dout, const float *dhT, float *dq,
+                           float *dk, float *dv, float *dlog_alpha, float *dbeta, float *dh0, void *workspace,
+                           int64_t workspace_bytes, const gdr_chunk_dims_t *dims, void *stream) {
+    return bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dlog_alpha, dbeta, dh0,
+                    workspace, workspace_bytes, dims, stream);
+}
+
+}  // extern "C"
+
 extern "C" {
 
 gdr_status_t gdr_selftest_mfma(const float *a, const float *b, float *d, void *stream) {

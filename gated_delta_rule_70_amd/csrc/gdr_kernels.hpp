@@ -68,12 +68,30 @@ struct Gdn2DecodeArgs {
     uint32_t flags;
 };
 
+// Backward of the scalar rule. Gradient buffers are fp32: dq, dk [B][Hk][T][dk] (summed over the
+// value heads of a key head), dv [B][Hv][T][dv], dlog_alpha, dbeta [B][Hv][T], dh0 like h0.
+// ws: states at the start of every kBwdBlock-token block (nslots per value head) followed by
+// one block of per-token states per (sequence, value head).
+constexpr int kBwdBlock = 32;
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *log_alpha, *beta, *h0, *dhT;
+    const int32_t *cu_seqlens;
+    float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dh0;
+    float *ws;
+    int64_t B, T, Hk, Hv;
+    int64_t units;   // sequences x value heads
+    int64_t nslots;  // block-start states per value head
+    uint32_t flags;
+};
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream);
 bool chunk_fwd_fast_supported(int dtype, int chunk, int dk);
 hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream);
 bool gdn2_chunk_supported(int dtype, int chunk, int dk);
 hipError_t launch_gdn2_chunk_fwd(const Gdn2Args &a, int dtype, int chunk, int dk, hipStream_t stream);
 hipError_t launch_gdn2_decode(const Gdn2DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 // softplus without overflow: max(x, 0) + log(1 + e^{-|x|}); the second term is below 2^-24
 // (and lost next to 1) only where it is negligible against the first or is itself < 6e-8

@@ -190,6 +190,42 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
                                    const gdr_decode_dims_t *dims, void *stream);
 
 /*
+ * gdr_chunk_bwd - gradients of gdr_chunk_fwd (the backward pass for training through it).
+ *
+ * Given the upstream gradients dout (of out) and dhT (of the final state), computes the
+ * gradients of sum(out * dout) + sum(hT * dhT) with respect to every input: the derivative of
+ * the per-token recurrence (the pages print no backward; the "Prizma seq/delta.py" page requires
+ * the chunked form to agree with the recurrence in gradient, and the other pages train through
+ * the operation). Same flags, layouts and segments as gdr_chunk_fwd (GDR_ACCUMULATE does not
+ * change the gradients; GDR_QK_L2NORM is not taken: pass q, k as the forward saw them).
+ *
+ *   q, k, v, log_alpha, beta, h0, cu_seqlens, dims: exactly as given to gdr_chunk_fwd
+ *   dout        [B][Hv][T][dv]  dtype
+ *   dhT         [S][Hv][dk][dv] fp32, or NULL for zero
+ *   dq, dk      [B][Hk][T][dk]  fp32 (a key head receives the sum over its value heads)
+ *   dv          [B][Hv][T][dv]  fp32
+ *   dlog_alpha, dbeta [B][Hv][T] fp32
+ *   dh0         [S][Hv][dk][dv] fp32, or NULL when not wanted
+ *   workspace   DEVICE scratch of at least gdr_chunk_bwd_workspace_bytes(dims, cu_seqlens != NULL)
+ *               bytes, 16-byte aligned, owned by the caller; its contents are not needed
+ *               before or after the call. Calls that share a workspace must not overlap.
+ *
+ * dk and dv must be 64 or 128. Every output is fully written (dq and dk are cleared on the
+ * stream first). Outputs and workspace must not overlap inputs or each other (GDR_ERR_ALIAS).
+ * Errors as gdr_chunk_fwd, plus GDR_ERR_DIMS when workspace_bytes is too small.
+ * The state before every token is recomputed from states kept at the start of each block of
+ * 32 tokens, so the workspace holds (blocks + one block per sequence-head) fp32 states.
+ */
+int64_t gdr_chunk_bwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t packed);
+gdr_status_t gdr_chunk_bwd(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const float *h0, const int32_t *cu_seqlens,
+                           const void *dout, const float *dhT,
+                           float *dq, float *dk, float *dv, float *dlog_alpha, float *dbeta, float *dh0,
+                           void *workspace, int64_t workspace_bytes,
+                           const gdr_chunk_dims_t *dims, void *stream);
+
+/*
  * gdr_delta_product_fwd - DeltaProduct: n_delta delta sub-steps per token (the n_delta branch of
  * `_delta_reference` and `chunked_delta` on the "Prizma seq/delta.py" page). For token t and
  * sub-step j = 0 .. n_delta-1, with alpha_tj = exp(log_alpha_t) for j = 0 and 1 otherwise (the

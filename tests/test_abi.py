@@ -257,3 +257,27 @@ def test_delta_product_rejects():
     # k holds n rows per token: an output placed after a one-row-per-token k still overlaps it
     st, msg = call(n=4, out=FAKE * 2 + 2 * 128 * 64 * 2 + 64)
     assert st == "GDR_ERR_ALIAS" and "out overlaps k" in msg, msg
+
+
+@needs_lib
+def test_backward_rejects():
+    lib = binding.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(flags=0, dk=64, ws=FAKE * 20, ws_bytes=1 << 40, dq=FAKE * 10):
+        dims = binding.ChunkDims(1, 128, 2, 2, dk, 64, 0, 1, flags)
+        st = lib.gdr_chunk_bwd(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5), None, None,
+                               vp(FAKE * 6), None, vp(dq), vp(FAKE * 11), vp(FAKE * 12), vp(FAKE * 13),
+                               vp(FAKE * 14), None, vp(ws), ctypes.c_int64(ws_bytes), ctypes.byref(dims), None)
+        return binding.STATUS[st], lib.gdr_last_error().decode()
+
+    assert call(flags=8)[0] == "GDR_ERR_FLAGS"
+    assert call(dk=96)[0] == "GDR_ERR_UNSUPPORTED"
+    st, msg = call(ws_bytes=1024)
+    assert st == "GDR_ERR_DIMS" and "workspace_bytes" in msg, msg
+    assert call(ws=None)[0] == "GDR_ERR_NULL"
+    st, msg = call(dq=FAKE + 64)
+    assert st == "GDR_ERR_ALIAS" and "dq overlaps q" in msg, msg
+    dims = binding.ChunkDims(4, 4096, 16, 16, 128, 128, 0, 1, 0)
+    # (16 heads x 4 x 128 block starts + 64 sequence-heads x 32) states of 64 KiB
+    assert lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), 0) == (16 * 4 * 128 + 64 * 32) * 128 * 128 * 4
