@@ -235,6 +235,41 @@ def bench_gdn2(binding, inputs, steps):
     return chunk, dict(ms=dms, state_bytes=sbytes, io_bytes=io, tokens=N)
 
 
+def bench_delta_product(binding, inputs, steps):
+    """DeltaProduct with two sub-steps per token on the workload-1 shapes (B4 H16 T4096 d128 bf16),
+    pre-write read (the page's), chunk 64 of sub-steps."""
+    import torch
+    dev = torch.device("cuda:0")
+    c = inputs.delta_product_case(B=4, T=4096, n=2, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16,
+                                  seed=1001, h0_std=0.1)
+    q, k, v, la, b, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.log_alpha, c.beta, c.h0))
+    out, hT = torch.empty((4, 16, 4096, 128), dtype=torch.bfloat16, device=dev), torch.empty_like(h0)
+    fn = lambda: binding.delta_product_fwd(q, k, v, la, b, h0, chunk=64, read="pre", out=out, hT=hT)
+    ms, _ = timed(fn, steps, 100, torch.cuda.current_stream(dev))
+    tok = 4 * 16 * 4096
+    nbytes = tok * 128 * 2 * (1 + 2 + 2 + 1) + tok * 4 * (1 + 2) + 2 * 4 * 16 * 128 * 128 * 4
+    return dict(ms=ms, tokens=4 * 4096, bytes=nbytes)
+
+
+def bench_backward(binding, inputs, steps):
+    """Gradients of the workload-1 forward (B4 H16 T4096 d128, bf16 inputs, post-write read) with
+    respect to every input, from random upstream gradients of the outputs and final state."""
+    import torch
+    dev = torch.device("cuda:0")
+    c = inputs.workload1()
+    q, k, v, la, b, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.log_alpha, c.beta, c.h0))
+    g = torch.Generator(device="cpu").manual_seed(5)
+    dout = torch.randn(tuple(c.v.shape), generator=g).to(torch.bfloat16).to(dev)
+    dhT = torch.randn(tuple(c.h0.shape), generator=g).to(dev)
+    ws = torch.empty(binding.chunk_bwd_workspace_bytes(4, 4096, 16, 16, 128, 128), dtype=torch.uint8, device=dev)
+    fn = lambda: binding.chunk_bwd(q, k, v, la, b, dout, h0, None, dhT, workspace=ws)
+    ms, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev))
+    tok = 4 * 16 * 4096
+    # inputs, dout read once; gradients written once (dq, dk, dv fp32); h0, dhT, dh0
+    nbytes = tok * 128 * 2 * 4 + tok * 4 * 4 + tok * 128 * 4 * 3 + 3 * 4 * 16 * 128 * 128 * 4
+    return dict(ms=ms, tokens=4 * 4096, bytes=nbytes, ws_bytes=ws.numel())
+
+
 def cpu_baseline(inputs, min_wall=1.5, max_reps=20):
     """The fp64 oracle, as it is, on this host's cores: the whole B4 H16 T4096 d128 workload,
     repeated until at least `min_wall` seconds have passed (a bounded sample)."""
@@ -277,8 +312,8 @@ def main():
     # timed 16% slower than with 300); 500 calls are about 50 ms
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "all"], default="all",
-                    help="gdn2: only the GDN-2 workloads (for profiling them)")
+    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "all"], default="all",
+                    help="gdn2, bwd: only the GDN-2 workloads or the backward (for profiling them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -295,6 +330,10 @@ def main():
     binding.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.only == "bwd":
+        r = bench_backward(binding, inputs, args.steps)
+        print(json.dumps({"bwd_ms": r["ms"], "steps": args.steps, "workspace_bytes": r["ws_bytes"]}), flush=True)
+        return
     if args.only == "gdn2":
         g2, g2d = bench_gdn2(binding, inputs, args.steps)
         print(json.dumps({"gdn2_chunk_ms": g2["ms"], "gdn2_chunk_bytes": g2["bytes"], "steps": args.steps,
@@ -340,6 +379,8 @@ def main():
         bd = bench_bidir(binding, inputs, max(3, args.steps // 4))
         fu = bench_fused(binding, inputs, max(3, args.steps // 4))
         g2, g2d = bench_gdn2(binding, inputs, max(3, args.steps // 8))
+        dpr = bench_delta_product(binding, inputs, max(3, args.steps // 4))
+        bwr = bench_backward(binding, inputs, 3)
         res["other_workloads"] = {
             inputs.WORKLOADS[2]: {"tokens_per_s": vl["tokens"] / (vl["ms"] / 1e3), "ms": vl["ms"],
                                   "hbm_frac": vl["bytes"] / (vl["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -356,6 +397,15 @@ def main():
                              "bytes_per_launch": g2["bytes"], "kernel": "gdn2_chunk_kernel<bf16, 32, 128>",
                              "traffic": measured_traffic("gdn2_chunk_B4_H16_T4096_d128_hbm_traffic.md",
                                                          "gdn2_fwd.hip", "HBM bytes per launch")}},
+            "delta-product-n2-pre-bf16-B4-H16-T4096-d128-c64": {
+                "tokens_per_s": dpr["tokens"] / (dpr["ms"] / 1e3), "ms": dpr["ms"],
+                "hbm_frac": dpr["bytes"] / (dpr["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "kernel": "chunk_fwd_kernel<bf16, 64, 128> over 2 sub-steps per token"},
+            "gdr-backward-bf16-B4-H16-T4096-d128": {
+                "tokens_per_s": bwr["tokens"] / (bwr["ms"] / 1e3), "ms": bwr["ms"],
+                "hbm_frac": bwr["bytes"] / (bwr["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "workspace_bytes": bwr["ws_bytes"], "kernel": "bwd_kernel<bf16, 128, 128>",
+                "note": "per-token adjoint recurrence, one workgroup per sequence-head"},
             "gdn2-decode-bf16-N256-Hk16-Hv32-d128": {
                 "state_GB_per_s": g2d["state_bytes"] / (g2d["ms"] / 1e3) / 1e9, "us_per_step": g2d["ms"] * 1e3,
                 "roofline": {"bound": "hbm",
