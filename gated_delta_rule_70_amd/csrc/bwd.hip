@@ -12,15 +12,18 @@
 // The pages print no backward; this is the derivative of the recurrence they define (the
 // "Prizma seq/delta.py" page requires forward and gradient agreement with it).
 //
-// One workgroup of 256 threads per (sequence, value head), with the state layout of the decode
-// step: each thread holds 4 adjacent columns of a band of rows of the state H and of its
-// adjoint dH in registers. Reductions over rows go through LDS (one barrier per token, the
-// partials double-buffered); reductions over columns stay inside a row band (32 lanes for
-// d_v = 128) as lane shuffles. Three sweeps per sequence: a forward sweep that stores the state
-// at the start of every 32-token block in the workspace; then, block by block from the last,
-// a forward recompute that stores the state before each token of the block (workspace), and the
-// reverse adjoint sweep over the block. dq and dk are summed over the value heads that share a
-// key head with float atomics (the buffers are cleared first by a fill kernel).
+// One workgroup of 256 threads per (sequence, value head, 32 columns of d_v), with the state
+// layout of the decode step: each thread holds 4 adjacent columns of a band of rows of its slice
+// of the state H and of the adjoint dH in registers. Every quantity of the recurrence is either
+// per column (x, u, du, dv) or a sum over columns of per-column terms (dq, dk, the scalars of
+// dbeta and dlog alpha), so the column slices run independently and add their partial sums with
+// float atomics into buffers a fill kernel clears first (this also sums dq and dk over the value
+// heads that share a key head). Reductions over rows go through LDS (one barrier per token, the
+// partials double-buffered); reductions over the slice's columns stay inside a row band (8
+// lanes) as lane shuffles. Three sweeps per sequence: a forward sweep that stores the slice of
+// the state at the start of every 32-token block in the workspace; then, block by block from the
+// last, a forward recompute that stores the slice before each token of the block (workspace),
+// and the reverse adjoint sweep over the block.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -51,8 +54,9 @@ __device__ __forceinline__ float band_sum(float x) {
     return x;
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
+    constexpr int DV = kBwdCols;       // columns of the slice
     constexpr int CG = DV / 4;         // threads per row band (4 columns each)
     constexpr int RG = kThreads / CG;  // row bands
     constexpr int RPT = DK / RG;       // rows per thread
@@ -63,10 +67,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     __shared__ float sal[CB], sbe[CB];
     __shared__ f4 px[2][RG][CG], pd[2][RG][CG];
     __shared__ float pw[2][kThreads / 64];
+    constexpr int kRowWaves = kThreads / 64;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % CG, rg = tid / CG;
-    const int64_t unit = blockIdx.x;
+    const int64_t unit = blockIdx.x / a.ntiles;
+    const int tile = (int)(blockIdx.x % a.ntiles);
+    const int64_t dvf = a.ntiles * DV;  // full d_v
+    const int col0 = tile * DV;
     const int64_t seq = unit / a.Hv, head = unit % a.Hv;
     const int64_t kh = head / (a.Hv / a.Hk);
     const int64_t row = a.cu_seqlens ? 0 : seq;
@@ -85,18 +93,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 
     const E *qb = reinterpret_cast<const E *>(a.q) + (row * a.Hk + kh) * a.T * DK;
     const E *kb = reinterpret_cast<const E *>(a.k) + (row * a.Hk + kh) * a.T * DK;
-    const E *vb = reinterpret_cast<const E *>(a.v) + (row * a.Hv + head) * a.T * DV;
-    const E *dob = reinterpret_cast<const E *>(a.dout) + (row * a.Hv + head) * a.T * DV;
+    const E *vb = reinterpret_cast<const E *>(a.v) + (row * a.Hv + head) * a.T * dvf + col0;
+    const E *dob = reinterpret_cast<const E *>(a.dout) + (row * a.Hv + head) * a.T * dvf + col0;
     const float *lab = a.log_alpha + (row * a.Hv + head) * a.T;
     const float *beb = a.beta + (row * a.Hv + head) * a.T;
     float *dqb = a.dq + (row * a.Hk + kh) * a.T * DK;
     float *dkb = a.dk + (row * a.Hk + kh) * a.T * DK;
-    float *dvb = a.dv + (row * a.Hv + head) * a.T * DV;
+    float *dvb = a.dv + (row * a.Hv + head) * a.T * dvf + col0;
     float *dlab = a.dlog_alpha + (row * a.Hv + head) * a.T;
     float *dbeb = a.dbeta + (row * a.Hv + head) * a.T;
-    f4 *ckpt = reinterpret_cast<f4 *>(a.ws + (head * a.nslots + slot0) * (int64_t)(DK * DV));
-    f4 *cbuf = reinterpret_cast<f4 *>(a.ws + (a.Hv * a.nslots + unit * CB) * (int64_t)(DK * DV));
-    const int64_t st = DK * DV / 4;  // f4 per state
+    // states in the workspace: [head][slot][tile] and [unit][token of the block][tile] slices
+    const int64_t st = DK * DV / 4;  // f4 per slice
+    f4 *ckpt = reinterpret_cast<f4 *>(a.ws) + ((head * a.nslots + slot0) * a.ntiles + tile) * st;
+    f4 *cbuf = reinterpret_cast<f4 *>(a.ws) + ((a.Hv * a.nslots + unit * CB) * a.ntiles + tile) * st;
+    const int64_t sstride = a.ntiles * st;  // from one slot (or token) to the next
 
     // stage block b of the scan into LDS (the inputs the sweeps read token by token)
     auto stage = [&](int64_t blk, bool adjoint) {
@@ -110,8 +120,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         for (int i = tid; i < CB * DV; i += kThreads) {
             const int r = i / DV, c = i % DV;
             const int64_t t = r < n ? span.token(blk * CB + r) : 0;
-            sv[r][c] = r < n ? ld_f(vb, t * DV + c) : 0.f;
-            if (adjoint) sdo[r][c] = r < n ? ld_f(dob, t * DV + c) : 0.f;
+            sv[r][c] = r < n ? ld_f(vb, t * dvf + c) : 0.f;
+            if (adjoint) sdo[r][c] = r < n ? ld_f(dob, t * dvf + c) : 0.f;
         }
         if (tid < CB) {
             const int64_t t = tid < n ? span.token(blk * CB + tid) : 0;
@@ -140,15 +150,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     };
 
     f4 h[RPT];
-    const int64_t sbase = (seq * a.Hv + head) * st;
+    // element (row, col0 + 4 cg) of this unit's full [dk][dv] state, in f4 units
+    const int64_t sbase = (seq * a.Hv + head) * (DK * dvf / 4) + col0 / 4 + cg;
+    const int64_t srow = dvf / 4;
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-        h[r] = a.h0 ? reinterpret_cast<const f4 *>(a.h0)[sbase + (rg * RPT + r) * CG + cg] : f4{0.f, 0.f, 0.f, 0.f};
+        h[r] = a.h0 ? reinterpret_cast<const f4 *>(a.h0)[sbase + (rg * RPT + r) * srow] : f4{0.f, 0.f, 0.f, 0.f};
 
     // sweep 1: states at the block starts
     for (int64_t blk = 0; blk < nblk; ++blk) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) ckpt[blk * st + (rg * RPT + r) * CG + cg] = h[r];
+        for (int r = 0; r < RPT; ++r) ckpt[blk * sstride + (rg * RPT + r) * CG + cg] = h[r];
         stage(blk, false);
         __syncthreads();
         const int n = (int)min((int64_t)CB, span.len - blk * CB);
@@ -160,21 +172,21 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     f4 g[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-        g[r] = a.dhT ? reinterpret_cast<const f4 *>(a.dhT)[sbase + (rg * RPT + r) * CG + cg] : f4{0.f, 0.f, 0.f, 0.f};
+        g[r] = a.dhT ? reinterpret_cast<const f4 *>(a.dhT)[sbase + (rg * RPT + r) * srow] : f4{0.f, 0.f, 0.f, 0.f};
     for (int64_t blk = nblk - 1; blk >= 0; --blk) {
         stage(blk, true);
         __syncthreads();
         const int n = (int)min((int64_t)CB, span.len - blk * CB);
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) h[r] = ckpt[blk * st + (rg * RPT + r) * CG + cg];
+        for (int r = 0; r < RPT; ++r) h[r] = ckpt[blk * sstride + (rg * RPT + r) * CG + cg];
         for (int i = 0; i < n; ++i) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) cbuf[i * st + (rg * RPT + r) * CG + cg] = h[r];
+            for (int r = 0; r < RPT; ++r) cbuf[i * sstride + (rg * RPT + r) * CG + cg] = h[r];
             forward_step(h, i);
         }
         for (int i = n - 1; i >= 0; --i) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) h[r] = cbuf[i * st + (rg * RPT + r) * CG + cg];  // state before token i
+            for (int r = 0; r < RPT; ++r) h[r] = cbuf[i * sstride + (rg * RPT + r) * CG + cg];  // state before token i
             const float al = sal[i], be = sbe[i];
             const f4 do4 = {sdo[i][4 * cg], sdo[i][4 * cg + 1], sdo[i][4 * cg + 2], sdo[i][4 * cg + 3]};
             const f4 v4 = {sv[i][4 * cg], sv[i][4 * cg + 1], sv[i][4 * cg + 2], sv[i][4 * cg + 3]};
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
             hd = 0.f;
 #pragma unroll
-            for (int w = 0; w < kThreads / 64; ++w) hd += pw[buf][w];
+            for (int w = 0; w < kRowWaves; ++w) hd += pw[buf][w];
             buf ^= 1;
             const f4 e = v4 - al * x;
             const f4 u = be * e;
@@ -235,11 +247,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             if (rg == 0) {
                 const f4 dvv = be * du;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) dvb[t * DV + 4 * cg + c] = dvv[c];
+                for (int c = 0; c < 4; ++c) dvb[t * dvf + 4 * cg + c] = dvv[c];
             }
-            if (tid == 0) {
-                dbeb[t] = s_due;
-                dlab[t] = al * (hd - be * s_dux);
+            if (tid == 0) {  // this slice's share of the sums over columns
+                atomicAdd(dbeb + t, s_due);
+                atomicAdd(dlab + t, al * (hd - be * s_dux));
             }
             // dH = alpha dH' + k dx^T (+ q do^T for the pre-write read)
 #pragma unroll
@@ -253,43 +265,48 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     }
     if (a.dh0) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) reinterpret_cast<f4 *>(a.dh0)[sbase + (rg * RPT + r) * CG + cg] = g[r];
+        for (int r = 0; r < RPT; ++r) reinterpret_cast<f4 *>(a.dh0)[sbase + (rg * RPT + r) * srow] = g[r];
     }
 }
 
-__global__ void zero_kernel(float4 *p, int64_t n4) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+__global__ void zero_kernel(float *p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK>
 hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_kernel<E, DK, DV>), dim3((unsigned)a.units), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<E, DK>), dim3((unsigned)(a.units * a.ntiles)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 template <typename E>
-hipError_t launch_e(const BwdArgs &a, int dk, int dv, hipStream_t s) {
-    if (dk == 64) return dv == 64 ? launch_t<E, 64, 64>(a, s) : launch_t<E, 64, 128>(a, s);
-    return dv == 64 ? launch_t<E, 128, 64>(a, s) : launch_t<E, 128, 128>(a, s);
+hipError_t launch_e(const BwdArgs &a, int dk, hipStream_t s) {
+    return dk == 64 ? launch_t<E, 64>(a, s) : launch_t<E, 128>(a, s);
 }
 
 }  // namespace
 
+// clear n floats with a kernel (not a memset node, so the call stays safe to capture in a graph)
+hipError_t clear(float *p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd(const BwdArgs &a, int dtype, int dk, int dv, hipStream_t stream) {
-    // dq and dk are sums over value heads: clear them first (a kernel, not a memset node)
-    const int64_t n4 = a.B * a.Hk * a.T * dk / 4;
-    if (n4 > 0) {
-        const int64_t blocks = (n4 + 255) / 256;
-        const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
-        hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<float4 *>(a.dq), n4);
-        hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<float4 *>(a.dk), n4);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    (void)dv;
+    // the sums over columns and value heads start from zero
+    hipError_t e;
+    if ((e = clear(a.dq, a.B * a.Hk * a.T * dk, stream)) != hipSuccess) return e;
+    if ((e = clear(a.dk, a.B * a.Hk * a.T * dk, stream)) != hipSuccess) return e;
+    if ((e = clear(a.dlog_alpha, a.B * a.Hv * a.T, stream)) != hipSuccess) return e;
+    if ((e = clear(a.dbeta, a.B * a.Hv * a.T, stream)) != hipSuccess) return e;
     if (a.units == 0) return hipSuccess;
-    if (dtype == kDtypeBf16) return launch_e<__bf16>(a, dk, dv, stream);
-    return launch_e<float>(a, dk, dv, stream);
+    if (dtype == kDtypeBf16) return launch_e<__bf16>(a, dk, stream);
+    return launch_e<float>(a, dk, stream);
 }
 
 }  // namespace gdr

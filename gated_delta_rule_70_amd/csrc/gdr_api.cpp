@@ -425,8 +425,8 @@ gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *
         return fail(GDR_ERR_FLAGS, "flags 0x%x: the backward takes GDR_READ_PRE, GDR_REVERSE and GDR_ACCUMULATE", d.flags);
     if (d.B < 0 || d.T < 0) return fail(GDR_ERR_DIMS, "B (%lld) and T (%lld) must be >= 0", (long long)d.B, (long long)d.T);
     if (d.Hk < 1 || d.Hv < 1 || d.Hv % d.Hk) return fail(GDR_ERR_DIMS, "Hv (%lld) must be a positive multiple of Hk (%lld)", (long long)d.Hv, (long long)d.Hk);
-    if ((d.dk != 64 && d.dk != 128) || (d.dv != 64 && d.dv != 128))
-        return fail(GDR_ERR_UNSUPPORTED, "the backward takes dk and dv of 64 or 128 (got %lld, %lld)", (long long)d.dk, (long long)d.dv);
+    if (d.dk != 64 && d.dk != 128) return fail(GDR_ERR_UNSUPPORTED, "dk %lld is not 64 or 128", (long long)d.dk);
+    if (d.dv < 32 || d.dv > 256 || d.dv % 32) return fail(GDR_ERR_UNSUPPORTED, "dv %lld is not a multiple of 32 in [32, 256]", (long long)d.dv);
     int64_t nseq = d.B;
     if (cu_seqlens) {
         if (d.B != 1) return fail(GDR_ERR_DIMS, "cu_seqlens needs B == 1 (got %lld)", (long long)d.B);
@@ -475,8 +475,9 @@ gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *
     a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv;
     a.units = nseq * d.Hv;
     a.nslots = bwd_slots(d, cu_seqlens != nullptr);
+    a.ntiles = d.dv / gdr::kBwdCols;
     a.flags = d.flags;
-    if (a.units > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units");
+    if (a.units * a.ntiles > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units");
     const hipError_t e = gdr::launch_bwd(a, d.dtype, (int)d.dk, (int)d.dv, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return GDR_OK;

@@ -73,6 +73,7 @@ struct Gdn2DecodeArgs {
 // ws: states at the start of every kBwdBlock-token block (nslots per value head) followed by
 // one block of per-token states per (sequence, value head).
 constexpr int kBwdBlock = 32;
+constexpr int kBwdCols = 32;  // value columns per workgroup of the backward
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *log_alpha, *beta, *h0, *dhT;
@@ -82,6 +83,7 @@ struct BwdArgs {
     int64_t B, T, Hk, Hv;
     int64_t units;   // sequences x value heads
     int64_t nslots;  // block-start states per value head
+    int64_t ntiles;  // dv / kBwdCols
     uint32_t flags;
 };
 

@@ -210,8 +210,8 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
  *               bytes, 16-byte aligned, owned by the caller; its contents are not needed
  *               before or after the call. Calls that share a workspace must not overlap.
  *
- * dk and dv must be 64 or 128. Every output is fully written (dq and dk are cleared on the
- * stream first). Outputs and workspace must not overlap inputs or each other (GDR_ERR_ALIAS).
+ * dk must be 64 or 128, dv a multiple of 32 up to 256. Every output is fully written (dq, dk,
+ * dlog_alpha and dbeta are sums, cleared on the stream first). Outputs and workspace must not overlap inputs or each other (GDR_ERR_ALIAS).
  * Errors as gdr_chunk_fwd, plus GDR_ERR_DIMS when workspace_bytes is too small.
  * The state before every token is recomputed from states kept at the start of each block of
  * 32 tokens, so the workspace holds (blocks + one block per sequence-head) fp32 states.

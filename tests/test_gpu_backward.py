@@ -76,6 +76,7 @@ CASES = [
     dict(B=1, T=100, Hk=1, Hv=2, dk=128, dv=64, dtype=torch.float32),
     dict(B=1, T=65, Hk=2, Hv=4, dk=64, dv=128, dtype=torch.bfloat16),
     dict(B=2, T=45, Hk=1, Hv=1, dk=128, dv=128, dtype=torch.bfloat16),
+    dict(B=1, T=40, Hk=1, Hv=1, dk=64, dv=96, dtype=torch.float32),
 ]
 
 
