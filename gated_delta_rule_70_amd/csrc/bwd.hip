@@ -19,8 +19,8 @@
 // dbeta and dlog alpha), so the column slices run independently and add their partial sums with
 // float atomics into buffers a fill kernel clears first (this also sums dq and dk over the value
 // heads that share a key head). Reductions over rows go through LDS (one barrier per token, the
-// partials double-buffered); reductions over the slice's columns stay inside a row band (8
-// lanes) as lane shuffles. Three sweeps per sequence: a forward sweep that stores the slice of
+// partials double-buffered: each wave first adds its bands with lane shuffles); reductions over
+// the slice's columns stay inside a row band (8 lanes) as lane shuffles. Three sweeps per sequence: a forward sweep that stores the slice of
 // the state at the start of every 32-token block in the workspace; then, block by block from the
 // last, a forward recompute that stores the slice before each token of the block (workspace),
 // and the reverse adjoint sweep over the block.
@@ -54,6 +54,17 @@ __device__ __forceinline__ float band_sum(float x) {
     return x;
 }
 
+// sum over the row bands of one wave: the lanes with the same lane % W (W lanes per band)
+template <int W>
+__device__ __forceinline__ f4 wave_bands_sum(f4 v) {
+#pragma unroll
+    for (int off = W; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], off, 64);
+    }
+    return v;
+}
+
 template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     constexpr int DV = kBwdCols;       // columns of the slice
@@ -65,9 +76,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 
     __shared__ float sk[CB][DK], sq[CB][DK], sv[CB][DV], sdo[CB][DV];
     __shared__ float sal[CB], sbe[CB];
-    __shared__ f4 px[2][RG][CG], pd[2][RG][CG];
-    __shared__ float pw[2][kThreads / 64];
-    constexpr int kRowWaves = kThreads / 64;
+    constexpr int NW = kThreads / 64;  // waves; row sums are reduced per wave first, then over waves
+    __shared__ f4 px[2][NW][CG], pd[2][NW][CG];
+    __shared__ float pw[2][NW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % CG, rg = tid / CG;
@@ -136,11 +147,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RPT; ++r) x += h[r] * sk[i][rg * RPT + r];
-        px[buf][rg][cg] = x;
+        x = wave_bands_sum<CG>(x);
+        if (lane < CG) px[buf][wave][cg] = x;
         __syncthreads();
         x = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < RG; ++j) x += px[buf][j][cg];
+        for (int j = 0; j < NW; ++j) x += px[buf][j][cg];
         buf ^= 1;
         const float al = sal[i], be = sbe[i];
         const f4 v4 = {sv[i][4 * cg], sv[i][4 * cg + 1], sv[i][4 * cg + 2], sv[i][4 * cg + 3]};
@@ -205,21 +217,25 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const f4 m = g[r] * h[r];
                 hd += m[0] + m[1] + m[2] + m[3];
             }
-            px[buf][rg][cg] = xp;
-            pd[buf][rg][cg] = dp;
+            xp = wave_bands_sum<CG>(xp);
+            dp = wave_bands_sum<CG>(dp);
+            if (lane < CG) {
+                px[buf][wave][cg] = xp;
+                pd[buf][wave][cg] = dp;
+            }
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) hd += __shfl_xor(hd, off, 64);
             if (lane == 0) pw[buf][wave] = hd;
             __syncthreads();
             f4 x = {0.f, 0.f, 0.f, 0.f}, du = x;
 #pragma unroll
-            for (int j = 0; j < RG; ++j) {
+            for (int j = 0; j < NW; ++j) {
                 x += px[buf][j][cg];
                 du += pd[buf][j][cg];
             }
             hd = 0.f;
 #pragma unroll
-            for (int w = 0; w < kRowWaves; ++w) hd += pw[buf][w];
+            for (int w = 0; w < NW; ++w) hd += pw[buf][w];
             buf ^= 1;
             const f4 e = v4 - al * x;
             const f4 u = be * e;
