@@ -399,18 +399,16 @@ gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v, c
 
 namespace {
 
-// block-start states per value head: one slot per 32-token block of every sequence
+// chunk-start states per value head: one slot per 32-token chunk of every sequence
 int64_t bwd_slots(const gdr_chunk_dims_t &d, bool packed) {
     const int64_t CB = gdr::kBwdBlock;
     if (packed) return d.T / CB + d.num_seqs + 1;
     return d.B * ((d.T + CB - 1) / CB);
 }
 
+// the state at the start of every chunk of every sequence-head
 int64_t bwd_workspace_bytes(const gdr_chunk_dims_t &d, bool packed) {
-    const int64_t nseq = packed ? d.num_seqs : d.B;
-    const int64_t states = d.Hv * bwd_slots(d, packed) + nseq * d.Hv * gdr::kBwdBlock;
-    const int64_t b = prod({states, d.dk, d.dv, 4});
-    return b;
+    return prod({d.Hv, bwd_slots(d, packed), d.dk, d.dv, 4});
 }
 
 gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,

@@ -70,8 +70,7 @@ struct Gdn2DecodeArgs {
 
 // Backward of the scalar rule. Gradient buffers are fp32: dq, dk [B][Hk][T][dk] (summed over the
 // value heads of a key head), dv [B][Hv][T][dv], dlog_alpha, dbeta [B][Hv][T], dh0 like h0.
-// ws: states at the start of every kBwdBlock-token block (nslots per value head) followed by
-// one block of per-token states per (sequence, value head).
+// ws: the state at the start of every kBwdBlock-token chunk (nslots per value head).
 constexpr int kBwdBlock = 32;
 constexpr int kBwdCols = 32;  // value columns per workgroup of the backward
 struct BwdArgs {

@@ -213,8 +213,9 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
  * dk must be 64 or 128, dv a multiple of 32 up to 256. Every output is fully written (dq, dk,
  * dlog_alpha and dbeta are sums, cleared on the stream first). Outputs and workspace must not overlap inputs or each other (GDR_ERR_ALIAS).
  * Errors as gdr_chunk_fwd, plus GDR_ERR_DIMS when workspace_bytes is too small.
- * The state before every token is recomputed from states kept at the start of each block of
- * 32 tokens, so the workspace holds (blocks + one block per sequence-head) fp32 states.
+ * The backward runs the chunk form (32-token chunks) forward once, keeping each chunk's entry
+ * state in the workspace (one fp32 state per chunk of every sequence-head), then walks the chunks
+ * back, recomputing each chunk's quantities from its entry state.
  */
 int64_t gdr_chunk_bwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t packed);
 gdr_status_t gdr_chunk_bwd(const void *q, const void *k, const void *v,

@@ -279,5 +279,5 @@ def test_backward_rejects():
     st, msg = call(dq=FAKE + 64)
     assert st == "GDR_ERR_ALIAS" and "dq overlaps q" in msg, msg
     dims = binding.ChunkDims(4, 4096, 16, 16, 128, 128, 0, 1, 0)
-    # (16 heads x 4 x 128 block starts + 64 sequence-heads x 32) states of 64 KiB
-    assert lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), 0) == (16 * 4 * 128 + 64 * 32) * 128 * 128 * 4
+    # 16 heads x 4 sequences x 128 chunk starts, states of 64 KiB
+    assert lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), 0) == 16 * 4 * 128 * 128 * 128 * 4
