@@ -60,7 +60,8 @@ struct Seq {
 
 template <int DK>
 struct Smem {
-    static constexpr int KP = DK + 4, VP = TV + 4, CP = CB + 1;
+    // odd pitches: a column read across the lanes of a wave hits distinct banks
+    static constexpr int KP = DK + 1, VP = TV + 1, CP = CB + 1;
     float K[CB][KP], Q[CB][KP];
     float V[CB][VP], dO[CB][VP];
     float H[DK][VP], D[DK][VP];  // the chunk's entry state and the adjoint of its exit state
@@ -390,24 +391,25 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
-        // dQ, dK (CB x DK; QI rows x 4 columns per thread) and the exponent gradient of the read
+        // dQ, dK (CB x DK; QI rows x NV columns per thread, columns n0 + 32 v so that the lanes of a
+        // wave read 32 consecutive rows of H and D) and the exponent gradient of the read
         {
-            constexpr int QI = CB * DK / (kThreads * 4);
-            const int n0 = (tid % (DK / 4)) * 4, i0 = (tid / (DK / 4)) * QI;
+            constexpr int NV = DK / 32, QI = CB / 8;
+            const int n0 = tid % 32, i0 = (tid / 32) * QI;
             for (int u = 0; u < QI; ++u) {
                 const int i = i0 + u;
                 const float er = __expf(sm.r[i]);
                 const float wi = __expf(fminf(blast - sm.b[i], 0.f));
                 const float bg = sm.beta[i] * __expf(sm.b[i]);
-                float dq[4], dk[4], oh[4];
+                float dq[NV], dk[NV], oh[NV];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) dq[v] = dk[v] = oh[v] = 0.f;
+                for (int v = 0; v < NV; ++v) dq[v] = dk[v] = oh[v] = 0.f;
                 #pragma unroll 4
                 for (int cc = 0; cc < TV; ++cc) {
                     const float o = sm.dO[i][cc], uu = sm.U[i][cc], dr = sm.dR[i][cc];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float h = sm.H[n0 + v][cc], d = sm.D[n0 + v][cc];
+                    for (int v = 0; v < NV; ++v) {
+                        const float h = sm.H[n0 + 32 * v][cc], d = sm.D[n0 + 32 * v][cc];
                         oh[v] += o * h;
                         dk[v] += wi * uu * d - bg * dr * h;
                     }
@@ -417,25 +419,25 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                     const float mij = sm.M[i][j], mji = sm.M[j][i];
                     const float nn = sm.beta[i] * sm.N[i][j] + sm.beta[j] * sm.N[j][i];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float kj = sm.K[j][n0 + v], qj = sm.Q[j][n0 + v];
+                    for (int v = 0; v < NV; ++v) {
+                        const float kj = sm.K[j][n0 + 32 * v], qj = sm.Q[j][n0 + 32 * v];
                         dq[v] += mij * kj;
                         dk[v] += mji * qj + nn * kj;
                     }
                 }
                 float rq = 0.f;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
+                for (int v = 0; v < NV; ++v) {
                     dq[v] += er * oh[v];
-                    rq += er * oh[v] * sm.Q[i][n0 + v];
+                    rq += er * oh[v] * sm.Q[i][n0 + 32 * v];
                 }
                 atomicAdd(&sm.dr[i], rq);
                 if (i < n) {
                     const int64_t t = sq.token(c * CB + i);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        atomicAdd(dqb + t * DK + n0 + v, dq[v]);
-                        atomicAdd(dkb + t * DK + n0 + v, dk[v]);
+                    for (int v = 0; v < NV; ++v) {
+                        atomicAdd(dqb + t * DK + n0 + 32 * v, dq[v]);
+                        atomicAdd(dkb + t * DK + n0 + 32 * v, dk[v]);
                     }
                 }
             }
