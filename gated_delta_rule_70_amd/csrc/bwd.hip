@@ -34,12 +34,16 @@
 // chunk-form forward from h0, storing the slice of the state at each chunk start in the
 // workspace; then the chunks from the last, each recomputing its forward quantities from its
 // stored entry state and applying the adjoint above. All matrices of a chunk live in LDS in
-// fp32; the products are register-blocked fp32 FMAs spread over the 256 threads.
+// fp32; the products run on the matrix cores in fp32 (16x16 output tiles shared out over the four
+// waves), the triangular inverse is the one the chunk forward kernels use, and the gate
+// gradients are sums on the vector units.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "gdr_kernels.hpp"
+#include "gdr_mfma.hpp"
+#include "gdr_solve.hpp"
 
 namespace gdr {
 
@@ -59,23 +63,52 @@ struct Seq {
 };
 
 template <int DK>
-struct Smem {
-    // odd pitches: a column read across the lanes of a wave hits distinct banks
-    static constexpr int KP = DK + 1, VP = TV + 1, CP = CB + 1;
+struct alignas(16) Smem {
+    static constexpr int KP = DK + 4, VP = TV + 4, AP = CB + 4, TP = CB + 4;
     float K[CB][KP], Q[CB][KP];
     float V[CB][VP], dO[CB][VP];
     float H[DK][VP], D[DK][VP];  // the chunk's entry state and the adjoint of its exit state
-    float X[CB][VP], U[CB][VP], dU[CB][VP], dR[CB][VP];
-    float T[CB][CP], P[CB][CP], G[CB][CP], M[CB][CP], N[CB][CP];
+    float X[CB][VP], U[CB][VP], dU[CB][VP], dR[CB][VP], eO[CB][VP], bR[CB][VP];
+    float A[CB * AP], T[CB * TP];  // flat: the shared triangular inverse reads them so
+    float P[CB][TP], G[CB][TP], M[CB][TP], Nb[CB][TP];
     float la[CB], beta[CB], b[CB], r[CB];
     float db[CB], dr[CB], dbeta[CB], dw[CB];
     float hd;  // <dH', H> of the chunk
 };
 
+// acc += A (16 x KD) B (KD x 16) with both operands in LDS. A is X[m0 + m][k] (or, with AT,
+// X[k][m0 + m]); B is Y[k][n0 + n] (or, with BT, Y[n0 + n][k]). Output tile in the accumulator
+// layout: lane (g, c), register r <-> [m0 + 4g + r][n0 + c].
+template <int KD, bool AT, bool BT>
+__device__ __forceinline__ floatx4 mm(floatx4 acc, const float *X, int ldx, int m0, const float *Y, int ldy, int n0) {
+#pragma unroll
+    for (int k0 = 0; k0 < KD; k0 += 32) {
+        const Frag<float> fa = AT ? frag_cols<float>(X, ldx, m0, k0) : frag_rows<float>(X, ldx, m0, k0);
+        const Frag<float> fb = BT ? frag_rows<float>(Y, ldy, n0, k0) : frag_cols<float>(Y, ldy, n0, k0);
+        acc = mma32(acc, fa, fb);
+    }
+    return acc;
+}
+
+// sum of x over the 16 lanes of a lane group (the columns of a tile row)
+__device__ __forceinline__ float row16(float x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+// sum of x over the 4 lane groups (the rows 4g + r of a tile column, for fixed r)
+__device__ __forceinline__ float col4(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
-    __shared__ Smem<DK> sm;
-    const int tid = threadIdx.x;
+    typedef Smem<DK> SM;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, cc = lane & 15;
     const int64_t unit = blockIdx.x / a.ntiles;
     const int tile = (int)(blockIdx.x % a.ntiles);
     const int64_t seq = unit / a.Hv, head = unit % a.Hv;
@@ -117,30 +150,62 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     // the DK x TV elements of a state slice this thread handles: SR rows x 4 columns
     constexpr int SR = DK * TV / (kThreads * 4);
     const int sc0 = (tid % (TV / 4)) * 4, sr0 = (tid / (TV / 4)) * SR;
-    // the 2 x 2 block of a CB x TV or CB x CB matrix this thread handles
-    const int bi0 = (tid / 16) * 2, bj0 = (tid % 16) * 2;
+    // the 4 elements of a CB x TV matrix this thread handles (row ei, columns ej .. ej + 3)
+    const int ei = tid / (TV / 4), ej = (tid % (TV / 4)) * 4;
+
+    // matrices whose strictly upper 16x16 tiles are read as zeros and never written
+    for (int i = tid; i < CB * SM::TP; i += kThreads) {
+        sm.T[i] = 0.f;
+        (&sm.P[0][0])[i] = 0.f;
+        (&sm.G[0][0])[i] = 0.f;
+        (&sm.M[0][0])[i] = 0.f;
+        (&sm.Nb[0][0])[i] = 0.f;
+    }
+    for (int i = tid; i < CB * SM::AP; i += kThreads) sm.A[i] = 0.f;
 
     auto n_rows = [&](int64_t c) __attribute__((always_inline)) -> int { return (int)min((int64_t)CB, sq.len - c * CB); };
 
-    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write)
+    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write); all loads
+    // of a thread are issued before its stores
     auto stage = [&](int64_t c, bool adjoint) __attribute__((always_inline)) {
         const int n = n_rows(c);
-        for (int i = tid; i < CB * DK; i += kThreads) {
-            const int rr = i / DK, cc = i % DK;
+        constexpr int KPT = CB * DK / kThreads, VPT = CB * TV / kThreads;
+        float kv[KPT], qv[KPT], vv[VPT], ov[VPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int i = tid + e * kThreads, rr = i / DK, c2 = i % DK;
             const int64_t t = rr < n ? sq.token(c * CB + rr) : 0;
-            sm.K[rr][cc] = rr < n ? ld_f(kb, t * DK + cc) : 0.f;
-            if (adjoint) sm.Q[rr][cc] = rr < n ? ld_f(qb, t * DK + cc) : 0.f;
+            kv[e] = rr < n ? ld_f(kb, t * DK + c2) : 0.f;
+            qv[e] = (adjoint && rr < n) ? ld_f(qb, t * DK + c2) : 0.f;
         }
-        for (int i = tid; i < CB * TV; i += kThreads) {
-            const int rr = i / TV, cc = i % TV;
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+            const int i = tid + e * kThreads, rr = i / TV, c2 = i % TV;
             const int64_t t = rr < n ? sq.token(c * CB + rr) : 0;
-            sm.V[rr][cc] = rr < n ? ld_f(vb, t * dvf + cc) : 0.f;
-            if (adjoint) sm.dO[rr][cc] = rr < n ? ld_f(dob, t * dvf + cc) : 0.f;
+            vv[e] = rr < n ? ld_f(vb, t * dvf + c2) : 0.f;
+            ov[e] = (adjoint && rr < n) ? ld_f(dob, t * dvf + c2) : 0.f;
+        }
+        float lv = 0.f, bv = 0.f;
+        if (tid < CB && tid < n) {
+            const int64_t t = sq.token(c * CB + tid);
+            lv = lab[t];
+            bv = beb[t];
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int i = tid + e * kThreads, rr = i / DK, c2 = i % DK;
+            sm.K[rr][c2] = kv[e];
+            sm.Q[rr][c2] = qv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+            const int i = tid + e * kThreads, rr = i / TV, c2 = i % TV;
+            sm.V[rr][c2] = vv[e];
+            sm.dO[rr][c2] = ov[e];
         }
         if (tid < CB) {
-            const int64_t t = tid < n ? sq.token(c * CB + tid) : 0;
-            sm.la[tid] = tid < n ? lab[t] : 0.f;
-            sm.beta[tid] = tid < n ? beb[t] : 0.f;
+            sm.la[tid] = lv;
+            sm.beta[tid] = bv;
             sm.db[tid] = 0.f;
             sm.dr[tid] = 0.f;
             sm.dbeta[tid] = 0.f;
@@ -163,65 +228,48 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
         }
     };
-    // forward quantities of the chunk from its entry state in sm.H: X, G, P (adjoint only), T, U
+    // forward quantities of the chunk from its entry state in sm.H: X, G and A, P (adjoint only), T, U
     auto forward_parts = [&](bool adjoint) __attribute__((always_inline)) {
+        // X = K H (4 tiles, one per wave); G = K K^T and P = Q K^T on the lower tiles (00, 10, 11)
         {
-            float x[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, g[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            float p[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            #pragma unroll 4
-            for (int n = 0; n < DK; ++n) {
-                const float k0 = sm.K[bi0][n], k1 = sm.K[bi0 + 1][n];
-                const float h0 = sm.H[n][bj0], h1 = sm.H[n][bj0 + 1];
-                const float kj0 = sm.K[bj0][n], kj1 = sm.K[bj0 + 1][n];
-                x[0][0] += k0 * h0; x[0][1] += k0 * h1; x[1][0] += k1 * h0; x[1][1] += k1 * h1;
-                g[0][0] += k0 * kj0; g[0][1] += k0 * kj1; g[1][0] += k1 * kj0; g[1][1] += k1 * kj1;
-                if (adjoint) {
-                    const float q0 = sm.Q[bi0][n], q1 = sm.Q[bi0 + 1][n];
-                    p[0][0] += q0 * kj0; p[0][1] += q0 * kj1; p[1][0] += q1 * kj0; p[1][1] += q1 * kj1;
-                }
-            }
+            const int mt = wave >> 1, nt = wave & 1;
+            const floatx4 x = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    const int i = bi0 + u, j = bj0 + v;
-                    sm.X[i][j] = x[u][v];
-                    sm.G[i][j] = j < i ? g[u][v] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
-                    if (adjoint) {
-                        const bool keep = pre ? j < i : j <= i;
-                        sm.P[i][j] = keep ? p[u][v] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
-                    }
-                }
+            for (int r = 0; r < 4; ++r) sm.X[16 * mt + 4 * g + r][16 * nt + cc] = x[r];
         }
-        __syncthreads();
-        // T = (I + diag(beta) G)^{-1}: one lane per column, forward substitution down the column
-        // (in place in LDS: each lane reads back only what it wrote)
-        if (tid < CB) {
-            const int c = tid;
-            for (int i = 0; i < CB; ++i) {
-                float s = 0.f;
-                #pragma unroll 4
-                for (int j = c; j < i; ++j) s += sm.G[i][j] * sm.T[j][c];
-                sm.T[i][c] = i < c ? 0.f : ((i == c ? 1.f : 0.f) - sm.beta[i] * s);
+        for (int t = wave; t < (adjoint ? 6 : 3); t += 4) {
+            const bool isp = t >= 3;
+            const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
+            const floatx4 v = mm<DK, false, true>(zero4(), isp ? &sm.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt,
+                                                  &sm.K[0][0], SM::KP, 16 * nt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+                if (isp) {
+                    const bool keep = pre ? j < i : j <= i;
+                    sm.P[i][j] = keep ? v[r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
+                } else {
+                    const float gg = j < i ? v[r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
+                    sm.G[i][j] = gg;
+                    sm.A[i * SM::AP + j] = sm.beta[i] * gg;
+                }
             }
         }
         __syncthreads();
-        // U = T R, R = diag(beta) (V - diag(gamma) X)
+        // T = (I + A)^{-1}; R = diag(beta) (V - diag(gamma) X) into dR
+        if (wave == 0) solve_unit_lower_inverse<float, CB>(sm);
         {
-            float u[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            #pragma unroll 4
-            for (int m = 0; m <= bi0 + 1; ++m) {
-                const float be = sm.beta[m], ga = __expf(sm.b[m]);
-                const float r0 = be * (sm.V[m][bj0] - ga * sm.X[m][bj0]);
-                const float r1 = be * (sm.V[m][bj0 + 1] - ga * sm.X[m][bj0 + 1]);
-                const float t0 = sm.T[bi0][m], t1 = sm.T[bi0 + 1][m];
-                u[0][0] += t0 * r0; u[0][1] += t0 * r1; u[1][0] += t1 * r0; u[1][1] += t1 * r1;
-            }
+            const float be = sm.beta[ei], ga = __expf(sm.b[ei]);
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                sm.U[bi0][bj0 + v] = u[0][v];
-                sm.U[bi0 + 1][bj0 + v] = u[1][v];
-            }
+            for (int v = 0; v < 4; ++v) sm.dR[ei][ej + v] = be * (sm.V[ei][ej + v] - ga * sm.X[ei][ej + v]);
+        }
+        __syncthreads();
+        // U = T R
+        {
+            const int mt = wave >> 1, nt = wave & 1;
+            const floatx4 u = mm<CB, false, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dR[0][0], SM::VP, 16 * nt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.U[16 * mt + 4 * g + r][16 * nt + cc] = u[r];
         }
         __syncthreads();
     };
@@ -230,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     for (int u = 0; u < SR; ++u)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int n = sr0 + u, cc = sc0 + v;
-            sm.H[n][cc] = a.h0 ? a.h0[sbase + (int64_t)n * dvf + cc] : 0.f;
+            const int n = sr0 + u, c2 = sc0 + v;
+            sm.H[n][c2] = a.h0 ? a.h0[sbase + (int64_t)n * dvf + c2] : 0.f;
         }
     __syncthreads();
     for (int64_t c = 0; c < nch; ++c) {
@@ -243,25 +291,23 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         gates();
         __syncthreads();
         forward_parts(false);
-        // H' = gamma_last H + K^T diag(w) U
-        const float blast = sm.b[CB - 1];
-        float hn[SR][4];
-        for (int u = 0; u < SR; ++u)
+        // H' = gamma_last H + K^T diag(w) U (wU into dU first)
+        const float blast = sm.b[CB - 1], glast = __expf(blast);
+        {
+            const float wi = __expf(fminf(blast - sm.b[ei], 0.f));
 #pragma unroll
-            for (int v = 0; v < 4; ++v) hn[u][v] = __expf(blast) * sm.H[sr0 + u][sc0 + v];
-        #pragma unroll 4
-        for (int j = 0; j < CB; ++j) {
-            const float wj = __expf(fminf(blast - sm.b[j], 0.f));
-            for (int u = 0; u < SR; ++u) {
-                const float kw = sm.K[j][sr0 + u] * wj;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) hn[u][v] += kw * sm.U[j][sc0 + v];
-            }
+            for (int v = 0; v < 4; ++v) sm.dU[ei][ej + v] = wi * sm.U[ei][ej + v];
         }
         __syncthreads();
-        for (int u = 0; u < SR; ++u)
+        for (int t = wave; t < (DK / 16) * (TV / 16); t += 4) {
+            const int mt = t / (TV / 16), nt = t % (TV / 16);
+            floatx4 h;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sm.H[sr0 + u][sc0 + v] = hn[u][v];
+            for (int r = 0; r < 4; ++r) h[r] = glast * sm.H[16 * mt + 4 * g + r][16 * nt + cc];
+            h = mm<CB, true, false>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.H[16 * mt + 4 * g + r][16 * nt + cc] = h[r];
+        }
         __syncthreads();
     }
 
@@ -269,8 +315,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     for (int u = 0; u < SR; ++u)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int n = sr0 + u, cc = sc0 + v;
-            sm.D[n][cc] = a.dhT ? a.dhT[sbase + (int64_t)n * dvf + cc] : 0.f;
+            const int n = sr0 + u, c2 = sc0 + v;
+            sm.D[n][c2] = a.dhT ? a.dhT[sbase + (int64_t)n * dvf + c2] : 0.f;
         }
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = n_rows(c);
@@ -284,182 +330,146 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         forward_parts(true);
         const float blast = sm.b[CB - 1], glast = __expf(blast);
 
-        // dU = diag(w) K D + P^T dO, and dw_i = (K D)_i . U_i
+        // dU = diag(w) K D + P^T dO; dw_i = (K D)_i . U_i; and <D, H>
         {
-            float kd[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, pd[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            #pragma unroll 4
-            for (int m = 0; m < DK; ++m) {
-                const float k0 = sm.K[bi0][m], k1 = sm.K[bi0 + 1][m];
-                const float d0 = sm.D[m][bj0], d1 = sm.D[m][bj0 + 1];
-                kd[0][0] += k0 * d0; kd[0][1] += k0 * d1; kd[1][0] += k1 * d0; kd[1][1] += k1 * d1;
-            }
-            #pragma unroll 4
-            for (int m = bi0; m < CB; ++m) {
-                const float p0 = sm.P[m][bi0], p1 = sm.P[m][bi0 + 1];
-                const float o0 = sm.dO[m][bj0], o1 = sm.dO[m][bj0 + 1];
-                pd[0][0] += p0 * o0; pd[0][1] += p0 * o1; pd[1][0] += p1 * o0; pd[1][1] += p1 * o1;
-            }
+            const int mt = wave >> 1, nt = wave & 1;
+            const floatx4 kd = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
+            const floatx4 pd = mm<CB, true, false>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = bi0 + u;
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
                 const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-                float dwp = 0.f;
-#pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    sm.dU[i][bj0 + v] = wi * kd[u][v] + pd[u][v];
-                    dwp += kd[u][v] * sm.U[i][bj0 + v];
-                }
-                atomicAdd(&sm.dw[i], dwp);
+                sm.dU[i][j] = wi * kd[r] + pd[r];
+                const float dwp = row16(kd[r] * sm.U[i][j]);
+                if (cc == 0) atomicAdd(&sm.dw[i], dwp);
             }
-        }
-        // <D, H> of the chunk (for the exit decay)
-        {
             float s = 0.f;
             for (int u = 0; u < SR; ++u)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) s += sm.D[sr0 + u][sc0 + v] * sm.H[sr0 + u][sc0 + v];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-            if ((tid & 63) == 0) atomicAdd(&sm.hd, s);
+            if (lane == 0) atomicAdd(&sm.hd, s);
         }
         __syncthreads();
         // dR = T^T dU
         {
-            float d[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            #pragma unroll 4
-            for (int m = bi0; m < CB; ++m) {
-                const float t0 = sm.T[m][bi0], t1 = sm.T[m][bi0 + 1];
-                const float u0 = sm.dU[m][bj0], u1 = sm.dU[m][bj0 + 1];
-                d[0][0] += t0 * u0; d[0][1] += t0 * u1; d[1][0] += t1 * u0; d[1][1] += t1 * u1;
-            }
+            const int mt = wave >> 1, nt = wave & 1;
+            const floatx4 d = mm<CB, true, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int v = 0; v < 2; ++v) sm.dR[bi0 + u][bj0 + v] = d[u][v];
+            for (int r = 0; r < 4; ++r) sm.dR[16 * mt + 4 * g + r][16 * nt + cc] = d[r];
         }
         __syncthreads();
-        // dP = dO U^T -> M; dA = -dR U^T -> N; the exponent gradients of P and A; dbeta from A
-        {
-            float dp[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, da[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            #pragma unroll 4
-            for (int cc = 0; cc < TV; ++cc) {
-                const float o0 = sm.dO[bi0][cc], o1 = sm.dO[bi0 + 1][cc];
-                const float r0 = sm.dR[bi0][cc], r1 = sm.dR[bi0 + 1][cc];
-                const float u0 = sm.U[bj0][cc], u1 = sm.U[bj0 + 1][cc];
-                dp[0][0] += o0 * u0; dp[0][1] += o0 * u1; dp[1][0] += o1 * u0; dp[1][1] += o1 * u1;
-                da[0][0] -= r0 * u0; da[0][1] -= r0 * u1; da[1][0] -= r1 * u0; da[1][1] -= r1 * u1;
-            }
+        // dP = dO U^T -> M, dA = -dR U^T -> beta N on the lower tiles; their exponent and beta
+        // gradients; then dV, R's gradients, and the scaled copies for the products below
+        for (int t = wave; t < 6; t += 4) {
+            const bool isa = t >= 3;
+            const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
+            floatx4 v = mm<TV, false, true>(zero4(), isa ? &sm.dR[0][0] : &sm.dO[0][0], SM::VP, 16 * mt, &sm.U[0][0],
+                                            SM::VP, 16 * nt);
+            if (isa) v = -v;
+            float colsum[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = bi0 + u;
-                float rrow = 0.f, brow = 0.f, bet = 0.f;
-#pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    const int j = bj0 + v;
-                    const bool pk = pre ? j < i : j <= i;
-                    sm.M[i][j] = pk ? dp[u][v] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
-                    sm.N[i][j] = j < i ? da[u][v] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
-                    const float pp = pk ? dp[u][v] * sm.P[i][j] : 0.f;                 // dP_ij Pm_ij
-                    const float gg = j < i ? da[u][v] * sm.G[i][j] : 0.f;              // dA_ij G_ij
-                    rrow += pp;
-                    brow += sm.beta[i] * gg;                                           // dA_ij A_ij
-                    bet += gg;
-                    atomicAdd(&sm.db[j], -(pp + sm.beta[i] * gg));
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+                float rs = 0.f, rb = 0.f;
+                if (!isa) {
+                    const bool keep = pre ? j < i : j <= i;
+                    sm.M[i][j] = keep ? v[r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
+                    rs = keep ? v[r] * sm.P[i][j] : 0.f;  // dP_ij Pm_ij
+                } else {
+                    const bool keep = j < i;
+                    sm.Nb[i][j] = keep ? sm.beta[i] * v[r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
+                    rs = keep ? v[r] * sm.A[i * SM::AP + j] : 0.f;  // dA_ij A_ij
+                    rb = keep ? v[r] * sm.G[i][j] : 0.f;  // dA_ij G_ij
                 }
-                atomicAdd(&sm.dr[i], rrow);
-                atomicAdd(&sm.db[i], brow);
-                atomicAdd(&sm.dbeta[i], bet);
+                colsum[r] = rs;
+                const float rsum = row16(rs), bsum = row16(rb);
+                if (cc == 0) {
+                    if (isa) {
+                        atomicAdd(&sm.db[i], rsum);
+                        atomicAdd(&sm.dbeta[i], bsum);
+                    } else {
+                        atomicAdd(&sm.dr[i], rsum);
+                    }
+                }
             }
+            // column sums (over the 16 rows of the tile) go to d b_j with a minus sign
+            float cs = colsum[0] + colsum[1] + colsum[2] + colsum[3];
+            cs = col4(cs);
+            if (g == 0) atomicAdd(&sm.db[16 * nt + cc], -cs);
         }
-        // dV, and dbeta and the exponent gradient from R
         {
+            const int i = ei;
+            const float be = sm.beta[i], ga = __expf(sm.b[i]), er = __expf(sm.r[i]);
+            const float wi = __expf(fminf(blast - sm.b[i], 0.f));
+            float sb = 0.f, sx = 0.f;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = bi0 + u;
-                const float be = sm.beta[i], ga = __expf(sm.b[i]);
-                float sb = 0.f, sx = 0.f;
-#pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    const int j = bj0 + v;
-                    const float dr = sm.dR[i][j];
-                    sb += dr * (sm.V[i][j] - ga * sm.X[i][j]);
-                    sx += dr * sm.X[i][j];
-                    if (i < n) dvb[sq.token(c * CB + i) * dvf + j] = be * dr;
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int j = ej + v;
+                const float dr = sm.dR[i][j];
+                sb += dr * (sm.V[i][j] - ga * sm.X[i][j]);
+                sx += dr * sm.X[i][j];
+                if (i < n) dvb[sq.token(c * CB + i) * dvf + j] = be * dr;
+                sm.eO[i][j] = er * sm.dO[i][j];
+                sm.bR[i][j] = -be * ga * dr;
+                sm.dU[i][j] = wi * sm.U[i][j];
+            }
+            sb += __shfl_xor(sb, 1, 64); sb += __shfl_xor(sb, 2, 64); sb += __shfl_xor(sb, 4, 64);
+            sx += __shfl_xor(sx, 1, 64); sx += __shfl_xor(sx, 2, 64); sx += __shfl_xor(sx, 4, 64);
+            if ((tid % (TV / 4)) == 0) {
                 atomicAdd(&sm.dbeta[i], sb);
                 atomicAdd(&sm.db[i], -be * ga * sx);
             }
         }
         __syncthreads();
-        // dQ, dK (CB x DK; QI rows x NV columns per thread, columns n0 + 32 v so that the lanes of a
-        // wave read 32 consecutive rows of H and D) and the exponent gradient of the read
-        {
-            constexpr int NV = DK / 32, QI = CB / 8;
-            const int n0 = tid % 32, i0 = (tid / 32) * QI;
-            for (int u = 0; u < QI; ++u) {
-                const int i = i0 + u;
+        // dQ = diag(e^r) dO H^T + M K;  dK = wU D^T + bR H^T + M^T Q + Nb K + Nb^T K
+        // (wU = diag(w) U in dU, bR = -diag(beta gamma) dR); the read's exponent gradient
+        for (int t = wave; t < 2 * (DK / 16); t += 4) {
+            const int mt = t / (DK / 16), nt = t % (DK / 16);
+            floatx4 oh = mm<TV, false, true>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+            floatx4 dq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r;
                 const float er = __expf(sm.r[i]);
-                const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-                const float bg = sm.beta[i] * __expf(sm.b[i]);
-                float dq[NV], dk[NV], oh[NV];
+                dq[r] = er * oh[r];
+                const float rq = row16(dq[r] * sm.Q[i][16 * nt + cc]);
+                if (cc == 0) atomicAdd(&sm.dr[i], rq);
+            }
+            dq = mm<CB, false, false>(dq, &sm.M[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            floatx4 dk = mm<TV, false, true>(zero4(), &sm.dU[0][0], SM::VP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
+            dk = mm<TV, false, true>(dk, &sm.bR[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+            dk = mm<CB, true, false>(dk, &sm.M[0][0], SM::TP, 16 * mt, &sm.Q[0][0], SM::KP, 16 * nt);
+            dk = mm<CB, false, false>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            dk = mm<CB, true, false>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) dq[v] = dk[v] = oh[v] = 0.f;
-                #pragma unroll 4
-                for (int cc = 0; cc < TV; ++cc) {
-                    const float o = sm.dO[i][cc], uu = sm.U[i][cc], dr = sm.dR[i][cc];
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        const float h = sm.H[n0 + 32 * v][cc], d = sm.D[n0 + 32 * v][cc];
-                        oh[v] += o * h;
-                        dk[v] += wi * uu * d - bg * dr * h;
-                    }
-                }
-                #pragma unroll 4
-                for (int j = 0; j < CB; ++j) {
-                    const float mij = sm.M[i][j], mji = sm.M[j][i];
-                    const float nn = sm.beta[i] * sm.N[i][j] + sm.beta[j] * sm.N[j][i];
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        const float kj = sm.K[j][n0 + 32 * v], qj = sm.Q[j][n0 + 32 * v];
-                        dq[v] += mij * kj;
-                        dk[v] += mji * qj + nn * kj;
-                    }
-                }
-                float rq = 0.f;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    dq[v] += er * oh[v];
-                    rq += er * oh[v] * sm.Q[i][n0 + 32 * v];
-                }
-                atomicAdd(&sm.dr[i], rq);
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r;
                 if (i < n) {
-                    const int64_t t = sq.token(c * CB + i);
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        atomicAdd(dqb + t * DK + n0 + 32 * v, dq[v]);
-                        atomicAdd(dkb + t * DK + n0 + 32 * v, dk[v]);
-                    }
+                    const int64_t tk = sq.token(c * CB + i);
+                    atomicAdd(dqb + tk * DK + 16 * nt + cc, dq[r]);
+                    atomicAdd(dkb + tk * DK + 16 * nt + cc, dk[r]);
                 }
             }
         }
-        // dH = gamma_last D + Q^T diag(e^r) dO - K^T diag(beta gamma) dR
-        float dh[SR][4];
-        for (int u = 0; u < SR; ++u)
+        // dH = gamma_last D + Q^T eO + K^T bR
+        floatx4 dh[(DK / 16) * (TV / 16) / 4];
+        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += 4, ++s) {
+            const int mt = t / (TV / 16), nt = t % (TV / 16);
+            floatx4 h;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) dh[u][v] = glast * sm.D[sr0 + u][sc0 + v];
-        #pragma unroll 4
-        for (int j = 0; j < CB; ++j) {
-            const float er = __expf(sm.r[j]), bg = sm.beta[j] * __expf(sm.b[j]);
-            for (int u = 0; u < SR; ++u) {
-                const float qe = sm.Q[j][sr0 + u] * er, kg = sm.K[j][sr0 + u] * bg;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) dh[u][v] += qe * sm.dO[j][sc0 + v] - kg * sm.dR[j][sc0 + v];
-            }
+            for (int r = 0; r < 4; ++r) h[r] = glast * sm.D[16 * mt + 4 * g + r][16 * nt + cc];
+            h = mm<CB, true, false>(h, &sm.Q[0][0], SM::KP, 16 * mt, &sm.eO[0][0], SM::VP, 16 * nt);
+            h = mm<CB, true, false>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.bR[0][0], SM::VP, 16 * nt);
+            dh[s] = h;
         }
         __syncthreads();
-        for (int u = 0; u < SR; ++u)
+        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += 4, ++s) {
+            const int mt = t / (TV / 16), nt = t % (TV / 16);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sm.D[sr0 + u][sc0 + v] = dh[u][v];
+            for (int r = 0; r < 4; ++r) sm.D[16 * mt + 4 * g + r][16 * nt + cc] = dh[s][r];
+        }
         // gate gradients of the chunk: the exit decay terms on the last row, then suffix sums
         if (tid < 64) {
             const int i = tid;
@@ -498,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         for (int u = 0; u < SR; ++u)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int nn = sr0 + u, cc = sc0 + v;
-                a.dh0[sbase + (int64_t)nn * dvf + cc] = sm.D[nn][cc];
+                const int nn = sr0 + u, c2 = sc0 + v;
+                a.dh0[sbase + (int64_t)nn * dvf + c2] = sm.D[nn][c2];
             }
     }
 }
