@@ -312,8 +312,9 @@ def main():
     # timed 16% slower than with 300); 500 calls are about 50 ms
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "all"], default="all",
-                    help="gdn2, bwd: only the GDN-2 workloads or the backward (for profiling them)")
+    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "dp", "all"], default="all",
+                    help="gdn2, bwd, dp: only the GDN-2 workloads, the backward or DeltaProduct (for "
+                         "profiling them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -333,6 +334,10 @@ def main():
     if args.only == "bwd":
         r = bench_backward(binding, inputs, args.steps)
         print(json.dumps({"bwd_ms": r["ms"], "steps": args.steps, "workspace_bytes": r["ws_bytes"]}), flush=True)
+        return
+    if args.only == "dp":
+        r = bench_delta_product(binding, inputs, args.steps)
+        print(json.dumps({"delta_product_ms": r["ms"], "bytes": r["bytes"], "steps": args.steps}), flush=True)
         return
     if args.only == "gdn2":
         g2, g2d = bench_gdn2(binding, inputs, args.steps)

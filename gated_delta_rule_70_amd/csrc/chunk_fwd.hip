@@ -482,7 +482,13 @@ hipError_t launch_dk(const ChunkArgs &a, int chunk, int dk, hipStream_t s) {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int chunk, int dk, hipStream_t stream) {
     if (a.units == 0 || a.ntiles == 0) return hipSuccess;
-    if (a.n_sub == 1 && chunk_fwd_fast_supported(dtype, chunk, dk)) return launch_chunk_fwd_fast(a, stream);
+    // The fast kernel takes 1, 2, 4, 8 or 16 delta sub-steps per token (they divide its chunk,
+    // so a chunk starts on a token) and head slabs whose byte offsets fit its 32-bit copies.
+    const bool pow2 = (a.n_sub & (a.n_sub - 1)) == 0;
+    const int64_t slab_rows = a.T * (int64_t)a.n_sub;
+    const int64_t row_bytes = a.dv * 2 > 256 ? a.dv * 2 : 256;
+    if (pow2 && slab_rows * row_bytes < INT32_MAX && chunk_fwd_fast_supported(dtype, chunk, dk))
+        return launch_chunk_fwd_fast(a, stream);
     if (dtype == kDtypeBf16) return launch_dk<__bf16>(a, chunk, dk, stream);
     return launch_dk<float>(a, chunk, dk, stream);
 }

@@ -178,46 +178,63 @@ __device__ __forceinline__ int row_swz(int r) {
     const int a = (r >> 2) & 3;
     return ((r & 3) << 2) | ((((a ^ (a >> 1)) & 1) << 1) | (a >> 1));
 }
+// With 2^sh delta sub-steps per token (scan rows), k, v and beta have a row per sub-step and
+// q, log alpha and the output a row per token: scan row r of a chunk reads q row r >> sh
+// (relative to the chunk's first token, lo >> sh; chunks start on a token since 2^sh divides
+// the chunk), takes log alpha on the token's first sub-step only and gives the output of its
+// token on one sub-step. With sh = 0 the two sets of offsets coincide.
 struct CopyOffsets {
-    int kq[16], v[4], gate;
-    __device__ __forceinline__ void init(const ChunkRows &cr, int64_t dv) {
+    int kq[16], q[16], v[4], o[4], gate, gate_la;
+    __device__ __forceinline__ void init(const ChunkRows &cr, int64_t dv, int sh) {
         const int lane = threadIdx.x & 63;
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             const int row = 4 * n + (lane >> 4);
-            kq[n] = cr.off(row) * 256 + (((lane & 15) ^ row_swz(row)) << 4);
+            const int piece = ((lane & 15) ^ row_swz(row)) << 4;
+            kq[n] = cr.off(row) * 256 + piece;
+            q[n] = (cr.off(row) >> sh) * 256 + piece;
         }
         const int rowb = (int)(dv * 2);
         const int piece = (lane & 3) ^ (lane >> 4);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) v[n] = cr.off(16 * n + (lane >> 2)) * rowb + piece * 16;
+        for (int n = 0; n < 4; ++n) {
+            v[n] = cr.off(16 * n + (lane >> 2)) * rowb + piece * 16;
+            o[n] = (cr.off(16 * n + (lane >> 2)) >> sh) * rowb + piece * 16;
+        }
         // rows past the end get an offset beyond the buffer, which reads as zero
         gate = lane <= cr.rmax ? cr.off(lane) * 4 : 0x40000000;
+        gate_la = (lane <= cr.rmax && (lane & ((1 << sh) - 1)) == 0) ? (cr.off(lane) >> sh) * 4 : 0x40000000;
         // opaque to the optimiser, so they stay in their registers instead of being
         // recomputed into temporaries next to each copy
 #pragma unroll
         for (int n = 0; n < 16; ++n) asm volatile("" : "+v"(kq[n]));
 #pragma unroll
+        for (int n = 0; n < 16; ++n) asm volatile("" : "+v"(q[n]));
+#pragma unroll
         for (int n = 0; n < 4; ++n) asm volatile("" : "+v"(v[n]));
+#pragma unroll
+        for (int n = 0; n < 4; ++n) asm volatile("" : "+v"(o[n]));
         asm volatile("" : "+v"(gate));
+        asm volatile("" : "+v"(gate_la));
     }
 };
-__device__ __forceinline__ void copy_kq(char *dst, u32x4 rsrc, const CopyOffsets &co, int64_t lo) {
+__device__ __forceinline__ void copy_kq(char *dst, u32x4 rsrc, const int (&offs)[16], int64_t lo) {
     const int soff = __builtin_amdgcn_readfirstlane((int)(lo * 256));
     const unsigned base = lds_addr(dst);
 #pragma unroll
-    for (int n = 0; n < 16; ++n) dma_b128(base + n * 1024, rsrc, co.kq[n], soff);
+    for (int n = 0; n < 16; ++n) dma_b128(base + n * 1024, rsrc, offs[n], soff);
 }
-__device__ __forceinline__ void copy_v(char *dst, u32x4 rsrc, const CopyOffsets &co, int64_t lo, int64_t dv) {
+__device__ __forceinline__ void copy_v(char *dst, u32x4 rsrc, const int (&offs)[4], int64_t lo, int64_t dv) {
     const int soff = __builtin_amdgcn_readfirstlane((int)(lo * dv * 2));
     const unsigned base = lds_addr(dst);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) dma_b128(base + n * 1024, rsrc, co.v[n], soff);
+    for (int n = 0; n < 4; ++n) dma_b128(base + n * 1024, rsrc, offs[n], soff);
 }
 // Gates of the chunk (log alpha, beta) straight into the raw buffer: lane r loads row r.
-__device__ __forceinline__ void copy_gates(char *raw, u32x4 ra, u32x4 rb, const CopyOffsets &co, int64_t lo) {
+__device__ __forceinline__ void copy_gates(char *raw, u32x4 ra, u32x4 rb, const CopyOffsets &co, int64_t lo, int sh) {
+    const int soff_la = __builtin_amdgcn_readfirstlane((int)((lo >> sh) * 4));
     const int soff = __builtin_amdgcn_readfirstlane((int)(lo * 4));
-    dma_b32(lds_addr(raw + kRawLa), ra, co.gate, soff);
+    dma_b32(lds_addr(raw + kRawLa), ra, co.gate_la, soff_la);
     dma_b32(lds_addr(raw + kRawBeta), rb, co.gate, soff);
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -646,9 +663,11 @@ __device__ __forceinline__ void prep_a(const char *raw, char *der, const RowFrag
 // parity) and rows 16r + 4(i%4) .. +3, so that lane i receives row 16r + i, columns 8g + 4h
 // .. +3: the two reads give it 16 contiguous bytes of the output row.
 // With acc_out, prv holds the output's previous values of the chunk in the V-slice layout
-// (row R at 64 R bytes, 16-byte piece p at p ^ ((R % 16) / 4)).
+// (row R at 64 R bytes, 16-byte piece p at p ^ ((R % 16) / 4)). With 2^sh sub-steps per
+// token, obase is the chunk's first token and row R is the output of token R >> sh when
+// R % 2^sh = jread (the reading sub-step), and is dropped otherwise.
 __device__ __forceinline__ void write_back(const char *stg, const char *prv, __bf16 *obase, const ChunkRows &cr,
-                                           int64_t dv, bool acc_out) {
+                                           int64_t dv, bool acc_out, int sh, int jread) {
     const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
     bf16x8 val[4], prev[4];
 #pragma unroll
@@ -666,8 +685,8 @@ __device__ __forceinline__ void write_back(const char *stg, const char *prv, __b
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = 16 * r + j;
-        if (row <= cr.rmax) {
-            bf16x8 *dst = reinterpret_cast<bf16x8 *>(obase + (int64_t)cr.off(row) * dv + 8 * g);
+        if (row <= cr.rmax && (row & ((1 << sh) - 1)) == jread) {
+            bf16x8 *dst = reinterpret_cast<bf16x8 *>(obase + (int64_t)(cr.off(row) >> sh) * dv + 8 * g);
             bf16x8 v = val[r];
             if (acc_out) {
 #pragma unroll
@@ -722,10 +741,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
         }
     }
     const int64_t row = a.cu_seqlens ? 0 : seq;
-    int64_t t0 = 0, len = a.T;
+    // scan rows: 2^sh delta sub-steps per token (sh = 0 for the plain rule); t0 and len count
+    // scan rows, Ts is the scan length of a row of the batch
+    const int sh = __builtin_ctz((unsigned)a.n_sub);
+    const int64_t Ts = a.T << sh;
+    int64_t t0 = 0, len = Ts;
     if (a.cu_seqlens) {
-        t0 = a.cu_seqlens[seq];
-        len = a.cu_seqlens[seq + 1] - t0;
+        t0 = (int64_t)a.cu_seqlens[seq] << sh;
+        len = ((int64_t)a.cu_seqlens[seq + 1] << sh) - t0;
     }
     const bool fwd = (a.flags & kFlagReverse) == 0;
     const bool pre = (a.flags & kFlagReadPre) != 0;
@@ -734,12 +757,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     const int64_t nchunks = (len + kC - 1) / kC;
     const int dcol0 = tile * kDVT;
 
-    const __bf16 *kb = reinterpret_cast<const __bf16 *>(a.k) + (row * a.Hk + kh) * a.T * kDK;
+    const __bf16 *kb = reinterpret_cast<const __bf16 *>(a.k) + (row * a.Hk + kh) * Ts * kDK;
     const __bf16 *qb = reinterpret_cast<const __bf16 *>(a.q) + (row * a.Hk + kh) * a.T * kDK;
-    const __bf16 *vb = reinterpret_cast<const __bf16 *>(a.v) + (row * a.Hv + head) * a.T * a.dv;
+    const __bf16 *vb = reinterpret_cast<const __bf16 *>(a.v) + (row * a.Hv + head) * Ts * a.dv;
     const float *ab = a.log_alpha + (row * a.Hv + head) * a.T;
-    const float *bb = a.beta + (row * a.Hv + head) * a.T;
+    const float *bb = a.beta + (row * a.Hv + head) * Ts;
     __bf16 *ob = reinterpret_cast<__bf16 *>(a.out) + (row * a.Hv + head) * a.T * a.dv;
+    // the sub-step whose row gives a token's output: its first (pre-write read) or last
+    const int jread = pre ? 0 : (1 << sh) - 1;
 
     // The roles run separate loops with the same barrier sequence (two barriers in the
     // prologue, one per chunk), so each role's registers are live only in its own loop.
@@ -777,15 +802,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             }
             u32x4 rsrc0, rsrc1, rsrc2, rsrc3, rsrc4;
             if constexpr (R == kKW) {
-                rsrc0 = slab_rsrc(kb, a.T * kDK * 2);
+                rsrc0 = slab_rsrc(kb, Ts * kDK * 2);
                 // the prologue form copies Q here too: this wave then owns both operands whose
                 // row norms it computes
                 if constexpr (kPro) rsrc1 = slab_rsrc(qb, a.T * kDK * 2);
             } else if constexpr (R == kGW) {
                 rsrc0 = slab_rsrc(qb, a.T * kDK * 2);
-                rsrc1 = slab_rsrc(vb + dcol0, a.T * a.dv * 2 - dcol0 * 2);
+                rsrc1 = slab_rsrc(vb + dcol0, Ts * a.dv * 2 - dcol0 * 2);
                 rsrc4 = slab_rsrc(ob + dcol0, a.T * a.dv * 2 - dcol0 * 2);
-                rsrc2 = slab_rsrc(ab, (t0 + len) * 4);
+                rsrc2 = slab_rsrc(ab, ((t0 + len) >> sh) * 4);
                 rsrc3 = slab_rsrc(bb, (t0 + len) * 4);
             }
             // lane offsets of a full chunk (rmax = 63) and of the last chunk
@@ -795,20 +820,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 full.lo = 0;
                 full.rmax = kC - 1;
                 full.fwd = fwd;
-                cfull.init(full, a.dv);
-                clast.init(chunk_rows(t0, len, fwd, nchunks - 1), a.dv);
+                cfull.init(full, a.dv, sh);
+                clast.init(chunk_rows(t0, len, fwd, nchunks - 1), a.dv, sh);
             }
             // two explicit paths, so that each copy addresses with one of the fixed sets
             auto issue = [&](int64_t ch, const CopyOffsets &co) __attribute__((always_inline)) {
                 char *rawn = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
                 const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
                 if constexpr (R == kKW) {
-                    copy_kq(rawn + kRawK, rsrc0, co, lo);
-                    if constexpr (kPro) copy_kq(rawn + kRawQ, rsrc1, co, lo);
+                    copy_kq(rawn + kRawK, rsrc0, co.kq, lo);
+                    if constexpr (kPro) copy_kq(rawn + kRawQ, rsrc1, co.q, lo >> sh);
                 } else if constexpr (R == kGW) {
-                    if constexpr (!kPro) copy_kq(rawn + kRawQ, rsrc0, co, lo);
-                    copy_v(rawn + kRawV, rsrc1, co, lo, a.dv);
-                    copy_gates(rawn, rsrc2, rsrc3, co, lo);
+                    if constexpr (!kPro) copy_kq(rawn + kRawQ, rsrc0, co.q, lo >> sh);
+                    copy_v(rawn + kRawV, rsrc1, co.v, lo, a.dv);
+                    copy_gates(rawn, rsrc2, rsrc3, co, lo, sh);
                 }
             };
             auto prep = [&](int64_t ch) __attribute__((always_inline)) {
@@ -832,7 +857,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
             auto store = [&](int64_t ch) __attribute__((always_inline)) {
                 const ChunkRows cr = chunk_rows(t0, len, fwd, ch);
                 write_back(smem + kOffStage + (int)(ch & 1) * kStageBytes, smem + kOffPrev + (int)(ch & 1) * kPrevBytes,
-                           ob + cr.lo * a.dv + dcol0, cr, a.dv, acc_out);
+                           ob + (cr.lo >> sh) * a.dv + dcol0, cr, a.dv, acc_out, sh, jread);
             };
             // the wave that copies the gates builds the chunk's gate tables as soon as its copies
             // have landed, one chunk ahead of the prep waves that read them
@@ -865,8 +890,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                     if (acc_out) {
                         char *prv = smem + kOffPrev + (int)(ch & 1) * kPrevBytes;
                         const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
-                        if (ch == nchunks - 1) copy_v(prv, rsrc4, clast, lo, a.dv);
-                        else copy_v(prv, rsrc4, cfull, lo, a.dv);
+                        if (ch == nchunks - 1) copy_v(prv, rsrc4, clast.o, lo >> sh, a.dv);
+                        else copy_v(prv, rsrc4, cfull.o, lo >> sh, a.dv);
                     }
                 }
                 if constexpr (R == kWaveStore) {

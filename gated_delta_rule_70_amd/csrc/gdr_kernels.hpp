@@ -28,7 +28,8 @@ struct ChunkArgs {
     int64_t ntiles;  // dv / 32
     uint32_t flags;
     // delta sub-steps per token (DeltaProduct; 1 for the plain rule): k, v and beta hold n_sub
-    // rows per token ([..][T][n_sub][..]); the generic kernel serves n_sub > 1
+    // rows per token ([..][T][n_sub][..]); the fast kernel serves powers of two, the generic
+    // kernel any count
     int32_t n_sub;
 };
 

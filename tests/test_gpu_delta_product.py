@@ -128,3 +128,51 @@ def test_full_size_sampled(gdr):
         ro, rh = dp.scan(sl(c.q), sl(c.k), sl(c.v), sl(c.log_alpha), sl(c.beta), sl(c.h0), read="pre")
         check(o[bi:bi + 1, h:h + 1], ro, torch.bfloat16, "out (%d, %d)" % (bi, h))
         check(hT[bi:bi + 1, h:h + 1], rh, torch.bfloat16, "hT (%d, %d)" % (bi, h))
+
+
+# bf16, d_k 128, chunk 64: 1, 2, 4, 8 and 16 sub-steps per token take the fast kernel (a chunk
+# then starts on a token), other counts the generic one; both against the oracle, with ragged
+# chunk tails, packed segments (empty, single-token, multi-chunk), accumulation and unit-norm rows
+FAST_N = [2, 3, 4, 8, 16]
+
+
+@pytest.mark.parametrize("n", FAST_N)
+@pytest.mark.parametrize("read", ["pre", "post"])
+def test_chunk64_substeps(gdr, n, read):
+    _say("delta product chunk64 n=%d %s" % (n, read))
+    c = inputs.delta_product_case(B=2, T=53, n=n, Hk=1, Hv=2, dk=128, dv=128, dtype=torch.bfloat16, seed=41 + n,
+                                  h0_std=0.5, regime="slow")
+    o, hT = _run(gdr, c, 64, read)
+    ro, rh = dp.scan(c.q, c.k, c.v, c.log_alpha, c.beta, c.h0, read=read)
+    check(o, ro, torch.bfloat16, "out")
+    check(hT, rh, torch.bfloat16, "hT")
+
+
+@pytest.mark.parametrize("n", [2, 4, 16])
+def test_chunk64_varlen_accumulate_l2norm(gdr, n):
+    lengths = [0, 1, 5, 16, 33, 47]
+    _say("delta product chunk64 varlen n=%d" % n)
+    c = inputs.delta_product_case(B=1, n=n, Hk=2, Hv=4, dk=128, dv=64, dtype=torch.bfloat16, seed=57 + n,
+                                  h0_std=0.5, lengths=lengths, regime="slow")
+    g = torch.Generator().manual_seed(58)
+    c.q = (c.q.float() * (torch.rand(c.q.shape[:-1] + (1,), generator=g) * 3 + 0.5)).to(torch.bfloat16).contiguous()
+    c.k = (c.k.float() * (torch.rand(c.k.shape[:-1] + (1,), generator=g) * 3 + 0.5)).to(torch.bfloat16).contiguous()
+    base = torch.randn(1, 4, sum(lengths), 64, generator=g).to(torch.bfloat16)
+    for read in ("pre", "post"):
+        o, hT = _run(gdr, c, 64, read, l2norm=True, accumulate=base)
+        ref = base.double().numpy().copy()
+        _, rh = dp.scan(c.q, c.k, c.v, c.log_alpha, c.beta, c.h0, c.cu_seqlens, read=read, out=ref, l2norm=True)
+        check(o, ref, torch.bfloat16, "out %s" % read)
+        check(hT, rh, torch.bfloat16, "hT %s" % read)
+
+
+def test_chunk64_plain_varlen(gdr):
+    # packed segments without normalisation or accumulation, post-write read, two sub-steps
+    lengths = [31, 0, 64, 2, 97]
+    _say("delta product chunk64 plain varlen")
+    c = inputs.delta_product_case(B=1, n=2, Hk=1, Hv=1, dk=128, dv=128, dtype=torch.bfloat16, seed=71, h0_std=0.5,
+                                  lengths=lengths)
+    o, hT = _run(gdr, c, 64, "post")
+    ro, rh = dp.scan(c.q, c.k, c.v, c.log_alpha, c.beta, c.h0, c.cu_seqlens, read="post")
+    check(o, ro, torch.bfloat16, "out")
+    check(hT, rh, torch.bfloat16, "hT")
