@@ -218,10 +218,16 @@ def bench_gdn2(binding, inputs, steps):
                          h0_std=0.1)
     q, k, v, g, b, w, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.g, c.b, c.w, c.h0))
     out, hT = torch.empty_like(v), torch.empty_like(h0)
-    fn = lambda: binding.gdn2_chunk_fwd(q, k, v, g, b, w, h0, chunk=32, out=out, hT=hT)
+    ws = torch.empty(binding.gdn2_chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, 32), dtype=torch.uint8,
+                     device=dev)
+    fn = lambda: binding.gdn2_chunk_fwd(q, k, v, g, b, w, h0, chunk=32, out=out, hT=hT, workspace=ws)
     ms, _ = timed(fn, steps, 50, torch.cuda.current_stream(dev))
-    chunk = dict(ms=ms, tokens=4 * 4096, bytes=gdn2_bytes(4, 16, 16, 4096, 128, 128, 2, 4))
-    del q, k, v, g, b, w, h0, out, hT
+    # the one-pass kernel (no workspace) on the same inputs, for reference
+    fn1 = lambda: binding.gdn2_chunk_fwd(q, k, v, g, b, w, h0, chunk=32, out=out, hT=hT, fused=True)
+    ms1, _ = timed(fn1, max(3, steps // 4), 5, torch.cuda.current_stream(dev))
+    chunk = dict(ms=ms, fused_ms=ms1, ws_bytes=ws.numel(), tokens=4 * 4096,
+                 bytes=gdn2_bytes(4, 16, 16, 4096, 128, 128, 2, 4))
+    del q, k, v, g, b, w, h0, out, hT, ws
     N, Hk, Hv = 256, 16, 32
     dc = inputs.gdn2_case(B=N, T=1, Hk=Hk, Hv=Hv, dk=128, dv=128, dtype=torch.bfloat16, seed=1003, h0_std=0.1)
     one = lambda t: t[:, :, 0].contiguous().to(dev)
@@ -341,7 +347,8 @@ def main():
         return
     if args.only == "gdn2":
         g2, g2d = bench_gdn2(binding, inputs, args.steps)
-        print(json.dumps({"gdn2_chunk_ms": g2["ms"], "gdn2_chunk_bytes": g2["bytes"], "steps": args.steps,
+        print(json.dumps({"gdn2_chunk_ms": g2["ms"], "gdn2_chunk_fused_ms": g2["fused_ms"],
+                          "gdn2_chunk_bytes": g2["bytes"], "steps": args.steps,
                           "gdn2_decode_us": g2d["ms"] * 1e3}), flush=True)
         return
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -25,7 +25,8 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
 
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
-           "gdr_gdn2_chunk_fwd", "gdr_gdn2_decode_step", "gdr_delta_product_fwd",
+           "gdr_gdn2_chunk_fwd", "gdr_gdn2_chunk_fwd_workspace_bytes", "gdr_gdn2_decode_step",
+           "gdr_delta_product_fwd",
            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_bytes",
            "gdr_status_string", "gdr_last_error", "gdr_abi_version", "gdr_selftest_mfma")
 
@@ -69,8 +70,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_chunk_bwd_workspace_bytes.restype = ctypes.c_int64
     lib.gdr_delta_product_fwd.argtypes = [p, p, p, p, p, p, p, i32, i32, p, p, ctypes.POINTER(ChunkDims), p]
     lib.gdr_delta_product_fwd.restype = ctypes.c_int
-    lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, p, ctypes.c_int64,
+                                       ctypes.POINTER(ChunkDims), p]
     lib.gdr_gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_gdn2_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDims), i32, i32]
+    lib.gdr_gdn2_chunk_fwd_workspace_bytes.restype = ctypes.c_int64
     lib.gdr_gdn2_decode_step.argtypes = [p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
     lib.gdr_gdn2_decode_step.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -353,12 +357,14 @@ def delta_product_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chu
 
 def gdn2_chunk_fwd(q, k, v, g, b, w, h0=None, cu_seqlens=None, *, chunk: int = 64, read: str = "post",
                    reverse: bool = False, out=None, accumulate: bool = False, hT=None, want_state: bool = True,
-                   l2norm: bool = False):
+                   l2norm: bool = False, workspace=None, fused: bool = False):
     """GDN-2 chunked forward (``gdr_gdn2_chunk_fwd``).
 
     q, k [B, Hk, T, dk] and v [B, Hv, T, dv] (bf16 or fp32, one dtype); g [B, Hk, T, dk] fp32 log
     decay per key channel; b [B, Hk, T, dk] erase gate and w [B, Hv, T, dv] write gate in the
-    dtype of q. The rest as ``chunk_fwd``.
+    dtype of q. The rest as ``chunk_fwd``. The two-pass form runs with ``workspace`` (a uint8 GPU
+    tensor of at least ``gdn2_chunk_fwd_workspace_bytes`` bytes, allocated here when not given);
+    ``fused=True`` passes no workspace and runs the one-pass kernel.
     """
     _need(q, "q")
     dev, dt = q.device, q.dtype
@@ -391,10 +397,25 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, h0=None, cu_seqlens=None, *, chunk: int = 6
     flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0) | \
         (GDR_ACCUMULATE if accumulate else 0) | (GDR_QK_L2NORM if l2norm else 0)
     dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    ws_ptr, ws_bytes = None, 0
+    if not fused:
+        need = lib().gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), int(chunk), int(cu_seqlens is not None))
+        if need < 0:
+            raise ValueError("invalid sizes for the GDN-2 workspace")
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, None, dev)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     _check(lib().gdr_gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0),
-                                    _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT), ctypes.byref(dims),
-                                    _stream(q)))
+                                    _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT), ws_ptr, ws_bytes,
+                                    ctypes.byref(dims), _stream(q)))
     return out, hT
+
+
+def gdn2_chunk_fwd_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace the two-pass ``gdr_gdn2_chunk_fwd`` needs (num_seqs > 0: packed)."""
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, num_seqs, _dtype_code(dtype), 0)
+    return int(lib().gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), int(chunk), int(num_seqs > 0)))
 
 
 def gdn2_decode_step(q, k, v, g, b, w, state_in, state_out=None, out=None, *, read: str = "post",

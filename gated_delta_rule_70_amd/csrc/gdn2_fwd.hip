@@ -636,12 +636,499 @@ __global__ __launch_bounds__(kThreads) void gdn2_chunk_kernel(Gdn2Args a) {
     }
 }
 
+// ============================================================ two-pass form
+// With a workspace the forward runs in two passes. The first computes, for every chunk at once
+// (one workgroup per chunk and key head), what depends on the chunk alone:
+//
+//   Wc = T (B * K * e^{G})        [C][d_k]   (the WY form: U = T (W*V) - Wc H0)
+//   Qc = Q * e^{Gr}               [C][d_k]
+//   Kt = (K * e^{G_C - G})^T      [d_k][C]
+//   P                             [C][C]
+//   e^{G_C}                       [d_k] fp32
+//   Uc = T (W * V)                [C][d_v]   (per value head)
+//
+// from the same per-block operands as above (LA, LP and R times the products of block decays
+// that make them relative to the chunk start or end; every factor <= 1). The second walks the
+// chunks of each (sequence, value head, 32 columns of d_v) with the state in registers:
+//
+//   U = Uc - Wc H,   O = Qc H + P U,   H <- Diag(e^{G_C}) H + Kt U
+//
+// so the serial part holds only products against the state.
+template <typename E, int C, int DK>
+struct WsKey {  // bytes of one (chunk, key head) block, every part 16-byte aligned
+    static constexpr int64_t kW = 0;
+    static constexpr int64_t kQ = kW + (int64_t)C * DK * sizeof(E);
+    static constexpr int64_t kKt = kQ + (int64_t)C * DK * sizeof(E);
+    static constexpr int64_t kP = kKt + (int64_t)C * DK * sizeof(E);
+    static constexpr int64_t kEgc = kP + (int64_t)C * C * sizeof(E);
+    static constexpr int64_t kBytes = kEgc + DK * 4;
+};
+
+// workspace slot of chunk c of sequence seq (packed: cu[seq] / C + seq + c, which keeps the
+// slots of consecutive sequences apart; else seq * ceil(T / C) + c)
+template <int C>
+__device__ __forceinline__ int64_t ws_slot(const Gdn2Args &a, int64_t seq, int64_t c) {
+    if (a.cu_seqlens) return a.cu_seqlens[seq] / C + seq + c;
+    return seq * ((a.T + C - 1) / C) + c;
+}
+
+// 16-byte pieces between global memory and a padded LDS matrix (rows of rb bytes)
+template <int ROWS, int RB>
+__device__ __forceinline__ void lds_to_global(char *dst, const char *src, int src_pitch) {
+    constexpr int PR = RB / 16, N = ROWS * PR;
+    for (int i = threadIdx.x; i < N; i += kThreads) {
+        const int r = i / PR, p = i % PR;
+        *reinterpret_cast<uint4 *>(dst + r * RB + p * 16) = *reinterpret_cast<const uint4 *>(src + r * src_pitch + p * 16);
+    }
+}
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
+    typedef Smem<E, C, DK> SM;
+    typedef WsKey<E, C, DK> WK;
+    constexpr int NT = SM::NT;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, cc = lane & 15;
+
+    // workgroup -> (slot, key head) -> (sequence, chunk); slots between sequences are idle
+    const int64_t slot = blockIdx.x / a.Hk, kh = blockIdx.x % a.Hk;
+    int64_t seq, c;
+    if (a.cu_seqlens) {
+        // the last sequence whose first slot is <= slot
+        int64_t lo = 0, hi = a.units / a.Hv - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (a.cu_seqlens[mid] / C + mid <= slot) lo = mid;
+            else hi = mid - 1;
+        }
+        seq = lo;
+        c = slot - (a.cu_seqlens[seq] / C + seq);
+    } else {
+        const int64_t per = (a.T + C - 1) / C;
+        seq = slot / per;
+        c = slot % per;
+    }
+    SeqView sv;
+    sv.t0 = 0;
+    sv.len = a.T;
+    if (a.cu_seqlens) {
+        sv.t0 = a.cu_seqlens[seq];
+        sv.len = a.cu_seqlens[seq + 1] - sv.t0;
+    }
+    sv.rev = (a.flags & kFlagReverse) != 0;
+    if (c < 0 || c * C >= sv.len) return;
+    const bool pre = (a.flags & kFlagReadPre) != 0;
+    const bool l2 = (a.flags & kFlagL2Norm) != 0;
+    const int64_t row = a.cu_seqlens ? 0 : seq;
+    const int grp = (int)(a.Hv / a.Hk);
+
+    Bases bs;
+    const int64_t kq_off = (row * a.Hk + kh) * a.T * DK;
+    const int64_t v_off0 = (row * a.Hv + kh * grp) * a.T * a.dv;
+    bs.k = reinterpret_cast<const char *>(a.k) + kq_off * (int64_t)sizeof(E);
+    bs.q = reinterpret_cast<const char *>(a.q) + kq_off * (int64_t)sizeof(E);
+    bs.b = reinterpret_cast<const char *>(a.b) + kq_off * (int64_t)sizeof(E);
+    bs.g = reinterpret_cast<const char *>(a.g) + kq_off * 4;
+    bs.v = reinterpret_cast<const char *>(a.v) + v_off0 * (int64_t)sizeof(E);
+    bs.w = reinterpret_cast<const char *>(a.w) + v_off0 * (int64_t)sizeof(E);
+    bs.dv = a.dv;
+    bs.dcol0 = 0;
+
+    for (int i = tid; i < C * SM::TP; i += kThreads) {
+        sm.T[i] = static_cast<E>(0.f);
+        sm.P[i] = static_cast<E>(0.f);
+    }
+    {
+        Prefetch<E, C, DK> pf;
+        prefetch_chunk<E, C, DK>(pf, sv, c, bs);
+        store_chunk<E, C, DK>(pf, sm);
+    }
+    __syncthreads();
+    if (l2) {
+        normalize_rows<E, C, DK>(sm);
+        __syncthreads();
+    }
+    block_decays<E, C, DK>(sm);
+    __syncthreads();
+    bool any_unsafe = false;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) any_unsafe |= sm.unsafe[i] != 0;
+    if (any_unsafe) {
+        for (int i = wave; i < NT; i += kThreads / 64)
+            if (sm.unsafe[i]) exact_diag_block<E, C, DK>(sm, i, pre);
+        __syncthreads();
+    }
+    form_operands<E, C, DK>(sm, pre);
+    __syncthreads();
+    gram_tiles<E, C, DK>(sm, pre);
+    __syncthreads();
+    if (wave == 0) solve_unit_lower_inverse<E, C>(sm);
+
+    char *kb = reinterpret_cast<char *>(a.ws) + (ws_slot<C>(a, seq, c) * a.Hk + kh) * WK::kBytes;
+    // chunk-relative operands in place: LA and LP times e^{G_ref} of their block, R times the
+    // decay of the blocks after its own; e^{G_C} = the product of all block decays
+    for (int i = tid; i < NT * DK; i += kThreads) {
+        const int blk = i / DK, ch = i % DK;
+        const float er = sm.eref[blk * DK + ch];
+        float tail = 1.f;
+        for (int j = blk + 1; j < NT; ++j) tail *= sm.dec[j * DK + ch];
+#pragma unroll 4
+        for (int r = 16 * blk; r < 16 * blk + 16; ++r) {
+            sm.Bk[r * SM::KP + ch] = static_cast<E>(to_f(sm.Bk[r * SM::KP + ch]) * er);
+            sm.Q[r * SM::KP + ch] = static_cast<E>(to_f(sm.Q[r * SM::KP + ch]) * er);
+            sm.K[r * SM::KP + ch] = static_cast<E>(to_f(sm.K[r * SM::KP + ch]) * tail);
+        }
+        if (blk == 0) {
+            float e = 1.f;
+            for (int j = 0; j < NT; ++j) e *= sm.dec[j * DK + ch];
+            reinterpret_cast<float *>(kb + WK::kEgc)[ch] = e;
+        }
+    }
+    __syncthreads();
+    // Wc = T LAe on the matrix cores: NT x DK/16 output tiles over the waves
+    constexpr int NWT = NT * (DK / 16);
+    constexpr int PER = (NWT + 3) / 4;
+    floatx4 wt[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int t = wave + 4 * j;
+        wt[j] = zero4();
+        if (t < NWT) {
+            const int mi = t / (DK / 16), nj = t % (DK / 16);
+            if constexpr (C == 16) {
+                wt[j] = mma16(wt[j], frag_rows_lo<E>(sm.T, SM::TP, 0, 0), frag_cols_lo<E>(sm.Bk, SM::KP, 16 * nj, 0));
+            } else {
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += 32)
+                    wt[j] = mma32(wt[j], frag_rows<E>(sm.T, SM::TP, 16 * mi, k0), frag_cols<E>(sm.Bk, SM::KP, 16 * nj, k0));
+            }
+        }
+    }
+    // the rest of the key part while the products are in registers: Qc, Kt (transposed), P
+    lds_to_global<C, DK * sizeof(E)>(kb + WK::kQ, reinterpret_cast<const char *>(sm.Q), SM::KP * sizeof(E));
+    lds_to_global<C, C * sizeof(E)>(kb + WK::kP, reinterpret_cast<const char *>(sm.P), SM::TP * sizeof(E));
+    {
+        constexpr int EPP = 16 / sizeof(E);  // elements per 16-byte piece
+        constexpr int PR = C / EPP, N = DK * PR;
+        for (int i = tid; i < N; i += kThreads) {
+            const int d = i / PR, t0 = (i % PR) * EPP;
+            uint4 piece;
+            E *v = reinterpret_cast<E *>(&piece);
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) v[e] = sm.K[(t0 + e) * SM::KP + d];
+            *reinterpret_cast<uint4 *>(kb + WK::kKt + ((int64_t)d * C + t0) * sizeof(E)) = piece;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int t = wave + 4 * j;
+        if (t < NWT) {
+            const int mi = t / (DK / 16), nj = t % (DK / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.Bk[(16 * mi + 4 * g + r) * SM::KP + 16 * nj + cc] = static_cast<E>(wt[j][r]);
+        }
+    }
+    __syncthreads();
+    lds_to_global<C, DK * sizeof(E)>(kb + WK::kW, reinterpret_cast<const char *>(sm.Bk), SM::KP * sizeof(E));
+
+    // Uc = T (W * V) for each value head of the key head, 32 columns at a time
+    char *ub = reinterpret_cast<char *>(a.ws) + a.ws_u_off;
+    constexpr int NUT = NT * 2;  // output tiles of one 32-column slice
+    for (int vh = 0; vh < grp; ++vh) {
+        const int64_t head = kh * grp + vh;
+        char *ud = ub + ((ws_slot<C>(a, seq, c) * a.Hv + head) * C * a.dv) * (int64_t)sizeof(E);
+        for (int dcol = 0; dcol < a.dv; dcol += kDvTile) {
+            // W * V of the slice into V
+            constexpr int VPR = kDvTile * (int)sizeof(E) / 16;
+            const int64_t hoff = (int64_t)vh * a.T * a.dv;
+            for (int i = tid; i < C * VPR; i += kThreads) {
+                const int r = i / VPR, p = i % VPR;
+                const int64_t pos = c * C + r;
+                uint4 vv = make_uint4(0, 0, 0, 0), ww = make_uint4(0, 0, 0, 0);
+                if (pos < sv.len) {
+                    const int64_t off = ((hoff + sv.token(pos) * a.dv + dcol) * (int64_t)sizeof(E)) + p * 16;
+                    vv = *reinterpret_cast<const uint4 *>(bs.v + off);
+                    ww = *reinterpret_cast<const uint4 *>(bs.w + off);
+                }
+                constexpr int EPP = 16 / sizeof(E);
+                const E *ve = reinterpret_cast<const E *>(&vv);
+                const E *we = reinterpret_cast<const E *>(&ww);
+                uint4 piece;
+                E *pr = reinterpret_cast<E *>(&piece);
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) pr[e] = static_cast<E>(to_f(ve[e]) * to_f(we[e]));
+                *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(sm.V) + r * SM::VP * (int)sizeof(E) + p * 16) = piece;
+            }
+            __syncthreads();
+            floatx4 ut[(NUT + 3) / 4];
+#pragma unroll
+            for (int j = 0; j < (NUT + 3) / 4; ++j) {
+                const int t = wave + 4 * j;
+                ut[j] = zero4();
+                if (t < NUT) {
+                    const int mi = t / 2, nj = t % 2;
+                    if constexpr (C == 16) {
+                        ut[j] = mma16(ut[j], frag_rows_lo<E>(sm.T, SM::TP, 0, 0), frag_cols_lo<E>(sm.V, SM::VP, 16 * nj, 0));
+                    } else {
+#pragma unroll
+                        for (int k0 = 0; k0 < C; k0 += 32)
+                            ut[j] = mma32(ut[j], frag_rows<E>(sm.T, SM::TP, 16 * mi, k0), frag_cols<E>(sm.V, SM::VP, 16 * nj, k0));
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < (NUT + 3) / 4; ++j) {
+                const int t = wave + 4 * j;
+                if (t < NUT) {
+                    const int mi = t / 2, nj = t % 2;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.W[(16 * mi + 4 * g + r) * SM::VP + 16 * nj + cc] = static_cast<E>(ut[j][r]);
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < C * VPR; i += kThreads) {
+                const int r = i / VPR, p = i % VPR;
+                *reinterpret_cast<uint4 *>(ud + ((int64_t)r * a.dv + dcol) * (int64_t)sizeof(E) + p * 16) =
+                    *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(sm.W) + r * SM::VP * (int)sizeof(E) + p * 16);
+            }
+            // the next slice overwrites V and W only after this one's reads
+            __syncthreads();
+        }
+    }
+}
+
+// Chain buffers: one chunk's operands, padded rows (E elements unless noted)
+template <typename E, int C, int DK>
+struct alignas(16) ChainBuf {
+    static constexpr int KP = DK + Pad<E>::v;        // Wc, Qc
+    static constexpr int CP = C + Pad<E>::v;         // Kt, P
+    static constexpr int UP = kDvTile + Pad<E>::v;   // Uc slice
+    E W[C * KP];
+    E Q[C * KP];
+    E Kt[DK * CP];
+    E P[C * CP];
+    E U[C * UP];
+    float egc[DK];
+};
+template <typename E, int C, int DK>
+struct ChainPieces {  // 16-byte pieces of one chunk's operands, in load order
+    static constexpr int EPP = 16 / sizeof(E);
+    static constexpr int NW = C * DK / EPP, NQ = NW, NK = DK * C / EPP, NP = C * C / EPP;
+    static constexpr int NU = C * kDvTile / EPP, NE = DK / 4;
+    static constexpr int N = NW + NQ + NK + NP + NU + NE;
+    static constexpr int kLoaders = kThreads / 2;  // waves 2 and 3 copy, waves 0 and 1 compute
+    static constexpr int PER = (N + kLoaders - 1) / kLoaders;
+};
+
+// piece i of a chunk: its byte offset from the chunk's key block (or, with from_u, from its Uc
+// rows, pitch dv elements) and its byte offset inside ChainBuf
+template <typename E, int C, int DK>
+__device__ __forceinline__ void chain_piece(int i, int64_t dv, int64_t &src, bool &from_u, int &dst) {
+    typedef ChainPieces<E, C, DK> CPc;
+    typedef ChainBuf<E, C, DK> CB;
+    typedef WsKey<E, C, DK> WK;
+    constexpr int es = sizeof(E), EPP = CPc::EPP;
+    if (i < CPc::NW + CPc::NQ) {
+        const int m = i < CPc::NW ? 0 : 1, j = i - m * CPc::NW;
+        const int r = j / (DK / EPP), p = j % (DK / EPP);
+        src = (m ? WK::kQ : WK::kW) + (int64_t)j * 16;
+        from_u = false;
+        dst = (m ? offsetof(CB, Q) : offsetof(CB, W)) + r * CB::KP * es + p * 16;
+        return;
+    }
+    i -= CPc::NW + CPc::NQ;
+    if (i < CPc::NK + CPc::NP) {
+        const int m = i < CPc::NK ? 0 : 1, j = i - m * CPc::NK;
+        const int r = j / (C / EPP), p = j % (C / EPP);
+        src = (m ? WK::kP : WK::kKt) + (int64_t)j * 16;
+        from_u = false;
+        dst = (m ? offsetof(CB, P) : offsetof(CB, Kt)) + r * CB::CP * es + p * 16;
+        return;
+    }
+    i -= CPc::NK + CPc::NP;
+    if (i < CPc::NU) {
+        const int r = i / (kDvTile / EPP), p = i % (kDvTile / EPP);
+        src = (int64_t)r * dv * es + p * 16;
+        from_u = true;
+        dst = offsetof(CB, U) + r * CB::UP * es + p * 16;
+        return;
+    }
+    i -= CPc::NU;
+    src = WK::kEgc + (int64_t)i * 16;
+    from_u = false;
+    dst = offsetof(CB, egc) + i * 16;
+}
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kThreads) void gdn2_chain_kernel(Gdn2Args a) {
+    typedef ChainBuf<E, C, DK> CB;
+    typedef ChainPieces<E, C, DK> CPc;
+    typedef WsKey<E, C, DK> WK;
+    constexpr int NT = C / 16;
+    constexpr int HT = DK / 16;
+    __shared__ CB buf[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, cc = lane & 15;
+    const int64_t blk = blockIdx.x;
+    const int64_t xcd = blk & 7, sl = blk >> 3;
+    const int64_t unit = (sl / a.ntiles) * 8 + xcd;
+    const int tile = (int)(sl % a.ntiles);
+    if (unit >= a.units) return;
+    const int64_t seq = unit / a.Hv, head = unit % a.Hv;
+    const int64_t kh = head / (a.Hv / a.Hk);
+    const int64_t row = a.cu_seqlens ? 0 : seq;
+    SeqView sv;
+    sv.t0 = 0;
+    sv.len = a.T;
+    if (a.cu_seqlens) {
+        sv.t0 = a.cu_seqlens[seq];
+        sv.len = a.cu_seqlens[seq + 1] - sv.t0;
+    }
+    sv.rev = (a.flags & kFlagReverse) != 0;
+    const bool acc_out = (a.flags & kFlagAccumulate) != 0;
+    const int64_t nchunks = (sv.len + C - 1) / C;
+    const int dcol0 = tile * kDvTile;
+    const char *wsk = reinterpret_cast<const char *>(a.ws);
+    const char *wsu = reinterpret_cast<const char *>(a.ws) + a.ws_u_off;
+    E *ob = reinterpret_cast<E *>(a.out) + (row * a.Hv + head) * a.T * a.dv;
+
+    // copies by the loader waves (thread lt = tid - 128)
+    const int lt = tid - kThreads / 2;
+    const bool chain = wave < 2;
+    const int lcol = wave * 16;
+    const int dcol = dcol0 + lcol + cc;
+    floatx4 H[HT];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) H[t] = zero4();
+    if (chain && a.h0) {
+        const float *hb = a.h0 + (seq * a.Hv + head) * DK * a.dv;
+#pragma unroll
+        for (int t = 0; t < HT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) H[t][r] = hb[(16 * t + 4 * g + r) * a.dv + dcol];
+    }
+    // the loader waves copy chunk c + 1 into the other buffer (last read in step c - 1) while
+    // the chain waves work on chunk c; the copy lives in the loaders' registers only there
+    auto copy = [&](int64_t ch) __attribute__((always_inline)) {
+        const int64_t s = ws_slot<C>(a, seq, ch);
+        const char *kb = wsk + (s * a.Hk + kh) * WK::kBytes;
+        const char *ub = wsu + ((s * a.Hv + head) * C * a.dv + dcol0) * (int64_t)sizeof(E);
+        char *base = reinterpret_cast<char *>(&buf[ch & 1]);
+        uint4 pf[CPc::PER];
+        int dsts[CPc::PER];
+#pragma unroll
+        for (int j = 0; j < CPc::PER; ++j) {
+            const int i = lt + j * CPc::kLoaders;
+            int64_t src = 0;
+            bool from_u = false;
+            dsts[j] = -1;
+            if (i < CPc::N) chain_piece<E, C, DK>(i, a.dv, src, from_u, dsts[j]);
+            pf[j] = dsts[j] >= 0 ? *reinterpret_cast<const uint4 *>((from_u ? ub : kb) + src) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < CPc::PER; ++j)
+            if (dsts[j] >= 0) *reinterpret_cast<uint4 *>(base + dsts[j]) = pf[j];
+    };
+    if (nchunks > 0 && !chain) copy(0);
+    __syncthreads();
+    for (int64_t c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks && !chain) copy(c + 1);
+        const CB &cb = buf[c & 1];
+        if (chain) {
+            floatx4 XW[NT], XQ[NT];
+#pragma unroll
+            for (int mi = 0; mi < NT; ++mi) {
+                XW[mi] = zero4();
+                XQ[mi] = zero4();
+            }
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const Frag<E> hb = frag_from_acc<E>(H[2 * ks], H[2 * ks + 1]);
+#pragma unroll
+                for (int mi = 0; mi < NT; ++mi) {
+                    XW[mi] = mma32(XW[mi], frag_rows<E>(cb.W, CB::KP, 16 * mi, 32 * ks), hb);
+                    XQ[mi] = mma32(XQ[mi], frag_rows<E>(cb.Q, CB::KP, 16 * mi, 32 * ks), hb);
+                }
+            }
+            floatx4 U[NT];
+#pragma unroll
+            for (int mi = 0; mi < NT; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) U[mi][r] = to_f(cb.U[(16 * mi + 4 * g + r) * CB::UP + lcol + cc]) - XW[mi][r];
+            // O = Qc H + P U
+#pragma unroll
+            for (int mi = 0; mi < NT; ++mi) {
+                floatx4 o = XQ[mi];
+#pragma unroll
+                for (int kt = 0; kt <= mi; kt += 2) {
+                    if (kt + 1 < NT)
+                        o = mma32(o, frag_rows<E>(cb.P, CB::CP, 16 * mi, 16 * kt), frag_from_acc<E>(U[kt], U[kt + 1]));
+                    else
+                        o = mma16(o, frag_rows_lo<E>(cb.P, CB::CP, 16 * mi, 16 * kt), cvt4<E>(U[kt]));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t pos = c * C + 16 * mi + 4 * g + r;
+                    if (pos < sv.len) {
+                        E *dst = ob + sv.token(pos) * a.dv + dcol;
+                        const float prev = acc_out ? to_f(*dst) : 0.f;
+                        *dst = static_cast<E>(prev + o[r]);
+                    }
+                }
+            }
+            // H <- Diag(e^{G_C}) H + Kt U
+#pragma unroll
+            for (int t = 0; t < HT; ++t) {
+                H[t] *= *reinterpret_cast<const floatx4 *>(cb.egc + 16 * t + 4 * g);
+                if constexpr (C == 16) {
+                    H[t] = mma16(H[t], frag_rows_lo<E>(cb.Kt, CB::CP, 16 * t, 0), cvt4<E>(U[0]));
+                } else {
+#pragma unroll
+                    for (int k0 = 0; k0 < C; k0 += 32)
+                        H[t] = mma32(H[t], frag_rows<E>(cb.Kt, CB::CP, 16 * t, k0), frag_from_acc<E>(U[k0 / 16], U[k0 / 16 + 1]));
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (chain && a.hT) {
+        float *hb = a.hT + (seq * a.Hv + head) * DK * a.dv;
+#pragma unroll
+        for (int t = 0; t < HT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hb[(16 * t + 4 * g + r) * a.dv + dcol] = H[t][r];
+    }
+}
+
+template <typename E, int C, int DK>
+hipError_t launch_two_pass(const Gdn2Args &a, hipStream_t stream) {
+    const int64_t prep_blocks = a.nslots * a.Hk;
+    if (prep_blocks > 0) {
+        hipLaunchKernelGGL((gdn2_prep_kernel<E, C, DK>), dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
+    hipLaunchKernelGGL((gdn2_chain_kernel<E, C, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <typename E, int C, int DK>
 hipError_t launch_typed(const Gdn2Args &a, hipStream_t stream) {
     const int64_t groups = (a.units + 7) / 8;
     const int64_t blocks = groups * 8 * a.ntiles;
     hipLaunchKernelGGL((gdn2_chunk_kernel<E, C, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+// without a workspace the fused one-pass kernel, with one the two passes
+template <typename E, int C, int DK>
+hipError_t launch_form(const Gdn2Args &a, hipStream_t stream) {
+    static_assert(WsKey<E, C, DK>::kBytes % 16 == 0, "workspace blocks keep 16-byte alignment");
+    return a.ws ? launch_two_pass<E, C, DK>(a, stream) : launch_typed<E, C, DK>(a, stream);
 }
 
 }  // namespace
@@ -657,21 +1144,26 @@ hipError_t launch_gdn2_chunk_fwd(const Gdn2Args &a, int dtype, int chunk, int dk
     if (!gdn2_chunk_supported(dtype, chunk, dk)) return hipErrorInvalidValue;
     if (dtype == kDtypeBf16) {
         if (dk == 64) {
-            if (chunk == 16) return launch_typed<__bf16, 16, 64>(a, s);
-            if (chunk == 32) return launch_typed<__bf16, 32, 64>(a, s);
-            return launch_typed<__bf16, 64, 64>(a, s);
+            if (chunk == 16) return launch_form<__bf16, 16, 64>(a, s);
+            if (chunk == 32) return launch_form<__bf16, 32, 64>(a, s);
+            return launch_form<__bf16, 64, 64>(a, s);
         }
-        if (chunk == 16) return launch_typed<__bf16, 16, 128>(a, s);
-        if (chunk == 32) return launch_typed<__bf16, 32, 128>(a, s);
-        return launch_typed<__bf16, 64, 128>(a, s);
+        if (chunk == 16) return launch_form<__bf16, 16, 128>(a, s);
+        if (chunk == 32) return launch_form<__bf16, 32, 128>(a, s);
+        return launch_form<__bf16, 64, 128>(a, s);
     }
     if (dk == 64) {
-        if (chunk == 16) return launch_typed<float, 16, 64>(a, s);
-        if (chunk == 32) return launch_typed<float, 32, 64>(a, s);
-        return launch_typed<float, 64, 64>(a, s);
+        if (chunk == 16) return launch_form<float, 16, 64>(a, s);
+        if (chunk == 32) return launch_form<float, 32, 64>(a, s);
+        return launch_form<float, 64, 64>(a, s);
     }
-    if (chunk == 16) return launch_typed<float, 16, 128>(a, s);
-    return launch_typed<float, 32, 128>(a, s);
+    if (chunk == 16) return launch_form<float, 16, 128>(a, s);
+    return launch_form<float, 32, 128>(a, s);
+}
+
+int64_t gdn2_ws_key_bytes(int dtype, int chunk, int dk) {
+    const int64_t es = dtype == kDtypeBf16 ? 2 : 4;
+    return es * (3 * (int64_t)chunk * dk + (int64_t)chunk * chunk) + 4 * (int64_t)dk;
 }
 
 }  // namespace gdr

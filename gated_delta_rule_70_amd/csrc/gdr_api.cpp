@@ -267,9 +267,31 @@ gdr_status_t decode_impl(const void *q, const void *k, const void *v, const floa
 
 namespace {
 
+// Two-pass GDN-2 workspace: one slot per chunk of every sequence (packed: T / C + S + 1, which
+// covers the slots cu[s] / C + s + c the kernels use), each holding a block per key head and a
+// C x dv slice per value head. Returns -1 for sizes that do not make sense.
+int64_t gdn2_slots(const gdr_chunk_dims_t &d, int64_t chunk, bool packed) {
+    if (packed) return d.T / chunk + d.num_seqs + 1;
+    return d.B * ((d.T + chunk - 1) / chunk);
+}
+int64_t gdn2_ws_bytes(const gdr_chunk_dims_t &d, int32_t chunk, bool packed, int64_t *key_part) {
+    if ((d.dtype != GDR_F32 && d.dtype != GDR_BF16) || (chunk != 16 && chunk != 32 && chunk != 64) ||
+        (d.dk != 64 && d.dk != 128) || d.T < 0 || d.B < 0 || d.Hk < 1 || d.Hv < 1 || d.dv < 0 ||
+        (packed && d.num_seqs < 1))
+        return -1;
+    const int dt = d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32;
+    const int64_t slots = gdn2_slots(d, chunk, packed);
+    const int64_t key = prod({slots, d.Hk, gdr::gdn2_ws_key_bytes(dt, chunk, (int)d.dk)});
+    const int64_t val = prod({slots, d.Hv, chunk, d.dv, elem_size(d.dtype)});
+    if (key < 0 || val < 0) return -1;
+    if (key_part) *key_part = key;
+    return key + val;
+}
+
 gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
                              const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out,
-                             float *hT, const gdr_chunk_dims_t *dims, void *stream) {
+                             float *hT, void *workspace, int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
+                             void *stream) {
     g_last_error[0] = '\0';
     if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
     const gdr_chunk_dims_t d = *dims;
@@ -313,6 +335,21 @@ gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const 
     }
     if (overlap(ro, rhT)) return fail(GDR_ERR_ALIAS, "out overlaps hT");
     if (overlap(rhT, rh0) && rhT.lo != rh0.lo) return fail(GDR_ERR_ALIAS, "hT partially overlaps h0");
+    int64_t ws_key = 0, nslots = 0;
+    if (workspace) {
+        const int64_t need = gdn2_ws_bytes(d, chunk, cu_seqlens != nullptr, &ws_key);
+        if (need < 0) return fail(GDR_ERR_DIMS, "workspace size overflows");
+        if (workspace_bytes < need)
+            return fail(GDR_ERR_DIMS, "workspace_bytes %lld is below the %lld bytes needed", (long long)workspace_bytes,
+                        (long long)need);
+        if (!aligned(workspace, 16)) return fail(GDR_ERR_ALIGN, "workspace is not 16-byte aligned");
+        const Range rws = rng("workspace", workspace, need);
+        for (const Range &r : ins)
+            if (overlap(rws, r)) return fail(GDR_ERR_ALIAS, "workspace overlaps %s", r.name);
+        if (overlap(rws, ro) || overlap(rws, rhT)) return fail(GDR_ERR_ALIAS, "workspace overlaps out or hT");
+        nslots = gdn2_slots(d, chunk, cu_seqlens != nullptr);
+        if (nslots * d.Hk > INT32_MAX) return fail(GDR_ERR_DIMS, "too many chunks for the workspace pass");
+    }
 
     gdr::Gdn2Args a;
     a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
@@ -323,6 +360,9 @@ gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const 
     a.units = nseq * d.Hv;
     a.ntiles = d.dv / 32;
     a.flags = d.flags;
+    a.ws = workspace;
+    a.nslots = nslots;
+    a.ws_u_off = ws_key;
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
     if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
     const hipError_t e = gdr::launch_gdn2_chunk_fwd(a, d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32, chunk,
@@ -385,8 +425,15 @@ extern "C" {
 
 gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *b,
                                 const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk,
-                                void *out, float *hT, const gdr_chunk_dims_t *dims, void *stream) {
-    return gdn2_chunk_impl(q, k, v, g, b, w, h0, cu_seqlens, chunk, out, hT, dims, stream);
+                                void *out, float *hT, void *workspace, int64_t workspace_bytes,
+                                const gdr_chunk_dims_t *dims, void *stream) {
+    return gdn2_chunk_impl(q, k, v, g, b, w, h0, cu_seqlens, chunk, out, hT, workspace, workspace_bytes, dims,
+                           stream);
+}
+
+int64_t gdr_gdn2_chunk_fwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t chunk, int32_t packed) {
+    if (!dims) return -1;
+    return gdn2_ws_bytes(*dims, chunk, packed != 0, nullptr);
 }
 
 gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v, const float *g, const void *b,

@@ -56,6 +56,9 @@ struct Gdn2Args {
     int64_t units;   // sequences x value heads
     int64_t ntiles;  // dv / 32
     uint32_t flags;
+    // two-pass form (ws non-null): chunk slots, and the byte offset of the per-value-head part
+    void *ws;
+    int64_t nslots, ws_u_off;
 };
 
 // GDN-2 decode: g, b [N][Hk][dk] (g fp32), w [N][Hv][dv].
@@ -92,6 +95,8 @@ bool chunk_fwd_fast_supported(int dtype, int chunk, int dk);
 hipError_t launch_chunk_fwd_fast(const ChunkArgs &a, hipStream_t stream);
 bool gdn2_chunk_supported(int dtype, int chunk, int dk);
 hipError_t launch_gdn2_chunk_fwd(const Gdn2Args &a, int dtype, int chunk, int dk, hipStream_t stream);
+// bytes of one (chunk, key head) block of the two-pass workspace
+int64_t gdn2_ws_key_bytes(int dtype, int chunk, int dk);
 hipError_t launch_gdn2_decode(const Gdn2DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int dk, int dv, hipStream_t stream);

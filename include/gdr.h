@@ -280,19 +280,41 @@ gdr_status_t gdr_delta_product_fwd(const void *q, const void *k, const void *v,
  *   b           [B][Hk][T][dk]  dtype erase gate per key channel
  *   w           [B][Hv][T][dv]  dtype write gate per value channel
  *   h0, cu_seqlens, out, hT, dims, stream: as gdr_chunk_fwd (all four flags apply).
+ *   workspace   DEVICE scratch of at least gdr_gdn2_chunk_fwd_workspace_bytes(dims, chunk,
+ *               cu_seqlens != NULL) bytes, or NULL. Owned by the caller; its contents do not
+ *               matter before or after the call; calls that share a workspace must not
+ *               overlap. With a workspace the forward runs in two passes: the first computes
+ *               every chunk's state-independent operands at once (for each chunk and key head:
+ *               the WY-form right factor T (b * k * e^G), q * e^{Gr}, (k * e^{G_C - G})^T, the
+ *               intra-chunk read matrix and e^{G_C}; for each value head T (w * v)), the second
+ *               walks the chunks with the state. Without one a single fused pass does both
+ *               (allocation-free, slower). The results agree up to rounding.
+ *   workspace_bytes  its size in bytes.
  *
  * Every tensor pointer 16-byte aligned. chunk 16, 32 or 64, except that fp32 with dk = 128
  * takes 16 or 32 only (GDR_ERR_CHUNK): the fp32 operands of a 64-token chunk do not fit in the
  * 160 KB of shared memory of a compute unit. A 16-token block whose decay summed over the block
  * is below -60 on some channel is computed exactly on a slower path (see gdn2_fwd.hip);
  * results do not depend on which path a block takes beyond rounding.
- * Errors: as gdr_chunk_fwd; GDR_ERR_NULL also when g, b or w is NULL with T > 0.
+ * Errors: as gdr_chunk_fwd; GDR_ERR_NULL also when g, b or w is NULL with T > 0; with a
+ * workspace, GDR_ERR_DIMS when workspace_bytes is too small, GDR_ERR_ALIGN when it is not
+ * 16-byte aligned and GDR_ERR_ALIAS when it overlaps an input or output.
  */
 gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                                 const float *g, const void *b, const void *w,
                                 const float *h0, const int32_t *cu_seqlens, int32_t chunk,
-                                void *out, float *hT,
+                                void *out, float *hT, void *workspace, int64_t workspace_bytes,
                                 const gdr_chunk_dims_t *dims, void *stream);
+
+/*
+ * gdr_gdn2_chunk_fwd_workspace_bytes - bytes of workspace gdr_gdn2_chunk_fwd's two-pass form
+ * needs for these sizes, chunk and packing (packed != 0: cu_seqlens with dims->num_seqs
+ * sequences). Host-only arithmetic: one slot per chunk of every sequence (packed: T / chunk +
+ * num_seqs + 1), each with Hk blocks of es (3 chunk dk + chunk^2) + 4 dk bytes and Hv slices of
+ * es chunk dv bytes (es = 2 for bf16, 4 for fp32). Returns -1 for an unsupported dtype, chunk or
+ * dk, or negative sizes.
+ */
+int64_t gdr_gdn2_chunk_fwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t chunk, int32_t packed);
 
 /*
  * gdr_gdn2_decode_step - one GDN-2 token for N independent sequences.

@@ -176,7 +176,7 @@ def test_decode_gated_rejects():
 def _gdn2_chunk(lib, **over):
     d = dict(B=1, T=128, Hk=2, Hv=2, dk=64, dv=64, num_seqs=0, dtype=1, flags=8)
     ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, b=FAKE * 5, w=FAKE * 7, h0=None, cu=None,
-               out=FAKE * 6, hT=None, chunk=64)
+               out=FAKE * 6, hT=None, chunk=64, ws=None, ws_bytes=0)
     for k_, v_ in over.items():
         (d if k_ in d else ptr)[k_] = v_
     dims = binding.ChunkDims(d["B"], d["T"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["num_seqs"],
@@ -184,7 +184,7 @@ def _gdn2_chunk(lib, **over):
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     st = lib.gdr_gdn2_chunk_fwd(vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["g"]), vp(ptr["b"]),
                                 vp(ptr["w"]), vp(ptr["h0"]), vp(ptr["cu"]), ptr["chunk"], vp(ptr["out"]),
-                                vp(ptr["hT"]), ctypes.byref(dims), None)
+                                vp(ptr["hT"]), vp(ptr["ws"]), ptr["ws_bytes"], ctypes.byref(dims), None)
     return binding.STATUS[st], lib.gdr_last_error().decode()
 
 
@@ -200,6 +200,10 @@ GDN2_REJECTS = [
     (dict(flags=16), "GDR_ERR_FLAGS", "flags"),
     (dict(dv=40), "GDR_ERR_UNSUPPORTED", "dv"),
     (dict(Hk=4, Hv=2), "GDR_ERR_DIMS", "Hv"),
+    # the two-pass form's workspace (this call needs 2 x 2 x 33024 + 2 x 2 x 64 x 64 x 2 bytes)
+    (dict(ws=FAKE * 9, ws_bytes=1024), "GDR_ERR_DIMS", "workspace_bytes"),
+    (dict(ws=FAKE * 9 + 8, ws_bytes=1 << 20), "GDR_ERR_ALIGN", "workspace"),
+    (dict(ws=FAKE * 7 + 4096, ws_bytes=1 << 20), "GDR_ERR_ALIAS", "workspace overlaps w"),
 ]
 
 
@@ -208,6 +212,25 @@ GDN2_REJECTS = [
 def test_gdn2_chunk_rejects(over, status, text):
     st, msg = _gdn2_chunk(binding.load(), **over)
     assert st == status and text in msg, (st, msg)
+
+
+@needs_lib
+def test_gdn2_workspace_bytes():
+    lib = binding.load()
+    # B4 H16 T4096 d128 bf16, chunk 32: 4 x 128 chunk slots; per slot 16 key-head blocks of
+    # 2 (3 x 32 x 128 + 32 x 32) + 4 x 128 bytes and 16 value-head slices of 32 x 128 x 2 bytes
+    dims = binding.ChunkDims(4, 4096, 16, 16, 128, 128, 0, 1, 0)
+    want = 512 * 16 * (2 * (3 * 32 * 128 + 32 * 32) + 4 * 128) + 512 * 16 * 32 * 128 * 2
+    assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 32, 0) == want
+    # packed: T / chunk + num_seqs + 1 slots; fp32 doubles the element bytes; Hk < Hv
+    dims = binding.ChunkDims(1, 1000, 2, 4, 64, 32, 3, 0, 0)
+    want = 66 * 2 * (4 * (3 * 16 * 64 + 16 * 16) + 4 * 64) + 66 * 4 * 16 * 32 * 4
+    assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 16, 1) == want
+    assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 8, 1) == -1
+    assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(None, 16, 0) == -1
+    # a workspace of the size asked for passes validation (no sequences: nothing is launched)
+    st, msg = _gdn2_chunk(lib, B=0, ws=FAKE * 9, ws_bytes=0)
+    assert st == "GDR_OK", msg
 
 
 @needs_lib

@@ -75,13 +75,14 @@ def _ids(c):
                                                  str(c["dtype"]).split(".")[-1], c["chunk"])
 
 
-def _run(gdr, c, chunk, read="post", reverse=False, l2norm=False, accumulate=None):
+def _run(gdr, c, chunk, read="post", reverse=False, l2norm=False, accumulate=None, fused=False, workspace=None):
     q, k, v, g, b, w, h0, cu = _dev(c)
     out = None
     if accumulate is not None:
         out = accumulate.cuda().clone()
     o, hT = gdr.gdn2_chunk_fwd(q, k, v, g, b, w, h0, cu, chunk=chunk, read=read, reverse=reverse,
-                               l2norm=l2norm, out=out, accumulate=accumulate is not None)
+                               l2norm=l2norm, out=out, accumulate=accumulate is not None, fused=fused,
+                               workspace=workspace)
     torch.cuda.synchronize()
     return gpu_np(o), gpu_np(hT)
 
@@ -100,16 +101,46 @@ def test_chunk_parity(gdr, cfg, regime, read):
     check(hT, rh, dtype, "hT")
 
 
+# The one-pass kernel (no workspace) on a subset: every dtype, chunk and d_k it takes
+@pytest.mark.parametrize("cfg", CHUNK, ids=_ids)
+@pytest.mark.parametrize("read", ["post", "pre"])
+def test_chunk_parity_fused(gdr, cfg, read):
+    cfg = dict(cfg)
+    chunk, dtype = cfg.pop("chunk"), cfg["dtype"]
+    _say("gdn2 fused chunk %s %s" % (_ids(dict(cfg, chunk=chunk)), read))
+    c = inputs.gdn2_case(**cfg, seed=13, h0_std=0.5, regime="mixed")
+    o, hT = _run(gdr, c, chunk, read=read, fused=True)
+    ro, rh = gdn2.scan(c.q, c.k, c.v, c.g, c.b, c.w, c.h0, read=read)
+    check(o, ro, dtype, "out")
+    check(hT, rh, dtype, "hT")
+
+
+def test_chunk_workspace_reused(gdr):
+    # one workspace for two calls, the second smaller and packed: nothing carries over
+    _say("gdn2 workspace reuse")
+    c1 = inputs.gdn2_case(B=2, T=150, Hk=1, Hv=2, dk=64, dv=64, dtype=torch.bfloat16, seed=71, h0_std=0.5)
+    c2 = inputs.gdn2_case(B=1, Hk=1, Hv=2, dk=64, dv=64, dtype=torch.bfloat16, seed=72, h0_std=0.5,
+                          lengths=[40, 0, 3], regime="strong")
+    need = gdr.gdn2_chunk_fwd_workspace_bytes(2, 150, 1, 2, 64, 64, 32)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    for c in (c1, c2):
+        o, hT = _run(gdr, c, 32, workspace=ws)
+        ro, rh = gdn2.scan(c.q, c.k, c.v, c.g, c.b, c.w, c.h0, c.cu_seqlens)
+        check(o, ro, torch.bfloat16, "out")
+        check(hT, rh, torch.bfloat16, "hT")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("reverse", [False, True])
-def test_chunk_varlen_reverse_accumulate(gdr, dtype, reverse):
+@pytest.mark.parametrize("fused", [False, True])
+def test_chunk_varlen_reverse_accumulate(gdr, dtype, reverse, fused):
     lengths = [0, 1, 15, 16, 17, 64, 65, 130]
-    _say("gdn2 varlen %s reverse=%s" % (dtype, reverse))
+    _say("gdn2 varlen %s reverse=%s fused=%s" % (dtype, reverse, fused))
     c = inputs.gdn2_case(B=1, Hk=2, Hv=4, dk=64, dv=64, dtype=dtype, seed=21, h0_std=0.5, lengths=lengths,
                          regime="mixed")
     base = inputs._normal(inputs._gen(5), (1, 4, sum(lengths), 64)).to(dtype)
     for read in ("post", "pre"):
-        o, hT = _run(gdr, c, 32, read=read, reverse=reverse, accumulate=base)
+        o, hT = _run(gdr, c, 32, read=read, reverse=reverse, accumulate=base, fused=fused)
         ref_out = base.double().numpy().copy()
         _, rh = gdn2.scan(c.q, c.k, c.v, c.g, c.b, c.w, c.h0, c.cu_seqlens, read=read, reverse=reverse,
                           out=ref_out)
