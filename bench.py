@@ -404,11 +404,13 @@ def main():
                                   "calls": 2},
             "gdn2-chunk-fwd-bf16-B4-H16-T4096-d128-c32": {
                 "tokens_per_s": g2["tokens"] / (g2["ms"] / 1e3), "ms": g2["ms"],
+                "one_pass_ms": g2["fused_ms"], "workspace_bytes": g2["ws_bytes"],
                 "roofline": {"bound": "hbm", "achieved": g2["bytes"] / (g2["ms"] / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": g2["bytes"] / (g2["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                             "bytes_per_launch": g2["bytes"], "kernel": "gdn2_chunk_kernel<bf16, 32, 128>",
+                             "bytes_per_launch": g2["bytes"],
+                             "kernel": "gdn2_prep_kernel + gdn2_chain_kernel <bf16, 32, 128> (one call)",
                              "traffic": measured_traffic("gdn2_chunk_B4_H16_T4096_d128_hbm_traffic.md",
-                                                         "gdn2_fwd.hip", "HBM bytes per launch")}},
+                                                         "gdn2_fwd.hip", "HBM bytes per call")}},
             "delta-product-n2-pre-bf16-B4-H16-T4096-d128-c64": {
                 "tokens_per_s": dpr["tokens"] / (dpr["ms"] / 1e3), "ms": dpr["ms"],
                 "hbm_frac": dpr["bytes"] / (dpr["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,

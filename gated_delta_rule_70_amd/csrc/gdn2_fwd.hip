@@ -167,7 +167,7 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<E, C, DK> &pf, const Seq
         if (piece < PF::VPIECES) {
             const int r = piece / PF::VROW, cp = piece % PF::VROW;
             const int64_t pos = c * C + r;
-            if (pos < sv.len) {
+            if (pos < sv.len && bs.v) {
                 const int64_t off = (sv.token(pos) * bs.dv + bs.dcol0) * (int64_t)sizeof(E) + cp * 16;
                 pf.v[i] = *reinterpret_cast<const uint4 *>(bs.v + off);
                 pf.w[i] = *reinterpret_cast<const uint4 *>(bs.w + off);
@@ -459,7 +459,8 @@ __global__ __launch_bounds__(kThreads) void gdn2_chunk_kernel(Gdn2Args a) {
     constexpr int HT = DK / 16;
     __shared__ SM sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int g = lane >> 4, cc = lane & 15;
 
     // block -> (unit, d_v tile); the tiles of one unit land on one XCD and share K/Q in its L2
@@ -638,29 +639,29 @@ __global__ __launch_bounds__(kThreads) void gdn2_chunk_kernel(Gdn2Args a) {
 
 // ============================================================ two-pass form
 // With a workspace the forward runs in two passes. The first computes, for every chunk at once
-// (one workgroup per chunk and key head), what depends on the chunk alone:
+// (one workgroup per chunk and key head), what depends on the chunk's keys and gates alone:
 //
-//   Wc = T (B * K * e^{G})        [C][d_k]   (the WY form: U = T (W*V) - Wc H0)
+//   Wc = T (B * K * e^{G})        [C][d_k]   (the WY form: U = T (W * V) - Wc H0)
 //   Qc = Q * e^{Gr}               [C][d_k]
 //   Kt = (K * e^{G_C - G})^T      [d_k][C]
-//   P                             [C][C]
+//   P, T                          [C][C]
 //   e^{G_C}                       [d_k] fp32
-//   Uc = T (W * V)                [C][d_v]   (per value head)
 //
-// from the same per-block operands as above (LA, LP and R times the products of block decays
-// that make them relative to the chunk start or end; every factor <= 1). The second walks the
-// chunks of each (sequence, value head, 32 columns of d_v) with the state in registers:
+// from the per-block operands above (LA, LP and R times the products of block decays that make
+// them relative to the chunk start or end; every factor <= 1). The second walks the chunks of
+// each (sequence, value head, 32 columns of d_v) with the state in registers:
 //
-//   U = Uc - Wc H,   O = Qc H + P U,   H <- Diag(e^{G_C}) H + Kt U
+//   U = T (W * V) - Wc H,   O = Qc H + P U,   H <- Diag(e^{G_C}) H + Kt U
 //
-// so the serial part holds only products against the state.
+// so that its serial part holds only the products against the state.
 template <typename E, int C, int DK>
 struct WsKey {  // bytes of one (chunk, key head) block, every part 16-byte aligned
     static constexpr int64_t kW = 0;
     static constexpr int64_t kQ = kW + (int64_t)C * DK * sizeof(E);
     static constexpr int64_t kKt = kQ + (int64_t)C * DK * sizeof(E);
     static constexpr int64_t kP = kKt + (int64_t)C * DK * sizeof(E);
-    static constexpr int64_t kEgc = kP + (int64_t)C * C * sizeof(E);
+    static constexpr int64_t kT = kP + (int64_t)C * C * sizeof(E);
+    static constexpr int64_t kEgc = kT + (int64_t)C * C * sizeof(E);
     static constexpr int64_t kBytes = kEgc + DK * 4;
 };
 
@@ -672,7 +673,7 @@ __device__ __forceinline__ int64_t ws_slot(const Gdn2Args &a, int64_t seq, int64
     return seq * ((a.T + C - 1) / C) + c;
 }
 
-// 16-byte pieces between global memory and a padded LDS matrix (rows of rb bytes)
+// 16-byte pieces from a padded LDS matrix (rows of RB bytes) to a dense global one
 template <int ROWS, int RB>
 __device__ __forceinline__ void lds_to_global(char *dst, const char *src, int src_pitch) {
     constexpr int PR = RB / 16, N = ROWS * PR;
@@ -688,7 +689,8 @@ __global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
     typedef WsKey<E, C, DK> WK;
     constexpr int NT = SM::NT;
     __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int g = lane >> 4, cc = lane & 15;
 
     // workgroup -> (slot, key head) -> (sequence, chunk); slots between sequences are idle
@@ -721,17 +723,15 @@ __global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
     const bool pre = (a.flags & kFlagReadPre) != 0;
     const bool l2 = (a.flags & kFlagL2Norm) != 0;
     const int64_t row = a.cu_seqlens ? 0 : seq;
-    const int grp = (int)(a.Hv / a.Hk);
 
     Bases bs;
     const int64_t kq_off = (row * a.Hk + kh) * a.T * DK;
-    const int64_t v_off0 = (row * a.Hv + kh * grp) * a.T * a.dv;
     bs.k = reinterpret_cast<const char *>(a.k) + kq_off * (int64_t)sizeof(E);
     bs.q = reinterpret_cast<const char *>(a.q) + kq_off * (int64_t)sizeof(E);
     bs.b = reinterpret_cast<const char *>(a.b) + kq_off * (int64_t)sizeof(E);
     bs.g = reinterpret_cast<const char *>(a.g) + kq_off * 4;
-    bs.v = reinterpret_cast<const char *>(a.v) + v_off0 * (int64_t)sizeof(E);
-    bs.w = reinterpret_cast<const char *>(a.w) + v_off0 * (int64_t)sizeof(E);
+    bs.v = nullptr;  // the value side is the second pass's
+    bs.w = nullptr;
     bs.dv = a.dv;
     bs.dcol0 = 0;
 
@@ -766,8 +766,9 @@ __global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
     if (wave == 0) solve_unit_lower_inverse<E, C>(sm);
 
     char *kb = reinterpret_cast<char *>(a.ws) + (ws_slot<C>(a, seq, c) * a.Hk + kh) * WK::kBytes;
-    // chunk-relative operands in place: LA and LP times e^{G_ref} of their block, R times the
-    // decay of the blocks after its own; e^{G_C} = the product of all block decays
+    // chunk-relative operands in place (while wave 0 solves): LA and LP times e^{G_ref} of their
+    // block, R times the decay of the blocks after its own; e^{G_C} = the product of all block
+    // decays
     for (int i = tid; i < NT * DK; i += kThreads) {
         const int blk = i / DK, ch = i % DK;
         const float er = sm.eref[blk * DK + ch];
@@ -805,9 +806,10 @@ __global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
             }
         }
     }
-    // the rest of the key part while the products are in registers: Qc, Kt (transposed), P
+    // the rest of the block while the products are in registers: Qc, Kt (transposed), P, T
     lds_to_global<C, DK * sizeof(E)>(kb + WK::kQ, reinterpret_cast<const char *>(sm.Q), SM::KP * sizeof(E));
     lds_to_global<C, C * sizeof(E)>(kb + WK::kP, reinterpret_cast<const char *>(sm.P), SM::TP * sizeof(E));
+    lds_to_global<C, C * sizeof(E)>(kb + WK::kT, reinterpret_cast<const char *>(sm.T), SM::TP * sizeof(E));
     {
         constexpr int EPP = 16 / sizeof(E);  // elements per 16-byte piece
         constexpr int PR = C / EPP, N = DK * PR;
@@ -832,145 +834,76 @@ __global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
     }
     __syncthreads();
     lds_to_global<C, DK * sizeof(E)>(kb + WK::kW, reinterpret_cast<const char *>(sm.Bk), SM::KP * sizeof(E));
-
-    // Uc = T (W * V) for each value head of the key head, 32 columns at a time
-    char *ub = reinterpret_cast<char *>(a.ws) + a.ws_u_off;
-    constexpr int NUT = NT * 2;  // output tiles of one 32-column slice
-    for (int vh = 0; vh < grp; ++vh) {
-        const int64_t head = kh * grp + vh;
-        char *ud = ub + ((ws_slot<C>(a, seq, c) * a.Hv + head) * C * a.dv) * (int64_t)sizeof(E);
-        for (int dcol = 0; dcol < a.dv; dcol += kDvTile) {
-            // W * V of the slice into V
-            constexpr int VPR = kDvTile * (int)sizeof(E) / 16;
-            const int64_t hoff = (int64_t)vh * a.T * a.dv;
-            for (int i = tid; i < C * VPR; i += kThreads) {
-                const int r = i / VPR, p = i % VPR;
-                const int64_t pos = c * C + r;
-                uint4 vv = make_uint4(0, 0, 0, 0), ww = make_uint4(0, 0, 0, 0);
-                if (pos < sv.len) {
-                    const int64_t off = ((hoff + sv.token(pos) * a.dv + dcol) * (int64_t)sizeof(E)) + p * 16;
-                    vv = *reinterpret_cast<const uint4 *>(bs.v + off);
-                    ww = *reinterpret_cast<const uint4 *>(bs.w + off);
-                }
-                constexpr int EPP = 16 / sizeof(E);
-                const E *ve = reinterpret_cast<const E *>(&vv);
-                const E *we = reinterpret_cast<const E *>(&ww);
-                uint4 piece;
-                E *pr = reinterpret_cast<E *>(&piece);
-#pragma unroll
-                for (int e = 0; e < EPP; ++e) pr[e] = static_cast<E>(to_f(ve[e]) * to_f(we[e]));
-                *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(sm.V) + r * SM::VP * (int)sizeof(E) + p * 16) = piece;
-            }
-            __syncthreads();
-            floatx4 ut[(NUT + 3) / 4];
-#pragma unroll
-            for (int j = 0; j < (NUT + 3) / 4; ++j) {
-                const int t = wave + 4 * j;
-                ut[j] = zero4();
-                if (t < NUT) {
-                    const int mi = t / 2, nj = t % 2;
-                    if constexpr (C == 16) {
-                        ut[j] = mma16(ut[j], frag_rows_lo<E>(sm.T, SM::TP, 0, 0), frag_cols_lo<E>(sm.V, SM::VP, 16 * nj, 0));
-                    } else {
-#pragma unroll
-                        for (int k0 = 0; k0 < C; k0 += 32)
-                            ut[j] = mma32(ut[j], frag_rows<E>(sm.T, SM::TP, 16 * mi, k0), frag_cols<E>(sm.V, SM::VP, 16 * nj, k0));
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < (NUT + 3) / 4; ++j) {
-                const int t = wave + 4 * j;
-                if (t < NUT) {
-                    const int mi = t / 2, nj = t % 2;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.W[(16 * mi + 4 * g + r) * SM::VP + 16 * nj + cc] = static_cast<E>(ut[j][r]);
-                }
-            }
-            __syncthreads();
-            for (int i = tid; i < C * VPR; i += kThreads) {
-                const int r = i / VPR, p = i % VPR;
-                *reinterpret_cast<uint4 *>(ud + ((int64_t)r * a.dv + dcol) * (int64_t)sizeof(E) + p * 16) =
-                    *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(sm.W) + r * SM::VP * (int)sizeof(E) + p * 16);
-            }
-            // the next slice overwrites V and W only after this one's reads
-            __syncthreads();
-        }
-    }
 }
 
-// Chain buffers: one chunk's operands, padded rows (E elements unless noted)
+// Chain buffers: one chunk's operands, padded rows (E elements unless noted); WV = W * V of
+// the workgroup's 32 columns
 template <typename E, int C, int DK>
 struct alignas(16) ChainBuf {
     static constexpr int KP = DK + Pad<E>::v;        // Wc, Qc
-    static constexpr int CP = C + Pad<E>::v;         // Kt, P
-    static constexpr int UP = kDvTile + Pad<E>::v;   // Uc slice
+    static constexpr int CP = C + Pad<E>::v;         // Kt, P, T
+    static constexpr int UP = kDvTile + Pad<E>::v;   // WV
     E W[C * KP];
     E Q[C * KP];
     E Kt[DK * CP];
     E P[C * CP];
-    E U[C * UP];
+    E T[C * CP];
+    E WV[C * UP];
     float egc[DK];
 };
+// The copy of one chunk by a pair of loader waves (128 threads): the key block is contiguous
+// in the workspace (piece i at byte 16 i); v and w pieces come in pairs and are multiplied on
+// the way into LDS. R pairs of loader waves take every R-th chunk, each pair with one set of
+// registers, so that R copies are in flight and each has R chain steps to arrive.
 template <typename E, int C, int DK>
-struct ChainPieces {  // 16-byte pieces of one chunk's operands, in load order
+struct ChainCopy {
     static constexpr int EPP = 16 / sizeof(E);
-    static constexpr int NW = C * DK / EPP, NQ = NW, NK = DK * C / EPP, NP = C * C / EPP;
-    static constexpr int NU = C * kDvTile / EPP, NE = DK / 4;
-    static constexpr int N = NW + NQ + NK + NP + NU + NE;
-    static constexpr int kLoaders = kThreads / 2;  // waves 2 and 3 copy, waves 0 and 1 compute
-    static constexpr int PER = (N + kLoaders - 1) / kLoaders;
+    static constexpr int NW = C * DK / EPP, NP = C * C / EPP, NE = DK / 4;
+    static constexpr int NKEY = 3 * NW + 2 * NP + NE;
+    static constexpr int NV = C * kDvTile / EPP;
+    static constexpr int kLoaders = kThreads / 2;
+    static constexpr int PK = (NKEY + kLoaders - 1) / kLoaders;
+    static constexpr int PV = (NV + kLoaders - 1) / kLoaders;
+    static constexpr int kRegs = 4 * (PK + 2 * PV);  // VGPRs of one set
+    static constexpr int R = kRegs <= 72 ? 3 : kRegs <= 100 ? 2 : 1;
+    static constexpr int kWaves = 2 + 2 * R;  // two chain waves, R loader pairs
+    // double-buffered operands must fit in the 160 KB of LDS
+    static constexpr bool kFits = 2 * sizeof(ChainBuf<E, C, DK>) <= 160 * 1024;
 };
 
-// piece i of a chunk: its byte offset from the chunk's key block (or, with from_u, from its Uc
-// rows, pitch dv elements) and its byte offset inside ChainBuf
+// LDS byte offset inside ChainBuf of key piece i
 template <typename E, int C, int DK>
-__device__ __forceinline__ void chain_piece(int i, int64_t dv, int64_t &src, bool &from_u, int &dst) {
-    typedef ChainPieces<E, C, DK> CPc;
+__device__ __forceinline__ int key_piece_dst(int i) {
+    typedef ChainCopy<E, C, DK> CC;
     typedef ChainBuf<E, C, DK> CB;
-    typedef WsKey<E, C, DK> WK;
-    constexpr int es = sizeof(E), EPP = CPc::EPP;
-    if (i < CPc::NW + CPc::NQ) {
-        const int m = i < CPc::NW ? 0 : 1, j = i - m * CPc::NW;
-        const int r = j / (DK / EPP), p = j % (DK / EPP);
-        src = (m ? WK::kQ : WK::kW) + (int64_t)j * 16;
-        from_u = false;
-        dst = (m ? offsetof(CB, Q) : offsetof(CB, W)) + r * CB::KP * es + p * 16;
-        return;
+    constexpr int es = sizeof(E), EPP = CC::EPP;
+    if (i < 2 * CC::NW) {
+        const int m = i < CC::NW ? 0 : 1, j = i - m * CC::NW;
+        return (m ? offsetof(CB, Q) : offsetof(CB, W)) + (j / (DK / EPP)) * CB::KP * es + (j % (DK / EPP)) * 16;
     }
-    i -= CPc::NW + CPc::NQ;
-    if (i < CPc::NK + CPc::NP) {
-        const int m = i < CPc::NK ? 0 : 1, j = i - m * CPc::NK;
-        const int r = j / (C / EPP), p = j % (C / EPP);
-        src = (m ? WK::kP : WK::kKt) + (int64_t)j * 16;
-        from_u = false;
-        dst = (m ? offsetof(CB, P) : offsetof(CB, Kt)) + r * CB::CP * es + p * 16;
-        return;
+    i -= 2 * CC::NW;
+    if (i < CC::NW) return offsetof(CB, Kt) + (i / (C / EPP)) * CB::CP * es + (i % (C / EPP)) * 16;
+    i -= CC::NW;
+    if (i < 2 * CC::NP) {
+        const int m = i < CC::NP ? 0 : 1, j = i - m * CC::NP;
+        return (m ? offsetof(CB, T) : offsetof(CB, P)) + (j / (C / EPP)) * CB::CP * es + (j % (C / EPP)) * 16;
     }
-    i -= CPc::NK + CPc::NP;
-    if (i < CPc::NU) {
-        const int r = i / (kDvTile / EPP), p = i % (kDvTile / EPP);
-        src = (int64_t)r * dv * es + p * 16;
-        from_u = true;
-        dst = offsetof(CB, U) + r * CB::UP * es + p * 16;
-        return;
-    }
-    i -= CPc::NU;
-    src = WK::kEgc + (int64_t)i * 16;
-    from_u = false;
-    dst = offsetof(CB, egc) + i * 16;
+    i -= 2 * CC::NP;
+    return offsetof(CB, egc) + i * 16;
 }
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kThreads) void gdn2_chain_kernel(Gdn2Args a) {
+__global__ __launch_bounds__((64 * ChainCopy<E, C, DK>::kWaves)) void gdn2_chain_kernel(Gdn2Args a) {
     typedef ChainBuf<E, C, DK> CB;
-    typedef ChainPieces<E, C, DK> CPc;
+    typedef ChainCopy<E, C, DK> CC;
     typedef WsKey<E, C, DK> WK;
     constexpr int NT = C / 16;
     constexpr int HT = DK / 16;
+    constexpr int R = CC::R;
     __shared__ CB buf[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int g = lane >> 4, cc = lane & 15;
     const int64_t blk = blockIdx.x;
     const int64_t xcd = blk & 7, sl = blk >> 3;
@@ -991,110 +924,211 @@ __global__ __launch_bounds__(kThreads) void gdn2_chain_kernel(Gdn2Args a) {
     const bool acc_out = (a.flags & kFlagAccumulate) != 0;
     const int64_t nchunks = (sv.len + C - 1) / C;
     const int dcol0 = tile * kDvTile;
-    const char *wsk = reinterpret_cast<const char *>(a.ws);
-    const char *wsu = reinterpret_cast<const char *>(a.ws) + a.ws_u_off;
+    const int64_t v_off = (row * a.Hv + head) * a.T * a.dv + dcol0;
     E *ob = reinterpret_cast<E *>(a.out) + (row * a.Hv + head) * a.T * a.dv;
 
-    // copies by the loader waves (thread lt = tid - 128)
-    const int lt = tid - kThreads / 2;
-    const bool chain = wave < 2;
+    if (wave >= 2) {
+        // loader pair G = (wave - 2) / 2 copies the chunks j with j % R == G; the same barrier
+        // sequence as the chain waves (one after the first copy, one per chunk)
+        const int G = (wave - 2) >> 1;
+        const int lt = tid - 128 * (G + 1);
+        const char *wsk = reinterpret_cast<const char *>(a.ws);
+        const E *vb = reinterpret_cast<const E *>(a.v) + v_off;
+        const E *wb = reinterpret_cast<const E *>(a.w) + v_off;
+        int kdst[CC::PK];
+#pragma unroll
+        for (int j = 0; j < CC::PK; ++j) {
+            const int i = lt + j * CC::kLoaders;
+            kdst[j] = i < CC::NKEY ? key_piece_dst<E, C, DK>(i) : -1;
+        }
+        uint4 rk[CC::PK], rv[CC::PV], rw[CC::PV];
+        auto issue = [&](int64_t ch) __attribute__((always_inline)) {
+            const char *kb = wsk + (ws_slot<C>(a, seq, ch) * a.Hk + kh) * WK::kBytes;
+#pragma unroll
+            for (int j = 0; j < CC::PK; ++j) {
+                const int i = lt + j * CC::kLoaders;
+                rk[j] = make_uint4(0, 0, 0, 0);
+                if (i < CC::NKEY) rk[j] = *reinterpret_cast<const uint4 *>(kb + (int64_t)i * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < CC::PV; ++j) {
+                const int i = lt + j * CC::kLoaders;
+                rv[j] = make_uint4(0, 0, 0, 0);
+                rw[j] = make_uint4(0, 0, 0, 0);
+                if (i < CC::NV) {
+                    const int r = i / (kDvTile / CC::EPP), p = i % (kDvTile / CC::EPP);
+                    const int64_t pos = ch * C + r;
+                    if (pos < sv.len) {
+                        const int64_t off = sv.token(pos) * a.dv + p * CC::EPP;
+                        rv[j] = *reinterpret_cast<const uint4 *>(vb + off);
+                        rw[j] = *reinterpret_cast<const uint4 *>(wb + off);
+                    }
+                }
+            }
+        };
+        auto store = [&](int64_t ch) __attribute__((always_inline)) {
+            char *base = reinterpret_cast<char *>(&buf[ch & 1]);
+#pragma unroll
+            for (int j = 0; j < CC::PK; ++j)
+                if (kdst[j] >= 0) *reinterpret_cast<uint4 *>(base + kdst[j]) = rk[j];
+#pragma unroll
+            for (int j = 0; j < CC::PV; ++j) {
+                const int i = lt + j * CC::kLoaders;
+                if (i < CC::NV) {
+                    const int r = i / (kDvTile / CC::EPP), p = i % (kDvTile / CC::EPP);
+                    uint4 piece;
+                    const uint4 vv = rv[j], ww = rw[j];
+                    E *pr = reinterpret_cast<E *>(&piece);
+                    const E *ve = reinterpret_cast<const E *>(&vv);
+                    const E *we = reinterpret_cast<const E *>(&ww);
+#pragma unroll
+                    for (int e = 0; e < CC::EPP; ++e) pr[e] = static_cast<E>(to_f(ve[e]) * to_f(we[e]));
+                    *reinterpret_cast<uint4 *>(base + offsetof(CB, WV) + r * CB::UP * sizeof(E) + p * 16) = piece;
+                }
+            }
+        };
+        // chunk j is issued R steps before it is stored (at step j - 1, into buffer j & 1)
+        if (G < nchunks) issue(G);
+        if (G == 0 && nchunks > 0) {
+            store(0);
+            if (R < nchunks) issue(R);
+        }
+        __syncthreads();
+        int turn = 1 % R;  // the pair whose chunk is stored in this step: (c + 1) % R
+        for (int64_t c = 0; c < nchunks; ++c) {
+            if (turn == G && c + 1 < nchunks) {
+                store(c + 1);
+                if (c + 1 + R < nchunks) issue(c + 1 + R);
+            }
+            turn = turn + 1 == R ? 0 : turn + 1;
+            __syncthreads();
+        }
+        return;
+    }
+
+    // chain waves: 16 columns each
     const int lcol = wave * 16;
     const int dcol = dcol0 + lcol + cc;
     floatx4 H[HT];
 #pragma unroll
     for (int t = 0; t < HT; ++t) H[t] = zero4();
-    if (chain && a.h0) {
+    if (a.h0) {
         const float *hb = a.h0 + (seq * a.Hv + head) * DK * a.dv;
 #pragma unroll
         for (int t = 0; t < HT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) H[t][r] = hb[(16 * t + 4 * g + r) * a.dv + dcol];
     }
-    // the loader waves copy chunk c + 1 into the other buffer (last read in step c - 1) while
-    // the chain waves work on chunk c; the copy lives in the loaders' registers only there
-    auto copy = [&](int64_t ch) __attribute__((always_inline)) {
-        const int64_t s = ws_slot<C>(a, seq, ch);
-        const char *kb = wsk + (s * a.Hk + kh) * WK::kBytes;
-        const char *ub = wsu + ((s * a.Hv + head) * C * a.dv + dcol0) * (int64_t)sizeof(E);
-        char *base = reinterpret_cast<char *>(&buf[ch & 1]);
-        uint4 pf[CPc::PER];
-        int dsts[CPc::PER];
-#pragma unroll
-        for (int j = 0; j < CPc::PER; ++j) {
-            const int i = lt + j * CPc::kLoaders;
-            int64_t src = 0;
-            bool from_u = false;
-            dsts[j] = -1;
-            if (i < CPc::N) chain_piece<E, C, DK>(i, a.dv, src, from_u, dsts[j]);
-            pf[j] = dsts[j] >= 0 ? *reinterpret_cast<const uint4 *>((from_u ? ub : kb) + src) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < CPc::PER; ++j)
-            if (dsts[j] >= 0) *reinterpret_cast<uint4 *>(base + dsts[j]) = pf[j];
-    };
-    if (nchunks > 0 && !chain) copy(0);
+    // The state's loads complete here. Otherwise the compiler's wait for them stays at the top
+    // of the chunk loop, where on later chunks it would wait for the previous chunk's output
+    // stores (loads and stores share one counter).
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    // output rows: token t0 + pos (t0 + len - 1 - pos reversed); a lane writes rows 4g + r of
+    // each 16-row tile, column dcol
+    const int64_t ostep = sv.rev ? -a.dv : a.dv;
+    E *const ofirst = ob + (sv.rev ? sv.t0 + sv.len - 1 : sv.t0) * a.dv + dcol + 4 * g * ostep;
     __syncthreads();
     for (int64_t c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks && !chain) copy(c + 1);
         const CB &cb = buf[c & 1];
-        if (chain) {
-            floatx4 XW[NT], XQ[NT];
+        // every operand of the step read from LDS up front, so that the reads overlap each other
+        // and the products below wait on them once rather than one at a time
+        constexpr int NK = DK / 32;
+        Frag<E> fw[NT][NK], fq[NT][NK];
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
             for (int mi = 0; mi < NT; ++mi) {
-                XW[mi] = zero4();
-                XQ[mi] = zero4();
+                fw[mi][ks] = frag_rows<E>(cb.W, CB::KP, 16 * mi, 32 * ks);
+                fq[mi][ks] = frag_rows<E>(cb.Q, CB::KP, 16 * mi, 32 * ks);
             }
+        floatx4 U[NT];
+        // T (W * V): independent of the state
+        if constexpr (C == 16) {
+            U[0] = mma16(zero4(), frag_rows_lo<E>(cb.T, CB::CP, 0, 0), frag_cols_lo<E>(cb.WV, CB::UP, lcol, 0));
+        } else {
+            Frag<E> wv[NT / 2];
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                const Frag<E> hb = frag_from_acc<E>(H[2 * ks], H[2 * ks + 1]);
+            for (int kc = 0; kc < NT / 2; ++kc) wv[kc] = frag_cols<E>(cb.WV, CB::UP, lcol, 32 * kc);
 #pragma unroll
-                for (int mi = 0; mi < NT; ++mi) {
-                    XW[mi] = mma32(XW[mi], frag_rows<E>(cb.W, CB::KP, 16 * mi, 32 * ks), hb);
-                    XQ[mi] = mma32(XQ[mi], frag_rows<E>(cb.Q, CB::KP, 16 * mi, 32 * ks), hb);
-                }
+            for (int mi = 0; mi < NT; ++mi) {
+                U[mi] = zero4();
+#pragma unroll
+                for (int kc = 0; kc <= mi / 2; ++kc) U[mi] = mma32(U[mi], frag_rows<E>(cb.T, CB::CP, 16 * mi, 32 * kc), wv[kc]);
             }
-            floatx4 U[NT];
+        }
+        floatx4 XW[NT], XQ[NT];
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi) {
+            XW[mi] = zero4();
+            XQ[mi] = zero4();
+        }
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            const Frag<E> hb = frag_from_acc<E>(H[2 * ks], H[2 * ks + 1]);
+#pragma unroll
+            for (int mi = 0; mi < NT; ++mi) {
+                XW[mi] = mma32(XW[mi], fw[mi][ks], hb);
+                XQ[mi] = mma32(XQ[mi], fq[mi][ks], hb);
+            }
+        }
+        // operands of the state update and the output, read while the products above run
+        Frag<E> fk[HT][C >= 32 ? C / 32 : 1];
+        typename Vec4<E>::type fk16[C == 16 ? HT : 1];
+        floatx4 eg[HT];
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            eg[t] = *reinterpret_cast<const floatx4 *>(cb.egc + 16 * t + 4 * g);
+            if constexpr (C == 16) {
+                fk16[t] = frag_rows_lo<E>(cb.Kt, CB::CP, 16 * t, 0);
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < C / 32; ++kc) fk[t][kc] = frag_rows<E>(cb.Kt, CB::CP, 16 * t, 32 * kc);
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi) U[mi] -= XW[mi];
+        // H <- Diag(e^{G_C}) H + Kt U
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            H[t] *= eg[t];
+            if constexpr (C == 16) {
+                H[t] = mma16(H[t], fk16[t], cvt4<E>(U[0]));
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < C / 32; ++kc) H[t] = mma32(H[t], fk[t][kc], frag_from_acc<E>(U[2 * kc], U[2 * kc + 1]));
+            }
+        }
+        // O = Qc H + P U, stored (with accumulation, the previous values are read first, all
+        // at once)
+        E *orow = ofirst + c * C * ostep;
+        floatx4 O[NT];
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi) {
+            O[mi] = XQ[mi];
+#pragma unroll
+            for (int kt = 0; kt <= mi; kt += 2) {
+                if (kt + 1 < NT)
+                    O[mi] = mma32(O[mi], frag_rows<E>(cb.P, CB::CP, 16 * mi, 16 * kt), frag_from_acc<E>(U[kt], U[kt + 1]));
+                else
+                    O[mi] = mma16(O[mi], frag_rows_lo<E>(cb.P, CB::CP, 16 * mi, 16 * kt), cvt4<E>(U[kt]));
+            }
+        }
+        const int64_t left = sv.len - c * C - 4 * g;  // rows 16 mi + r of this lane exist below left
+        if (acc_out) {
 #pragma unroll
             for (int mi = 0; mi < NT; ++mi)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) U[mi][r] = to_f(cb.U[(16 * mi + 4 * g + r) * CB::UP + lcol + cc]) - XW[mi][r];
-            // O = Qc H + P U
-#pragma unroll
-            for (int mi = 0; mi < NT; ++mi) {
-                floatx4 o = XQ[mi];
-#pragma unroll
-                for (int kt = 0; kt <= mi; kt += 2) {
-                    if (kt + 1 < NT)
-                        o = mma32(o, frag_rows<E>(cb.P, CB::CP, 16 * mi, 16 * kt), frag_from_acc<E>(U[kt], U[kt + 1]));
-                    else
-                        o = mma16(o, frag_rows_lo<E>(cb.P, CB::CP, 16 * mi, 16 * kt), cvt4<E>(U[kt]));
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t pos = c * C + 16 * mi + 4 * g + r;
-                    if (pos < sv.len) {
-                        E *dst = ob + sv.token(pos) * a.dv + dcol;
-                        const float prev = acc_out ? to_f(*dst) : 0.f;
-                        *dst = static_cast<E>(prev + o[r]);
-                    }
-                }
-            }
-            // H <- Diag(e^{G_C}) H + Kt U
-#pragma unroll
-            for (int t = 0; t < HT; ++t) {
-                H[t] *= *reinterpret_cast<const floatx4 *>(cb.egc + 16 * t + 4 * g);
-                if constexpr (C == 16) {
-                    H[t] = mma16(H[t], frag_rows_lo<E>(cb.Kt, CB::CP, 16 * t, 0), cvt4<E>(U[0]));
-                } else {
-#pragma unroll
-                    for (int k0 = 0; k0 < C; k0 += 32)
-                        H[t] = mma32(H[t], frag_rows<E>(cb.Kt, CB::CP, 16 * t, k0), frag_from_acc<E>(U[k0 / 16], U[k0 / 16 + 1]));
-                }
-            }
+                for (int r = 0; r < 4; ++r)
+                    if (16 * mi + r < left) O[mi][r] += to_f(orow[(16 * mi + r) * ostep]);
         }
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * mi + r < left) orow[(16 * mi + r) * ostep] = static_cast<E>(O[mi][r]);
         __syncthreads();
     }
-    if (chain && a.hT) {
+    if (a.hT) {
         float *hb = a.hT + (seq * a.Hv + head) * DK * a.dv;
 #pragma unroll
         for (int t = 0; t < HT; ++t)
@@ -1112,7 +1146,8 @@ hipError_t launch_two_pass(const Gdn2Args &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
-    hipLaunchKernelGGL((gdn2_chain_kernel<E, C, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((gdn2_chain_kernel<E, C, DK>), dim3((unsigned)blocks), dim3(64 * ChainCopy<E, C, DK>::kWaves), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -1128,7 +1163,12 @@ hipError_t launch_typed(const Gdn2Args &a, hipStream_t stream) {
 template <typename E, int C, int DK>
 hipError_t launch_form(const Gdn2Args &a, hipStream_t stream) {
     static_assert(WsKey<E, C, DK>::kBytes % 16 == 0, "workspace blocks keep 16-byte alignment");
-    return a.ws ? launch_two_pass<E, C, DK>(a, stream) : launch_typed<E, C, DK>(a, stream);
+    // fp32 with 64-token chunks: the chain's two operand buffers do not fit in LDS; the one-pass
+    // kernel serves it whether or not a workspace is given
+    if constexpr (ChainCopy<E, C, DK>::kFits) {
+        if (a.ws) return launch_two_pass<E, C, DK>(a, stream);
+    }
+    return launch_typed<E, C, DK>(a, stream);
 }
 
 }  // namespace
@@ -1163,7 +1203,7 @@ hipError_t launch_gdn2_chunk_fwd(const Gdn2Args &a, int dtype, int chunk, int dk
 
 int64_t gdn2_ws_key_bytes(int dtype, int chunk, int dk) {
     const int64_t es = dtype == kDtypeBf16 ? 2 : 4;
-    return es * (3 * (int64_t)chunk * dk + (int64_t)chunk * chunk) + 4 * (int64_t)dk;
+    return es * (3 * (int64_t)chunk * dk + 2 * (int64_t)chunk * chunk) + 4 * (int64_t)dk;
 }
 
 }  // namespace gdr

@@ -268,24 +268,20 @@ gdr_status_t decode_impl(const void *q, const void *k, const void *v, const floa
 namespace {
 
 // Two-pass GDN-2 workspace: one slot per chunk of every sequence (packed: T / C + S + 1, which
-// covers the slots cu[s] / C + s + c the kernels use), each holding a block per key head and a
-// C x dv slice per value head. Returns -1 for sizes that do not make sense.
+// covers the slots cu[s] / C + s + c the kernels use), each holding a block per key head.
+// Returns -1 for sizes that do not make sense.
 int64_t gdn2_slots(const gdr_chunk_dims_t &d, int64_t chunk, bool packed) {
     if (packed) return d.T / chunk + d.num_seqs + 1;
     return d.B * ((d.T + chunk - 1) / chunk);
 }
-int64_t gdn2_ws_bytes(const gdr_chunk_dims_t &d, int32_t chunk, bool packed, int64_t *key_part) {
+int64_t gdn2_ws_bytes(const gdr_chunk_dims_t &d, int32_t chunk, bool packed) {
     if ((d.dtype != GDR_F32 && d.dtype != GDR_BF16) || (chunk != 16 && chunk != 32 && chunk != 64) ||
         (d.dk != 64 && d.dk != 128) || d.T < 0 || d.B < 0 || d.Hk < 1 || d.Hv < 1 || d.dv < 0 ||
         (packed && d.num_seqs < 1))
         return -1;
     const int dt = d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32;
     const int64_t slots = gdn2_slots(d, chunk, packed);
-    const int64_t key = prod({slots, d.Hk, gdr::gdn2_ws_key_bytes(dt, chunk, (int)d.dk)});
-    const int64_t val = prod({slots, d.Hv, chunk, d.dv, elem_size(d.dtype)});
-    if (key < 0 || val < 0) return -1;
-    if (key_part) *key_part = key;
-    return key + val;
+    return prod({slots, d.Hk, gdr::gdn2_ws_key_bytes(dt, chunk, (int)d.dk)});
 }
 
 gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
@@ -335,9 +331,9 @@ gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const 
     }
     if (overlap(ro, rhT)) return fail(GDR_ERR_ALIAS, "out overlaps hT");
     if (overlap(rhT, rh0) && rhT.lo != rh0.lo) return fail(GDR_ERR_ALIAS, "hT partially overlaps h0");
-    int64_t ws_key = 0, nslots = 0;
+    int64_t nslots = 0;
     if (workspace) {
-        const int64_t need = gdn2_ws_bytes(d, chunk, cu_seqlens != nullptr, &ws_key);
+        const int64_t need = gdn2_ws_bytes(d, chunk, cu_seqlens != nullptr);
         if (need < 0) return fail(GDR_ERR_DIMS, "workspace size overflows");
         if (workspace_bytes < need)
             return fail(GDR_ERR_DIMS, "workspace_bytes %lld is below the %lld bytes needed", (long long)workspace_bytes,
@@ -362,7 +358,6 @@ gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const 
     a.flags = d.flags;
     a.ws = workspace;
     a.nslots = nslots;
-    a.ws_u_off = ws_key;
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
     if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
     const hipError_t e = gdr::launch_gdn2_chunk_fwd(a, d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32, chunk,
@@ -433,7 +428,7 @@ gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v, con
 
 int64_t gdr_gdn2_chunk_fwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t chunk, int32_t packed) {
     if (!dims) return -1;
-    return gdn2_ws_bytes(*dims, chunk, packed != 0, nullptr);
+    return gdn2_ws_bytes(*dims, chunk, packed != 0);
 }
 
 gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v, const float *g, const void *b,

@@ -56,9 +56,9 @@ struct Gdn2Args {
     int64_t units;   // sequences x value heads
     int64_t ntiles;  // dv / 32
     uint32_t flags;
-    // two-pass form (ws non-null): chunk slots, and the byte offset of the per-value-head part
+    // two-pass form (ws non-null): a block per (chunk slot, key head)
     void *ws;
-    int64_t nslots, ws_u_off;
+    int64_t nslots;
 };
 
 // GDN-2 decode: g, b [N][Hk][dk] (g fp32), w [N][Hv][dv].

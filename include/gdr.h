@@ -284,11 +284,11 @@ gdr_status_t gdr_delta_product_fwd(const void *q, const void *k, const void *v,
  *               cu_seqlens != NULL) bytes, or NULL. Owned by the caller; its contents do not
  *               matter before or after the call; calls that share a workspace must not
  *               overlap. With a workspace the forward runs in two passes: the first computes
- *               every chunk's state-independent operands at once (for each chunk and key head:
- *               the WY-form right factor T (b * k * e^G), q * e^{Gr}, (k * e^{G_C - G})^T, the
- *               intra-chunk read matrix and e^{G_C}; for each value head T (w * v)), the second
- *               walks the chunks with the state. Without one a single fused pass does both
- *               (allocation-free, slower). The results agree up to rounding.
+ *               the key side of every chunk at once (for each chunk and key head: the WY-form
+ *               factor T (b * k * e^G), q * e^{Gr}, (k * e^{G_C - G})^T, the intra-chunk read
+ *               matrix, T = (I + A)^{-1} and e^{G_C}), the second walks the chunks with the
+ *               state. Without one a single fused pass does both (allocation-free, slower); fp32
+ *               with chunk 64 always takes the fused pass. The results agree up to rounding.
  *   workspace_bytes  its size in bytes.
  *
  * Every tensor pointer 16-byte aligned. chunk 16, 32 or 64, except that fp32 with dk = 128
@@ -310,9 +310,8 @@ gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v,
  * gdr_gdn2_chunk_fwd_workspace_bytes - bytes of workspace gdr_gdn2_chunk_fwd's two-pass form
  * needs for these sizes, chunk and packing (packed != 0: cu_seqlens with dims->num_seqs
  * sequences). Host-only arithmetic: one slot per chunk of every sequence (packed: T / chunk +
- * num_seqs + 1), each with Hk blocks of es (3 chunk dk + chunk^2) + 4 dk bytes and Hv slices of
- * es chunk dv bytes (es = 2 for bf16, 4 for fp32). Returns -1 for an unsupported dtype, chunk or
- * dk, or negative sizes.
+ * num_seqs + 1), each with Hk blocks of es (3 chunk dk + 2 chunk^2) + 4 dk bytes (es = 2 for
+ * bf16, 4 for fp32). Returns -1 for an unsupported dtype, chunk or dk, or negative sizes.
  */
 int64_t gdr_gdn2_chunk_fwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t chunk, int32_t packed);
 

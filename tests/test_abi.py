@@ -200,7 +200,7 @@ GDN2_REJECTS = [
     (dict(flags=16), "GDR_ERR_FLAGS", "flags"),
     (dict(dv=40), "GDR_ERR_UNSUPPORTED", "dv"),
     (dict(Hk=4, Hv=2), "GDR_ERR_DIMS", "Hv"),
-    # the two-pass form's workspace (this call needs 2 x 2 x 33024 + 2 x 2 x 64 x 64 x 2 bytes)
+    # the two-pass form's workspace (this call needs 2 x 2 x 41216 bytes)
     (dict(ws=FAKE * 9, ws_bytes=1024), "GDR_ERR_DIMS", "workspace_bytes"),
     (dict(ws=FAKE * 9 + 8, ws_bytes=1 << 20), "GDR_ERR_ALIGN", "workspace"),
     (dict(ws=FAKE * 7 + 4096, ws_bytes=1 << 20), "GDR_ERR_ALIAS", "workspace overlaps w"),
@@ -218,13 +218,13 @@ def test_gdn2_chunk_rejects(over, status, text):
 def test_gdn2_workspace_bytes():
     lib = binding.load()
     # B4 H16 T4096 d128 bf16, chunk 32: 4 x 128 chunk slots; per slot 16 key-head blocks of
-    # 2 (3 x 32 x 128 + 32 x 32) + 4 x 128 bytes and 16 value-head slices of 32 x 128 x 2 bytes
+    # 2 (3 x 32 x 128 + 2 x 32 x 32) + 4 x 128 bytes
     dims = binding.ChunkDims(4, 4096, 16, 16, 128, 128, 0, 1, 0)
-    want = 512 * 16 * (2 * (3 * 32 * 128 + 32 * 32) + 4 * 128) + 512 * 16 * 32 * 128 * 2
+    want = 512 * 16 * (2 * (3 * 32 * 128 + 2 * 32 * 32) + 4 * 128)
     assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 32, 0) == want
-    # packed: T / chunk + num_seqs + 1 slots; fp32 doubles the element bytes; Hk < Hv
+    # packed: T / chunk + num_seqs + 1 slots; fp32 doubles the element bytes; blocks per key head
     dims = binding.ChunkDims(1, 1000, 2, 4, 64, 32, 3, 0, 0)
-    want = 66 * 2 * (4 * (3 * 16 * 64 + 16 * 16) + 4 * 64) + 66 * 4 * 16 * 32 * 4
+    want = 66 * 2 * (4 * (3 * 16 * 64 + 2 * 16 * 16) + 4 * 64)
     assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 16, 1) == want
     assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 8, 1) == -1
     assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(None, 16, 0) == -1
