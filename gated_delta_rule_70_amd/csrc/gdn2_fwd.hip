@@ -235,73 +235,64 @@ __device__ __forceinline__ void normalize_rows(Smem<E, C, DK> &sm) {
     }
 }
 
-// Per (pair of channels, block): e^{g} in place of g, the block decay D, its inverse where the
-// block is on the matrix-core path, and the flag of a block that needs the exact path.
+// Per (channel, block): e^{g} in place of g, the block decay D, its inverse where the block is
+// on the matrix-core path, and the flag of a block that needs the exact path.
 template <typename E, int C, int DK>
 __device__ __forceinline__ void block_decays(Smem<E, C, DK> &sm) {
     typedef Smem<E, C, DK> SM;
-    for (int pi = threadIdx.x; pi < (DK / 2) * SM::NT; pi += kThreads) {
-        const int c = 2 * (pi % (DK / 2)), blk = pi / (DK / 2);
-        float s0 = 0.f, s1 = 0.f, d0 = 1.f, d1 = 1.f;
+    for (int pi = threadIdx.x; pi < DK * SM::NT; pi += kThreads) {
+        const int c = pi % DK, blk = pi / DK;
+        float *p = sm.G + 16 * blk * SM::GP + c;
+        float gv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gv[i] = p[i * SM::GP];
+        float s = 0.f, d = 1.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float *p = sm.G + (16 * blk + i) * SM::GP + c;
-            float g0, g1;
-            ld2(p, g0, g1);
-            s0 += g0;
-            s1 += g1;
-            const float a0 = __expf(g0), a1 = __expf(g1);
-            d0 *= a0;
-            d1 *= a1;
-            st2(p, a0, a1);
+            s += gv[i];
+            const float a = __expf(gv[i]);
+            d *= a;
+            p[i * SM::GP] = a;
         }
-        const bool safe = s0 >= kSafeLogDecay && s1 >= kSafeLogDecay;
-        st2(sm.dec + blk * DK + c, d0, d1);
-        st2(sm.inv + blk * DK + c, safe ? 1.f / d0 : 0.f, safe ? 1.f / d1 : 0.f);
+        const bool safe = s >= kSafeLogDecay;
+        sm.dec[blk * DK + c] = d;
+        sm.inv[blk * DK + c] = safe ? 1.f / d : 0.f;
         if (!safe) atomicOr(&sm.unsafe[blk], 1);
     }
 }
 
 // The operands in place: LA = b k f, LP = q f (f of the previous row for the pre-write read),
-// R = k r, and e^{G_ref} per block.
+// R = k r, and e^{G_ref} per block; one (channel, block) per thread.
 template <typename E, int C, int DK>
 __device__ __forceinline__ void form_operands(Smem<E, C, DK> &sm, bool pre) {
     typedef Smem<E, C, DK> SM;
-    for (int pi = threadIdx.x; pi < (DK / 2) * SM::NT; pi += kThreads) {
-        const int c = 2 * (pi % (DK / 2)), blk = pi / (DK / 2);
-        float e0 = 1.f, e1 = 1.f;
-        for (int j = 0; j < blk; ++j) {
-            float x0, x1;
-            ld2(sm.dec + j * DK + c, x0, x1);
-            e0 *= x0;
-            e1 *= x1;
-        }
-        st2(sm.eref + blk * DK + c, e0, e1);
-        float f0 = 1.f, f1 = 1.f;
-        float a0[16], a1[16];
+    for (int pi = threadIdx.x; pi < DK * SM::NT; pi += kThreads) {
+        const int c = pi % DK, blk = pi / DK;
+        float e = 1.f;
+        for (int j = 0; j < blk; ++j) e *= sm.dec[j * DK + c];
+        sm.eref[blk * DK + c] = e;
+        const int r0 = 16 * blk;
+        float a[16], kv[16], qv[16], bv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int row = 16 * blk + i;
-            ld2(sm.G + row * SM::GP + c, a0[i], a1[i]);
-            float k0, k1, q0, q1, b0, b1;
-            ld2(sm.K + row * SM::KP + c, k0, k1);
-            ld2(sm.Q + row * SM::KP + c, q0, q1);
-            ld2(sm.Bk + row * SM::KP + c, b0, b1);
-            const float p0 = f0, p1 = f1;
-            f0 *= a0[i];
-            f1 *= a1[i];
-            st2(sm.Bk + row * SM::KP + c, b0 * k0 * f0, b1 * k1 * f1);
-            st2(sm.Q + row * SM::KP + c, q0 * (pre ? p0 : f0), q1 * (pre ? p1 : f1));
+            a[i] = sm.G[(r0 + i) * SM::GP + c];
+            kv[i] = to_f(sm.K[(r0 + i) * SM::KP + c]);
+            qv[i] = to_f(sm.Q[(r0 + i) * SM::KP + c]);
+            bv[i] = to_f(sm.Bk[(r0 + i) * SM::KP + c]);
         }
-        float r0 = 1.f, r1 = 1.f;
+        float f = 1.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float prev = f;
+            f *= a[i];
+            sm.Bk[(r0 + i) * SM::KP + c] = static_cast<E>(bv[i] * kv[i] * f);
+            sm.Q[(r0 + i) * SM::KP + c] = static_cast<E>(qv[i] * (pre ? prev : f));
+        }
+        float r = 1.f;
 #pragma unroll
         for (int i = 15; i >= 0; --i) {
-            const int row = 16 * blk + i;
-            float k0, k1;
-            ld2(sm.K + row * SM::KP + c, k0, k1);
-            st2(sm.K + row * SM::KP + c, k0 * r0, k1 * r1);
-            r0 *= a0[i];
-            r1 *= a1[i];
+            sm.K[(r0 + i) * SM::KP + c] = static_cast<E>(kv[i] * r);
+            r *= a[i];
         }
     }
 }
