@@ -165,25 +165,37 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 
     auto n_rows = [&](int64_t c) __attribute__((always_inline)) -> int { return (int)min((int64_t)CB, sq.len - c * CB); };
 
-    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write); all loads
-    // of a thread are issued before its stores
+    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write). Every load
+    // of a thread is a 16-byte piece issued before any of them is used, so that their latencies
+    // overlap; rows past the end read row 0 and are zeroed when stored.
     auto stage = [&](int64_t c, bool adjoint) __attribute__((always_inline)) {
         const int n = n_rows(c);
-        constexpr int KPT = CB * DK / kThreads, VPT = CB * TV / kThreads;
-        float kv[KPT], qv[KPT], vv[VPT], ov[VPT];
+        constexpr int EPP = 16 / (int)sizeof(E);  // elements per piece
+        constexpr int KPR = DK / EPP, VPR = TV / EPP;
+        constexpr int NKP = CB * KPR, NVP = CB * VPR;
+        constexpr int KPT = (NKP + kThreads - 1) / kThreads, VPT = (NVP + kThreads - 1) / kThreads;
+        uint4 kp[KPT], qp[KPT], vp[VPT], op[VPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / DK, c2 = i % DK;
-            const int64_t t = rr < n ? sq.token(c * CB + rr) : 0;
-            kv[e] = rr < n ? ld_f(kb, t * DK + c2) : 0.f;
-            qv[e] = (adjoint && rr < n) ? ld_f(qb, t * DK + c2) : 0.f;
+            const int i = tid + e * kThreads, rr = i / KPR, p = i % KPR;
+            kp[e] = make_uint4(0, 0, 0, 0);
+            qp[e] = make_uint4(0, 0, 0, 0);
+            if (i < NKP) {
+                const int64_t off = sq.token(c * CB + (rr < n ? rr : 0)) * DK + p * EPP;
+                kp[e] = *reinterpret_cast<const uint4 *>(kb + off);
+                if (adjoint) qp[e] = *reinterpret_cast<const uint4 *>(qb + off);
+            }
         }
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / TV, c2 = i % TV;
-            const int64_t t = rr < n ? sq.token(c * CB + rr) : 0;
-            vv[e] = rr < n ? ld_f(vb, t * dvf + c2) : 0.f;
-            ov[e] = (adjoint && rr < n) ? ld_f(dob, t * dvf + c2) : 0.f;
+            const int i = tid + e * kThreads, rr = i / VPR, p = i % VPR;
+            vp[e] = make_uint4(0, 0, 0, 0);
+            op[e] = make_uint4(0, 0, 0, 0);
+            if (i < NVP) {
+                const int64_t off = sq.token(c * CB + (rr < n ? rr : 0)) * dvf + p * EPP;
+                vp[e] = *reinterpret_cast<const uint4 *>(vb + off);
+                if (adjoint) op[e] = *reinterpret_cast<const uint4 *>(dob + off);
+            }
         }
         float lv = 0.f, bv = 0.f;
         if (tid < CB && tid < n) {
@@ -191,17 +203,42 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             lv = lab[t];
             bv = beb[t];
         }
+        // piece -> EPP floats of row rr (zero past the end), into LDS as 16-byte stores
+        auto put = [&](float *dst, const uint4 &piece, bool keep) __attribute__((always_inline)) {
+            float f[EPP];
+            if constexpr (sizeof(E) == 2) {
+                const unsigned w[4] = {piece.x, piece.y, piece.z, piece.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[2 * j] = __uint_as_float(w[j] << 16);
+                    f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                }
+            } else {
+                f[0] = __uint_as_float(piece.x);
+                f[1] = __uint_as_float(piece.y);
+                f[2] = __uint_as_float(piece.z);
+                f[3] = __uint_as_float(piece.w);
+            }
+#pragma unroll
+            for (int j = 0; j < EPP; j += 4)
+                *reinterpret_cast<float4 *>(dst + j) =
+                    keep ? make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        };
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / DK, c2 = i % DK;
-            sm.K[rr][c2] = kv[e];
-            sm.Q[rr][c2] = qv[e];
+            const int i = tid + e * kThreads, rr = i / KPR, p = i % KPR;
+            if (i < NKP) {
+                put(&sm.K[rr][p * EPP], kp[e], rr < n);
+                put(&sm.Q[rr][p * EPP], qp[e], rr < n);
+            }
         }
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / TV, c2 = i % TV;
-            sm.V[rr][c2] = vv[e];
-            sm.dO[rr][c2] = ov[e];
+            const int i = tid + e * kThreads, rr = i / VPR, p = i % VPR;
+            if (i < NVP) {
+                put(&sm.V[rr][p * EPP], vp[e], rr < n);
+                put(&sm.dO[rr][p * EPP], op[e], rr < n);
+            }
         }
         if (tid < CB) {
             sm.la[tid] = lv;
@@ -274,18 +311,24 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         __syncthreads();
     };
 
-    // ---- sweep 1: the chunk-form forward from h0, storing each chunk's entry state
-    for (int u = 0; u < SR; ++u)
+    // A thread's part of a state slice: SR rows of 4 consecutive columns, moved as 16-byte pieces
+    // (all loads issued before the stores).
+    auto load_slice = [&](float (*dst)[SM::VP], const float *src, int64_t pitch) __attribute__((always_inline)) {
+        float4 x[SR];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int n = sr0 + u, c2 = sc0 + v;
-            sm.H[n][c2] = a.h0 ? a.h0[sbase + (int64_t)n * dvf + c2] : 0.f;
-        }
+        for (int u = 0; u < SR; ++u)
+            x[u] = src ? *reinterpret_cast<const float4 *>(src + (int64_t)(sr0 + u) * pitch + sc0) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < SR; ++u) *reinterpret_cast<float4 *>(&dst[sr0 + u][sc0]) = x[u];
+    };
+    // ---- sweep 1: the chunk-form forward from h0, storing each chunk's entry state
+    load_slice(sm.H, a.h0 ? a.h0 + sbase : nullptr, dvf);
     __syncthreads();
     for (int64_t c = 0; c < nch; ++c) {
-        for (int u = 0; u < SR; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ckpt[c * cstride + (sr0 + u) * TV + sc0 + v] = sm.H[sr0 + u][sc0 + v];
+        for (int u = 0; u < SR; ++u)
+            *reinterpret_cast<float4 *>(ckpt + c * cstride + (sr0 + u) * TV + sc0) =
+                *reinterpret_cast<const float4 *>(&sm.H[sr0 + u][sc0]);
         stage(c, false);
         __syncthreads();
         gates();
@@ -312,17 +355,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     }
 
     // ---- sweep 2: the adjoint, chunk by chunk from the last
-    for (int u = 0; u < SR; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int n = sr0 + u, c2 = sc0 + v;
-            sm.D[n][c2] = a.dhT ? a.dhT[sbase + (int64_t)n * dvf + c2] : 0.f;
-        }
+    load_slice(sm.D, a.dhT ? a.dhT + sbase : nullptr, dvf);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = n_rows(c);
-        for (int u = 0; u < SR; ++u)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sm.H[sr0 + u][sc0 + v] = ckpt[c * cstride + (sr0 + u) * TV + sc0 + v];
+        load_slice(sm.H, ckpt + c * cstride, TV);
         stage(c, true);
         __syncthreads();
         gates();
@@ -505,12 +541,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         __syncthreads();
     }
     if (a.dh0) {
-        for (int u = 0; u < SR; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int nn = sr0 + u, c2 = sc0 + v;
-                a.dh0[sbase + (int64_t)nn * dvf + c2] = sm.D[nn][c2];
-            }
+        for (int u = 0; u < SR; ++u)
+            *reinterpret_cast<float4 *>(a.dh0 + sbase + (int64_t)(sr0 + u) * dvf + sc0) =
+                *reinterpret_cast<const float4 *>(&sm.D[sr0 + u][sc0]);
     }
 }
 
