@@ -49,7 +49,11 @@ namespace gdr {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+// the rows of a CB x TV matrix are shared out 8 threads to a row (4 columns each) over the first
+// CB * TV / 4 threads
+constexpr int kRowThreads = kBwdBlock * kBwdCols / 4;
 constexpr int CB = kBwdBlock;  // tokens per chunk
 constexpr int TV = kBwdCols;   // value columns per workgroup
 
@@ -126,7 +130,8 @@ template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     typedef Smem<DK> SM;
     __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int g = lane >> 4, cc = lane & 15;
     const int64_t unit = blockIdx.x / a.ntiles;
     const int tile = (int)(blockIdx.x % a.ntiles);
@@ -286,14 +291,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     };
     // forward quantities of the chunk from its entry state in sm.H: X, G and A, P (adjoint only), T, U
     auto forward_parts = [&](bool adjoint) __attribute__((always_inline)) {
-        // X = K H (4 tiles, one per wave); G = K K^T and P = Q K^T on the lower tiles (00, 10, 11)
-        {
-            const int mt = wave >> 1, nt = wave & 1;
-            const floatx4 x = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+        // X = K H (tasks 0-3, one tile each); G = K K^T and P = Q K^T on the lower tiles (00, 10,
+        // 11; tasks 4-6 and 7-9), shared out over the waves
+        for (int task = wave; task < (adjoint ? 10 : 7); task += kWaves) {
+            if (task < 4) {
+                const int mt = task >> 1, nt = task & 1;
+                const floatx4 x = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.X[16 * mt + 4 * g + r][16 * nt + cc] = x[r];
-        }
-        for (int t = wave; t < (adjoint ? 6 : 3); t += 4) {
+                for (int r = 0; r < 4; ++r) sm.X[16 * mt + 4 * g + r][16 * nt + cc] = x[r];
+                continue;
+            }
+            const int t = task - 4;
             const bool isp = t >= 3;
             const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
             const floatx4 v = mm<DK, false, true>(zero4(), isp ? &sm.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt,
@@ -314,14 +322,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         __syncthreads();
         // T = (I + A)^{-1}; R = diag(beta) (V - diag(gamma) X) into dR
         if (wave == 0) solve_unit_lower_inverse<float, CB>(sm);
-        {
+        if (tid < kRowThreads) {
             const float be = sm.beta[ei], ga = __expf(sm.b[ei]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) sm.dR[ei][ej + v] = be * (sm.V[ei][ej + v] - ga * sm.X[ei][ej + v]);
         }
         __syncthreads();
         // U = T R
-        {
+        if (wave < 4) {
             const int mt = wave >> 1, nt = wave & 1;
             const floatx4 u = mm<CB, false, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dR[0][0], SM::VP, 16 * nt);
 #pragma unroll
@@ -355,13 +363,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         forward_parts(false);
         // H' = gamma_last H + K^T diag(w) U (wU into dU first)
         const float blast = sm.b[CB - 1], glast = __expf(blast);
-        {
+        if (tid < kRowThreads) {
             const float wi = __expf(fminf(blast - sm.b[ei], 0.f));
 #pragma unroll
             for (int v = 0; v < 4; ++v) sm.dU[ei][ej + v] = wi * sm.U[ei][ej + v];
         }
         __syncthreads();
-        for (int t = wave; t < (DK / 16) * (TV / 16); t += 4) {
+        for (int t = wave; t < (DK / 16) * (TV / 16); t += kWaves) {
             const int mt = t / (TV / 16), nt = t % (TV / 16);
             floatx4 h;
 #pragma unroll
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         const float blast = sm.b[CB - 1], glast = __expf(blast);
 
         // dU = diag(w) K D + P^T dO; dw_i = (K D)_i . U_i; and <D, H>
-        {
+        if (wave < 4) {
             const int mt = wave >> 1, nt = wave & 1;
             const floatx4 kd = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
             const floatx4 pd = mm<CB, true, false>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
@@ -398,6 +406,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float dwp = row16(kd[r] * sm.U[i][j]);
                 if (cc == 0) atomicAdd(&sm.dw[i], dwp);
             }
+        }
+        {
             float s = 0.f;
             for (int u = 0; u < SR; ++u)
 #pragma unroll
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         }
         __syncthreads();
         // dR = T^T dU
-        {
+        if (wave < 4) {
             const int mt = wave >> 1, nt = wave & 1;
             const floatx4 d = mm<CB, true, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
 #pragma unroll
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         __syncthreads();
         // dP = dO U^T -> M, dA = -dR U^T -> beta N on the lower tiles; their exponent and beta
         // gradients; then dV, R's gradients, and the scaled copies for the products below
-        for (int t = wave; t < 6; t += 4) {
+        for (int t = wave; t < 6; t += kWaves) {
             const bool isa = t >= 3;
             const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
             floatx4 v = mm<TV, false, true>(zero4(), isa ? &sm.dR[0][0] : &sm.dO[0][0], SM::VP, 16 * mt, &sm.U[0][0],
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             cs = col4(cs);
             if (g == 0) atomicAdd(&sm.db[16 * nt + cc], -cs);
         }
-        {
+        if (tid < kRowThreads) {
             const int i = ei;
             const float be = sm.beta[i], ga = __expf(sm.b[i]), er = __expf(sm.r[i]);
             const float wi = __expf(fminf(blast - sm.b[i], 0.f));
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         __syncthreads();
         // dQ = diag(e^r) dO H^T + M K;  dK = wU D^T + bR H^T + M^T Q + Nb K + Nb^T K
         // (wU = diag(w) U in dU, bR = -diag(beta gamma) dR); the read's exponent gradient
-        for (int t = wave; t < 2 * (DK / 16); t += 4) {
+        for (int t = wave; t < 2 * (DK / 16); t += kWaves) {
             const int mt = t / (DK / 16), nt = t % (DK / 16);
             floatx4 oh = mm<TV, false, true>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
             floatx4 dq;
@@ -509,8 +519,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
         }
         // dH = gamma_last D + Q^T eO + K^T bR
-        floatx4 dh[(DK / 16) * (TV / 16) / 4];
-        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += 4, ++s) {
+        constexpr int NDH = ((DK / 16) * (TV / 16) + kWaves - 1) / kWaves;
+        floatx4 dh[NDH];
+        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += kWaves, ++s) {
             const int mt = t / (TV / 16), nt = t % (TV / 16);
             floatx4 h;
 #pragma unroll
@@ -520,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             dh[s] = h;
         }
         __syncthreads();
-        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += 4, ++s) {
+        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += kWaves, ++s) {
             const int mt = t / (TV / 16), nt = t % (TV / 16);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.D[16 * mt + 4 * g + r][16 * nt + cc] = dh[s][r];
