@@ -320,12 +320,39 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
-        // T = (I + A)^{-1}; R = diag(beta) (V - diag(gamma) X) into dR
+        // T = (I + A)^{-1} on wave 0; meanwhile R = diag(beta) (V - diag(gamma) X) into dR on
+        // waves 4-7 and, in the adjoint, the parts of dU that do not need U on waves 1-3 and 5:
+        // K D (kept in eO for dw), dU = diag(w) K D + P^T dO, and <D, H> on every thread
         if (wave == 0) solve_unit_lower_inverse<float, CB>(sm);
-        if (tid < kRowThreads) {
-            const float be = sm.beta[ei], ga = __expf(sm.b[ei]);
+        const int rt = tid - (kThreads - kRowThreads);
+        if (rt >= 0) {
+            const int i = rt / (TV / 4), j0 = (rt % (TV / 4)) * 4;
+            const float be = sm.beta[i], ga = __expf(sm.b[i]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sm.dR[ei][ej + v] = be * (sm.V[ei][ej + v] - ga * sm.X[ei][ej + v]);
+            for (int v = 0; v < 4; ++v) sm.dR[i][j0 + v] = be * (sm.V[i][j0 + v] - ga * sm.X[i][j0 + v]);
+        }
+        if (adjoint) {
+            const int tile = wave == 5 ? 0 : (wave >= 1 && wave <= 3) ? wave : -1;
+            if (tile >= 0) {
+                const float blast = sm.b[CB - 1];
+                const int mt = tile >> 1, nt = tile & 1;
+                const floatx4 kd = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
+                const floatx4 pd = mm<CB, true, false>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+                    const float wi = __expf(fminf(blast - sm.b[i], 0.f));
+                    sm.dU[i][j] = wi * kd[r] + pd[r];
+                    sm.eO[i][j] = kd[r];
+                }
+            }
+            float s = 0.f;
+            for (int u = 0; u < SR; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s += sm.D[sr0 + u][sc0 + v] * sm.H[sr0 + u][sc0 + v];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+            if (lane == 0) atomicAdd(&sm.hd, s);
         }
         __syncthreads();
         // U = T R
@@ -393,36 +420,22 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         forward_parts(true);
         const float blast = sm.b[CB - 1], glast = __expf(blast);
 
-        // dU = diag(w) K D + P^T dO; dw_i = (K D)_i . U_i; and <D, H>
-        if (wave < 4) {
-            const int mt = wave >> 1, nt = wave & 1;
-            const floatx4 kd = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
-            const floatx4 pd = mm<CB, true, false>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-                sm.dU[i][j] = wi * kd[r] + pd[r];
-                const float dwp = row16(kd[r] * sm.U[i][j]);
-                if (cc == 0) atomicAdd(&sm.dw[i], dwp);
-            }
-        }
-        {
-            float s = 0.f;
-            for (int u = 0; u < SR; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) s += sm.D[sr0 + u][sc0 + v] * sm.H[sr0 + u][sc0 + v];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-            if (lane == 0) atomicAdd(&sm.hd, s);
-        }
-        __syncthreads();
-        // dR = T^T dU
+        // dR = T^T dU on waves 0-3; dw_i = (K D)_i . U_i (K D in eO) on waves 4-7
         if (wave < 4) {
             const int mt = wave >> 1, nt = wave & 1;
             const floatx4 d = mm<CB, true, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.dR[16 * mt + 4 * g + r][16 * nt + cc] = d[r];
+        } else {
+            const int rt = tid - (kThreads - kRowThreads);
+            const int i = rt / (TV / 4), j0 = (rt % (TV / 4)) * 4;
+            float sw = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sw += sm.eO[i][j0 + v] * sm.U[i][j0 + v];
+            sw += __shfl_xor(sw, 1, 64);
+            sw += __shfl_xor(sw, 2, 64);
+            sw += __shfl_xor(sw, 4, 64);
+            if ((rt % (TV / 4)) == 0) sm.dw[i] = sw;
         }
         __syncthreads();
         // dP = dO U^T -> M, dA = -dR U^T -> beta N on the lower tiles; their exponent and beta
