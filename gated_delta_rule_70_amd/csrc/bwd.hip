@@ -516,11 +516,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 if (cc == 0) atomicAdd(&sm.dr[i], rq);
             }
             dq = mm<CB, false, false>(dq, &sm.M[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            // three independent partial sums, so that the products do not wait on each other
             floatx4 dk = mm<TV, false, true>(zero4(), &sm.dU[0][0], SM::VP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
-            dk = mm<TV, false, true>(dk, &sm.bR[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
-            dk = mm<CB, true, false>(dk, &sm.M[0][0], SM::TP, 16 * mt, &sm.Q[0][0], SM::KP, 16 * nt);
+            floatx4 dk2 = mm<TV, false, true>(zero4(), &sm.bR[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+            floatx4 dk3 = mm<CB, true, false>(zero4(), &sm.M[0][0], SM::TP, 16 * mt, &sm.Q[0][0], SM::KP, 16 * nt);
             dk = mm<CB, false, false>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
-            dk = mm<CB, true, false>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            dk2 = mm<CB, true, false>(dk2, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            dk += dk2 + dk3;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r;
@@ -556,11 +558,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             if (i < CB) {
                 const float wi = __expf(fminf(blast - sm.b[i], 0.f));
                 float dbi = sm.db[i] - wi * sm.dw[i];
-                if (i == CB - 1) {
-                    float s = glast * sm.hd;
-                    for (int j = 0; j < CB; ++j) s += __expf(fminf(blast - sm.b[j], 0.f)) * sm.dw[j];
-                    dbi += s;
-                }
+                // the last row also takes glast <D, H> + sum_j w_j dw_j (a sum over the wave)
+                float s = __expf(fminf(blast - sm.b[i], 0.f)) * sm.dw[i];
+#pragma unroll
+                for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off, 32);
+                if (i == CB - 1) dbi += glast * sm.hd + s;
                 // post: the read exponent is b itself; pre: b - log alpha leaves out row i's own
                 // log alpha, so its gradient enters the sums of the rows after it only
                 x = dbi + (pre ? 0.f : sm.dr[i]);
