@@ -215,7 +215,9 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
  * Errors as gdr_chunk_fwd, plus GDR_ERR_DIMS when workspace_bytes is too small.
  * The backward runs the chunk form (32-token chunks) forward once, keeping each chunk's entry
  * state in the workspace (one fp32 state per chunk of every sequence-head), then walks the chunks
- * back, recomputing each chunk's quantities from its entry state.
+ * back, recomputing each chunk's quantities from its entry state. Its products run on the bf16
+ * matrix cores with each fp32 operand split in two bf16 parts (hi*hi + hi*lo + lo*hi, fp32
+ * accumulation): a relative error near 2^-16 per product.
  */
 int64_t gdr_chunk_bwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t packed);
 gdr_status_t gdr_chunk_bwd(const void *q, const void *k, const void *v,
