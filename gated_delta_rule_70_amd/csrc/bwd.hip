@@ -189,90 +189,103 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 
     auto n_rows = [&](int64_t c) __attribute__((always_inline)) -> int { return (int)min((int64_t)CB, sq.len - c * CB); };
 
-    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write). Every load
-    // of a thread is a 16-byte piece issued before any of them is used, so that their latencies
-    // overlap; rows past the end read row 0 and are zeroed when stored.
-    auto stage = [&](int64_t c, bool adjoint) __attribute__((always_inline)) {
-        const int n = n_rows(c);
-        constexpr int EPP = 16 / (int)sizeof(E);  // elements per piece
-        constexpr int KPR = DK / EPP, VPR = TV / EPP;
-        constexpr int NKP = CB * KPR, NVP = CB * VPR;
-        constexpr int KPT = (NKP + kThreads - 1) / kThreads, VPT = (NVP + kThreads - 1) / kThreads;
+    constexpr int EPP = 16 / (int)sizeof(E);  // elements per piece
+    constexpr int KPR = DK / EPP, VPR = TV / EPP;
+    constexpr int NKP = CB * KPR, NVP = CB * VPR;
+    constexpr int KPT = (NKP + kThreads - 1) / kThreads, VPT = (NVP + kThreads - 1) / kThreads;
+    // a chunk's inputs in flight: 16-byte pieces of k, q, v, dout (rows past the end read row 0
+    // and are zeroed when stored), and the gates of the thread's row
+    struct StageRegs {
         uint4 kp[KPT], qp[KPT], vp[VPT], op[VPT];
+        float lv, bv;
+    };
+    auto stage_issue = [&](int64_t c, bool adjoint, StageRegs &sr) __attribute__((always_inline)) {
+        const int n = n_rows(c);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int i = tid + e * kThreads, rr = i / KPR, p = i % KPR;
-            kp[e] = make_uint4(0, 0, 0, 0);
-            qp[e] = make_uint4(0, 0, 0, 0);
+            sr.kp[e] = make_uint4(0, 0, 0, 0);
+            sr.qp[e] = make_uint4(0, 0, 0, 0);
             if (i < NKP) {
                 const int64_t off = sq.token(c * CB + (rr < n ? rr : 0)) * DK + p * EPP;
-                kp[e] = *reinterpret_cast<const uint4 *>(kb + off);
-                if (adjoint) qp[e] = *reinterpret_cast<const uint4 *>(qb + off);
+                sr.kp[e] = *reinterpret_cast<const uint4 *>(kb + off);
+                if (adjoint) sr.qp[e] = *reinterpret_cast<const uint4 *>(qb + off);
             }
         }
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
             const int i = tid + e * kThreads, rr = i / VPR, p = i % VPR;
-            vp[e] = make_uint4(0, 0, 0, 0);
-            op[e] = make_uint4(0, 0, 0, 0);
+            sr.vp[e] = make_uint4(0, 0, 0, 0);
+            sr.op[e] = make_uint4(0, 0, 0, 0);
             if (i < NVP) {
                 const int64_t off = sq.token(c * CB + (rr < n ? rr : 0)) * dvf + p * EPP;
-                vp[e] = *reinterpret_cast<const uint4 *>(vb + off);
-                if (adjoint) op[e] = *reinterpret_cast<const uint4 *>(dob + off);
+                sr.vp[e] = *reinterpret_cast<const uint4 *>(vb + off);
+                if (adjoint) sr.op[e] = *reinterpret_cast<const uint4 *>(dob + off);
             }
         }
-        float lv = 0.f, bv = 0.f;
+        sr.lv = 0.f;
+        sr.bv = 0.f;
         if (tid < CB && tid < n) {
             const int64_t t = sq.token(c * CB + tid);
-            lv = lab[t];
-            bv = beb[t];
+            sr.lv = lab[t];
+            sr.bv = beb[t];
         }
-        // piece -> EPP floats of row rr (zero past the end), into LDS as 16-byte stores
-        auto put = [&](float *dst, const uint4 &piece, bool keep) __attribute__((always_inline)) {
-            float f[EPP];
-            if constexpr (sizeof(E) == 2) {
-                const unsigned w[4] = {piece.x, piece.y, piece.z, piece.w};
+    };
+    // piece -> EPP floats of row rr (zero past the end), into LDS as 16-byte stores
+    auto put = [&](float *dst, const uint4 &piece, bool keep) __attribute__((always_inline)) {
+        float f[EPP];
+        if constexpr (sizeof(E) == 2) {
+            const unsigned w[4] = {piece.x, piece.y, piece.z, piece.w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f[2 * j] = __uint_as_float(w[j] << 16);
-                    f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-                }
-            } else {
-                f[0] = __uint_as_float(piece.x);
-                f[1] = __uint_as_float(piece.y);
-                f[2] = __uint_as_float(piece.z);
-                f[3] = __uint_as_float(piece.w);
+            for (int j = 0; j < 4; ++j) {
+                f[2 * j] = __uint_as_float(w[j] << 16);
+                f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
             }
+        } else {
+            f[0] = __uint_as_float(piece.x);
+            f[1] = __uint_as_float(piece.y);
+            f[2] = __uint_as_float(piece.z);
+            f[3] = __uint_as_float(piece.w);
+        }
 #pragma unroll
-            for (int j = 0; j < EPP; j += 4)
-                *reinterpret_cast<float4 *>(dst + j) =
-                    keep ? make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-        };
+        for (int j = 0; j < EPP; j += 4)
+            *reinterpret_cast<float4 *>(dst + j) =
+                keep ? make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto stage_store = [&](int64_t c, const StageRegs &sr) __attribute__((always_inline)) {
+        const int n = n_rows(c);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int i = tid + e * kThreads, rr = i / KPR, p = i % KPR;
             if (i < NKP) {
-                put(&sm.K[rr][p * EPP], kp[e], rr < n);
-                put(&sm.Q[rr][p * EPP], qp[e], rr < n);
+                put(&sm.K[rr][p * EPP], sr.kp[e], rr < n);
+                put(&sm.Q[rr][p * EPP], sr.qp[e], rr < n);
             }
         }
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
             const int i = tid + e * kThreads, rr = i / VPR, p = i % VPR;
             if (i < NVP) {
-                put(&sm.V[rr][p * EPP], vp[e], rr < n);
-                put(&sm.dO[rr][p * EPP], op[e], rr < n);
+                put(&sm.V[rr][p * EPP], sr.vp[e], rr < n);
+                put(&sm.dO[rr][p * EPP], sr.op[e], rr < n);
             }
         }
         if (tid < CB) {
-            sm.la[tid] = lv;
-            sm.beta[tid] = bv;
+            sm.la[tid] = sr.lv;
+            sm.beta[tid] = sr.bv;
             sm.db[tid] = 0.f;
             sm.dr[tid] = 0.f;
             sm.dbeta[tid] = 0.f;
             sm.dw[tid] = 0.f;
         }
         if (tid == 0) sm.hd = 0.f;
+    };
+    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write); every
+    // load of a thread is a 16-byte piece issued before any of them is used
+    auto stage = [&](int64_t c, bool adjoint) __attribute__((always_inline)) {
+        StageRegs sr;
+        stage_issue(c, adjoint, sr);
+        stage_store(c, sr);
     };
     // inclusive cumsum of log alpha and the read exponents (one wave)
     auto gates = [&]() __attribute__((always_inline)) {
@@ -376,14 +389,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         for (int u = 0; u < SR; ++u) *reinterpret_cast<float4 *>(&dst[sr0 + u][sc0]) = x[u];
     };
     // ---- sweep 1: the chunk-form forward from h0, storing each chunk's entry state
+    // (the inputs of chunk c + 1 are read into registers while chunk c is computed)
     load_slice(sm.H, a.h0 ? a.h0 + sbase : nullptr, dvf);
+    StageRegs nx;
+    if (nch > 0) stage_issue(0, false, nx);
     __syncthreads();
     for (int64_t c = 0; c < nch; ++c) {
 #pragma unroll
         for (int u = 0; u < SR; ++u)
             *reinterpret_cast<float4 *>(ckpt + c * cstride + (sr0 + u) * TV + sc0) =
                 *reinterpret_cast<const float4 *>(&sm.H[sr0 + u][sc0]);
-        stage(c, false);
+        stage_store(c, nx);
+        if (c + 1 < nch) stage_issue(c + 1, false, nx);
         __syncthreads();
         gates();
         __syncthreads();
@@ -408,12 +425,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         __syncthreads();
     }
 
-    // ---- sweep 2: the adjoint, chunk by chunk from the last
+    // ---- sweep 2: the adjoint, chunk by chunk from the last (the inputs of chunk c - 1 are read
+    // into registers while chunk c is computed)
     load_slice(sm.D, a.dhT ? a.dhT + sbase : nullptr, dvf);
+    if (nch > 0) stage_issue(nch - 1, true, nx);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = n_rows(c);
         load_slice(sm.H, ckpt + c * cstride, TV);
-        stage(c, true);
+        stage_store(c, nx);
+        if (c > 0) stage_issue(c - 1, true, nx);
         __syncthreads();
         gates();
         __syncthreads();
