@@ -119,3 +119,31 @@ def test_full_size_sampled(gdr):
     c = inputs.workload1(regime="slow")
     dout, dhT = _upstream(c, 34, 4)
     _run_and_check(gdr, c, dout, dhT, "post", False, "full", units=((0, 3), (3, 14)))
+
+
+@pytest.mark.parametrize("shape", ["gqa-packed", "full"])
+def test_deterministic(gdr, shape):
+    # every gradient is the same bits on a second call: the column slices' and value heads' shares
+    # are added in a fixed order, with no float atomics; the workspace is filled with other bytes
+    # between the calls so that nothing left from the first call can carry over
+    _say("backward determinism %s" % shape)
+    if shape == "full":
+        c = inputs.workload1(regime="slow")
+        dout, dhT = _upstream(c, 44, 4)
+    else:
+        c = inputs.chunk_case(Hk=2, Hv=4, dk=128, dv=128, dtype=torch.bfloat16, seed=45, h0_std=0.5,
+                              lengths=[100, 0, 33, 257], regime="p5")
+        dout, dhT = _upstream(c, 46, 4)
+    d = lambda t: None if t is None else t.cuda()
+    B, Hk, T, dk = c.q.shape
+    Hv, dv = c.v.shape[1], c.v.shape[3]
+    S = 0 if c.cu_seqlens is None else c.cu_seqlens.numel() - 1
+    need = gdr.chunk_bwd_workspace_bytes(B, T, Hk, Hv, dk, dv, S, c.q.dtype)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    args = (d(c.q), d(c.k), d(c.v), d(c.log_alpha), d(c.beta), d(dout), d(c.h0), d(c.cu_seqlens), d(dhT))
+    first = gdr.chunk_bwd(*args, workspace=ws)
+    ws.fill_(0x5a)
+    second = gdr.chunk_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, first, second):
+        assert torch.equal(x, y), "%s differs between two calls" % n

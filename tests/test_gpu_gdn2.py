@@ -281,3 +281,24 @@ def test_decode_steps_match_chunk(gdr):
     torch.cuda.synchronize()
     check(gpu_np(torch.stack(outs, dim=2)), o_c, torch.float32, "out")
     check(gpu_np(state), h_c, torch.float32, "state")
+
+
+@pytest.mark.parametrize("regime", ["page", "weak", "mixed"])
+def test_chunk_bench_shape_two_pass(gdr, regime):
+    # the launch the benchmark times: B4 H16 T4096 d_k = d_v = 128 bf16, chunk 32, two passes
+    # through a caller workspace; eight (sequence, head) units against the oracle, each output
+    # checked whole, per 64-token block and on its chunk-last rows, and each final state
+    from tests._parity import check_bf16_detailed, check_states, segments
+    _say("gdn2 benchmark shape, chunk 32, two passes, regime=%s" % regime)
+    c = inputs.gdn2_case(B=4, T=4096, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16, seed=1001,
+                         h0_std=0.1, regime=regime)
+    ws = torch.empty(gdr.gdn2_chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, 32), dtype=torch.uint8,
+                     device="cuda")
+    o, hT = _run(gdr, c, 32, workspace=ws)
+    for (bi, h) in ((0, 0), (0, 9), (1, 3), (1, 14), (2, 6), (2, 11), (3, 1), (3, 15)):
+        sl = lambda t: t[bi:bi + 1, h:h + 1]
+        ro, rh = gdn2.scan(sl(c.q), sl(c.k), sl(c.v), sl(c.g), sl(c.b), sl(c.w), sl(c.h0))
+        ou = o[bi:bi + 1, h:h + 1]
+        e = check_bf16_detailed(ou, ro, segments(ou.shape, None), "out (%d, %d)" % (bi, h))
+        check_states(hT[bi:bi + 1, h:h + 1], rh, "hT (%d, %d)" % (bi, h))
+        _say("  unit (%d, %d): whole %.2e, worst block %.2e, chunk-last rows %.2e" % ((bi, h) + e))

@@ -277,79 +277,5 @@ def test_chunk_fwd_deterministic(gdr):
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
-# ---------------------------------------------------------------- full workload sizes
-
-def _units_parity(o_gpu, h_gpu, case, units, read="post", reverse=False, dtype=torch.bfloat16):
-    """Oracle on selected (row/segment, head) units only."""
-    for (s, h) in units:
-        if case.cu_seqlens is None:
-            sl = lambda t: t[s:s + 1, h:h + 1]
-            ro, rh = oracle.scan(sl(case.q), sl(case.k), sl(case.v), sl(case.log_alpha), sl(case.beta),
-                                 None if case.h0 is None else case.h0[s:s + 1, h:h + 1],
-                                 read=read, reverse=reverse)
-            check(o_gpu[s:s + 1, h:h + 1], ro, dtype, "unit (%d,%d) o" % (s, h))
-        else:
-            a, e = int(case.cu_seqlens[s]), int(case.cu_seqlens[s + 1])
-            sl = lambda t: t[:, h:h + 1, a:e]
-            ro, rh = oracle.scan(sl(case.q), sl(case.k), sl(case.v), sl(case.log_alpha), sl(case.beta),
-                                 None if case.h0 is None else case.h0[s:s + 1, h:h + 1],
-                                 read=read, reverse=reverse)
-            check(o_gpu[:, h:h + 1, a:e], ro, dtype, "unit (%d,%d) o" % (s, h))
-        if h_gpu is not None:
-            check(h_gpu[s:s + 1, h:h + 1], rh, dtype, "unit (%d,%d) hT" % (s, h))
-
-
-@pytest.mark.parametrize("regime", ["config", "slow"])
-def test_workload1_full_size_sampled(gdr, regime):
-    """B4 H16 T4096 d128 bf16, chunk 64, nonzero h0: the launch the benchmark times,
-    checked on sampled (batch, head) units."""
-    case = inputs.workload1(regime=regime)
-    _say("workload1 full size regime=%s" % regime)
-    o, hT = run_chunk(gdr, case, 64)
-    _units_parity(o, hT, case, [(0, 0), (1, 7), (3, 15)])
-
-
-def test_workload2_full_size_sampled(gdr):
-    case = inputs.workload2()
-    _say("workload2 lengths %s" % np.diff(case.cu_seqlens.numpy()).tolist())
-    o, hT = run_chunk(gdr, case, 64)
-    n = case.cu_seqlens.numel() - 1
-    _units_parity(o, hT, case, [(0, 0), (n // 2, 31), (n - 1, 5)])
-
-
-def test_workload4_bidirectional_sampled(gdr):
-    """Forward pre-write scan + in-segment reversed pre-write scan with its own gates,
-    summed per token (two calls, the second accumulating)."""
-    case = inputs.workload4()
-    q, k, v, la, b, _, cu = to_dev(case)
-    la_b, b_b = case.extra["log_alpha_bwd"].cuda(), case.extra["beta_bwd"].cuda()
-    out, _ = gdr.chunk_fwd(q, k, v, la, b, None, cu, chunk=64, read="pre", want_state=False)
-    gdr.chunk_fwd(q, k, v, la_b, b_b, None, cu, chunk=64, read="pre", reverse=True, out=out,
-                  accumulate=True, want_state=False)
-    torch.cuda.synchronize()
-    o = gpu_np(out)
-    for (s, h) in [(0, 0), (2, 9), (3, 15)]:
-        a, e = int(case.cu_seqlens[s]), int(case.cu_seqlens[s + 1])
-        sl = lambda t: t[:, h:h + 1, a:e]
-        rf, _ = oracle.scan(sl(case.q), sl(case.k), sl(case.v), sl(case.log_alpha), sl(case.beta), read="pre")
-        rb, _ = oracle.scan(sl(case.q), sl(case.k), sl(case.v), sl(case.extra["log_alpha_bwd"]),
-                            sl(case.extra["beta_bwd"]), read="pre", reverse=True)
-        check(o[:, h:h + 1, a:e], rf + rb, torch.bfloat16, "bidirectional unit (%d,%d)" % (s, h))
-
-
-def test_workload3_decode_full_size_sampled(gdr):
-    """256 sequences, 16 key heads -> 32 value heads, d128, fp32 state, 64 consecutive steps
-    updated in place; sampled sequences checked against the oracle at every step."""
-    dc = inputs.workload3()
-    state = dc.state.cuda()
-    picks = [0, 131, 255]
-    ref_state = dc.state[picks].double().numpy()
-    worst = 0.0
-    for s in range(dc.q.shape[0]):
-        args = [t[s].cuda() for t in (dc.q, dc.k, dc.v, dc.log_alpha, dc.beta)]
-        o, state = gdr.decode_step(*args, state, state_out=state)
-        ro, ref_state = oracle.decode(dc.q[s][picks], dc.k[s][picks], dc.v[s][picks],
-                                      dc.log_alpha[s][picks], dc.beta[s][picks], ref_state)
-        worst = max(worst, check(gpu_np(o[picks]), ro, torch.bfloat16, "decode o step %d" % s))
-    check(gpu_np(state[picks]), ref_state, torch.bfloat16, "decode final state")
-    _say("workload3: worst rel err of o over 64 steps %.2e" % worst)
+# The full workload sizes (every unit, every gate regime, per-block and chunk-last-row checks) are
+# in test_gpu_full_size.py.
