@@ -27,16 +27,19 @@
 // This is the derivative of the chunk form of `chunked_delta` on the "Prizma seq/delta.py" page
 // (transposed to H = S^T), which equals the recurrence; the pages print no backward.
 //
-// One workgroup of 256 threads per (sequence, value head, 32 columns of d_v). Every quantity is
-// per column or a sum over columns of per-column terms, so the column slices are independent:
-// dq, dk, dbeta and dlog alpha are added with float atomics into buffers a fill kernel clears
-// first (this also sums dq and dk over the value heads that share a key head). Two sweeps: the
-// chunk-form forward from h0, storing the slice of the state at each chunk start in the
-// workspace; then the chunks from the last, each recomputing its forward quantities from its
-// stored entry state and applying the adjoint above. All matrices of a chunk live in LDS in
-// fp32; the products run on the matrix cores as split bf16 products with fp32 accumulation
-// (16x16 output tiles shared out over the four waves), the triangular inverse is the one the
-// chunk forward kernels use, and the gate gradients are sums on the vector units.
+// One workgroup of 512 threads (eight waves) per (sequence, value head, 32 columns of d_v).
+// Every quantity is per column or a sum over columns of per-column terms, so the column slices
+// are independent. Each workgroup writes its share of dq, dk, dbeta and dlog alpha into its own
+// partial buffer in the workspace, and a second kernel adds the partials of the column slices
+// (and, for dq and dk, of the value heads that share a key head) in a fixed order, so the
+// gradients are the same bits on every run; inside a workgroup every per-row sum likewise has
+// one slot per contributing tile, added in a fixed order. Two sweeps: the chunk-form forward from
+// h0, storing the slice of the state at each chunk start in the workspace; then the chunks from
+// the last, each recomputing its forward quantities from its stored entry state and applying the
+// adjoint above. All matrices of a chunk live in LDS in fp32; the products run on the matrix
+// cores as split bf16 products with fp32 accumulation (16x16 output tiles shared out over the
+// eight waves), the triangular inverse is the one the chunk forward kernels use, and the gate
+// gradients are sums on the vector units.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -76,8 +79,16 @@ struct alignas(16) Smem {
     float A[CB * AP], T[CB * TP];  // flat: the shared triangular inverse reads them so
     float P[CB][TP], G[CB][TP], M[CB][TP], Nb[CB][TP];
     float la[CB], beta[CB], b[CB], r[CB];
-    float db[CB], dr[CB], dbeta[CB], dw[CB];
-    float hd;  // <dH', H> of the chunk
+    float dw[CB];
+    // Per-row partial sums of the gate gradients, one slot per contributing tile or thread so
+    // that they are added in a fixed order (no float atomics):
+    //   pdr:    the read exponent r: the three dP tiles' row sums, then the DK / 16 dQ tiles'
+    //   pdb:    the cumulative decay b: the dP tiles' column sums (3), the dA tiles' row sums (3)
+    //           and column sums (3), and each row's own term from dR . X
+    //   pdbeta: beta: the dA tiles' row sums (3), and each row's own term from dR . (V - gamma X)
+    static constexpr int kPdr = 3 + DK / 16, kPdb = 10, kPdbeta = 4;
+    float pdr[kPdr][CB], pdb[kPdb][CB], pdbeta[kPdbeta][CB];
+    float hdp[kThreads / 64];  // <dH', H> of the chunk, per wave
 };
 
 // acc += A (16 x KD) B (KD x 16) with both operands in LDS. A is X[m0 + m][k] (or, with AT,
@@ -159,11 +170,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     const E *dob = reinterpret_cast<const E *>(a.dout) + (row * a.Hv + head) * a.T * dvf + col0;
     const float *lab = a.log_alpha + (row * a.Hv + head) * a.T;
     const float *beb = a.beta + (row * a.Hv + head) * a.T;
-    float *dqb = a.dq + (row * a.Hk + kh) * a.T * DK;
-    float *dkb = a.dk + (row * a.Hk + kh) * a.T * DK;
+    // this workgroup's partial buffers: [B][Hv][ntiles][T][DK] for dq, dk; [B][Hv][ntiles][T]
+    // for dlog alpha, dbeta (summed by bwd_reduce_kernel)
+    const int64_t part = (row * a.Hv + head) * a.ntiles + tile;
+    float *dqb = a.pq + part * a.T * DK;
+    float *dkb = a.pk + part * a.T * DK;
     float *dvb = a.dv + (row * a.Hv + head) * a.T * dvf + col0;
-    float *dlab = a.dlog_alpha + (row * a.Hv + head) * a.T;
-    float *dbeb = a.dbeta + (row * a.Hv + head) * a.T;
+    float *dlab = a.pla + part * a.T;
+    float *dbeb = a.pbeta + part * a.T;
     // chunk-start states: [head][slot][tile] slices of DK x TV floats
     constexpr int64_t kSlice = (int64_t)DK * TV;
     float *ckpt = a.ws + ((head * a.nslots + slot0) * a.ntiles + tile) * kSlice;
@@ -273,12 +287,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         if (tid < CB) {
             sm.la[tid] = sr.lv;
             sm.beta[tid] = sr.bv;
-            sm.db[tid] = 0.f;
-            sm.dr[tid] = 0.f;
-            sm.dbeta[tid] = 0.f;
             sm.dw[tid] = 0.f;
         }
-        if (tid == 0) sm.hd = 0.f;
+        // the tiles leave some slots of the row partials untouched: they read as zero
+        for (int i = tid; i < (SM::kPdr + SM::kPdb + SM::kPdbeta) * CB; i += kThreads) (&sm.pdr[0][0])[i] = 0.f;
     };
     // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write); every
     // load of a thread is a 16-byte piece issued before any of them is used
@@ -365,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 for (int v = 0; v < 4; ++v) s += sm.D[sr0 + u][sc0 + v] * sm.H[sr0 + u][sc0 + v];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-            if (lane == 0) atomicAdd(&sm.hd, s);
+            if (lane == 0) sm.hdp[wave] = s;
         }
         __syncthreads();
         // U = T R
@@ -485,17 +497,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float rsum = row16(rs), bsum = row16(rb);
                 if (cc == 0) {
                     if (isa) {
-                        atomicAdd(&sm.db[i], rsum);
-                        atomicAdd(&sm.dbeta[i], bsum);
+                        sm.pdb[3 + tt][i] = rsum;
+                        sm.pdbeta[tt][i] = bsum;
                     } else {
-                        atomicAdd(&sm.dr[i], rsum);
+                        sm.pdr[tt][i] = rsum;
                     }
                 }
             }
             // column sums (over the 16 rows of the tile) go to d b_j with a minus sign
             float cs = colsum[0] + colsum[1] + colsum[2] + colsum[3];
             cs = col4(cs);
-            if (g == 0) atomicAdd(&sm.db[16 * nt + cc], -cs);
+            if (g == 0) sm.pdb[(isa ? 6 : 0) + tt][16 * nt + cc] = -cs;
         }
         if (tid < kRowThreads) {
             const int i = ei;
@@ -516,8 +528,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             sb += __shfl_xor(sb, 1, 64); sb += __shfl_xor(sb, 2, 64); sb += __shfl_xor(sb, 4, 64);
             sx += __shfl_xor(sx, 1, 64); sx += __shfl_xor(sx, 2, 64); sx += __shfl_xor(sx, 4, 64);
             if ((tid % (TV / 4)) == 0) {
-                atomicAdd(&sm.dbeta[i], sb);
-                atomicAdd(&sm.db[i], -be * ga * sx);
+                sm.pdbeta[3][i] = sb;
+                sm.pdb[9][i] = -be * ga * sx;
             }
         }
         __syncthreads();
@@ -533,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float er = __expf(sm.r[i]);
                 dq[r] = er * oh[r];
                 const float rq = row16(dq[r] * sm.Q[i][16 * nt + cc]);
-                if (cc == 0) atomicAdd(&sm.dr[i], rq);
+                if (cc == 0) sm.pdr[3 + nt][i] = rq;
             }
             dq = mm<CB, false, false>(dq, &sm.M[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
             // three independent partial sums, so that the products do not wait on each other
@@ -548,8 +560,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const int i = 16 * mt + 4 * g + r;
                 if (i < n) {
                     const int64_t tk = sq.token(c * CB + i);
-                    atomicAdd(dqb + tk * DK + 16 * nt + cc, dq[r]);
-                    atomicAdd(dkb + tk * DK + 16 * nt + cc, dk[r]);
+                    dqb[tk * DK + 16 * nt + cc] = dq[r];
+                    dkb[tk * DK + 16 * nt + cc] = dk[r];
                 }
             }
         }
@@ -575,18 +587,31 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         if (tid < 64) {
             const int i = tid;
             float x = 0.f, z = 0.f;
+            float dbeta_i = 0.f;
             if (i < CB) {
                 const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-                float dbi = sm.db[i] - wi * sm.dw[i];
+                float dbi = 0.f, dri = 0.f;
+#pragma unroll
+                for (int p = 0; p < SM::kPdb; ++p) dbi += sm.pdb[p][i];
+#pragma unroll
+                for (int p = 0; p < SM::kPdr; ++p) dri += sm.pdr[p][i];
+#pragma unroll
+                for (int p = 0; p < SM::kPdbeta; ++p) dbeta_i += sm.pdbeta[p][i];
+                dbi -= wi * sm.dw[i];
                 // the last row also takes glast <D, H> + sum_j w_j dw_j (a sum over the wave)
                 float s = __expf(fminf(blast - sm.b[i], 0.f)) * sm.dw[i];
 #pragma unroll
                 for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off, 32);
-                if (i == CB - 1) dbi += glast * sm.hd + s;
+                if (i == CB - 1) {
+                    float hd = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w) hd += sm.hdp[w];
+                    dbi += glast * hd + s;
+                }
                 // post: the read exponent is b itself; pre: b - log alpha leaves out row i's own
                 // log alpha, so its gradient enters the sums of the rows after it only
-                x = dbi + (pre ? 0.f : sm.dr[i]);
-                z = pre ? sm.dr[i] : 0.f;
+                x = dbi + (pre ? 0.f : dri);
+                z = pre ? dri : 0.f;
             }
             const float zi = z;
 #pragma unroll
@@ -599,8 +624,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
             if (i < n) {
                 const int64_t t = sq.token(c * CB + i);
-                atomicAdd(dlab + t, x + z - zi);
-                atomicAdd(dbeb + t, sm.dbeta[i]);
+                dlab[t] = x + z - zi;
+                dbeb[t] = dbeta_i;
             }
         }
         __syncthreads();
@@ -613,18 +638,41 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     }
 }
 
-__global__ void zero_kernel(float *p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0.f;
-}
-
-// clear n floats with a kernel (not a memset node, so the call stays safe to capture in a graph)
-hipError_t clear(float *p, int64_t n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    const int64_t blocks = (n + 255) / 256;
-    const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
-    hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, stream, p, n);
-    return hipGetLastError();
+// dq, dk: the sum over the value heads of a key head and over the column slices of the
+// partials, 4 consecutive d_k elements per thread; dlog alpha, dbeta: the sum over the column
+// slices. Every sum runs in the same order on every call.
+__global__ void bwd_reduce_kernel(BwdArgs a, int dk) {
+    const int64_t grp = a.Hv / a.Hk;
+    const int64_t nq4 = a.B * a.Hk * a.T * dk / 4, ng = a.B * a.Hv * a.T;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nq4 + ng; e += stride) {
+        if (e < nq4) {
+            const int64_t i = 4 * e;                    // element of [B][Hk][T][dk]
+            const int64_t td = i % (a.T * dk), bk = i / (a.T * dk);
+            const int64_t b = bk / a.Hk, kh = bk % a.Hk;
+            float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
+            for (int64_t j = 0; j < grp; ++j)
+                for (int64_t t = 0; t < a.ntiles; ++t) {
+                    const int64_t src = ((b * a.Hv + kh * grp + j) * a.ntiles + t) * a.T * dk + td;
+                    const float4 x = *reinterpret_cast<const float4 *>(a.pq + src);
+                    const float4 y = *reinterpret_cast<const float4 *>(a.pk + src);
+                    sq.x += x.x; sq.y += x.y; sq.z += x.z; sq.w += x.w;
+                    sk.x += y.x; sk.y += y.y; sk.z += y.z; sk.w += y.w;
+                }
+            *reinterpret_cast<float4 *>(a.dq + i) = sq;
+            *reinterpret_cast<float4 *>(a.dk + i) = sk;
+        } else {
+            const int64_t i = e - nq4;                  // element of [B][Hv][T]
+            const int64_t tt = i % a.T, bh = i / a.T;
+            float sl = 0.f, sb = 0.f;
+            for (int64_t t = 0; t < a.ntiles; ++t) {
+                sl += a.pla[(bh * a.ntiles + t) * a.T + tt];
+                sb += a.pbeta[(bh * a.ntiles + t) * a.T + tt];
+            }
+            a.dlog_alpha[i] = sl;
+            a.dbeta[i] = sb;
+        }
+    }
 }
 
 template <typename E, int DK>
@@ -637,15 +685,19 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
 
 hipError_t launch_bwd(const BwdArgs &a, int dtype, int dk, int dv, hipStream_t stream) {
     (void)dv;
-    // the sums over columns and value heads start from zero
-    hipError_t e;
-    if ((e = clear(a.dq, a.B * a.Hk * a.T * dk, stream)) != hipSuccess) return e;
-    if ((e = clear(a.dk, a.B * a.Hk * a.T * dk, stream)) != hipSuccess) return e;
-    if ((e = clear(a.dlog_alpha, a.B * a.Hv * a.T, stream)) != hipSuccess) return e;
-    if ((e = clear(a.dbeta, a.B * a.Hv * a.T, stream)) != hipSuccess) return e;
-    if (a.units == 0) return hipSuccess;
-    if (dtype == kDtypeBf16) return dk == 64 ? launch_t<__bf16, 64>(a, stream) : launch_t<__bf16, 128>(a, stream);
-    return dk == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
+    hipError_t e = hipSuccess;
+    if (a.units > 0) {
+        if (dtype == kDtypeBf16) e = dk == 64 ? launch_t<__bf16, 64>(a, stream) : launch_t<__bf16, 128>(a, stream);
+        else e = dk == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
+        if (e != hipSuccess) return e;
+    }
+    // every element of dq, dk, dlog alpha and dbeta is written by the reduction (zero where no
+    // partial exists: no value heads or no column slices cannot happen, T = 0 has no elements)
+    const int64_t work = a.B * a.Hk * a.T * dk / 4 + a.B * a.Hv * a.T;
+    if (work <= 0) return hipSuccess;
+    const int64_t blocks = (work + 255) / 256;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, a, dk);
+    return hipGetLastError();
 }
 
 }  // namespace gdr

@@ -47,6 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gdr_kernels.hpp"
@@ -57,6 +58,7 @@ namespace gdr {
 namespace {
 
 constexpr int kC = 64, kDK = 128, kDVT = 32;
+constexpr int kMaxDevices = 64;
 // Wave roles. Waves w and w + 4 share a SIMD: each chain wave (0, 1) shares its SIMD with a
 // copy wave, which issues little; the four prep waves take the other two SIMDs.
 constexpr int kThreads = 512;
@@ -1162,15 +1164,28 @@ bool chunk_fwd_fast_supported(int dtype, int chunk, int dk) {
     return dtype == kDtypeBf16 && chunk == kC && dk == kDK;
 }
 
+// The LDS size attribute is set once per device and form; concurrent first launches from
+// several host threads are serialised by the mutex.
+template <bool kPro>
+hipError_t configure_form() {
+    static std::mutex mu;
+    static bool done[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_fwd_fast_kernel<kPro>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    if (e == hipSuccess) done[dev] = true;
+    return e;
+}
+
 template <bool kPro>
 hipError_t launch_form(const ChunkArgs &a, hipStream_t stream) {
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_fwd_fast_kernel<kPro>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    const hipError_t ce = configure_form<kPro>();
+    if (ce != hipSuccess) return ce;
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
     hipLaunchKernelGGL(chunk_fwd_fast_kernel<kPro>, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
     return hipGetLastError();

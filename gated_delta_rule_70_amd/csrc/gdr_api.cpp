@@ -448,9 +448,19 @@ int64_t bwd_slots(const gdr_chunk_dims_t &d, bool packed) {
     return d.B * ((d.T + CB - 1) / CB);
 }
 
-// the state at the start of every chunk of every sequence-head
-int64_t bwd_workspace_bytes(const gdr_chunk_dims_t &d, bool packed) {
+// the state at the start of every chunk of every sequence-head, then each 32-column slice's
+// partial dq, dk ([B][Hv][dv / 32][T][dk] each) and partial dlog_alpha, dbeta ([B][Hv][dv / 32][T]
+// each), which a second kernel adds up in a fixed order
+int64_t bwd_ckpt_bytes(const gdr_chunk_dims_t &d, bool packed) {
     return prod({d.Hv, bwd_slots(d, packed), d.dk, d.dv, 4});
+}
+int64_t bwd_part_elems(const gdr_chunk_dims_t &d) {
+    return prod({d.B, d.Hv, d.dv / gdr::kBwdCols, d.T});
+}
+int64_t bwd_workspace_bytes(const gdr_chunk_dims_t &d, bool packed) {
+    const int64_t c = bwd_ckpt_bytes(d, packed), p = bwd_part_elems(d);
+    if (c < 0 || p < 0) return -1;
+    return c + p * (2 * d.dk + 2) * 4;
 }
 
 gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
@@ -512,6 +522,14 @@ gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *
     a.cu_seqlens = cu_seqlens;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
     a.ws = static_cast<float *>(workspace);
+    {
+        const int64_t pe = bwd_part_elems(d);
+        char *p = static_cast<char *>(workspace) + bwd_ckpt_bytes(d, cu_seqlens != nullptr);
+        a.pq = reinterpret_cast<float *>(p);
+        a.pk = a.pq + pe * d.dk;
+        a.pla = a.pk + pe * d.dk;
+        a.pbeta = a.pla + pe;
+    }
     a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv;
     a.units = nseq * d.Hv;
     a.nslots = bwd_slots(d, cu_seqlens != nullptr);

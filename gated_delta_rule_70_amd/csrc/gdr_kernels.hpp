@@ -74,7 +74,9 @@ struct Gdn2DecodeArgs {
 
 // Backward of the scalar rule. Gradient buffers are fp32: dq, dk [B][Hk][T][dk] (summed over the
 // value heads of a key head), dv [B][Hv][T][dv], dlog_alpha, dbeta [B][Hv][T], dh0 like h0.
-// ws: the state at the start of every kBwdBlock-token chunk (nslots per value head).
+// ws: the state at the start of every kBwdBlock-token chunk (nslots per value head); pq, pk
+// [B][Hv][ntiles][T][dk] and pla, pbeta [B][Hv][ntiles][T]: each column slice's share of dq, dk,
+// dlog_alpha and dbeta, summed in a fixed order by a second kernel (all four in the workspace).
 constexpr int kBwdBlock = 32;
 constexpr int kBwdCols = 32;  // value columns per workgroup of the backward
 struct BwdArgs {
@@ -83,6 +85,7 @@ struct BwdArgs {
     const int32_t *cu_seqlens;
     float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dh0;
     float *ws;
+    float *pq, *pk, *pla, *pbeta;
     int64_t B, T, Hk, Hv;
     int64_t units;   // sequences x value heads
     int64_t nslots;  // block-start states per value head
