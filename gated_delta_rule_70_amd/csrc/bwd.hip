@@ -290,14 +290,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             sm.dw[tid] = 0.f;
         }
         // the tiles leave some slots of the row partials untouched: they read as zero
-        for (int i = tid; i < (SM::kPdr + SM::kPdb + SM::kPdbeta) * CB; i += kThreads) (&sm.pdr[0][0])[i] = 0.f;
-    };
-    // load chunk c's inputs into LDS (rows past the end are zero: no decay, no write); every
-    // load of a thread is a 16-byte piece issued before any of them is used
-    auto stage = [&](int64_t c, bool adjoint) __attribute__((always_inline)) {
-        StageRegs sr;
-        stage_issue(c, adjoint, sr);
-        stage_store(c, sr);
+        for (int i = tid; i < SM::kPdr * CB; i += kThreads) sm.pdr[i / CB][i % CB] = 0.f;
+        for (int i = tid; i < SM::kPdb * CB; i += kThreads) sm.pdb[i / CB][i % CB] = 0.f;
+        for (int i = tid; i < SM::kPdbeta * CB; i += kThreads) sm.pdbeta[i / CB][i % CB] = 0.f;
     };
     // inclusive cumsum of log alpha and the read exponents (one wave)
     auto gates = [&]() __attribute__((always_inline)) {
