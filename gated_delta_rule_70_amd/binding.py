@@ -25,7 +25,8 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
 
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
-           "gdr_gdn2_chunk_fwd", "gdr_gdn2_chunk_fwd_workspace_bytes", "gdr_gdn2_decode_step",
+           "gdr_gdn2_chunk_fwd", "gdr_gdn2_chunk_fwd_noalloc", "gdr_gdn2_chunk_fwd_workspace_bytes",
+           "gdr_gdn2_decode_step",
            "gdr_delta_product_fwd",
            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_bytes",
            "gdr_status_string", "gdr_last_error", "gdr_abi_version", "gdr_selftest_mfma")
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, p, ctypes.c_int64,
                                        ctypes.POINTER(ChunkDims), p]
     lib.gdr_gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_gdn2_chunk_fwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_gdn2_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_gdn2_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDims), i32, i32]
     lib.gdr_gdn2_chunk_fwd_workspace_bytes.restype = ctypes.c_int64
     lib.gdr_gdn2_decode_step.argtypes = [p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
@@ -409,6 +412,37 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, h0=None, cu_seqlens=None, *, chunk: int = 6
     _check(lib().gdr_gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0),
                                     _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT), ws_ptr, ws_bytes,
                                     ctypes.byref(dims), _stream(q)))
+    return out, hT
+
+
+def gdn2_chunk_fwd_noalloc(q, k, v, g, b, w, h0, cu_seqlens, out, hT, *, chunk: int = 64, read: str = "post",
+                           reverse: bool = False, accumulate: bool = False, l2norm: bool = False):
+    """``gdr_gdn2_chunk_fwd_noalloc``: the two-pass GDN-2 forward on the library's fixed device
+    scratch (no workspace, nothing allocated by the call). Arguments as ``gdn2_chunk_fwd``; ``out``
+    and ``hT`` (or None for no final state) must be given, so that nothing is allocated here either."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    for name, t, tdt, shape in (("k", k, dt, (B, Hk, T, dk)), ("v", v, dt, (B, Hv, T, dv)),
+                                ("g", g, torch.float32, (B, Hk, T, dk)), ("b", b, dt, (B, Hk, T, dk)),
+                                ("w", w, dt, (B, Hv, T, dv)), ("out", out, dt, (B, Hv, T, dv))):
+        _need(t, name, tdt, shape, dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    for name, t in (("h0", h0), ("hT", hT)):
+        if t is not None:
+            _need(t, name, torch.float32, (S, Hv, dk, dv), dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_REVERSE if reverse else 0) | \
+        (GDR_ACCUMULATE if accumulate else 0) | (GDR_QK_L2NORM if l2norm else 0)
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, _dtype_code(dt), flags)
+    _check(lib().gdr_gdn2_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0),
+                                            _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT), ctypes.byref(dims),
+                                            _stream(q)))
     return out, hT
 
 

@@ -426,6 +426,25 @@ gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v, con
                            stream);
 }
 
+gdr_status_t gdr_gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g, const void *b,
+                                        const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk,
+                                        void *out, float *hT, const gdr_chunk_dims_t *dims, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    const int64_t need = gdn2_ws_bytes(*dims, chunk, cu_seqlens != nullptr);
+    if (need > gdr::kScratchBytes)
+        return fail(GDR_ERR_DIMS, "these sizes need %lld bytes of workspace; the allocation-free entry point holds "
+                    "%lld (GDR_NOALLOC_SCRATCH_BYTES): call gdr_gdn2_chunk_fwd with a workspace instead",
+                    (long long)need, (long long)gdr::kScratchBytes);
+    // need < 0 (unsupported dtype, chunk, dk or sizes) is reported by the checks of the call itself
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = gdr::scratch_region(&ws);
+        if (e != hipSuccess) return fail(GDR_ERR_HIP, "device scratch: %s", hipGetErrorString(e));
+    }
+    return gdn2_chunk_impl(q, k, v, g, b, w, h0, cu_seqlens, chunk, out, hT, ws, gdr::kScratchBytes, dims, stream);
+}
+
 int64_t gdr_gdn2_chunk_fwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t chunk, int32_t packed) {
     if (!dims) return -1;
     return gdn2_ws_bytes(*dims, chunk, packed != 0);

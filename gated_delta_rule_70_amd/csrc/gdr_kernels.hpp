@@ -115,4 +115,9 @@ __device__ __forceinline__ float gate_beta(float b) { return __builtin_amdgcn_rc
 
 hipError_t launch_selftest_mfma(const float *a, const float *b, float *d, hipStream_t stream);
 
+// Size of the fixed device scratch of the allocation-free entry points (one copy per GPU).
+constexpr int64_t kScratchBytes = INT64_C(64) << 20;
+// Its device address on the current device (looked up on the first call per device).
+hipError_t scratch_region(void **ptr);
+
 }  // namespace gdr

@@ -313,6 +313,29 @@ gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                                 const gdr_chunk_dims_t *dims, void *stream);
 
 /*
+ * gdr_gdn2_chunk_fwd_noalloc - gdr_gdn2_chunk_fwd in its two-pass form without a caller
+ * workspace and without allocating: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, results and errors as gdr_gdn2_chunk_fwd with workspace = NULL replaced by the
+ * library's fixed device scratch of GDR_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU: a static array of
+ * the library's code object, held by each GPU from the library's first launch there until the
+ * process ends. Sizes whose workspace (gdr_gdn2_chunk_fwd_workspace_bytes) exceeds it are
+ * rejected with GDR_ERR_DIMS before anything runs (for bf16, d_k = 128 and chunk 32 that is about
+ * 2,300 (chunk, key head) blocks, e.g. B = 1, Hk = 16, T = 4096). The call allocates nothing and
+ * keeps the scratch's device address per device. All calls on one GPU share the scratch: calls
+ * that overlap in time on the same GPU (other streams or host threads) race on it and must be
+ * serialised by the caller. The scratch needs no clearing (the first pass writes every byte the
+ * second reads). The device is the current HIP device, which must own the stream.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES (INT64_C(64) << 20)
+gdr_status_t gdr_gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                        const float *g, const void *b, const void *w,
+                                        const float *h0, const int32_t *cu_seqlens, int32_t chunk,
+                                        void *out, float *hT,
+                                        const gdr_chunk_dims_t *dims, void *stream);
+
+/*
  * gdr_gdn2_chunk_fwd_workspace_bytes - bytes of workspace gdr_gdn2_chunk_fwd's two-pass form
  * needs for these sizes, chunk and packing (packed != 0: cu_seqlens with dims->num_seqs
  * sequences). Host-only arithmetic: one slot per chunk of every sequence (packed: T / chunk +

@@ -307,3 +307,19 @@ def test_backward_rejects():
     ckpt = 16 * 4 * 128 * 128 * 128 * 4
     parts = 4 * 16 * 4 * 4096 * (2 * 128 + 2) * 4
     assert lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), 0) == ckpt + parts
+
+
+@needs_lib
+def test_gdn2_noalloc_rejects_beyond_its_scratch():
+    # sizes whose two-pass workspace exceeds the fixed 64 MiB scratch are refused before anything
+    # runs (B4 H16 T4096 d128 bf16, chunk 32, needs 239 MB); no GPU is touched on the way
+    lib = binding.load()
+    dims = binding.ChunkDims(4, 4096, 16, 16, 128, 128, 0, 1, 0)
+    assert lib.gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), 32, 0) > (64 << 20)
+    vp = ctypes.c_void_p
+    st = lib.gdr_gdn2_chunk_fwd_noalloc(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5),
+                                        vp(FAKE * 6), None, None, 32, vp(FAKE * 7), None, ctypes.byref(dims), None)
+    msg = lib.gdr_last_error().decode()
+    assert binding.STATUS[st] == "GDR_ERR_DIMS" and "allocation-free" in msg, msg
+    assert lib.gdr_gdn2_chunk_fwd_noalloc(None, None, None, None, None, None, None, None, 32, None, None,
+                                          None, None) == 1  # dims NULL: GDR_ERR_NULL
