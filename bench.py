@@ -46,6 +46,26 @@ def chunk_flops(B, H, T, dk, dv, C=64):
     return B * H * T * per
 
 
+# Matrix-core instructions the fast chunk kernel issues per workgroup and 64-token chunk (one
+# workgroup per sequence-head and 32 value columns), counted from its source:
+#   two chain waves, each 16 x16x32 (K H) + 16 (Q H) + 16 (state update) + 6 (P U) + 2
+#   (substitution) = 56, and 6 x16x16 (substitution) -> 112 and 12;
+#   diagonal prep 16 x16x32 (Gram tiles) and 36 x16x16 (inverses); off-diagonal -A 24 x16x32;
+#   P tiles 40 x16x32.
+# That is 192 v_mfma_f32_16x16x32_bf16 (16,384 flops) and 48 v_mfma_f32_16x16x16_bf16 (8,192
+# flops); the matrix-core counters agree (SQ_INSTS_MFMA = 240 per workgroup-chunk).
+FAST_MFMA32_PER_WG_CHUNK = 192
+FAST_MFMA16_PER_WG_CHUNK = 48
+
+
+def chunk_flops_executed(B, H, T, dv, C=64):
+    """Flops the fast kernel's matrix cores execute per launch (whole triangular tiles, the
+    products that build the diagonal inverses): instructions per workgroup-chunk x workgroups x
+    chunks."""
+    wg_chunks = B * H * (dv // 32) * ((T + C - 1) // C)
+    return wg_chunks * (FAST_MFMA32_PER_WG_CHUNK * 16384 + FAST_MFMA16_PER_WG_CHUNK * 8192)
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
 
@@ -91,22 +111,73 @@ def copy_calibration(mib=1024, reps=3):
     print(json.dumps({"copy_calibration_bytes_each_way": mib * (1 << 20), "launches": reps}), flush=True)
 
 
-def timed(fn, steps, warmup, stream):
-    """Mean time per call in ms: HIP events on the launch stream around `steps` back-to-back
-    calls (after `warmup` untimed ones), bracketed by device synchronisation."""
+SETTLE_MS = 150.0  # untimed back-to-back calls before the warm-up, until the clock is steady
+
+
+def settle(fn, stream, ms=SETTLE_MS):
+    """Untimed back-to-back calls for about `ms` of GPU time: the GPU takes tens of milliseconds
+    of sustained work to reach its steady clock (with only a few warm-up calls the chunked
+    forward times 10-20% slower)."""
     import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done, n = 0.0, 1
+    while done < ms:
+        start.record(stream)
+        for _ in range(n):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        done += start.elapsed_time(end)
+        n = min(n * 2, 4096)
+    return done
+
+
+def timed(fn, steps, warmup, stream, settle_ms=SETTLE_MS):
+    """Per-call times in ms: a HIP event pair on the launch stream around each of `steps`
+    back-to-back calls (after the clock settles and `warmup` untimed calls), the whole timed
+    region bracketed by device synchronisation. Returns (median, mean of the bracket, wall s)."""
+    import torch
+    if settle_ms > 0:
+        settle(fn, stream, settle_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    for a, b in ev:
+        a.record(stream)
         fn()
-    end.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / steps, wall
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = ev[0][0].elapsed_time(ev[-1][1]) / steps
+    return per[len(per) // 2], mean, wall
+
+
+def measured_peaks(reps=10):
+    """What this GPU reaches on plain library work, beside the published peaks: a 1 GiB
+    device-to-device copy (bytes read + written per second) and a dense bf16 GEMM
+    (8192 x 8192 x 8192, torch.matmul -> hipBLASLt). Medians of `reps` timed calls."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    med, _, _ = timed(lambda: dst.copy_(src), reps, 3, stream, settle_ms=50.0)
+    copy_gbs = 2 * n * 4 / (med / 1e3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    med, _, _ = timed(lambda: torch.matmul(a, b, out=c), reps, 3, stream, settle_ms=50.0)
+    gemm_tflops = 2 * m ** 3 / (med / 1e3) / 1e12
+    del a, b, c
+    return {"hbm_copy_GBs": copy_gbs, "bf16_gemm_TFLOPs": gemm_tflops,
+            "how": "median of %d calls: a 1 GiB device copy (read + written bytes) and an 8192^3 bf16 "
+                   "torch.matmul (hipBLASLt)" % reps}
 
 
 def bench_chunk(binding, inputs, steps, warmup):
@@ -119,11 +190,12 @@ def bench_chunk(binding, inputs, steps, warmup):
     hT = torch.empty_like(h0)
     stream = torch.cuda.current_stream(dev)
     fn = lambda: binding.chunk_fwd(q, k, v, la, b, h0, None, chunk=64, out=out, hT=hT)
-    ms, wall = timed(fn, steps, warmup, stream)
+    ms, mean, wall = timed(fn, steps, warmup, stream)
     B, H, T, dk = case.q.shape
     dv = case.v.shape[-1]
-    return dict(ms=ms, wall=wall, tokens=B * T, bytes=chunk_bytes(B, H, T, dk, dv, 2, B),
-                flops=chunk_flops(B, H, T, dk, dv), shape=(B, H, T, dk, dv))
+    return dict(ms=ms, mean_ms=mean, wall=wall, tokens=B * T, bytes=chunk_bytes(B, H, T, dk, dv, 2, B),
+                flops=chunk_flops(B, H, T, dk, dv), flops_exec=chunk_flops_executed(B, H, T, dv),
+                shape=(B, H, T, dk, dv))
 
 
 def bench_decode(binding, inputs, reps):
@@ -135,22 +207,28 @@ def bench_decode(binding, inputs, reps):
     state = dc.state.to(dev)
     out = torch.empty((steps,) + tuple(dc.v.shape[1:]), dtype=dc.v.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
-    # one warm pass of the 64 steps, then `reps` timed passes (state keeps evolving in place)
+    # the clock settles and one warm pass of the 64 steps runs, then `reps` timed passes of the 64
+    # consecutive steps (the state keeps evolving in place), an event pair around every step
+    settle(lambda: binding.decode_step(q[0], k[0], v[0], la[0], b[0], state, state_out=state, out=out[0]), stream)
     for s in range(steps):
         binding.decode_step(q[s], k[s], v[s], la[s], b[s], state, state_out=state, out=out[s])
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps * reps)]
+    i = 0
     for r in range(reps):
         for s in range(steps):
+            ev[i][0].record(stream)
             binding.decode_step(q[s], k[s], v[s], la[s], b[s], state, state_out=state, out=out[s])
-    end.record(stream)
+            ev[i][1].record(stream)
+            i += 1
     torch.cuda.synchronize()
-    mean = start.elapsed_time(end) / (steps * reps)
+    mean = ev[0][0].elapsed_time(ev[-1][1]) / (steps * reps)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    median = per[len(per) // 2]
     N, Hv, dk, dv = dc.state.shape
     sbytes = 2 * N * Hv * dk * dv * 4
     io = (dc.q[0].numel() * 2 + dc.v[0].numel()) * 2 + N * Hv * 2 * 4 + N * Hv * dv * 2
-    return dict(ms=mean, state_bytes=sbytes, io_bytes=io, tokens=N, steps=steps * reps)
+    return dict(ms=mean, median_ms=median, state_bytes=sbytes, io_bytes=io, tokens=N, steps=steps * reps)
 
 
 def bench_varlen(binding, inputs, steps):
@@ -161,7 +239,7 @@ def bench_varlen(binding, inputs, steps):
     la, b, h0, cu = case.log_alpha.to(dev), case.beta.to(dev), case.h0.to(dev), case.cu_seqlens.to(dev)
     out, hT = torch.empty_like(v), torch.empty_like(h0)
     fn = lambda: binding.chunk_fwd(q, k, v, la, b, h0, cu, chunk=64, out=out, hT=hT)
-    ms, _ = timed(fn, steps, 200, torch.cuda.current_stream(dev))
+    ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
     T = case.q.shape[2]
     H, dk, dv = case.q.shape[1], case.q.shape[3], case.v.shape[3]
     nseq = case.cu_seqlens.numel() - 1
@@ -180,7 +258,7 @@ def bench_fused(binding, inputs, steps):
     q, k, v, a, b, A_log, dtb, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, c.h0))
     out, hT = torch.empty_like(v), torch.empty_like(h0)
     fn = lambda: binding.chunk_fwd_gated(q, k, v, a, b, A_log, dtb, h0, chunk=64, out=out, hT=hT, l2norm=True)
-    ms, _ = timed(fn, steps, 300, torch.cuda.current_stream(dev))
+    ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
     return dict(ms=ms, tokens=4 * 4096)
 
 
@@ -198,7 +276,7 @@ def bench_bidir(binding, inputs, steps):
         binding.chunk_fwd(q, k, v, la2, b2, None, cu, chunk=64, read="pre", reverse=True, out=out,
                           accumulate=True, want_state=False)
 
-    ms, _ = timed(fn, steps, 200, torch.cuda.current_stream(dev))
+    ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
     return dict(ms=ms, tokens=case.q.shape[2])
 
 
@@ -221,10 +299,10 @@ def bench_gdn2(binding, inputs, steps):
     ws = torch.empty(binding.gdn2_chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, 32), dtype=torch.uint8,
                      device=dev)
     fn = lambda: binding.gdn2_chunk_fwd(q, k, v, g, b, w, h0, chunk=32, out=out, hT=hT, workspace=ws)
-    ms, _ = timed(fn, steps, 50, torch.cuda.current_stream(dev))
+    ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
     # the one-pass kernel (no workspace) on the same inputs, for reference
     fn1 = lambda: binding.gdn2_chunk_fwd(q, k, v, g, b, w, h0, chunk=32, out=out, hT=hT, fused=True)
-    ms1, _ = timed(fn1, max(3, steps // 4), 5, torch.cuda.current_stream(dev))
+    ms1, _, _ = timed(fn1, max(3, steps // 4), 3, torch.cuda.current_stream(dev), settle_ms=20.0)
     chunk = dict(ms=ms, fused_ms=ms1, ws_bytes=ws.numel(), tokens=4 * 4096,
                  bytes=gdn2_bytes(4, 16, 16, 4096, 128, 128, 2, 4))
     del q, k, v, g, b, w, h0, out, hT, ws
@@ -235,7 +313,7 @@ def bench_gdn2(binding, inputs, steps):
     state = dc.h0.to(dev)
     dout = torch.empty((N, Hv, 128), dtype=torch.bfloat16, device=dev)
     fn = lambda: binding.gdn2_decode_step(dq, dk_, dv_, dg, db, dw, state, state_out=state, out=dout)
-    dms, _ = timed(fn, max(steps, 64), 300, torch.cuda.current_stream(dev))
+    dms, _, _ = timed(fn, max(steps, 64), 20, torch.cuda.current_stream(dev))
     sbytes = 2 * N * Hv * 128 * 128 * 4
     io = N * Hk * 128 * (3 * 2 + 4) + N * Hv * 128 * 3 * 2
     return chunk, dict(ms=dms, state_bytes=sbytes, io_bytes=io, tokens=N)
@@ -251,7 +329,7 @@ def bench_delta_product(binding, inputs, steps):
     q, k, v, la, b, h0 = (t.to(dev) for t in (c.q, c.k, c.v, c.log_alpha, c.beta, c.h0))
     out, hT = torch.empty((4, 16, 4096, 128), dtype=torch.bfloat16, device=dev), torch.empty_like(h0)
     fn = lambda: binding.delta_product_fwd(q, k, v, la, b, h0, chunk=64, read="pre", out=out, hT=hT)
-    ms, _ = timed(fn, steps, 100, torch.cuda.current_stream(dev))
+    ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
     tok = 4 * 16 * 4096
     nbytes = tok * 128 * 2 * (1 + 2 + 2 + 1) + tok * 4 * (1 + 2) + 2 * 4 * 16 * 128 * 128 * 4
     return dict(ms=ms, tokens=4 * 4096, bytes=nbytes)
@@ -269,55 +347,119 @@ def bench_backward(binding, inputs, steps):
     dhT = torch.randn(tuple(c.h0.shape), generator=g).to(dev)
     ws = torch.empty(binding.chunk_bwd_workspace_bytes(4, 4096, 16, 16, 128, 128), dtype=torch.uint8, device=dev)
     fn = lambda: binding.chunk_bwd(q, k, v, la, b, dout, h0, None, dhT, workspace=ws)
-    ms, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev))
+    ms, _, _ = timed(fn, steps, 2, torch.cuda.current_stream(dev), settle_ms=20.0)
     tok = 4 * 16 * 4096
     # inputs, dout read once; gradients written once (dq, dk, dv fp32); h0, dhT, dh0
     nbytes = tok * 128 * 2 * 4 + tok * 4 * 4 + tok * 128 * 4 * 3 + 3 * 4 * 16 * 128 * 128 * 4
     return dict(ms=ms, tokens=4 * 4096, bytes=nbytes, ws_bytes=ws.numel())
 
 
-def cpu_baseline(inputs, min_wall=1.5, max_reps=20):
-    """The fp64 oracle, as it is, on this host's cores: the whole B4 H16 T4096 d128 workload,
-    repeated until at least `min_wall` seconds have passed (a bounded sample)."""
-    import oracle
-    case = inputs.workload1()
-    threads = min(len(os.sched_getaffinity(0)), 64)
-    import numpy as np
-    args = [np.ascontiguousarray(t.double().numpy()) for t in
-            (case.q, case.k, case.v, case.log_alpha, case.beta, case.h0)]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.scan(*args, threads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_wall or reps >= max_reps:
-            break
-    tokens = case.q.shape[0] * case.q.shape[2] * reps
-    cpu_model = ""
+def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
+    return ""
+
+
+def _f64(*ts):
+    import numpy as np
+    return [None if t is None else np.ascontiguousarray(t.double().numpy()) for t in ts]
+
+
+def _repeat(fn, min_wall, max_reps):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_wall or reps >= max_reps:
+            return reps, dt
+
+
+def cpu_baseline(inputs, min_wall=1.5, max_reps=20):
+    """The fp64 oracle, as it is, on this host's cores: the whole B4 H16 T4096 d128 workload,
+    repeated until at least `min_wall` seconds have passed (a bounded sample). Inputs are
+    upcast before the clock starts."""
+    import oracle
+    case = inputs.workload1()
+    threads = min(len(os.sched_getaffinity(0)), 64)
+    args = _f64(case.q, case.k, case.v, case.log_alpha, case.beta, case.h0)
+    reps, dt = _repeat(lambda: oracle.scan(*args, threads=threads), min_wall, max_reps)
+    tokens = case.q.shape[0] * case.q.shape[2] * reps
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "the whole B4 H16 T4096 d128 workload (64 sequence-heads) %d times, fp64 "
                       "per-token recurrence, %.1f s wall on %d threads; CPU: %s"
-                      % (reps, dt, threads, cpu_model)}
+                      % (reps, dt, threads, _cpu_model())}
+
+
+def cpu_baseline_other(inputs, min_wall=1.0):
+    """The same oracle beside the other workloads, each a bounded sample on the same threads:
+    decode (consecutive fp64 steps over all 256 x 32 head-states, state GB/s counted with the
+    fp32 state's bytes read + written; the fp64 oracle moves twice that), the packed
+    variable-length workload and the bidirectional workload (both whole)."""
+    import oracle
+    threads = min(len(os.sched_getaffinity(0)), 64)
+    res = {}
+    dc = inputs.workload3(steps=16)
+    q, k, v, la, b, st = _f64(dc.q, dc.k, dc.v, dc.log_alpha, dc.beta, dc.state)
+    box = {"state": st, "step": 0}
+
+    def one():
+        s = box["step"] % q.shape[0]
+        _, box["state"] = oracle.decode(q[s], k[s], v[s], la[s], b[s], box["state"], threads=threads)
+        box["step"] += 1
+    reps, dt = _repeat(one, min_wall, 64)
+    N, Hv, dk, dv = dc.state.shape
+    sbytes = 2 * N * Hv * dk * dv * 4
+    res[inputs.WORKLOADS[3]] = {"value": sbytes * reps / dt / 1e9, "unit": "state GB/s", "cores": threads,
+                                "kind": "oracle", "sample": "%d consecutive decode steps, %.1f s wall" % (reps, dt)}
+    c2 = inputs.workload2()
+    args = _f64(c2.q, c2.k, c2.v, c2.log_alpha, c2.beta, c2.h0)
+    reps, dt = _repeat(lambda: oracle.scan(*args, c2.cu_seqlens, threads=threads), min_wall, 4)
+    res[inputs.WORKLOADS[2]] = {"value": c2.q.shape[2] * reps / dt, "unit": "tokens/s", "cores": threads,
+                                "kind": "oracle", "sample": "the whole packed workload %d times, %.1f s wall" % (reps, dt)}
+    c4 = inputs.workload4()
+    q, k, v, la, b, la2, b2 = _f64(c4.q, c4.k, c4.v, c4.log_alpha, c4.beta, c4.extra["log_alpha_bwd"],
+                                   c4.extra["beta_bwd"])
+
+    def both():
+        oracle.scan(q, k, v, la, b, None, c4.cu_seqlens, read="pre", want_state=False, threads=threads)
+        oracle.scan(q, k, v, la2, b2, None, c4.cu_seqlens, read="pre", reverse=True, want_state=False,
+                    threads=threads)
+    reps, dt = _repeat(both, min_wall, 4)
+    res[inputs.WORKLOADS[4]] = {"value": c4.q.shape[2] * reps / dt, "unit": "tokens/s", "cores": threads,
+                                "kind": "oracle", "sample": "both scans of the whole workload %d times, %.1f s wall" % (reps, dt)}
+    return res
+
+
+def bench_many_segments(binding, inputs, steps):
+    """Packed input of 2048 short segments (lengths U{16..48}), H16 d128 bf16, chunk 64, per-segment
+    h0: each workgroup ranks the segments by length before its first chunk."""
+    import torch
+    lengths = inputs.segment_lengths(2048, 16, 48, seed=4242)
+    case = inputs.chunk_case(Hk=16, dk=128, dv=128, dtype=torch.bfloat16, seed=1005, h0_std=0.1, lengths=lengths)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (case.q, case.k, case.v))
+    la, b, h0, cu = case.log_alpha.to(dev), case.beta.to(dev), case.h0.to(dev), case.cu_seqlens.to(dev)
+    out, hT = torch.empty_like(v), torch.empty_like(h0)
+    fn = lambda: binding.chunk_fwd(q, k, v, la, b, h0, cu, chunk=64, out=out, hT=hT)
+    ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
+    T = case.q.shape[2]
+    return dict(ms=ms, tokens=T, bytes=chunk_bytes(1, 16, T, 128, 128, 2, len(lengths)))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # untimed calls before the timed ones: the GPU takes tens of milliseconds of sustained work
-    # to reach its steady clock (with 50 warmup calls, about 5 ms, the chunked forward still
-    # timed 16% slower than with 300); 500 calls are about 50 ms
-    ap.add_argument("--warmup", type=int, default=500)
+    # untimed calls before the timed ones (after the clock-settling phase, see settle())
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / GEMM peaks")
     ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "dp", "all"], default="all",
                     help="gdn2, bwd, dp: only the GDN-2 workloads, the backward or DeltaProduct (for "
                          "profiling them)")
@@ -364,19 +506,39 @@ def main():
                      "chunk": 64, "read": "post", "h0": "N(0, 0.1)", "inputs": "bf16 q/k/v, fp32 gates/state"}
     gbs = c["bytes"] / (c["ms"] / 1e3) / 1e9
     tflops = c["flops"] / (c["ms"] / 1e3) / 1e12
+    res["ms_per_step_mean"] = c["mean_ms"]
+    res["timing"] = ("median of per-call HIP event pairs on the launch stream over the %d timed calls "
+                     "(ms_per_step_mean: the bracket of all of them / %d), after %.0f ms of untimed "
+                     "calls that bring the clock to its steady state and %d warm-up calls"
+                     % (args.steps, args.steps, SETTLE_MS, args.warmup))
+    tflops_exec = c["flops_exec"] / (c["ms"] / 1e3) / 1e12
     res["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": gbs / HBM_PEAK_GBS,
                        "traffic": measured_traffic("chunk_fwd_fast_B4_H16_T4096_d128_hbm_traffic.md",
                                                    "chunk_fwd_fast.hip", "HBM bytes per launch"),
                        "kernel": "chunk_fwd_fast_kernel", "bytes_per_launch": c["bytes"],
                        "mfma": {"achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": c["flops"]}}
+                                "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": c["flops"],
+                                "count": "algorithmic",
+                                "executed": {"achieved": tflops_exec, "frac": tflops_exec / BF16_PEAK_TFLOPS,
+                                             "flops_per_launch": c["flops_exec"],
+                                             "count": "executed (whole triangular tiles, the inverses' "
+                                                      "products; 192 x16x32 + 48 x16x16 bf16 MFMAs per "
+                                                      "workgroup-chunk)"}}}
+    if not args.no_peaks:
+        print("[bench] measured peaks (copy, bf16 GEMM) ...", file=sys.stderr, flush=True)
+        mp = measured_peaks()
+        res["roofline"]["measured_peak"] = mp
+        res["roofline"]["frac_of_measured"] = gbs / mp["hbm_copy_GBs"]
+        res["roofline"]["mfma"]["frac_of_measured"] = tflops / mp["bf16_gemm_TFLOPs"]
+        res["roofline"]["mfma"]["executed"]["frac_of_measured"] = tflops_exec / mp["bf16_gemm_TFLOPs"]
     if args.only in ("all", "decode"):
         print("[bench] decode 64 steps N256 Hv32 d128 ...", file=sys.stderr, flush=True)
         d = bench_decode(binding, inputs, reps=2)
         sgbs = d["state_bytes"] / (d["ms"] / 1e3) / 1e9
         res["decode"] = {"metric": "decode-step state GB/s", "value": sgbs, "unit": "GB/s",
-                         "us_per_step": d["ms"] * 1e3,
+                         "us_per_step": d["ms"] * 1e3, "us_per_step_median": d["median_ms"] * 1e3,
+                         "state_GBs_at_median": d["state_bytes"] / (d["median_ms"] / 1e3) / 1e9,
                          "tokens_per_s": d["tokens"] / (d["ms"] / 1e3),
                          "workload": inputs.WORKLOADS[3],
                          "roofline": {"bound": "hbm", "achieved": (d["state_bytes"] + d["io_bytes"]) / (d["ms"] / 1e3) / 1e9,
@@ -385,9 +547,13 @@ def main():
                                       "kernel": "decode_kernel<bf16, 128, 128>",
                                       "traffic": measured_traffic("decode_N256_Hv32_d128_hbm_traffic.md",
                                                                   "decode.hip", "HBM bytes per step")}}
+        if "measured_peak" in res["roofline"]:
+            res["decode"]["roofline"]["frac_of_measured"] = (res["decode"]["roofline"]["achieved"] /
+                                                            res["roofline"]["measured_peak"]["hbm_copy_GBs"])
     if args.only == "all":
         print("[bench] packed variable-length and bidirectional workloads ...", file=sys.stderr, flush=True)
         vl = bench_varlen(binding, inputs, max(3, args.steps // 4))
+        ms_ = bench_many_segments(binding, inputs, max(3, args.steps // 4))
         bd = bench_bidir(binding, inputs, max(3, args.steps // 4))
         fu = bench_fused(binding, inputs, max(3, args.steps // 4))
         g2, g2d = bench_gdn2(binding, inputs, max(3, args.steps // 8))
@@ -397,6 +563,10 @@ def main():
             inputs.WORKLOADS[2]: {"tokens_per_s": vl["tokens"] / (vl["ms"] / 1e3), "ms": vl["ms"],
                                   "hbm_frac": vl["bytes"] / (vl["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                                   "lengths": vl["lengths"]},
+            "gdr-varlen-bf16-2048seg-16..48-H16-d128-c64": {
+                "tokens_per_s": ms_["tokens"] / (ms_["ms"] / 1e3), "ms": ms_["ms"],
+                "hbm_frac": ms_["bytes"] / (ms_["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "note": "2048 short packed segments (beyond 128 segments the kernel keeps their order)"},
             "gdr-chunk-fwd-fused-prologue-bf16-B4-H16-T4096-d128-c64": {
                 "tokens_per_s": fu["tokens"] / (fu["ms"] / 1e3), "ms": fu["ms"],
                 "prologue": "q/k rows normalised and gates formed from raw inputs in the kernel"},
@@ -414,7 +584,7 @@ def main():
             "delta-product-n2-pre-bf16-B4-H16-T4096-d128-c64": {
                 "tokens_per_s": dpr["tokens"] / (dpr["ms"] / 1e3), "ms": dpr["ms"],
                 "hbm_frac": dpr["bytes"] / (dpr["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                "kernel": "chunk_fwd_kernel<bf16, 64, 128> over 2 sub-steps per token"},
+                "kernel": "chunk_fwd_fast_kernel<false> over 2 sub-steps per token"},
             "gdr-backward-bf16-B4-H16-T4096-d128": {
                 "tokens_per_s": bwr["tokens"] / (bwr["ms"] / 1e3), "ms": bwr["ms"],
                 "hbm_frac": bwr["bytes"] / (bwr["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -432,6 +602,8 @@ def main():
     if not args.no_cpu:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inputs)
+        if args.only == "all":
+            res["cpu_baseline_other"] = cpu_baseline_other(inputs)
     print(json.dumps(res), flush=True)
 
 

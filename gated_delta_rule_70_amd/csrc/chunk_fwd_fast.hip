@@ -86,12 +86,13 @@ constexpr int kOffRaw = 0;
 constexpr int kOffDer = kOffRaw + 3 * kRawBytes;
 constexpr int kOffStage = kOffDer + 2 * kDerBytes;  // output staging, two of [32 cols][64 rows] bf16
 constexpr int kStageBytes = 4096;
-constexpr int kSortMax = 2 * kStageBytes / 4 - 2;  // segments ranked by length in the staging area
+constexpr int kSortMax = 128;  // packed segments ranked by length (beyond, the order is kept)
 // with accumulation, the output's previous values of a chunk, copied in like the V slice
 constexpr int kOffPrev = kOffStage + 2 * kStageBytes;
 constexpr int kPrevBytes = 4096;
 constexpr int kSmemBytes = kOffPrev + 2 * kPrevBytes;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
+static_assert((kSortMax + 2) * 4 <= kRawBytes, "segment offsets fit in a raw slot");
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
@@ -719,12 +720,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
     const int64_t head = unit % a.Hv;
     const int64_t kh = head / (a.Hv / a.Hk);
     // Packed segments are taken longest first: unit ranks are dispatched in order, so the
-    // workgroups of long segments start early and short ones fill in at the end. Rank r
-    // goes to the segment with r longer segments before it (ties by index).
+    // workgroups of long segments start early and short ones fill in at the end (this is what
+    // balances a few long segments of unequal length). Rank r goes to the segment with r longer
+    // segments before it (ties by index), counted by the first nseq threads over all segments in
+    // LDS: nseq^2 / 512 steps per thread, well under a microsecond up to kSortMax segments. With
+    // more segments every workgroup is short and the order is kept as given.
     if (a.cu_seqlens) {
         const int nseq = (int)(a.units / a.Hv);
         if (nseq <= kSortMax) {
-            int *cu = reinterpret_cast<int *>(smem + kOffStage);  // unused until the first chunk
+            int *cu = reinterpret_cast<int *>(smem + kOffRaw + 2 * kRawBytes);  // unused until chunk 2 is copied
             for (int i = tid; i <= nseq; i += kThreads) cu[i] = a.cu_seqlens[i];
             __syncthreads();
             const int rank = (int)seq;

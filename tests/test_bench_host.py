@@ -46,3 +46,12 @@ def test_measured_traffic_checks_the_source(tmp_path, monkeypatch):
     assert bench.measured_traffic("t.md", "k.hip", "HBM bytes per launch") == 123456.0
     assert bench.measured_traffic("old.md", "k.hip", "HBM bytes per launch") is None
     assert bench.measured_traffic("missing.md", "k.hip", "HBM bytes per launch") is None
+
+
+def test_executed_mfma_count_matches_the_counter_summary():
+    # 240 matrix-core instructions per workgroup-chunk (SQ_INSTS_MFMA / (256 workgroups x 64 chunks)
+    # in the committed counter summary), 58 GFLOP per launch of the B4 H16 T4096 d128 workload
+    assert bench.FAST_MFMA32_PER_WG_CHUNK + bench.FAST_MFMA16_PER_WG_CHUNK == 240
+    ex = bench.chunk_flops_executed(4, 16, 4096, 128)
+    assert abs(ex - 1.132e8 * 512) / ex < 0.01
+    assert ex > bench.chunk_flops(4, 16, 4096, 128, 128)

@@ -185,10 +185,10 @@ def test_chunk_fwd_reverse_and_varlen(gdr, dtype, read):
         check(hT, rh, dtype, "varlen hT")
 
 
-@pytest.mark.parametrize("nseg", [40, 2100])
+@pytest.mark.parametrize("nseg", [40, 128, 129, 2100])
 def test_chunk_fwd_many_segments(gdr, nseg):
-    """Many packed segments of mixed lengths (the fast kernel ranks up to a few thousand of
-    them by length; beyond that it keeps their order)."""
+    """Many packed segments of mixed lengths (the fast kernel ranks up to 128 of them by
+    length; beyond that it keeps their order)."""
     g = torch.Generator().manual_seed(nseg)
     hi = 200 if nseg < 100 else 4
     lengths = torch.randint(0, hi, (nseg,), generator=g).tolist()
