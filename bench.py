@@ -114,11 +114,12 @@ def copy_calibration(mib=1024, reps=3):
 SETTLE_MS = 150.0  # untimed back-to-back calls before the warm-up, until the clock is steady
 
 
-def settle(fn, stream, ms=SETTLE_MS):
+def settle(fn, stream, ms=None):
     """Untimed back-to-back calls for about `ms` of GPU time: the GPU takes tens of milliseconds
     of sustained work to reach its steady clock (with only a few warm-up calls the chunked
     forward times 10-20% slower)."""
     import torch
+    ms = SETTLE_MS if ms is None else ms
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     done, n = 0.0, 1
     while done < ms:
@@ -132,11 +133,12 @@ def settle(fn, stream, ms=SETTLE_MS):
     return done
 
 
-def timed(fn, steps, warmup, stream, settle_ms=SETTLE_MS):
+def timed(fn, steps, warmup, stream, settle_ms=None):
     """Per-call times in ms: a HIP event pair on the launch stream around each of `steps`
     back-to-back calls (after the clock settles and `warmup` untimed calls), the whole timed
     region bracketed by device synchronisation. Returns (median, mean of the bracket, wall s)."""
     import torch
+    settle_ms = SETTLE_MS if settle_ms is None else min(settle_ms, SETTLE_MS)
     if settle_ms > 0:
         settle(fn, stream, settle_ms)
     for _ in range(warmup):
@@ -453,6 +455,7 @@ def bench_many_segments(binding, inputs, steps):
 
 
 def main():
+    global SETTLE_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -460,12 +463,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / GEMM peaks")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed GPU time before the warm-up of each workload (0 for counter runs)")
     ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "dp", "all"], default="all",
                     help="gdn2, bwd, dp: only the GDN-2 workloads, the backward or DeltaProduct (for "
                          "profiling them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
+    SETTLE_MS = max(0.0, args.settle_ms)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every workload here runs on a single MI355X "
               "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
