@@ -44,6 +44,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdr_kernels.hpp"
 #include "gdr_mfma.hpp"
 #include "gdr_solve.hpp"
@@ -98,7 +100,9 @@ struct alignas(16) Smem {
 // The products run as three bf16 products of split operands (x = hi + lo, hi = bf16(x),
 // lo = bf16(x - hi)): hi*hi + hi*lo + lo*hi, accumulated in fp32. The dropped lo*lo term and the
 // rounding of lo leave a relative error near 2^-16 per product, and three 16x16x32 bf16 products
-// take a sixth of the matrix-core time of the eight 16x16x4 fp32 ones they replace.
+// take a sixth of the matrix-core time of the eight 16x16x4 fp32 ones they replace. An operand
+// known to hold bf16 values exactly (AX, BX: q, k, v or dout of a bf16 call, staged in LDS as
+// fp32) has lo = 0, so its lo products are skipped: two products, or one when both are exact.
 __device__ __forceinline__ void split_bf16(const floatx4 &x, bf16x4 &hi, bf16x4 &lo) {
     hi = cvt4<__bf16>(x);
     floatx4 r;
@@ -106,19 +110,29 @@ __device__ __forceinline__ void split_bf16(const floatx4 &x, bf16x4 &hi, bf16x4 
     for (int i = 0; i < 4; ++i) r[i] = x[i] - (float)hi[i];
     lo = cvt4<__bf16>(r);
 }
-template <int KD, bool AT, bool BT>
+template <int KD, bool AT, bool BT, bool AX = false, bool BX = false>
 __device__ __forceinline__ floatx4 mm(floatx4 acc, const float *X, int ldx, int m0, const float *Y, int ldy, int n0) {
 #pragma unroll
     for (int k0 = 0; k0 < KD; k0 += 32) {
         const Frag<float> fa = AT ? frag_cols<float>(X, ldx, m0, k0) : frag_rows<float>(X, ldx, m0, k0);
         const Frag<float> fb = BT ? frag_rows<float>(Y, ldy, n0, k0) : frag_cols<float>(Y, ldy, n0, k0);
         Frag<__bf16> ah, al, bh, bl;
-        split_bf16(fa.lo, ah.lo, al.lo);
-        split_bf16(fa.hi, ah.hi, al.hi);
-        split_bf16(fb.lo, bh.lo, bl.lo);
-        split_bf16(fb.hi, bh.hi, bl.hi);
-        acc = mma32(acc, al, bh);
-        acc = mma32(acc, ah, bl);
+        if constexpr (AX) {
+            ah.lo = cvt4<__bf16>(fa.lo);
+            ah.hi = cvt4<__bf16>(fa.hi);
+        } else {
+            split_bf16(fa.lo, ah.lo, al.lo);
+            split_bf16(fa.hi, ah.hi, al.hi);
+        }
+        if constexpr (BX) {
+            bh.lo = cvt4<__bf16>(fb.lo);
+            bh.hi = cvt4<__bf16>(fb.hi);
+        } else {
+            split_bf16(fb.lo, bh.lo, bl.lo);
+            split_bf16(fb.hi, bh.hi, bl.hi);
+        }
+        if constexpr (!AX) acc = mma32(acc, al, bh);
+        if constexpr (!BX) acc = mma32(acc, ah, bl);
         acc = mma32(acc, ah, bh);
     }
     return acc;
@@ -141,6 +155,8 @@ template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     typedef Smem<DK> SM;
     __shared__ SM sm;
+    // q, k, v and dout of a bf16 call are staged in LDS as fp32 but hold bf16 values exactly
+    constexpr bool kX = std::is_same<E, __bf16>::value;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int g = lane >> 4, cc = lane & 15;
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         for (int task = wave; task < (adjoint ? 10 : 7); task += kWaves) {
             if (task < 4) {
                 const int mt = task >> 1, nt = task & 1;
-                const floatx4 x = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+                const floatx4 x = mm<DK, false, false, kX>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sm.X[16 * mt + 4 * g + r][16 * nt + cc] = x[r];
                 continue;
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             const int t = task - 4;
             const bool isp = t >= 3;
             const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
-            const floatx4 v = mm<DK, false, true>(zero4(), isp ? &sm.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt,
+            const floatx4 v = mm<DK, false, true, kX, kX>(zero4(), isp ? &sm.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt,
                                                   &sm.K[0][0], SM::KP, 16 * nt);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -356,8 +372,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             if (tile >= 0) {
                 const float blast = sm.b[CB - 1];
                 const int mt = tile >> 1, nt = tile & 1;
-                const floatx4 kd = mm<DK, false, false>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
-                const floatx4 pd = mm<CB, true, false>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
+                const floatx4 kd = mm<DK, false, false, kX>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
+                const floatx4 pd = mm<CB, true, false, false, kX>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
@@ -425,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             floatx4 h;
 #pragma unroll
             for (int r = 0; r < 4; ++r) h[r] = glast * sm.H[16 * mt + 4 * g + r][16 * nt + cc];
-            h = mm<CB, true, false>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
+            h = mm<CB, true, false, kX>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.H[16 * mt + 4 * g + r][16 * nt + cc] = h[r];
         }
@@ -436,9 +452,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     // into registers while chunk c is computed)
     load_slice(sm.D, a.dhT ? a.dhT + sbase : nullptr, dvf);
     if (nch > 0) stage_issue(nch - 1, true, nx);
+    // the entry state slice of the chunk after next is read into registers one chunk ahead
+    float4 hpre[SR];
+    auto slice_issue = [&](int64_t cc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < SR; ++u) hpre[u] = *reinterpret_cast<const float4 *>(ckpt + cc * cstride + (int64_t)(sr0 + u) * TV + sc0);
+    };
+    if (nch > 0) slice_issue(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = n_rows(c);
-        load_slice(sm.H, ckpt + c * cstride, TV);
+#pragma unroll
+        for (int u = 0; u < SR; ++u) *reinterpret_cast<float4 *>(&sm.H[sr0 + u][sc0]) = hpre[u];
+        if (c > 0) slice_issue(c - 1);
         stage_store(c, nx);
         if (c > 0) stage_issue(c - 1, true, nx);
         __syncthreads();
@@ -470,8 +495,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         for (int t = wave; t < 6; t += kWaves) {
             const bool isa = t >= 3;
             const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
-            floatx4 v = mm<TV, false, true>(zero4(), isa ? &sm.dR[0][0] : &sm.dO[0][0], SM::VP, 16 * mt, &sm.U[0][0],
-                                            SM::VP, 16 * nt);
+            floatx4 v = isa ? mm<TV, false, true>(zero4(), &sm.dR[0][0], SM::VP, 16 * mt, &sm.U[0][0], SM::VP, 16 * nt)
+                            : mm<TV, false, true, kX>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.U[0][0], SM::VP, 16 * nt);
             if (isa) v = -v;
             float colsum[4];
 #pragma unroll
@@ -532,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         // (wU = diag(w) U in dU, bR = -diag(beta gamma) dR); the read's exponent gradient
         for (int t = wave; t < 2 * (DK / 16); t += kWaves) {
             const int mt = t / (DK / 16), nt = t % (DK / 16);
-            floatx4 oh = mm<TV, false, true>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+            floatx4 oh = mm<TV, false, true, kX>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
             floatx4 dq;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -542,13 +567,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float rq = row16(dq[r] * sm.Q[i][16 * nt + cc]);
                 if (cc == 0) sm.pdr[3 + nt][i] = rq;
             }
-            dq = mm<CB, false, false>(dq, &sm.M[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            dq = mm<CB, false, false, false, kX>(dq, &sm.M[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
             // three independent partial sums, so that the products do not wait on each other
             floatx4 dk = mm<TV, false, true>(zero4(), &sm.dU[0][0], SM::VP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
             floatx4 dk2 = mm<TV, false, true>(zero4(), &sm.bR[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
-            floatx4 dk3 = mm<CB, true, false>(zero4(), &sm.M[0][0], SM::TP, 16 * mt, &sm.Q[0][0], SM::KP, 16 * nt);
-            dk = mm<CB, false, false>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
-            dk2 = mm<CB, true, false>(dk2, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            floatx4 dk3 = mm<CB, true, false, false, kX>(zero4(), &sm.M[0][0], SM::TP, 16 * mt, &sm.Q[0][0], SM::KP, 16 * nt);
+            dk = mm<CB, false, false, false, kX>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
+            dk2 = mm<CB, true, false, false, kX>(dk2, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
             dk += dk2 + dk3;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -568,8 +593,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             floatx4 h;
 #pragma unroll
             for (int r = 0; r < 4; ++r) h[r] = glast * sm.D[16 * mt + 4 * g + r][16 * nt + cc];
-            h = mm<CB, true, false>(h, &sm.Q[0][0], SM::KP, 16 * mt, &sm.eO[0][0], SM::VP, 16 * nt);
-            h = mm<CB, true, false>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.bR[0][0], SM::VP, 16 * nt);
+            h = mm<CB, true, false, kX>(h, &sm.Q[0][0], SM::KP, 16 * mt, &sm.eO[0][0], SM::VP, 16 * nt);
+            h = mm<CB, true, false, kX>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.bR[0][0], SM::VP, 16 * nt);
             dh[s] = h;
         }
         __syncthreads();
