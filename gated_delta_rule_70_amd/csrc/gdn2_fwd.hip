@@ -55,6 +55,14 @@ template <typename E>
 struct Pad {
     static constexpr int v = 16 / sizeof(E);
 };
+template <typename E>
+constexpr bool kIsBf16 = sizeof(E) == 2;
+// the chain's output staging (bf16 outputs only): two waves x up to 32 rows x 16 columns, fp32
+template <typename E, int C>
+struct OutStage {
+    static constexpr int kPitch = 20, kRows = C < 32 ? C : 32;
+    static constexpr int kFloats = kIsBf16<E> ? 2 * kRows * kPitch : 4;
+};
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
@@ -858,8 +866,8 @@ struct ChainCopy {
     static constexpr int kRegs = 4 * (PK + 2 * PV);  // VGPRs of one set
     static constexpr int R = kRegs <= 72 ? 3 : kRegs <= 100 ? 2 : 1;
     static constexpr int kWaves = 2 + 2 * R;  // two chain waves, R loader pairs
-    // double-buffered operands must fit in the 160 KB of LDS
-    static constexpr bool kFits = 2 * sizeof(ChainBuf<E, C, DK>) <= 160 * 1024;
+    // double-buffered operands and the output staging must fit in the 160 KB of LDS
+    static constexpr bool kFits = 2 * sizeof(ChainBuf<E, C, DK>) + 4 * OutStage<E, C>::kFloats <= 160 * 1024;
 };
 
 // LDS byte offset inside ChainBuf of key piece i
@@ -892,6 +900,11 @@ __global__ __launch_bounds__((64 * ChainCopy<E, C, DK>::kWaves)) void gdn2_chain
     constexpr int HT = DK / 16;
     constexpr int R = CC::R;
     __shared__ CB buf[2];
+    // each chain wave's output of a chunk, 32 rows at a time, fp32 [rows][16 columns]: written in
+    // the accumulator layout, read back as 8 consecutive columns of a row per lane, so that a
+    // bf16 output row piece goes out as one 16-byte store
+    constexpr int kOutP = OutStage<E, C>::kPitch, kOutRows = OutStage<E, C>::kRows;
+    __shared__ __align__(16) float ostage[OutStage<E, C>::kFloats];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
@@ -1104,19 +1117,51 @@ __global__ __launch_bounds__((64 * ChainCopy<E, C, DK>::kWaves)) void gdn2_chain
                     O[mi] = mma16(O[mi], frag_rows_lo<E>(cb.P, CB::CP, 16 * mi, 16 * kt), cvt4<E>(U[kt]));
             }
         }
-        const int64_t left = sv.len - c * C - 4 * g;  // rows 16 mi + r of this lane exist below left
-        if (acc_out) {
+        if constexpr (kIsBf16<E>) {
+            float *st = ostage + wave * kOutRows * kOutP;
+#pragma unroll
+            for (int rb = 0; rb < C; rb += kOutRows) {
+#pragma unroll
+            for (int mi = rb / 16; mi < (rb + kOutRows) / 16; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[(16 * mi - rb + 4 * g + r) * kOutP + cc] = O[mi][r];
+            // two 8-column pieces per row; rows past the end of the sequence are not written
+#pragma unroll
+            for (int pi = lane; pi < 2 * kOutRows; pi += 64) {
+                const int rr = pi >> 1, half = pi & 1;
+                const int64_t pos = c * C + rb + rr;
+                const float4 x0 = *reinterpret_cast<const float4 *>(st + rr * kOutP + 8 * half);
+                const float4 x1 = *reinterpret_cast<const float4 *>(st + rr * kOutP + 8 * half + 4);
+                if (pos < sv.len) {
+                    bf16x8 *dst = reinterpret_cast<bf16x8 *>(ob + sv.token(pos) * a.dv + dcol0 + lcol + 8 * half);
+                    float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    if (acc_out) {
+                        const bf16x8 old = *dst;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) f[e] += (float)old[e];
+                    }
+                    bf16x8 val;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) val[e] = (__bf16)f[e];
+                    *dst = val;
+                }
+            }
+            }
+        } else {
+            const int64_t left = sv.len - c * C - 4 * g;  // rows 16 mi + r of this lane exist below left
+            if (acc_out) {
+#pragma unroll
+                for (int mi = 0; mi < NT; ++mi)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * mi + r < left) O[mi][r] += to_f(orow[(16 * mi + r) * ostep]);
+            }
 #pragma unroll
             for (int mi = 0; mi < NT; ++mi)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (16 * mi + r < left) O[mi][r] += to_f(orow[(16 * mi + r) * ostep]);
+                    if (16 * mi + r < left) orow[(16 * mi + r) * ostep] = static_cast<E>(O[mi][r]);
         }
-#pragma unroll
-        for (int mi = 0; mi < NT; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (16 * mi + r < left) orow[(16 * mi + r) * ostep] = static_cast<E>(O[mi][r]);
         __syncthreads();
     }
     if (a.hT) {
