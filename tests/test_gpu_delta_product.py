@@ -176,3 +176,20 @@ def test_chunk64_plain_varlen(gdr):
     ro, rh = dp.scan(c.q, c.k, c.v, c.log_alpha, c.beta, c.h0, c.cu_seqlens, read="post")
     check(o, ro, torch.bfloat16, "out")
     check(hT, rh, torch.bfloat16, "hT")
+
+
+def test_full_size_slow_decay(gdr):
+    # the same launch with slow decays (log alpha ~ -U(0, 0.05)), where the carried state and the
+    # far terms of each chunk decide the result: eight units, output checked whole, per 64-token
+    # block and on chunk-last rows, and the final states
+    from tests._parity import check_bf16_detailed, check_states, segments
+    _say("delta product full size B4 H16 T4096 n2, slow decay")
+    c = inputs.delta_product_case(B=4, T=4096, n=2, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16, seed=38,
+                                  h0_std=0.1, regime="slow")
+    o, hT = _run(gdr, c, 64, "pre")
+    for (bi, h) in ((0, 0), (0, 11), (1, 5), (1, 14), (2, 2), (2, 10), (3, 7), (3, 15)):
+        sl = lambda t: t[bi:bi + 1, h:h + 1]
+        ro, rh = dp.scan(sl(c.q), sl(c.k), sl(c.v), sl(c.log_alpha), sl(c.beta), sl(c.h0), read="pre")
+        ou = o[bi:bi + 1, h:h + 1]
+        check_bf16_detailed(ou, ro, segments(ou.shape, None), "out (%d, %d)" % (bi, h))
+        check_states(hT[bi:bi + 1, h:h + 1], rh, "hT (%d, %d)" % (bi, h))

@@ -302,3 +302,24 @@ def test_chunk_bench_shape_two_pass(gdr, regime):
         e = check_bf16_detailed(ou, ro, segments(ou.shape, None), "out (%d, %d)" % (bi, h))
         check_states(hT[bi:bi + 1, h:h + 1], rh, "hT (%d, %d)" % (bi, h))
         _say("  unit (%d, %d): whole %.2e, worst block %.2e, chunk-last rows %.2e" % ((bi, h) + e))
+
+
+@pytest.mark.parametrize("read", ["post", "pre"])
+def test_decode_full_size(gdr, read):
+    # the decode step the benchmark times: 256 sequences, 16 key heads -> 32 value heads, d128,
+    # bf16 inputs, fp32 state updated in place; every head-state and every output vector
+    _say("gdn2 decode full size N256 Hk16 Hv32 d128 %s" % read)
+    c = inputs.gdn2_case(B=256, T=1, Hk=16, Hv=32, dk=128, dv=128, dtype=torch.bfloat16, seed=1003, h0_std=0.1)
+    one = lambda t: t[:, :, 0].contiguous()
+    state = c.h0.cuda().clone()
+    o, _ = gdr.gdn2_decode_step(*(one(t).cuda() for t in (c.q, c.k, c.v, c.g, c.b, c.w)), state, state_out=state,
+                                read=read)
+    torch.cuda.synchronize()
+    ro, rs = gdn2.decode(one(c.q), one(c.k), one(c.v), one(c.g), one(c.b), one(c.w), c.h0, read=read)
+    check(gpu_np(o), ro, torch.bfloat16, "out")
+    check(gpu_np(state), rs, torch.bfloat16, "state")
+    og, sg = gpu_np(o), gpu_np(state)
+    ev = np.sqrt(((og - ro) ** 2).sum(-1)) / np.maximum(np.sqrt((ro ** 2).sum(-1)), 1e-30)
+    es = np.sqrt(((sg - rs) ** 2).sum((-2, -1))) / np.maximum(np.sqrt((rs ** 2).sum((-2, -1))), 1e-30)
+    assert ev.max() <= BF16_REL and es.max() <= BF16_REL, (ev.max(), es.max())
+    _say("  worst output vector %.2e, worst head-state %.2e" % (ev.max(), es.max()))

@@ -166,3 +166,22 @@ def test_decode_prologue(gdr, cfg, mode, read):
         torch.cuda.synchronize()
         check(gpu_np(o), ref_o, dtype, "decode o step %d" % t)
         check(gpu_np(state), ref_state, dtype, "decode state step %d" % t)
+
+
+def test_chunk_prologue_full_size_every_unit(gdr):
+    # the launch the benchmark times for the fused prologue: B4 H16 T4096 d128 bf16, chunk 64,
+    # raw q/k rows normalised in the kernel and the gates formed from raw inputs; every
+    # (sequence, head) unit against the oracle, whole tensor, per 64-token block and chunk-last
+    # rows, and every final state
+    from tests._parity import check_bf16_detailed, check_states, segments
+    _say("prologue full size B4 H16 T4096 d128")
+    c = inputs.raw_case(B=4, T=4096, Hk=16, Hv=16, dk=128, dv=128, dtype=torch.bfloat16, seed=1001, h0_std=0.1)
+    d = lambda t: t.cuda()
+    out, hT = gdr.chunk_fwd_gated(d(c.q), d(c.k), d(c.v), d(c.a), d(c.b), d(c.A_log), d(c.dt_bias), d(c.h0),
+                                  chunk=64, l2norm=True)
+    torch.cuda.synchronize()
+    o, h = gpu_np(out), gpu_np(hT)
+    ro, rh = prologue.scan_fused(c.q, c.k, c.v, c.a, c.b, c.A_log, c.dt_bias, c.h0, l2norm=True)
+    e = check_bf16_detailed(o, ro, segments(o.shape, None), "prologue o")
+    eh = check_states(h, rh, "prologue hT")
+    _say("  o: whole %.2e, worst block %.2e, chunk-last rows %.2e; hT: whole %.2e, worst unit %.2e" % (e + eh))
