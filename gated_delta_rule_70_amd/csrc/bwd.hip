@@ -27,19 +27,28 @@
 // This is the derivative of the chunk form of `chunked_delta` on the "Prizma seq/delta.py" page
 // (transposed to H = S^T), which equals the recurrence; the pages print no backward.
 //
-// One workgroup of 512 threads (eight waves) per (sequence, value head, 32 columns of d_v).
-// Every quantity is per column or a sum over columns of per-column terms, so the column slices
-// are independent. Each workgroup writes its share of dq, dk, dbeta and dlog alpha into its own
-// partial buffer in the workspace, and a second kernel adds the partials of the column slices
-// (and, for dq and dk, of the value heads that share a key head) in a fixed order, so the
-// gradients are the same bits on every run; inside a workgroup every per-row sum likewise has
-// one slot per contributing tile, added in a fixed order. Two sweeps: the chunk-form forward from
-// h0, storing the slice of the state at each chunk start in the workspace; then the chunks from
-// the last, each recomputing its forward quantities from its stored entry state and applying the
-// adjoint above. All matrices of a chunk live in LDS in fp32; the products run on the matrix
-// cores as split bf16 products with fp32 accumulation (16x16 output tiles shared out over the
-// eight waves), the triangular inverse is the one the chunk forward kernels use, and the gate
-// gradients are sums on the vector units.
+// Only two of these quantities are carried from chunk to chunk: the state H (forward) and its
+// adjoint dH (backward). Everything else is local to a chunk once H and dH' are known. So the
+// backward runs as four kernels on one stream, 64-token chunks:
+//
+//   1. prep, one workgroup per (value head, chunk): the gate cumsums b and r, G, Pm and
+//      T = (I + A)^{-1}; T, T^T and Pm^T go to the workspace as ready matrix-core operands.
+//   2. sweeps, one workgroup per (sequence, value head, 32 value columns) and direction, the
+//      two directions in one launch: the forward sweep keeps H and per chunk forms X, R, U (U is
+//      stored) and the next H, storing each chunk's entry state; the adjoint sweep keeps dH and
+//      per chunk forms dU, dR (stored; dV = diag(beta) dR is written) and the previous dH,
+//      storing each chunk's exit adjoint. Neither needs the other.
+//   3. gradients, one workgroup per (key head, chunk): for each value head of the key head
+//      (in order) and each 32-column slice (in order) it reads H, dH', U and dR of the chunk and
+//      accumulates X, K dH', dP, dA, dO H^T and the dK terms over the slices; then M, N, the rest
+//      of dQ and dK, and the gate gradients. dq and dk are summed over the value heads in the
+//      workgroup's registers, so every gradient is written once, by one workgroup, in a fixed
+//      order: the same bits on every call, with no float atomics and no second reduction.
+//
+// All products run on the matrix cores as split bf16 products with fp32 accumulation: an fp32
+// operand x is split into hi = bf16(x) and lo = bf16(x - hi) and a 32-deep product is
+// hi*hi + hi*lo + lo*hi (relative error near 2^-16 per product); q, k, v and dout of a bf16 call
+// hold bf16 values exactly, so their lo parts are zero and those products are skipped.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -54,55 +63,84 @@ namespace gdr {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-// the rows of a CB x TV matrix are shared out 8 threads to a row (4 columns each) over the first
-// CB * TV / 4 threads
-constexpr int kRowThreads = kBwdBlock * kBwdCols / 4;
 constexpr int CB = kBwdBlock;  // tokens per chunk
-constexpr int TV = kBwdCols;   // value columns per workgroup
+constexpr int TV = kBwdCols;   // value columns per slice
+constexpr int NMT = CB / 16;   // 16-row tiles of a chunk
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kPrepThreads = 256;
+static_assert(CB == 64 && TV == 32, "the tile assignments are written for 64-token chunks and 32-column slices");
+constexpr int FP = TV + 4;  // pitch of fp32 [rows][TV] matrices
+constexpr int SP = CB + 4;  // pitch of fp32 [CB][CB] matrices
+template <typename E>
+constexpr int pad_of() { return 16 / (int)sizeof(E); }  // one 16-byte piece of padding per row
 
-__device__ __forceinline__ float ld_f(const float *p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float ld_f(const __bf16 *p, int64_t i) { return (float)p[i]; }
+// The record of one (value head, chunk slot): A-operand fragments of T, T^T and Pm^T as split bf16
+// ([16-row tile][32-deep slice][lane] of a 16-byte hi part and a 16-byte lo part, in the register
+// layout mma32 takes), then b[CB] and r[CB].
+constexpr int kSlabBytes = 64 * 32;
+constexpr int kSlices = CB / 32;
+constexpr int kMatBytes = NMT * kSlices * kSlabBytes;
+static_assert(3 * kMatBytes + 2 * CB * 4 == kBwdRecBytes, "record layout");
+enum { kRecT = 0, kRecTt = 1, kRecPt = 2 };
+
+// the lower 16x16 tiles (mt >= nt) of a CB x CB matrix, in a fixed order
+__device__ __forceinline__ void lower_tile(int idx, int &mt, int &nt) {
+    mt = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+    nt = idx - mt * (mt + 1) / 2;
+}
 
 struct Seq {
     int64_t t0, len;
     bool rev;
     __device__ __forceinline__ int64_t token(int64_t pos) const { return rev ? t0 + len - 1 - pos : t0 + pos; }
 };
-
-template <int DK>
-struct alignas(16) Smem {
-    static constexpr int KP = DK + 4, VP = TV + 4, AP = CB + 4, TP = CB + 4;
-    float K[CB][KP], Q[CB][KP];
-    float V[CB][VP], dO[CB][VP];
-    float H[DK][VP], D[DK][VP];  // the chunk's entry state and the adjoint of its exit state
-    float X[CB][VP], U[CB][VP], dU[CB][VP], dR[CB][VP], eO[CB][VP], bR[CB][VP];
-    float A[CB * AP], T[CB * TP];  // flat: the shared triangular inverse reads them so
-    float P[CB][TP], G[CB][TP], M[CB][TP], Nb[CB][TP];
-    float la[CB], beta[CB], b[CB], r[CB];
-    float dw[CB];
-    // Per-row partial sums of the gate gradients, one slot per contributing tile or thread so
-    // that they are added in a fixed order (no float atomics):
-    //   pdr:    the read exponent r: the three dP tiles' row sums, then the DK / 16 dQ tiles'
-    //   pdb:    the cumulative decay b: the dP tiles' column sums (3), the dA tiles' row sums (3)
-    //           and column sums (3), and each row's own term from dR . X
-    //   pdbeta: beta: the dA tiles' row sums (3), and each row's own term from dR . (V - gamma X)
-    static constexpr int kPdr = 3 + DK / 16, kPdb = 10, kPdbeta = 4;
-    float pdr[kPdr][CB], pdb[kPdb][CB], pdbeta[kPdbeta][CB];
-    float hdp[kThreads / 64];  // <dH', H> of the chunk, per wave
+struct Loc {
+    int64_t seq, row, slot0;  // row: the batch row of q, k, v (0 when packed)
+    Seq sq;
 };
+__device__ __forceinline__ Loc locate_seq(const BwdArgs &a, int64_t seq) {
+    Loc L;
+    L.seq = seq;
+    L.row = a.cu_seqlens ? 0 : seq;
+    L.sq.t0 = 0;
+    L.sq.len = a.T;
+    L.slot0 = seq * ((a.T + CB - 1) / CB);
+    if (a.cu_seqlens) {
+        L.sq.t0 = a.cu_seqlens[seq];
+        L.sq.len = a.cu_seqlens[seq + 1] - L.sq.t0;
+        L.slot0 = L.sq.t0 / CB + seq;
+    }
+    L.sq.rev = (a.flags & kFlagReverse) != 0;
+    return L;
+}
+// the sequence and chunk of a chunk slot; false for a slot that holds no chunk (packed inputs
+// leave gaps). Slots of sequence s start at cu[s] / CB + s, which increases with s.
+__device__ __forceinline__ bool locate_slot(const BwdArgs &a, int64_t slot, Loc &L, int64_t &c) {
+    if (!a.cu_seqlens) {
+        const int64_t nch = (a.T + CB - 1) / CB;
+        if (nch == 0) return false;
+        L = locate_seq(a, slot / nch);
+        c = slot % nch;
+        return L.seq < a.B;
+    }
+    int64_t lo = 0, hi = a.nseq - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if ((int64_t)a.cu_seqlens[mid] / CB + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    L = locate_seq(a, lo);
+    c = slot - L.slot0;
+    return c >= 0 && c * CB < L.sq.len;
+}
 
-// acc += A (16 x KD) B (KD x 16) with both operands in LDS. A is X[m0 + m][k] (or, with AT,
-// X[k][m0 + m]); B is Y[k][n0 + n] (or, with BT, Y[n0 + n][k]). Output tile in the accumulator
-// layout: lane (g, c), register r <-> [m0 + 4g + r][n0 + c].
-//
-// The products run as three bf16 products of split operands (x = hi + lo, hi = bf16(x),
-// lo = bf16(x - hi)): hi*hi + hi*lo + lo*hi, accumulated in fp32. The dropped lo*lo term and the
-// rounding of lo leave a relative error near 2^-16 per product, and three 16x16x32 bf16 products
-// take a sixth of the matrix-core time of the eight 16x16x4 fp32 ones they replace. An operand
-// known to hold bf16 values exactly (AX, BX: q, k, v or dout of a bf16 call, staged in LDS as
-// fp32) has lo = 0, so its lo products are skipped: two products, or one when both are exact.
+// ---------------------------------------------------------------- operands
+
+// An operand fragment split once (hi, lo); for an operand that holds bf16 values exactly only hi
+// is set, and the products below skip its lo part.
+struct Split {
+    Frag<__bf16> h, l;
+};
 __device__ __forceinline__ void split_bf16(const floatx4 &x, bf16x4 &hi, bf16x4 &lo) {
     hi = cvt4<__bf16>(x);
     floatx4 r;
@@ -110,32 +148,78 @@ __device__ __forceinline__ void split_bf16(const floatx4 &x, bf16x4 &hi, bf16x4 
     for (int i = 0; i < 4; ++i) r[i] = x[i] - (float)hi[i];
     lo = cvt4<__bf16>(r);
 }
-template <int KD, bool AT, bool BT, bool AX = false, bool BX = false>
-__device__ __forceinline__ floatx4 mm(floatx4 acc, const float *X, int ldx, int m0, const float *Y, int ldy, int n0) {
-#pragma unroll
-    for (int k0 = 0; k0 < KD; k0 += 32) {
-        const Frag<float> fa = AT ? frag_cols<float>(X, ldx, m0, k0) : frag_rows<float>(X, ldx, m0, k0);
-        const Frag<float> fb = BT ? frag_rows<float>(Y, ldy, n0, k0) : frag_cols<float>(Y, ldy, n0, k0);
-        Frag<__bf16> ah, al, bh, bl;
-        if constexpr (AX) {
-            ah.lo = cvt4<__bf16>(fa.lo);
-            ah.hi = cvt4<__bf16>(fa.hi);
-        } else {
-            split_bf16(fa.lo, ah.lo, al.lo);
-            split_bf16(fa.hi, ah.hi, al.hi);
-        }
-        if constexpr (BX) {
-            bh.lo = cvt4<__bf16>(fb.lo);
-            bh.hi = cvt4<__bf16>(fb.hi);
-        } else {
-            split_bf16(fb.lo, bh.lo, bl.lo);
-            split_bf16(fb.hi, bh.hi, bl.hi);
-        }
-        if constexpr (!AX) acc = mma32(acc, al, bh);
-        if constexpr (!BX) acc = mma32(acc, ah, bl);
-        acc = mma32(acc, ah, bh);
+__device__ __forceinline__ Split split_frag(const Frag<float> &f) {
+    Split s;
+    split_bf16(f.lo, s.h.lo, s.l.lo);
+    split_bf16(f.hi, s.h.hi, s.l.hi);
+    return s;
+}
+// acc += a b; AX / BX: the operand is exactly bf16 (lo = 0)
+template <bool AX, bool BX>
+__device__ __forceinline__ floatx4 mms(floatx4 acc, const Split &a, const Split &b) {
+    if constexpr (!AX) acc = mma32(acc, a.l, b.h);
+    if constexpr (!BX) acc = mma32(acc, a.h, b.l);
+    return mma32(acc, a.h, b.h);
+}
+// from an E-typed matrix in LDS: rows (A[m][k] = X[m][k] or B[k][n] = X[n][k]) or columns
+template <typename E>
+__device__ __forceinline__ Split ldr(const E *X, int ld, int row0, int k0) {
+    if constexpr (std::is_same<E, __bf16>::value) {
+        Split s{};
+        s.h = frag_rows<__bf16>(X, ld, row0, k0);
+        return s;
+    } else {
+        return split_frag(frag_rows<float>(X, ld, row0, k0));
     }
-    return acc;
+}
+template <typename E>
+__device__ __forceinline__ Split ldc(const E *X, int ld, int col0, int k0) {
+    if constexpr (std::is_same<E, __bf16>::value) {
+        Split s{};
+        s.h = frag_cols<__bf16>(X, ld, col0, k0);
+        return s;
+    } else {
+        return split_frag(frag_cols<float>(X, ld, col0, k0));
+    }
+}
+// rows of an fp32 matrix, each lane's row scaled by sc
+__device__ __forceinline__ Split ldr_scaled(const float *X, int ld, int row0, int k0, float sc) {
+    Frag<float> f = frag_rows<float>(X, ld, row0, k0);
+    f.lo *= sc;
+    f.hi *= sc;
+    return split_frag(f);
+}
+// columns of an E-typed matrix with row k scaled by sk[k]
+template <typename E>
+__device__ __forceinline__ Split ldc_kscaled(const E *X, int ld, int col0, int k0, const float *sk) {
+    const int lane = threadIdx.x & 63;
+    const int kb = k0 + 4 * (lane >> 4);
+    const E *p = X + kb * ld + col0 + (lane & 15);
+    Frag<float> f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        f.lo[s] = (float)p[s * ld] * sk[kb + s];
+        f.hi[s] = (float)p[(16 + s) * ld] * sk[kb + 16 + s];
+    }
+    return split_frag(f);
+}
+// a fragment slab of a record, as loaded (two 16-byte pieces per lane)
+struct Slab {
+    uint4 h, l;
+};
+__device__ __forceinline__ Slab ld_slab(const uint8_t *rec, int mat, int mt, int ks) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(rec + mat * kMatBytes + (mt * kSlices + ks) * kSlabBytes +
+                                                     (threadIdx.x & 63) * 32);
+    Slab s;
+    s.h = p[0];
+    s.l = p[1];
+    return s;
+}
+__device__ __forceinline__ Split slab_split(const Slab &s) {
+    Split r;
+    r.h = __builtin_bit_cast(Frag<__bf16>, s.h);
+    r.l = __builtin_bit_cast(Frag<__bf16>, s.l);
+    return r;
 }
 
 // sum of x over the 16 lanes of a lane group (the columns of a tile row)
@@ -151,488 +235,791 @@ __device__ __forceinline__ float col4(float x) {
     return x;
 }
 
+// The rows of one chunk of an E-typed [token][stride] matrix, W elements from the row start, as
+// 16-byte pieces shared out over NT threads: issued into registers, then stored into LDS (rows
+// past the chunk end read the chunk's first row and are stored as zeros).
+template <typename E, int W, int NT>
+struct Rows {
+    static constexpr int EPP = 16 / (int)sizeof(E), PR = W / EPP, N = CB * PR, PT = (N + NT - 1) / NT;
+    uint4 p[PT];
+    __device__ __forceinline__ void issue(const E *src, int64_t stride, const Seq &sq, int64_t c, int n, int tid) {
+#pragma unroll
+        for (int e = 0; e < PT; ++e) {
+            const int i = tid + e * NT, rr = i / PR, pc = i % PR;
+            p[e] = make_uint4(0, 0, 0, 0);
+            if (i < N) p[e] = *reinterpret_cast<const uint4 *>(src + sq.token(c * CB + (rr < n ? rr : 0)) * stride + pc * EPP);
+        }
+    }
+    __device__ __forceinline__ void store(E *dst, int pitch, int n, int tid) const {
+#pragma unroll
+        for (int e = 0; e < PT; ++e) {
+            const int i = tid + e * NT, rr = i / PR, pc = i % PR;
+            if (i < N) *reinterpret_cast<uint4 *>(dst + rr * pitch + pc * EPP) = rr < n ? p[e] : make_uint4(0, 0, 0, 0);
+        }
+    }
+};
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ float wave_scan(float x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------- 1. prep
+
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
-    typedef Smem<DK> SM;
+struct PrepSmem {
+    static constexpr int KP = DK + pad_of<E>(), AP = SP, TP = SP;
+    E K[CB][KP];
+    union {
+        E Q[CB][KP];
+        float P[CB][SP];  // Pm, once the products that read Q are done
+    } u;
+    float A[CB * SP], T[CB * SP];  // flat: the shared triangular inverse reads them so
+    float la[CB], beta[CB], b[CB], r[CB];
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
+    typedef PrepSmem<E, DK> SM;
     __shared__ SM sm;
-    // q, k, v and dout of a bf16 call are staged in LDS as fp32 but hold bf16 values exactly
     constexpr bool kX = std::is_same<E, __bf16>::value;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, cc = lane & 15;
-    const int64_t unit = blockIdx.x / a.ntiles;
-    const int tile = (int)(blockIdx.x % a.ntiles);
-    const int64_t seq = unit / a.Hv, head = unit % a.Hv;
+    const int64_t head = blockIdx.x / a.nslots, slot = blockIdx.x % a.nslots;
+    Loc L;
+    int64_t c;
+    if (!locate_slot(a, slot, L, c)) return;
+    const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
     const int64_t kh = head / (a.Hv / a.Hk);
-    const int64_t row = a.cu_seqlens ? 0 : seq;
     const bool pre = (a.flags & kFlagReadPre) != 0;
+    const E *qb = reinterpret_cast<const E *>(a.q) + (L.row * a.Hk + kh) * a.T * DK;
+    const E *kb = reinterpret_cast<const E *>(a.k) + (L.row * a.Hk + kh) * a.T * DK;
+    const float *lab = a.log_alpha + (L.row * a.Hv + head) * a.T;
+    const float *beb = a.beta + (L.row * a.Hv + head) * a.T;
+    {
+        Rows<E, DK, kPrepThreads> kp, qp;
+        kp.issue(kb, DK, L.sq, c, n, tid);
+        qp.issue(qb, DK, L.sq, c, n, tid);
+        float lv = 0.f, bv = 0.f;
+        if (tid < n) {
+            const int64_t t = L.sq.token(c * CB + tid);
+            lv = lab[t];
+            bv = beb[t];
+        }
+        kp.store(&sm.K[0][0], SM::KP, n, tid);
+        qp.store(&sm.u.Q[0][0], SM::KP, n, tid);
+        if (tid < CB) {
+            sm.la[tid] = lv;
+            sm.beta[tid] = bv;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const float x = wave_scan(sm.la[lane]);
+        sm.b[lane] = x;
+        sm.r[lane] = pre ? x - sm.la[lane] : x;
+    }
+    __syncthreads();
+    // the lower tiles of G (tasks 0-9) and Pm (10-19), five per wave, into registers: Pm is
+    // stored over Q, so every product must be done before any tile is stored
+    constexpr int kPer = 20 / (kPrepThreads / 64);
+    floatx4 acc[kPer];
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int task = wave + (kPrepThreads / 64) * s;
+        const bool isp = task >= 10;
+        int mt, nt;
+        lower_tile(task % 10, mt, nt);
+        acc[s] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+            acc[s] = mms<kX, kX>(acc[s], ldr<E>(isp ? &sm.u.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt, 32 * ks),
+                                 ldr<E>(&sm.K[0][0], SM::KP, 16 * nt, 32 * ks));
+    }
+    __syncthreads();
+    for (int i = tid; i < CB * SP; i += kPrepThreads) sm.T[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int task = wave + (kPrepThreads / 64) * s;
+        const bool isp = task >= 10;
+        int mt, nt;
+        lower_tile(task % 10, mt, nt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+            if (isp) {
+                const bool keep = pre ? j < i : j <= i;
+                sm.u.P[i][j] = keep ? acc[s][r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
+            } else {
+                sm.A[i * SP + j] = j < i ? sm.beta[i] * acc[s][r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
+            }
+            // the mirrored upper tile is zero
+            if (mt > nt) {
+                const int i2 = 16 * nt + 4 * g + r, j2 = 16 * mt + cc;
+                if (isp) sm.u.P[i2][j2] = 0.f;
+                else sm.A[i2 * SP + j2] = 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) solve_unit_lower_inverse<float, CB>(sm);
+    __syncthreads();
+    // T, T^T and Pm^T as A-operand fragments: lane (g, c) of slab (mt, ks) holds row 16 mt + c,
+    // columns 32 ks + 4g + s and 32 ks + 16 + 4g + s (s = 0..3)
+    uint8_t *rec = a.rec + (head * a.nslots + slot) * kBwdRecBytes;
+    for (int it = tid; it < 3 * NMT * kSlices * 64; it += kPrepThreads) {
+        const int mat = it / (NMT * kSlices * 64), sl = (it / 64) % (NMT * kSlices), ln = it % 64;
+        const int mt = sl / kSlices, ks = sl % kSlices;
+        const int row = 16 * mt + (ln & 15), kb0 = 32 * ks + 4 * (ln >> 4);
+        Frag<float> f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int k = kb0 + (s < 4 ? s : 12 + s);
+            const float x = mat == kRecT ? sm.T[row * SP + k] : mat == kRecTt ? sm.T[k * SP + row] : sm.u.P[k][row];
+            if (s < 4) f.lo[s] = x;
+            else f.hi[s - 4] = x;
+        }
+        const Split sp = split_frag(f);
+        uint4 *dst = reinterpret_cast<uint4 *>(rec + mat * kMatBytes + sl * kSlabBytes + ln * 32);
+        dst[0] = __builtin_bit_cast(uint4, sp.h);
+        dst[1] = __builtin_bit_cast(uint4, sp.l);
+    }
+    if (tid < CB) {
+        float *rb = reinterpret_cast<float *>(rec + 3 * kMatBytes);
+        rb[tid] = sm.b[tid];
+        rb[CB + tid] = sm.r[tid];
+    }
+}
+
+// ---------------------------------------------------------------- 2. sweeps
+
+template <typename E, int DK>
+struct FwdSmem {
+    static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
+    E K[CB][KP];
+    E V[CB][VP];
+    float H[DK][FP], R[CB][FP], wU[CB][FP];
+    float b[CB], beta[CB];
+};
+template <typename E, int DK>
+struct AdjSmem {
+    static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
+    E K[CB][KP], Q[CB][KP];
+    E dO[CB][VP];
+    float D[DK][FP], dU[CB][FP], bR[CB][FP];
+    float b[CB], er[CB], beta[CB];
+};
+template <typename E, int DK>
+constexpr size_t sweep_smem_bytes() {
+    return sizeof(FwdSmem<E, DK>) > sizeof(AdjSmem<E, DK>) ? sizeof(FwdSmem<E, DK>) : sizeof(AdjSmem<E, DK>);
+}
+
+// A thread's part of a DK x TV state slice: SR rows of 4 consecutive columns.
+template <int DK>
+struct SliceMap {
+    static constexpr int SR = DK * TV / (kThreads * 4);
+    int r0, c0;
+    __device__ __forceinline__ SliceMap(int tid) : r0((tid / (TV / 4)) * SR), c0((tid % (TV / 4)) * 4) {}
+};
+
+// Forward sweep of one (sequence, value head, column slice): per chunk, the entry state to the
+// workspace, X = K H, R, U = T R (U to the workspace) and H' = gamma_last H + K^T diag(w) U.
+template <typename E, int DK>
+__device__ __forceinline__ void fwd_sweep(const BwdArgs &a, int64_t unit, int tile, char *smraw) {
+    typedef FwdSmem<E, DK> SM;
+    SM &sm = *reinterpret_cast<SM *>(smraw);
+    constexpr bool kX = std::is_same<E, __bf16>::value;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, cc = lane & 15;
+    const int64_t seq = unit / a.Hv, head = unit % a.Hv, kh = head / (a.Hv / a.Hk);
+    const Loc L = locate_seq(a, seq);
+    const int64_t nch = (L.sq.len + CB - 1) / CB;
     const int64_t dvf = a.ntiles * TV;
     const int col0 = tile * TV;
-    Seq sq;
-    sq.t0 = 0;
-    sq.len = a.T;
-    int64_t slot0 = seq * ((a.T + CB - 1) / CB);
-    if (a.cu_seqlens) {
-        sq.t0 = a.cu_seqlens[seq];
-        sq.len = a.cu_seqlens[seq + 1] - sq.t0;
-        slot0 = sq.t0 / CB + seq;
-    }
-    sq.rev = (a.flags & kFlagReverse) != 0;
-    const int64_t nch = (sq.len + CB - 1) / CB;
-
-    const E *qb = reinterpret_cast<const E *>(a.q) + (row * a.Hk + kh) * a.T * DK;
-    const E *kb = reinterpret_cast<const E *>(a.k) + (row * a.Hk + kh) * a.T * DK;
-    const E *vb = reinterpret_cast<const E *>(a.v) + (row * a.Hv + head) * a.T * dvf + col0;
-    const E *dob = reinterpret_cast<const E *>(a.dout) + (row * a.Hv + head) * a.T * dvf + col0;
-    const float *lab = a.log_alpha + (row * a.Hv + head) * a.T;
-    const float *beb = a.beta + (row * a.Hv + head) * a.T;
-    // this workgroup's partial buffers: [B][Hv][ntiles][T][DK] for dq, dk; [B][Hv][ntiles][T]
-    // for dlog alpha, dbeta (summed by bwd_reduce_kernel)
-    const int64_t part = (row * a.Hv + head) * a.ntiles + tile;
-    float *dqb = a.pq + part * a.T * DK;
-    float *dkb = a.pk + part * a.T * DK;
-    float *dvb = a.dv + (row * a.Hv + head) * a.T * dvf + col0;
-    float *dlab = a.pla + part * a.T;
-    float *dbeb = a.pbeta + part * a.T;
-    // chunk-start states: [head][slot][tile] slices of DK x TV floats
+    const E *kb = reinterpret_cast<const E *>(a.k) + (L.row * a.Hk + kh) * a.T * DK;
+    const E *vb = reinterpret_cast<const E *>(a.v) + (L.row * a.Hv + head) * a.T * dvf + col0;
+    const float *beb = a.beta + (L.row * a.Hv + head) * a.T;
+    float *ub = a.us + (L.row * a.Hv + head) * a.T * dvf + col0;
     constexpr int64_t kSlice = (int64_t)DK * TV;
-    float *ckpt = a.ws + ((head * a.nslots + slot0) * a.ntiles + tile) * kSlice;
-    const int64_t cstride = a.ntiles * kSlice;
-    // the full [dk][dv] state of this unit, at this slice's columns
+    float *hs = a.hs + ((head * a.nslots + L.slot0) * a.ntiles + tile) * kSlice;
+    const int64_t hstride = a.ntiles * kSlice;
+    const uint8_t *rec0 = a.rec + (head * a.nslots + L.slot0) * kBwdRecBytes;
+    const SliceMap<DK> sl(tid);
+    constexpr int SR = SliceMap<DK>::SR;
     const int64_t sbase = (seq * a.Hv + head) * DK * dvf + col0;
+#pragma unroll
+    for (int u = 0; u < SR; ++u)
+        *reinterpret_cast<float4 *>(&sm.H[sl.r0 + u][sl.c0]) =
+            a.h0 ? *reinterpret_cast<const float4 *>(a.h0 + sbase + (int64_t)(sl.r0 + u) * dvf + sl.c0) : make_float4(0.f, 0.f, 0.f, 0.f);
 
-    // the DK x TV elements of a state slice this thread handles: SR rows x 4 columns
-    constexpr int SR = DK * TV / (kThreads * 4);
-    const int sc0 = (tid % (TV / 4)) * 4, sr0 = (tid / (TV / 4)) * SR;
-    // the 4 elements of a CB x TV matrix this thread handles (row ei, columns ej .. ej + 3)
-    const int ei = tid / (TV / 4), ej = (tid % (TV / 4)) * 4;
-
-    // matrices whose strictly upper 16x16 tiles are read as zeros and never written
-    for (int i = tid; i < CB * SM::TP; i += kThreads) {
-        sm.T[i] = 0.f;
-        (&sm.P[0][0])[i] = 0.f;
-        (&sm.G[0][0])[i] = 0.f;
-        (&sm.M[0][0])[i] = 0.f;
-        (&sm.Nb[0][0])[i] = 0.f;
-    }
-    for (int i = tid; i < CB * SM::AP; i += kThreads) sm.A[i] = 0.f;
-
-    auto n_rows = [&](int64_t c) __attribute__((always_inline)) -> int { return (int)min((int64_t)CB, sq.len - c * CB); };
-
-    constexpr int EPP = 16 / (int)sizeof(E);  // elements per piece
-    constexpr int KPR = DK / EPP, VPR = TV / EPP;
-    constexpr int NKP = CB * KPR, NVP = CB * VPR;
-    constexpr int KPT = (NKP + kThreads - 1) / kThreads, VPT = (NVP + kThreads - 1) / kThreads;
-    // a chunk's inputs in flight: 16-byte pieces of k, q, v, dout (rows past the end read row 0
-    // and are zeroed when stored), and the gates of the thread's row
-    struct StageRegs {
-        uint4 kp[KPT], qp[KPT], vp[VPT], op[VPT];
-        float lv, bv;
-    };
-    auto stage_issue = [&](int64_t c, bool adjoint, StageRegs &sr) __attribute__((always_inline)) {
-        const int n = n_rows(c);
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / KPR, p = i % KPR;
-            sr.kp[e] = make_uint4(0, 0, 0, 0);
-            sr.qp[e] = make_uint4(0, 0, 0, 0);
-            if (i < NKP) {
-                const int64_t off = sq.token(c * CB + (rr < n ? rr : 0)) * DK + p * EPP;
-                sr.kp[e] = *reinterpret_cast<const uint4 *>(kb + off);
-                if (adjoint) sr.qp[e] = *reinterpret_cast<const uint4 *>(qb + off);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / VPR, p = i % VPR;
-            sr.vp[e] = make_uint4(0, 0, 0, 0);
-            sr.op[e] = make_uint4(0, 0, 0, 0);
-            if (i < NVP) {
-                const int64_t off = sq.token(c * CB + (rr < n ? rr : 0)) * dvf + p * EPP;
-                sr.vp[e] = *reinterpret_cast<const uint4 *>(vb + off);
-                if (adjoint) sr.op[e] = *reinterpret_cast<const uint4 *>(dob + off);
-            }
-        }
-        sr.lv = 0.f;
-        sr.bv = 0.f;
-        if (tid < CB && tid < n) {
-            const int64_t t = sq.token(c * CB + tid);
-            sr.lv = lab[t];
-            sr.bv = beb[t];
-        }
-    };
-    // piece -> EPP floats of row rr (zero past the end), into LDS as 16-byte stores
-    auto put = [&](float *dst, const uint4 &piece, bool keep) __attribute__((always_inline)) {
-        float f[EPP];
-        if constexpr (sizeof(E) == 2) {
-            const unsigned w[4] = {piece.x, piece.y, piece.z, piece.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f[2 * j] = __uint_as_float(w[j] << 16);
-                f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-            }
-        } else {
-            f[0] = __uint_as_float(piece.x);
-            f[1] = __uint_as_float(piece.y);
-            f[2] = __uint_as_float(piece.z);
-            f[3] = __uint_as_float(piece.w);
-        }
-#pragma unroll
-        for (int j = 0; j < EPP; j += 4)
-            *reinterpret_cast<float4 *>(dst + j) =
-                keep ? make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-    };
-    auto stage_store = [&](int64_t c, const StageRegs &sr) __attribute__((always_inline)) {
-        const int n = n_rows(c);
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / KPR, p = i % KPR;
-            if (i < NKP) {
-                put(&sm.K[rr][p * EPP], sr.kp[e], rr < n);
-                put(&sm.Q[rr][p * EPP], sr.qp[e], rr < n);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-            const int i = tid + e * kThreads, rr = i / VPR, p = i % VPR;
-            if (i < NVP) {
-                put(&sm.V[rr][p * EPP], sr.vp[e], rr < n);
-                put(&sm.dO[rr][p * EPP], sr.op[e], rr < n);
-            }
-        }
+    // this wave's output tile of X, R and U
+    const int mt = wave >> 1, nt = wave & 1;
+    Rows<E, DK, kThreads> kp;
+    Rows<E, TV, kThreads> vp;
+    float bv = 0.f, betav = 0.f;
+    Slab tr[kSlices];
+    auto issue = [&](int64_t c) __attribute__((always_inline)) {
+        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
+        kp.issue(kb, DK, L.sq, c, n, tid);
+        vp.issue(vb, dvf, L.sq, c, n, tid);
         if (tid < CB) {
-            sm.la[tid] = sr.lv;
-            sm.beta[tid] = sr.bv;
-            sm.dw[tid] = 0.f;
-        }
-        // the tiles leave some slots of the row partials untouched: they read as zero
-        for (int i = tid; i < SM::kPdr * CB; i += kThreads) sm.pdr[i / CB][i % CB] = 0.f;
-        for (int i = tid; i < SM::kPdb * CB; i += kThreads) sm.pdb[i / CB][i % CB] = 0.f;
-        for (int i = tid; i < SM::kPdbeta * CB; i += kThreads) sm.pdbeta[i / CB][i % CB] = 0.f;
-    };
-    // inclusive cumsum of log alpha and the read exponents (one wave)
-    auto gates = [&]() __attribute__((always_inline)) {
-        if (tid < 64) {
-            float x = tid < CB ? sm.la[tid] : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (tid >= off) x += y;
-            }
-            if (tid < CB) {
-                sm.b[tid] = x;
-                sm.r[tid] = pre ? x - sm.la[tid] : x;
-            }
+            bv = reinterpret_cast<const float *>(rec0 + c * kBwdRecBytes + 3 * kMatBytes)[tid];
+            betav = tid < n ? beb[L.sq.token(c * CB + tid)] : 0.f;
         }
     };
-    // forward quantities of the chunk from its entry state in sm.H: X, G and A, P (adjoint only), T, U
-    auto forward_parts = [&](bool adjoint) __attribute__((always_inline)) {
-        // X = K H (tasks 0-3, one tile each); G = K K^T and P = Q K^T on the lower tiles (00, 10,
-        // 11; tasks 4-6 and 7-9), shared out over the waves
-        for (int task = wave; task < (adjoint ? 10 : 7); task += kWaves) {
-            if (task < 4) {
-                const int mt = task >> 1, nt = task & 1;
-                const floatx4 x = mm<DK, false, false, kX>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
+    // T's rows 16 mt .. 16 mt + 15 are zero past column 16 mt + 15
+    auto issue_t = [&](int64_t c) __attribute__((always_inline)) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.X[16 * mt + 4 * g + r][16 * nt + cc] = x[r];
-                continue;
-            }
-            const int t = task - 4;
-            const bool isp = t >= 3;
-            const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
-            const floatx4 v = mm<DK, false, true, kX, kX>(zero4(), isp ? &sm.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt,
-                                                  &sm.K[0][0], SM::KP, 16 * nt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                if (isp) {
-                    const bool keep = pre ? j < i : j <= i;
-                    sm.P[i][j] = keep ? v[r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
-                } else {
-                    const float gg = j < i ? v[r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
-                    sm.G[i][j] = gg;
-                    sm.A[i * SM::AP + j] = sm.beta[i] * gg;
-                }
-            }
-        }
-        __syncthreads();
-        // T = (I + A)^{-1} on wave 0; meanwhile R = diag(beta) (V - diag(gamma) X) into dR on
-        // waves 4-7 and, in the adjoint, the parts of dU that do not need U on waves 1-3 and 5:
-        // K D (kept in eO for dw), dU = diag(w) K D + P^T dO, and <D, H> on every thread
-        if (wave == 0) solve_unit_lower_inverse<float, CB>(sm);
-        const int rt = tid - (kThreads - kRowThreads);
-        if (rt >= 0) {
-            const int i = rt / (TV / 4), j0 = (rt % (TV / 4)) * 4;
-            const float be = sm.beta[i], ga = __expf(sm.b[i]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sm.dR[i][j0 + v] = be * (sm.V[i][j0 + v] - ga * sm.X[i][j0 + v]);
-        }
-        if (adjoint) {
-            const int tile = wave == 5 ? 0 : (wave >= 1 && wave <= 3) ? wave : -1;
-            if (tile >= 0) {
-                const float blast = sm.b[CB - 1];
-                const int mt = tile >> 1, nt = tile & 1;
-                const floatx4 kd = mm<DK, false, false, kX>(zero4(), &sm.K[0][0], SM::KP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
-                const floatx4 pd = mm<CB, true, false, false, kX>(zero4(), &sm.P[0][0], SM::TP, 16 * mt, &sm.dO[0][0], SM::VP, 16 * nt);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                    const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-                    sm.dU[i][j] = wi * kd[r] + pd[r];
-                    sm.eO[i][j] = kd[r];
-                }
-            }
-            float s = 0.f;
-            for (int u = 0; u < SR; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) s += sm.D[sr0 + u][sc0 + v] * sm.H[sr0 + u][sc0 + v];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-            if (lane == 0) sm.hdp[wave] = s;
-        }
-        __syncthreads();
-        // U = T R
-        if (wave < 4) {
-            const int mt = wave >> 1, nt = wave & 1;
-            const floatx4 u = mm<CB, false, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dR[0][0], SM::VP, 16 * nt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.U[16 * mt + 4 * g + r][16 * nt + cc] = u[r];
-        }
-        __syncthreads();
+        for (int ks = 0; ks < kSlices; ++ks)
+            if (32 * ks <= 16 * mt + 15) tr[ks] = ld_slab(rec0 + c * kBwdRecBytes, kRecT, mt, ks);
     };
-
-    // A thread's part of a state slice: SR rows of 4 consecutive columns, moved as 16-byte pieces
-    // (all loads issued before the stores).
-    auto load_slice = [&](float (*dst)[SM::VP], const float *src, int64_t pitch) __attribute__((always_inline)) {
-        float4 x[SR];
-#pragma unroll
-        for (int u = 0; u < SR; ++u)
-            x[u] = src ? *reinterpret_cast<const float4 *>(src + (int64_t)(sr0 + u) * pitch + sc0) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < SR; ++u) *reinterpret_cast<float4 *>(&dst[sr0 + u][sc0]) = x[u];
-    };
-    // ---- sweep 1: the chunk-form forward from h0, storing each chunk's entry state
-    // (the inputs of chunk c + 1 are read into registers while chunk c is computed)
-    load_slice(sm.H, a.h0 ? a.h0 + sbase : nullptr, dvf);
-    StageRegs nx;
-    if (nch > 0) stage_issue(0, false, nx);
+    if (nch > 0) {
+        issue(0);
+        issue_t(0);
+    }
     __syncthreads();
     for (int64_t c = 0; c < nch; ++c) {
+        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
 #pragma unroll
         for (int u = 0; u < SR; ++u)
-            *reinterpret_cast<float4 *>(ckpt + c * cstride + (sr0 + u) * TV + sc0) =
-                *reinterpret_cast<const float4 *>(&sm.H[sr0 + u][sc0]);
-        stage_store(c, nx);
-        if (c + 1 < nch) stage_issue(c + 1, false, nx);
-        __syncthreads();
-        gates();
-        __syncthreads();
-        forward_parts(false);
-        // H' = gamma_last H + K^T diag(w) U (wU into dU first)
-        const float blast = sm.b[CB - 1], glast = __expf(blast);
-        if (tid < kRowThreads) {
-            const float wi = __expf(fminf(blast - sm.b[ei], 0.f));
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sm.dU[ei][ej + v] = wi * sm.U[ei][ej + v];
+            *reinterpret_cast<float4 *>(hs + c * hstride + (sl.r0 + u) * TV + sl.c0) =
+                *reinterpret_cast<const float4 *>(&sm.H[sl.r0 + u][sl.c0]);
+        kp.store(&sm.K[0][0], SM::KP, n, tid);
+        vp.store(&sm.V[0][0], SM::VP, n, tid);
+        if (tid < CB) {
+            sm.b[tid] = bv;
+            sm.beta[tid] = betav;
         }
+        if (c + 1 < nch) issue(c + 1);
         __syncthreads();
-        for (int t = wave; t < (DK / 16) * (TV / 16); t += kWaves) {
-            const int mt = t / (TV / 16), nt = t % (TV / 16);
-            floatx4 h;
+        // X = K H, R = diag(beta) (V - diag(gamma) X)
+        {
+            floatx4 x = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = glast * sm.H[16 * mt + 4 * g + r][16 * nt + cc];
-            h = mm<CB, true, false, kX>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.H[16 * mt + 4 * g + r][16 * nt + cc] = h[r];
-        }
-        __syncthreads();
-    }
-
-    // ---- sweep 2: the adjoint, chunk by chunk from the last (the inputs of chunk c - 1 are read
-    // into registers while chunk c is computed)
-    load_slice(sm.D, a.dhT ? a.dhT + sbase : nullptr, dvf);
-    if (nch > 0) stage_issue(nch - 1, true, nx);
-    // the entry state slice of the chunk after next is read into registers one chunk ahead
-    float4 hpre[SR];
-    auto slice_issue = [&](int64_t cc) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < SR; ++u) hpre[u] = *reinterpret_cast<const float4 *>(ckpt + cc * cstride + (int64_t)(sr0 + u) * TV + sc0);
-    };
-    if (nch > 0) slice_issue(nch - 1);
-    for (int64_t c = nch - 1; c >= 0; --c) {
-        const int n = n_rows(c);
-#pragma unroll
-        for (int u = 0; u < SR; ++u) *reinterpret_cast<float4 *>(&sm.H[sr0 + u][sc0]) = hpre[u];
-        if (c > 0) slice_issue(c - 1);
-        stage_store(c, nx);
-        if (c > 0) stage_issue(c - 1, true, nx);
-        __syncthreads();
-        gates();
-        __syncthreads();
-        forward_parts(true);
-        const float blast = sm.b[CB - 1], glast = __expf(blast);
-
-        // dR = T^T dU on waves 0-3; dw_i = (K D)_i . U_i (K D in eO) on waves 4-7
-        if (wave < 4) {
-            const int mt = wave >> 1, nt = wave & 1;
-            const floatx4 d = mm<CB, true, false>(zero4(), sm.T, SM::TP, 16 * mt, &sm.dU[0][0], SM::VP, 16 * nt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.dR[16 * mt + 4 * g + r][16 * nt + cc] = d[r];
-        } else {
-            const int rt = tid - (kThreads - kRowThreads);
-            const int i = rt / (TV / 4), j0 = (rt % (TV / 4)) * 4;
-            float sw = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sw += sm.eO[i][j0 + v] * sm.U[i][j0 + v];
-            sw += __shfl_xor(sw, 1, 64);
-            sw += __shfl_xor(sw, 2, 64);
-            sw += __shfl_xor(sw, 4, 64);
-            if ((rt % (TV / 4)) == 0) sm.dw[i] = sw;
-        }
-        __syncthreads();
-        // dP = dO U^T -> M, dA = -dR U^T -> beta N on the lower tiles; their exponent and beta
-        // gradients; then dV, R's gradients, and the scaled copies for the products below
-        for (int t = wave; t < 6; t += kWaves) {
-            const bool isa = t >= 3;
-            const int tt = t % 3, mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
-            floatx4 v = isa ? mm<TV, false, true>(zero4(), &sm.dR[0][0], SM::VP, 16 * mt, &sm.U[0][0], SM::VP, 16 * nt)
-                            : mm<TV, false, true, kX>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.U[0][0], SM::VP, 16 * nt);
-            if (isa) v = -v;
-            float colsum[4];
+            for (int ks = 0; ks < DK / 32; ++ks)
+                x = mms<kX, false>(x, ldr<E>(&sm.K[0][0], SM::KP, 16 * mt, 32 * ks), ldc<float>(&sm.H[0][0], FP, 16 * nt, 32 * ks));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                float rs = 0.f, rb = 0.f;
+                sm.R[i][j] = sm.beta[i] * ((float)sm.V[i][j] - __expf(sm.b[i]) * x[r]);
+            }
+        }
+        __syncthreads();
+        // U = T R (to the workspace), diag(w) U
+        {
+            floatx4 u = zero4();
+#pragma unroll
+            for (int ks = 0; ks < kSlices; ++ks)
+                if (32 * ks <= 16 * mt + 15) u = mms<false, false>(u, slab_split(tr[ks]), ldc<float>(&sm.R[0][0], FP, 16 * nt, 32 * ks));
+            const float blast = sm.b[CB - 1];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+                if (i < n) ub[L.sq.token(c * CB + i) * dvf + j] = u[r];
+                sm.wU[i][j] = __expf(fminf(blast - sm.b[i], 0.f)) * u[r];
+            }
+        }
+        if (c + 1 < nch) issue_t(c + 1);
+        __syncthreads();
+        // H' = gamma_last H + K^T diag(w) U, each wave on its own tiles of H
+        {
+            const float glast = __expf(sm.b[CB - 1]);
+            for (int t = wave; t < (DK / 16) * (TV / 16); t += kWaves) {
+                const int hm = t / (TV / 16), hn = t % (TV / 16);
+                floatx4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[r] = glast * sm.H[16 * hm + 4 * g + r][16 * hn + cc];
+#pragma unroll
+                for (int ks = 0; ks < kSlices; ++ks)
+                    h = mms<kX, false>(h, ldc<E>(&sm.K[0][0], SM::KP, 16 * hm, 32 * ks), ldc<float>(&sm.wU[0][0], FP, 16 * hn, 32 * ks));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.H[16 * hm + 4 * g + r][16 * hn + cc] = h[r];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Adjoint sweep of one (sequence, value head, column slice), from the last chunk: per chunk, the
+// exit adjoint D to the workspace, dU = diag(w) K D + Pm^T dO, dR = T^T dU (to the workspace;
+// dV = diag(beta) dR) and D <- gamma_last D + Q^T diag(e^r) dO - K^T diag(beta gamma) dR.
+template <typename E, int DK>
+__device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int tile, char *smraw) {
+    typedef AdjSmem<E, DK> SM;
+    SM &sm = *reinterpret_cast<SM *>(smraw);
+    constexpr bool kX = std::is_same<E, __bf16>::value;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, cc = lane & 15;
+    const int64_t seq = unit / a.Hv, head = unit % a.Hv, kh = head / (a.Hv / a.Hk);
+    const Loc L = locate_seq(a, seq);
+    const int64_t nch = (L.sq.len + CB - 1) / CB;
+    const int64_t dvf = a.ntiles * TV;
+    const int col0 = tile * TV;
+    const E *kb = reinterpret_cast<const E *>(a.k) + (L.row * a.Hk + kh) * a.T * DK;
+    const E *qb = reinterpret_cast<const E *>(a.q) + (L.row * a.Hk + kh) * a.T * DK;
+    const E *ob = reinterpret_cast<const E *>(a.dout) + (L.row * a.Hv + head) * a.T * dvf + col0;
+    const float *beb = a.beta + (L.row * a.Hv + head) * a.T;
+    float *drb = a.drs + (L.row * a.Hv + head) * a.T * dvf + col0;
+    float *dvb = a.dv + (L.row * a.Hv + head) * a.T * dvf + col0;
+    constexpr int64_t kSlice = (int64_t)DK * TV;
+    float *ds = a.ds + ((head * a.nslots + L.slot0) * a.ntiles + tile) * kSlice;
+    const int64_t dstride = a.ntiles * kSlice;
+    const uint8_t *rec0 = a.rec + (head * a.nslots + L.slot0) * kBwdRecBytes;
+    const SliceMap<DK> sl(tid);
+    constexpr int SR = SliceMap<DK>::SR;
+    const int64_t sbase = (seq * a.Hv + head) * DK * dvf + col0;
+#pragma unroll
+    for (int u = 0; u < SR; ++u)
+        *reinterpret_cast<float4 *>(&sm.D[sl.r0 + u][sl.c0]) =
+            a.dhT ? *reinterpret_cast<const float4 *>(a.dhT + sbase + (int64_t)(sl.r0 + u) * dvf + sl.c0) : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    const int mt = wave >> 1, nt = wave & 1;
+    Rows<E, DK, kThreads> kp, qp;
+    Rows<E, TV, kThreads> op;
+    float bv = 0.f, rv = 0.f, betav = 0.f;
+    // T^T and Pm^T: rows 16 mt .. 16 mt + 15 are zero before column 16 mt
+    Slab tt[kSlices], pt[kSlices];
+    auto issue = [&](int64_t c) __attribute__((always_inline)) {
+        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
+        kp.issue(kb, DK, L.sq, c, n, tid);
+        qp.issue(qb, DK, L.sq, c, n, tid);
+        op.issue(ob, dvf, L.sq, c, n, tid);
+        if (tid < CB) {
+            const float *rb = reinterpret_cast<const float *>(rec0 + c * kBwdRecBytes + 3 * kMatBytes);
+            bv = rb[tid];
+            rv = rb[CB + tid];
+            betav = tid < n ? beb[L.sq.token(c * CB + tid)] : 0.f;
+        }
+    };
+    auto issue_f = [&](int64_t c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < kSlices; ++ks)
+            if (32 * ks + 31 >= 16 * mt) {
+                tt[ks] = ld_slab(rec0 + c * kBwdRecBytes, kRecTt, mt, ks);
+                pt[ks] = ld_slab(rec0 + c * kBwdRecBytes, kRecPt, mt, ks);
+            }
+    };
+    if (nch > 0) {
+        issue(nch - 1);
+        issue_f(nch - 1);
+    }
+    __syncthreads();
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
+#pragma unroll
+        for (int u = 0; u < SR; ++u)
+            *reinterpret_cast<float4 *>(ds + c * dstride + (sl.r0 + u) * TV + sl.c0) =
+                *reinterpret_cast<const float4 *>(&sm.D[sl.r0 + u][sl.c0]);
+        kp.store(&sm.K[0][0], SM::KP, n, tid);
+        qp.store(&sm.Q[0][0], SM::KP, n, tid);
+        op.store(&sm.dO[0][0], SM::VP, n, tid);
+        if (tid < CB) {
+            sm.b[tid] = bv;
+            sm.er[tid] = __expf(rv);
+            sm.beta[tid] = betav;
+        }
+        if (c > 0) issue(c - 1);
+        __syncthreads();
+        // dU = diag(w) K D + Pm^T dO
+        {
+            floatx4 y = zero4(), p = zero4();
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                y = mms<kX, false>(y, ldr<E>(&sm.K[0][0], SM::KP, 16 * mt, 32 * ks), ldc<float>(&sm.D[0][0], FP, 16 * nt, 32 * ks));
+#pragma unroll
+            for (int ks = 0; ks < kSlices; ++ks)
+                if (32 * ks + 31 >= 16 * mt) p = mms<false, kX>(p, slab_split(pt[ks]), ldc<E>(&sm.dO[0][0], SM::VP, 16 * nt, 32 * ks));
+            const float blast = sm.b[CB - 1];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+                sm.dU[i][j] = __expf(fminf(blast - sm.b[i], 0.f)) * y[r] + p[r];
+            }
+        }
+        __syncthreads();
+        // dR = T^T dU (to the workspace), dV = diag(beta) dR, -diag(beta gamma) dR
+        {
+            floatx4 d = zero4();
+#pragma unroll
+            for (int ks = 0; ks < kSlices; ++ks)
+                if (32 * ks + 31 >= 16 * mt) d = mms<false, false>(d, slab_split(tt[ks]), ldc<float>(&sm.dU[0][0], FP, 16 * nt, 32 * ks));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
+                const float be = sm.beta[i];
+                if (i < n) {
+                    const int64_t t = L.sq.token(c * CB + i);
+                    drb[t * dvf + j] = d[r];
+                    dvb[t * dvf + j] = be * d[r];
+                }
+                sm.bR[i][j] = -be * __expf(sm.b[i]) * d[r];
+            }
+        }
+        if (c > 0) issue_f(c - 1);
+        __syncthreads();
+        // D <- gamma_last D + (diag(e^r) Q)^T dO + K^T bR, each wave on its own tiles of D
+        {
+            const float glast = __expf(sm.b[CB - 1]);
+            for (int t = wave; t < (DK / 16) * (TV / 16); t += kWaves) {
+                const int hm = t / (TV / 16), hn = t % (TV / 16);
+                floatx4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[r] = glast * sm.D[16 * hm + 4 * g + r][16 * hn + cc];
+#pragma unroll
+                for (int ks = 0; ks < kSlices; ++ks) {
+                    h = mms<false, kX>(h, ldc_kscaled<E>(&sm.Q[0][0], SM::KP, 16 * hm, 32 * ks, sm.er),
+                                       ldc<E>(&sm.dO[0][0], SM::VP, 16 * hn, 32 * ks));
+                    h = mms<kX, false>(h, ldc<E>(&sm.K[0][0], SM::KP, 16 * hm, 32 * ks), ldc<float>(&sm.bR[0][0], FP, 16 * hn, 32 * ks));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.D[16 * hm + 4 * g + r][16 * hn + cc] = h[r];
+            }
+        }
+        __syncthreads();
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int u = 0; u < SR; ++u)
+            *reinterpret_cast<float4 *>(a.dh0 + sbase + (int64_t)(sl.r0 + u) * dvf + sl.c0) =
+                *reinterpret_cast<const float4 *>(&sm.D[sl.r0 + u][sl.c0]);
+    }
+}
+
+// Both sweeps in one launch: workgroups [0, n) run the forward sweep, [n, 2n) the adjoint sweep
+// (n = units x column slices). Workgroup ids are spread so that the column slices of a unit
+// run on the same XCD (workgroups go to the XCDs round robin) and share its L2.
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char smraw[sweep_smem_bytes<E, DK>()];
+    const int64_t n = a.units * a.ntiles, nb = 2 * n;
+    int64_t id = blockIdx.x;
+    if (nb % 8 == 0) id = (id % 8) * (nb / 8) + id / 8;
+    const bool adjoint = id >= n;
+    const int64_t w = adjoint ? id - n : id;
+    if (adjoint) adj_sweep<E, DK>(a, w / a.ntiles, (int)(w % a.ntiles), smraw);
+    else fwd_sweep<E, DK>(a, w / a.ntiles, (int)(w % a.ntiles), smraw);
+}
+
+// ---------------------------------------------------------------- 3. gradients
+
+template <typename E, int DK>
+struct GradSmem {
+    static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
+    E K[CB][KP], Q[CB][KP];
+    union {
+        struct {
+            float H[DK][FP], D[DK][FP];  // a column slice of the entry state and the exit adjoint
+        } t;
+        struct {
+            float M[CB][SP], N[CB][SP];  // once every slice is done
+        } m;
+    } u;
+    float U[CB][FP], dR[CB][FP];
+    E dO[CB][VP], V[CB][VP];
+    float b[CB], r[CB], beta[CB];
+    // Per-row partial sums, one slot per contributing tile, added in a fixed order:
+    //   sx, sb, sw: dR . X, dR . (V - gamma X) and (K D) . U over the two 16-column halves
+    //   pr, ar, gr: row sums of dP Pm, dA A and dA G per column tile; pc, ac: their column sums
+    //   (negated) per row tile; rq: e^r (dO H^T) . q per 16-column tile of d_k
+    float sx[2][CB], sb[2][CB], sw[2][CB];
+    float pr[NMT][CB], pc[NMT][CB], ar[NMT][CB], ac[NMT][CB], gr[NMT][CB];
+    float rq[DK / 16][CB];
+    float hd[kWaves];
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
+    typedef GradSmem<E, DK> SM;
+    __shared__ SM sm;
+    constexpr bool kX = std::is_same<E, __bf16>::value;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, cc = lane & 15;
+    const int64_t kh = blockIdx.x / a.nslots, slot = blockIdx.x % a.nslots;
+    Loc L;
+    int64_t c;
+    if (!locate_slot(a, slot, L, c)) return;
+    const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
+    const bool pre = (a.flags & kFlagReadPre) != 0;
+    const int64_t grp = a.Hv / a.Hk, dvf = a.ntiles * TV;
+    const int64_t nit = grp * a.ntiles;
+    constexpr int64_t kSlice = (int64_t)DK * TV;
+    const E *qb = reinterpret_cast<const E *>(a.q) + (L.row * a.Hk + kh) * a.T * DK;
+    const E *kb = reinterpret_cast<const E *>(a.k) + (L.row * a.Hk + kh) * a.T * DK;
+    {
+        Rows<E, DK, kThreads> kp, qp;
+        kp.issue(kb, DK, L.sq, c, n, tid);
+        qp.issue(qb, DK, L.sq, c, n, tid);
+        kp.store(&sm.K[0][0], SM::KP, n, tid);
+        qp.store(&sm.Q[0][0], SM::KP, n, tid);
+    }
+    // staged inputs of one (value head, column slice) step
+    const SliceMap<DK> sl(tid);
+    constexpr int SR = SliceMap<DK>::SR;
+    float4 hpre[SR], dpre[SR], upre, rpre;
+    Rows<E, TV, kThreads> op, vp;
+    float gb = 0.f, gr_ = 0.f, gbeta = 0.f;
+    const int ur = tid / (TV / 4), uc = (tid % (TV / 4)) * 4;  // the thread's 4 elements of U and dR
+    static_assert(CB * TV / 4 == kThreads, "one 16-byte piece of U and of dR per thread");
+    auto issue = [&](int64_t it) __attribute__((always_inline)) {
+        const int64_t head = kh * grp + it / a.ntiles;
+        const int tile = (int)(it % a.ntiles);
+        const int64_t sidx = ((head * a.nslots + slot) * a.ntiles + tile) * kSlice;
+#pragma unroll
+        for (int u = 0; u < SR; ++u) {
+            hpre[u] = *reinterpret_cast<const float4 *>(a.hs + sidx + (sl.r0 + u) * TV + sl.c0);
+            dpre[u] = *reinterpret_cast<const float4 *>(a.ds + sidx + (sl.r0 + u) * TV + sl.c0);
+        }
+        const int64_t vbase = (L.row * a.Hv + head) * a.T * dvf + tile * TV;
+        const int64_t tu = L.sq.token(c * CB + (ur < n ? ur : 0));
+        upre = *reinterpret_cast<const float4 *>(a.us + vbase + tu * dvf + uc);
+        rpre = *reinterpret_cast<const float4 *>(a.drs + vbase + tu * dvf + uc);
+        op.issue(reinterpret_cast<const E *>(a.dout) + vbase, dvf, L.sq, c, n, tid);
+        vp.issue(reinterpret_cast<const E *>(a.v) + vbase, dvf, L.sq, c, n, tid);
+        if (tid < CB) {
+            const float *rb = reinterpret_cast<const float *>(a.rec + (head * a.nslots + slot) * kBwdRecBytes + 3 * kMatBytes);
+            gb = rb[tid];
+            gr_ = rb[CB + tid];
+            gbeta = tid < n ? a.beta[(L.row * a.Hv + head) * a.T + L.sq.token(c * CB + tid)] : 0.f;
+        }
+    };
+
+    // tile assignments: X and K D: tile (xm, xn) of the CB x TV slice; dP, dA: lower tiles
+    // wave, wave + 8, wave + 16 of the twenty; dQ, dK: d_k tile qn, row tiles qm(s)
+    const int xm = wave >> 1, xn = wave & 1;
+    constexpr int NQ = DK / 16, NQT = NMT * NQ / kWaves;
+    const int qn = wave % NQ;
+    auto qm = [&](int s) __attribute__((always_inline)) -> int { return wave / NQ + s * (kWaves / NQ); };
+    floatx4 dQ[NQT], dK[NQT], dQH[NQT], pa[3];
+#pragma unroll
+    for (int s = 0; s < NQT; ++s) {
+        dQ[s] = zero4();
+        dK[s] = zero4();
+    }
+    float ax[4], bx[4], wy[4], hsum = 0.f;
+
+    if (nit > 0) issue(0);
+    for (int64_t it = 0; it < nit; ++it) {
+        const int64_t v = it / a.ntiles;
+        const int tile = (int)(it % a.ntiles);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < SR; ++u) {
+            *reinterpret_cast<float4 *>(&sm.u.t.H[sl.r0 + u][sl.c0]) = hpre[u];
+            *reinterpret_cast<float4 *>(&sm.u.t.D[sl.r0 + u][sl.c0]) = dpre[u];
+        }
+        const bool urow = ur < n;
+        *reinterpret_cast<float4 *>(&sm.U[ur][uc]) = urow ? upre : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(&sm.dR[ur][uc]) = urow ? rpre : make_float4(0.f, 0.f, 0.f, 0.f);
+        op.store(&sm.dO[0][0], SM::VP, n, tid);
+        vp.store(&sm.V[0][0], SM::VP, n, tid);
+        if (tile == 0) {
+            if (tid < CB) {
+                sm.b[tid] = gb;
+                sm.r[tid] = gr_;
+                sm.beta[tid] = gbeta;
+            }
+#pragma unroll
+            for (int s = 0; s < NQT; ++s) dQH[s] = zero4();
+#pragma unroll
+            for (int s = 0; s < 3; ++s) pa[s] = zero4();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ax[r] = bx[r] = wy[r] = 0.f;
+            hsum = 0.f;
+        }
+        if (it + 1 < nit) issue(it + 1);
+        __syncthreads();
+        const float blast = sm.b[CB - 1];
+        // X = K H and Y = K D on this wave's tile: dR . X, dR . (V - gamma X), Y . U per row
+        {
+            floatx4 x = zero4(), y = zero4();
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const Split ka = ldr<E>(&sm.K[0][0], SM::KP, 16 * xm, 32 * ks);
+                x = mms<kX, false>(x, ka, ldc<float>(&sm.u.t.H[0][0], FP, 16 * xn, 32 * ks));
+                y = mms<kX, false>(y, ka, ldc<float>(&sm.u.t.D[0][0], FP, 16 * xn, 32 * ks));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * xm + 4 * g + r, j = 16 * xn + cc;
+                const float dr = sm.dR[i][j];
+                ax[r] += dr * x[r];
+                bx[r] += dr * ((float)sm.V[i][j] - __expf(sm.b[i]) * x[r]);
+                wy[r] += y[r] * sm.U[i][j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SR; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hsum += sm.u.t.D[sl.r0 + u][sl.c0 + q] * sm.u.t.H[sl.r0 + u][sl.c0 + q];
+        // dP = dO U^T and -dA = dR U^T on the lower tiles
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const int task = wave + kWaves * s;
+            if (task < 20) {
+                int pm, pn;
+                lower_tile(task % 10, pm, pn);
+                const Split ub = ldr<float>(&sm.U[0][0], FP, 16 * pn, 0);
+                if (task >= 10) pa[s] = mms<false, false>(pa[s], ldr<float>(&sm.dR[0][0], FP, 16 * pm, 0), ub);
+                else pa[s] = mms<kX, false>(pa[s], ldr<E>(&sm.dO[0][0], SM::VP, 16 * pm, 0), ub);
+            }
+        }
+        // dO H^T, and diag(w) U dH'^T - diag(beta gamma) dR H^T into dK
+        {
+            const Split hB = ldr<float>(&sm.u.t.H[0][0], FP, 16 * qn, 0);
+            const Split dB = ldr<float>(&sm.u.t.D[0][0], FP, 16 * qn, 0);
+#pragma unroll
+            for (int s = 0; s < NQT; ++s) {
+                const int m = qm(s), row = 16 * m + cc;
+                dQH[s] = mms<kX, false>(dQH[s], ldr<E>(&sm.dO[0][0], SM::VP, 16 * m, 0), hB);
+                const float wr = __expf(fminf(blast - sm.b[row], 0.f));
+                const float br = -sm.beta[row] * __expf(sm.b[row]);
+                dK[s] = mms<false, false>(dK[s], ldr_scaled(&sm.U[0][0], FP, 16 * m, 0, wr), dB);
+                dK[s] = mms<false, false>(dK[s], ldr_scaled(&sm.dR[0][0], FP, 16 * m, 0, br), hB);
+            }
+        }
+        if (tile + 1 < a.ntiles) continue;
+
+        // ---- every slice of value head v is in: M, N, the rest of dQ and dK, the gates
+        __syncthreads();
+        {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * xm + 4 * g + r;
+                const float s1 = row16(ax[r]), s2 = row16(bx[r]), s3 = row16(wy[r]);
+                if (cc == 0) {
+                    sm.sx[xn][i] = s1;
+                    sm.sb[xn][i] = s2;
+                    sm.sw[xn][i] = s3;
+                }
+            }
+            float h = hsum;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) h += __shfl_xor(h, off, 64);
+            if (lane == 0) sm.hd[wave] = h;
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const int task = wave + kWaves * s;
+            if (task >= 20) continue;
+            const bool isa = task >= 10;
+            int pm, pn;
+            lower_tile(task % 10, pm, pn);
+            // the tile of G (isa) or Pm, again
+            floatx4 gv = zero4();
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                gv = mms<kX, kX>(gv, ldr<E>(isa ? &sm.K[0][0] : &sm.Q[0][0], SM::KP, 16 * pm, 32 * ks),
+                                 ldr<E>(&sm.K[0][0], SM::KP, 16 * pn, 32 * ks));
+            float csum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * pm + 4 * g + r, j = 16 * pn + cc;
+                float rs, rb = 0.f;
                 if (!isa) {
                     const bool keep = pre ? j < i : j <= i;
-                    sm.M[i][j] = keep ? v[r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
-                    rs = keep ? v[r] * sm.P[i][j] : 0.f;  // dP_ij Pm_ij
+                    const float e = __expf(fminf(sm.r[i] - sm.b[j], 0.f));
+                    const float dp = pa[s][r];
+                    sm.u.m.M[i][j] = keep ? dp * e : 0.f;
+                    rs = keep ? dp * gv[r] * e : 0.f;  // dP_ij Pm_ij
                 } else {
                     const bool keep = j < i;
-                    sm.Nb[i][j] = keep ? sm.beta[i] * v[r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
-                    rs = keep ? v[r] * sm.A[i * SM::AP + j] : 0.f;  // dA_ij A_ij
-                    rb = keep ? v[r] * sm.G[i][j] : 0.f;  // dA_ij G_ij
+                    const float e = __expf(fminf(sm.b[i] - sm.b[j], 0.f));
+                    const float da = -pa[s][r], gij = keep ? gv[r] * e : 0.f;
+                    sm.u.m.N[i][j] = keep ? sm.beta[i] * da * e : 0.f;
+                    rs = da * sm.beta[i] * gij;  // dA_ij A_ij
+                    rb = da * gij;               // dA_ij G_ij
                 }
-                colsum[r] = rs;
-                const float rsum = row16(rs), bsum = row16(rb);
-                if (cc == 0) {
-                    if (isa) {
-                        sm.pdb[3 + tt][i] = rsum;
-                        sm.pdbeta[tt][i] = bsum;
-                    } else {
-                        sm.pdr[tt][i] = rsum;
+                csum += rs;
+                const float rsum = row16(rs);
+                if (isa) {
+                    const float bsum = row16(rb);
+                    if (cc == 0) {
+                        sm.ar[pn][i] = rsum;
+                        sm.gr[pn][i] = bsum;
                     }
+                } else if (cc == 0) {
+                    sm.pr[pn][i] = rsum;
+                }
+                if (pm > pn) {
+                    const int i2 = 16 * pn + 4 * g + r, j2 = 16 * pm + cc;
+                    if (isa) sm.u.m.N[i2][j2] = 0.f;
+                    else sm.u.m.M[i2][j2] = 0.f;
                 }
             }
-            // column sums (over the 16 rows of the tile) go to d b_j with a minus sign
-            float cs = colsum[0] + colsum[1] + colsum[2] + colsum[3];
-            cs = col4(cs);
-            if (g == 0) sm.pdb[(isa ? 6 : 0) + tt][16 * nt + cc] = -cs;
-        }
-        if (tid < kRowThreads) {
-            const int i = ei;
-            const float be = sm.beta[i], ga = __expf(sm.b[i]), er = __expf(sm.r[i]);
-            const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-            float sb = 0.f, sx = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int j = ej + v;
-                const float dr = sm.dR[i][j];
-                sb += dr * (sm.V[i][j] - ga * sm.X[i][j]);
-                sx += dr * sm.X[i][j];
-                if (i < n) dvb[sq.token(c * CB + i) * dvf + j] = be * dr;
-                sm.eO[i][j] = er * sm.dO[i][j];
-                sm.bR[i][j] = -be * ga * dr;
-                sm.dU[i][j] = wi * sm.U[i][j];
-            }
-            sb += __shfl_xor(sb, 1, 64); sb += __shfl_xor(sb, 2, 64); sb += __shfl_xor(sb, 4, 64);
-            sx += __shfl_xor(sx, 1, 64); sx += __shfl_xor(sx, 2, 64); sx += __shfl_xor(sx, 4, 64);
-            if ((tid % (TV / 4)) == 0) {
-                sm.pdbeta[3][i] = sb;
-                sm.pdb[9][i] = -be * ga * sx;
+            // column sums over the tile's 16 rows enter d b_j with a minus sign
+            csum = col4(csum);
+            if (g == 0) {
+                if (isa) sm.ac[pm][16 * pn + cc] = -csum;
+                else sm.pc[pm][16 * pn + cc] = -csum;
             }
         }
         __syncthreads();
-        // dQ = diag(e^r) dO H^T + M K;  dK = wU D^T + bR H^T + M^T Q + Nb K + Nb^T K
-        // (wU = diag(w) U in dU, bR = -diag(beta gamma) dR); the read's exponent gradient
-        for (int t = wave; t < 2 * (DK / 16); t += kWaves) {
-            const int mt = t / (DK / 16), nt = t % (DK / 16);
-            floatx4 oh = mm<TV, false, true, kX>(zero4(), &sm.dO[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
-            floatx4 dq;
+        // dQ += diag(e^r) dO H^T + M K;  dK += M^T Q + N K + N^T K (N holds diag(beta) N)
+#pragma unroll
+        for (int s = 0; s < NQT; ++s) {
+            const int m = qm(s);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * g + r;
-                const float er = __expf(sm.r[i]);
-                dq[r] = er * oh[r];
-                const float rq = row16(dq[r] * sm.Q[i][16 * nt + cc]);
-                if (cc == 0) sm.pdr[3 + nt][i] = rq;
+                const int i = 16 * m + 4 * g + r;
+                const float qh = __expf(sm.r[i]) * dQH[s][r];
+                const float rqv = row16(qh * (float)sm.Q[i][16 * qn + cc]);
+                if (cc == 0) sm.rq[qn][i] = rqv;
+                dQ[s][r] += qh;
             }
-            dq = mm<CB, false, false, false, kX>(dq, &sm.M[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
-            // three independent partial sums, so that the products do not wait on each other
-            floatx4 dk = mm<TV, false, true>(zero4(), &sm.dU[0][0], SM::VP, 16 * mt, &sm.D[0][0], SM::VP, 16 * nt);
-            floatx4 dk2 = mm<TV, false, true>(zero4(), &sm.bR[0][0], SM::VP, 16 * mt, &sm.H[0][0], SM::VP, 16 * nt);
-            floatx4 dk3 = mm<CB, true, false, false, kX>(zero4(), &sm.M[0][0], SM::TP, 16 * mt, &sm.Q[0][0], SM::KP, 16 * nt);
-            dk = mm<CB, false, false, false, kX>(dk, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
-            dk2 = mm<CB, true, false, false, kX>(dk2, &sm.Nb[0][0], SM::TP, 16 * mt, &sm.K[0][0], SM::KP, 16 * nt);
-            dk += dk2 + dk3;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * g + r;
-                if (i < n) {
-                    const int64_t tk = sq.token(c * CB + i);
-                    dqb[tk * DK + 16 * nt + cc] = dq[r];
-                    dkb[tk * DK + 16 * nt + cc] = dk[r];
+            for (int ks = 0; ks < kSlices; ++ks) {
+                const Split kB = ldc<E>(&sm.K[0][0], SM::KP, 16 * qn, 32 * ks);
+                if (32 * ks <= 16 * m + 15) {  // rows of M and N: zero past column 16 m + 15
+                    dQ[s] = mms<false, kX>(dQ[s], ldr<float>(&sm.u.m.M[0][0], SP, 16 * m, 32 * ks), kB);
+                    dK[s] = mms<false, kX>(dK[s], ldr<float>(&sm.u.m.N[0][0], SP, 16 * m, 32 * ks), kB);
+                }
+                if (32 * ks + 31 >= 16 * m) {  // columns of M and N: zero above row 16 m
+                    dK[s] = mms<false, kX>(dK[s], ldc<float>(&sm.u.m.M[0][0], SP, 16 * m, 32 * ks),
+                                           ldc<E>(&sm.Q[0][0], SM::KP, 16 * qn, 32 * ks));
+                    dK[s] = mms<false, kX>(dK[s], ldc<float>(&sm.u.m.N[0][0], SP, 16 * m, 32 * ks), kB);
                 }
             }
-        }
-        // dH = gamma_last D + Q^T eO + K^T bR
-        constexpr int NDH = ((DK / 16) * (TV / 16) + kWaves - 1) / kWaves;
-        floatx4 dh[NDH];
-        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += kWaves, ++s) {
-            const int mt = t / (TV / 16), nt = t % (TV / 16);
-            floatx4 h;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = glast * sm.D[16 * mt + 4 * g + r][16 * nt + cc];
-            h = mm<CB, true, false, kX>(h, &sm.Q[0][0], SM::KP, 16 * mt, &sm.eO[0][0], SM::VP, 16 * nt);
-            h = mm<CB, true, false, kX>(h, &sm.K[0][0], SM::KP, 16 * mt, &sm.bR[0][0], SM::VP, 16 * nt);
-            dh[s] = h;
         }
         __syncthreads();
-        for (int t = wave, s = 0; t < (DK / 16) * (TV / 16); t += kWaves, ++s) {
-            const int mt = t / (TV / 16), nt = t % (TV / 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.D[16 * mt + 4 * g + r][16 * nt + cc] = dh[s][r];
-        }
-        // gate gradients of the chunk: the exit decay terms on the last row, then suffix sums
-        if (tid < 64) {
-            const int i = tid;
-            float x = 0.f, z = 0.f;
-            float dbeta_i = 0.f;
-            if (i < CB) {
-                const float wi = __expf(fminf(blast - sm.b[i], 0.f));
-                float dbi = 0.f, dri = 0.f;
-#pragma unroll
-                for (int p = 0; p < SM::kPdb; ++p) dbi += sm.pdb[p][i];
-#pragma unroll
-                for (int p = 0; p < SM::kPdr; ++p) dri += sm.pdr[p][i];
-#pragma unroll
-                for (int p = 0; p < SM::kPdbeta; ++p) dbeta_i += sm.pdbeta[p][i];
-                dbi -= wi * sm.dw[i];
-                // the last row also takes glast <D, H> + sum_j w_j dw_j (a sum over the wave)
-                float s = __expf(fminf(blast - sm.b[i], 0.f)) * sm.dw[i];
-#pragma unroll
-                for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off, 32);
-                if (i == CB - 1) {
-                    float hd = 0.f;
-#pragma unroll
-                    for (int w = 0; w < kWaves; ++w) hd += sm.hdp[w];
-                    dbi += glast * hd + s;
-                }
-                // post: the read exponent is b itself; pre: b - log alpha leaves out row i's own
-                // log alpha, so its gradient enters the sums of the rows after it only
-                x = dbi + (pre ? 0.f : dri);
-                z = pre ? dri : 0.f;
+        // gate gradients of value head v: per-row sums, then suffix sums through the cumsum
+        if (wave == 0) {
+            const int i = lane, mi = i / 16;
+            const float wi = __expf(fminf(blast - sm.b[i], 0.f)), gi = __expf(sm.b[i]);
+            const float dwi = sm.sw[0][i] + sm.sw[1][i];
+            float db = 0.f, dr = 0.f, dbeta = sm.sb[0][i] + sm.sb[1][i];
+            for (int t = 0; t <= mi; ++t) {
+                db += sm.ar[t][i];
+                dr += sm.pr[t][i];
+                dbeta += sm.gr[t][i];
             }
+            for (int t = mi; t < NMT; ++t) db += sm.pc[t][i] + sm.ac[t][i];
+#pragma unroll
+            for (int t = 0; t < DK / 16; ++t) dr += sm.rq[t][i];
+            db -= sm.beta[i] * gi * (sm.sx[0][i] + sm.sx[1][i]);
+            db -= wi * dwi;
+            // the last row also takes gamma_last <D, H> + sum_j w_j (K D)_j . U_j
+            float s = wi * dwi;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+            if (i == CB - 1) {
+                float hd = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) hd += sm.hd[w];
+                db += __expf(blast) * hd + s;
+            }
+            // post: the read exponent is b itself; pre: b - log alpha leaves out row i's own
+            // log alpha, so its gradient enters the sums of the rows after it only
+            float x = db + (pre ? 0.f : dr), z = pre ? dr : 0.f;
             const float zi = z;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -643,81 +1030,57 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 }
             }
             if (i < n) {
-                const int64_t t = sq.token(c * CB + i);
-                dlab[t] = x + z - zi;
-                dbeb[t] = dbeta_i;
+                const int64_t head = kh * grp + v;
+                const int64_t t = (L.row * a.Hv + head) * a.T + L.sq.token(c * CB + i);
+                a.dlog_alpha[t] = x + z - zi;
+                a.dbeta[t] = dbeta;
             }
         }
-        __syncthreads();
     }
-    if (a.dh0) {
+    // dq, dk of the key head: the sum over its value heads, in order
+    const int64_t qbase = (L.row * a.Hk + kh) * a.T * DK;
 #pragma unroll
-        for (int u = 0; u < SR; ++u)
-            *reinterpret_cast<float4 *>(a.dh0 + sbase + (int64_t)(sr0 + u) * dvf + sc0) =
-                *reinterpret_cast<const float4 *>(&sm.D[sr0 + u][sc0]);
-    }
-}
-
-// dq, dk: the sum over the value heads of a key head and over the column slices of the
-// partials, 4 consecutive d_k elements per thread; dlog alpha, dbeta: the sum over the column
-// slices. Every sum runs in the same order on every call.
-__global__ void bwd_reduce_kernel(BwdArgs a, int dk) {
-    const int64_t grp = a.Hv / a.Hk;
-    const int64_t nq4 = a.B * a.Hk * a.T * dk / 4, ng = a.B * a.Hv * a.T;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nq4 + ng; e += stride) {
-        if (e < nq4) {
-            const int64_t i = 4 * e;                    // element of [B][Hk][T][dk]
-            const int64_t td = i % (a.T * dk), bk = i / (a.T * dk);
-            const int64_t b = bk / a.Hk, kh = bk % a.Hk;
-            float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
-            for (int64_t j = 0; j < grp; ++j)
-                for (int64_t t = 0; t < a.ntiles; ++t) {
-                    const int64_t src = ((b * a.Hv + kh * grp + j) * a.ntiles + t) * a.T * dk + td;
-                    const float4 x = *reinterpret_cast<const float4 *>(a.pq + src);
-                    const float4 y = *reinterpret_cast<const float4 *>(a.pk + src);
-                    sq.x += x.x; sq.y += x.y; sq.z += x.z; sq.w += x.w;
-                    sk.x += y.x; sk.y += y.y; sk.z += y.z; sk.w += y.w;
-                }
-            *reinterpret_cast<float4 *>(a.dq + i) = sq;
-            *reinterpret_cast<float4 *>(a.dk + i) = sk;
-        } else {
-            const int64_t i = e - nq4;                  // element of [B][Hv][T]
-            const int64_t tt = i % a.T, bh = i / a.T;
-            float sl = 0.f, sb = 0.f;
-            for (int64_t t = 0; t < a.ntiles; ++t) {
-                sl += a.pla[(bh * a.ntiles + t) * a.T + tt];
-                sb += a.pbeta[(bh * a.ntiles + t) * a.T + tt];
+    for (int s = 0; s < NQT; ++s) {
+        const int m = qm(s);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * m + 4 * g + r;
+            if (i < n) {
+                const int64_t o = qbase + L.sq.token(c * CB + i) * DK + 16 * qn + cc;
+                a.dq[o] = dQ[s][r];
+                a.dk[o] = dK[s][r];
             }
-            a.dlog_alpha[i] = sl;
-            a.dbeta[i] = sb;
         }
     }
 }
 
 template <typename E, int DK>
 hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_kernel<E, DK>), dim3((unsigned)(a.units * a.ntiles)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    const int64_t np = a.Hv * a.nslots, nsw = 2 * a.units * a.ntiles, ng = a.Hk * a.nslots;
+    if (np > 0) {
+        hipLaunchKernelGGL((bwd_prep_kernel<E, DK>), dim3((unsigned)np), dim3(kPrepThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (nsw > 0) {
+        hipLaunchKernelGGL((bwd_sweep_kernel<E, DK>), dim3((unsigned)nsw), dim3(kThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (ng > 0) {
+        hipLaunchKernelGGL((bwd_grad_kernel<E, DK>), dim3((unsigned)ng), dim3(kThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, int dtype, int dk, int dv, hipStream_t stream) {
     (void)dv;
-    hipError_t e = hipSuccess;
-    if (a.units > 0) {
-        if (dtype == kDtypeBf16) e = dk == 64 ? launch_t<__bf16, 64>(a, stream) : launch_t<__bf16, 128>(a, stream);
-        else e = dk == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
-        if (e != hipSuccess) return e;
-    }
-    // every element of dq, dk, dlog alpha and dbeta is written by the reduction (zero where no
-    // partial exists: no value heads or no column slices cannot happen, T = 0 has no elements)
-    const int64_t work = a.B * a.Hk * a.T * dk / 4 + a.B * a.Hv * a.T;
-    if (work <= 0) return hipSuccess;
-    const int64_t blocks = (work + 255) / 256;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, a, dk);
-    return hipGetLastError();
+    if (dtype == kDtypeBf16) return dk == 64 ? launch_t<__bf16, 64>(a, stream) : launch_t<__bf16, 128>(a, stream);
+    return dk == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
 }
 
 }  // namespace gdr

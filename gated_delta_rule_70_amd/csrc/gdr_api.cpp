@@ -460,27 +460,31 @@ gdr_status_t gdr_gdn2_decode_step(const void *q, const void *k, const void *v, c
 
 namespace {
 
-// chunk-start states per value head: one slot per 32-token chunk of every sequence
+// chunk slots per value head: one per 64-token chunk of every sequence (packed: the slots of
+// segment s start at cu[s] / 64 + s, so that no two segments share one)
 int64_t bwd_slots(const gdr_chunk_dims_t &d, bool packed) {
     const int64_t CB = gdr::kBwdBlock;
     if (packed) return d.T / CB + d.num_seqs + 1;
     return d.B * ((d.T + CB - 1) / CB);
 }
 
-// the state at the start of every chunk of every sequence-head, then each 32-column slice's
-// partial dq, dk ([B][Hv][dv / 32][T][dk] each) and partial dlog_alpha, dbeta ([B][Hv][dv / 32][T]
-// each), which a second kernel adds up in a fixed order
-int64_t bwd_ckpt_bytes(const gdr_chunk_dims_t &d, bool packed) {
-    return prod({d.Hv, bwd_slots(d, packed), d.dk, d.dv, 4});
+// Workspace of the backward, in this order: a record per (value head, slot) (the chunk's
+// triangular inverse and read matrix as matrix-core operands, and its gate cumsums); the entry
+// state and the exit-state adjoint of every chunk (dk x dv fp32 each); U and dR of every token
+// ([B][Hv][T][dv] fp32 each).
+struct BwdLayout {
+    int64_t rec, states, tokens, total;
+};
+BwdLayout bwd_layout(const gdr_chunk_dims_t &d, bool packed) {
+    BwdLayout l;
+    const int64_t slots = bwd_slots(d, packed);
+    l.rec = prod({d.Hv, slots, gdr::kBwdRecBytes});
+    l.states = prod({d.Hv, slots, d.dk, d.dv, 4});
+    l.tokens = prod({d.B, d.Hv, d.T, d.dv, 4});
+    l.total = (l.rec < 0 || l.states < 0 || l.tokens < 0) ? -1 : l.rec + 2 * l.states + 2 * l.tokens;
+    return l;
 }
-int64_t bwd_part_elems(const gdr_chunk_dims_t &d) {
-    return prod({d.B, d.Hv, d.dv / gdr::kBwdCols, d.T});
-}
-int64_t bwd_workspace_bytes(const gdr_chunk_dims_t &d, bool packed) {
-    const int64_t c = bwd_ckpt_bytes(d, packed), p = bwd_part_elems(d);
-    if (c < 0 || p < 0) return -1;
-    return c + p * (2 * d.dk + 2) * 4;
-}
+int64_t bwd_workspace_bytes(const gdr_chunk_dims_t &d, bool packed) { return bwd_layout(d, packed).total; }
 
 gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
                       const float *h0, const int32_t *cu_seqlens, const void *dout, const float *dhT, float *dq,
@@ -540,21 +544,23 @@ gdr_status_t bwd_impl(const void *q, const void *k, const void *v, const float *
     a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0; a.dhT = dhT;
     a.cu_seqlens = cu_seqlens;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
-    a.ws = static_cast<float *>(workspace);
     {
-        const int64_t pe = bwd_part_elems(d);
-        char *p = static_cast<char *>(workspace) + bwd_ckpt_bytes(d, cu_seqlens != nullptr);
-        a.pq = reinterpret_cast<float *>(p);
-        a.pk = a.pq + pe * d.dk;
-        a.pla = a.pk + pe * d.dk;
-        a.pbeta = a.pla + pe;
+        const BwdLayout l = bwd_layout(d, cu_seqlens != nullptr);
+        char *p = static_cast<char *>(workspace);
+        a.rec = reinterpret_cast<uint8_t *>(p);
+        a.hs = reinterpret_cast<float *>(p + l.rec);
+        a.ds = reinterpret_cast<float *>(p + l.rec + l.states);
+        a.us = reinterpret_cast<float *>(p + l.rec + 2 * l.states);
+        a.drs = reinterpret_cast<float *>(p + l.rec + 2 * l.states + l.tokens);
     }
     a.B = d.B; a.T = d.T; a.Hk = d.Hk; a.Hv = d.Hv;
+    a.nseq = nseq;
     a.units = nseq * d.Hv;
     a.nslots = bwd_slots(d, cu_seqlens != nullptr);
     a.ntiles = d.dv / gdr::kBwdCols;
     a.flags = d.flags;
-    if (a.units * a.ntiles > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units");
+    if (2 * a.units * a.ntiles > INT32_MAX || a.Hv * a.nslots > INT32_MAX)
+        return fail(GDR_ERR_DIMS, "too many (sequence, head) units or chunks");
     const hipError_t e = gdr::launch_bwd(a, d.dtype, (int)d.dk, (int)d.dv, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return GDR_OK;

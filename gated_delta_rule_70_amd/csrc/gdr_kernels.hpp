@@ -74,21 +74,25 @@ struct Gdn2DecodeArgs {
 
 // Backward of the scalar rule. Gradient buffers are fp32: dq, dk [B][Hk][T][dk] (summed over the
 // value heads of a key head), dv [B][Hv][T][dv], dlog_alpha, dbeta [B][Hv][T], dh0 like h0.
-// ws: the state at the start of every kBwdBlock-token chunk (nslots per value head); pq, pk
-// [B][Hv][ntiles][T][dk] and pla, pbeta [B][Hv][ntiles][T]: each column slice's share of dq, dk,
-// dlog_alpha and dbeta, summed in a fixed order by a second kernel (all four in the workspace).
-constexpr int kBwdBlock = 32;
-constexpr int kBwdCols = 32;  // value columns per workgroup of the backward
+// The workspace holds, per chunk slot of every value head (nslots per head, kBwdBlock tokens per
+// chunk): a record of kBwdRecBytes (the chunk's inverse and read matrix as matrix-core operands,
+// and its gate cumsums), the entry state hs and the exit-state adjoint ds of the chunk (per
+// kBwdCols-column slice, dk x kBwdCols fp32 each); and us, drs [B][Hv][T][dv] fp32, the chunk
+// form's U and dR of every token.
+constexpr int kBwdBlock = 64;
+constexpr int kBwdCols = 32;  // value columns per workgroup of the state sweeps
+constexpr int64_t kBwdRecBytes = 3 * 16384 + 2 * kBwdBlock * 4;
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *log_alpha, *beta, *h0, *dhT;
     const int32_t *cu_seqlens;
     float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dh0;
-    float *ws;
-    float *pq, *pk, *pla, *pbeta;
+    uint8_t *rec;
+    float *hs, *ds, *us, *drs;
     int64_t B, T, Hk, Hv;
+    int64_t nseq;    // sequences (B, or the packed segments)
     int64_t units;   // sequences x value heads
-    int64_t nslots;  // block-start states per value head
+    int64_t nslots;  // chunk slots per value head
     int64_t ntiles;  // dv / kBwdCols
     uint32_t flags;
 };
