@@ -74,14 +74,19 @@ constexpr int SP = CB + 4;  // pitch of fp32 [CB][CB] matrices
 template <typename E>
 constexpr int pad_of() { return 16 / (int)sizeof(E); }  // one 16-byte piece of padding per row
 
-// The record of one (value head, chunk slot): A-operand fragments of T, T^T and Pm^T as split bf16
-// ([16-row tile][32-deep slice][lane] of a 16-byte hi part and a 16-byte lo part, in the register
-// layout mma32 takes), then b[CB] and r[CB].
+// The record of one (value head, chunk slot): A-operand fragments of T, T^T and Pm^T as split
+// bf16 ([16-row tile][32-deep slice][lane] of a 16-byte hi part and a 16-byte lo part, in the
+// register layout mma32 takes), then b[CB] and r[CB].
 constexpr int kSlabBytes = 64 * 32;
 constexpr int kSlices = CB / 32;
 constexpr int kMatBytes = NMT * kSlices * kSlabBytes;
-static_assert(3 * kMatBytes + 2 * CB * 4 == kBwdRecBytes, "record layout");
-enum { kRecT = 0, kRecTt = 1, kRecPt = 2 };
+constexpr int kRecT = 0, kRecTt = kMatBytes, kRecPt = 2 * kMatBytes;
+template <int DK>
+struct Rec {
+    static constexpr int64_t kBytes = kBwdRecBytes;
+    static constexpr int kGates = 3 * kMatBytes;
+    static_assert(kGates + 2 * CB * 4 == kBytes, "record layout");
+};
 
 // the lower 16x16 tiles (mt >= nt) of a CB x CB matrix, in a fixed order
 __device__ __forceinline__ void lower_tile(int idx, int &mt, int &nt) {
@@ -93,6 +98,10 @@ struct Seq {
     int64_t t0, len;
     bool rev;
     __device__ __forceinline__ int64_t token(int64_t pos) const { return rev ? t0 + len - 1 - pos : t0 + pos; }
+    // the lowest token of chunk c (n rows), and row r's distance from it: per-lane addresses are a
+    // uniform base plus a small unsigned offset, which the loads take in scalar-base form
+    __device__ __forceinline__ int64_t low(int64_t c, int n) const { return rev ? token(c * CB + n - 1) : token(c * CB); }
+    __device__ __forceinline__ int off(int r, int n) const { return rev ? n - 1 - r : r; }
 };
 struct Loc {
     int64_t seq, row, slot0;  // row: the batch row of q, k, v (0 when packed)
@@ -161,6 +170,22 @@ __device__ __forceinline__ floatx4 mms(floatx4 acc, const Split &a, const Split 
     if constexpr (!BX) acc = mma32(acc, a.h, b.l);
     return mma32(acc, a.h, b.h);
 }
+// gfx950 transpose read: in each 16-lane group, lane i receives element i % 4 of the 8-byte
+// pieces addressed by lanes 4v + i / 4 (v = 0..3)
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+__device__ __forceinline__ bf16x4 tr16(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p)));
+}
+// columns of a row-major bf16 matrix (as frag_cols): lane j of group g addresses row
+// k0 + 4g + j / 4, columns col0 + 4 (j % 4) .. + 3, so that lane c receives X[k0 + 4g + v][col0 + c]
+__device__ __forceinline__ Frag<__bf16> cols_tr(const __bf16 *X, int ld, int col0, int k0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
+    const __bf16 *p = X + (k0 + 4 * g + (j >> 2)) * ld + col0 + 4 * (j & 3);
+    Frag<__bf16> f;
+    f.lo = tr16(p);
+    f.hi = tr16(p + 16 * ld);
+    return f;
+}
 // from an E-typed matrix in LDS: rows (A[m][k] = X[m][k] or B[k][n] = X[n][k]) or columns
 template <typename E>
 __device__ __forceinline__ Split ldr(const E *X, int ld, int row0, int k0) {
@@ -176,7 +201,7 @@ template <typename E>
 __device__ __forceinline__ Split ldc(const E *X, int ld, int col0, int k0) {
     if constexpr (std::is_same<E, __bf16>::value) {
         Split s{};
-        s.h = frag_cols<__bf16>(X, ld, col0, k0);
+        s.h = cols_tr(X, ld, col0, k0);
         return s;
     } else {
         return split_frag(frag_cols<float>(X, ld, col0, k0));
@@ -189,27 +214,71 @@ __device__ __forceinline__ Split ldr_scaled(const float *X, int ld, int row0, in
     f.hi *= sc;
     return split_frag(f);
 }
-// columns of an E-typed matrix with row k scaled by sk[k]
-template <typename E>
-__device__ __forceinline__ Split ldc_kscaled(const E *X, int ld, int col0, int k0, const float *sk) {
+// An fp32 matrix held in LDS already split: planes h (bf16(x)) and l (bf16(x - h)), R x C each.
+// Split once where a value is produced instead of at every read: a row fragment is then two 8-byte
+// reads per plane and a column fragment two transposed reads per plane, with no conversions.
+template <int R, int C>
+struct SplitMat {
+    static constexpr int P = C + 8;  // pitch in bf16: one 16-byte piece of padding per row
+    __bf16 h[R][P], l[R][P];
+};
+template <int R, int C>
+__device__ __forceinline__ Split sm_rows(const SplitMat<R, C> &X, int row0, int k0) {
+    Split s;
+    s.h = frag_rows<__bf16>(&X.h[0][0], SplitMat<R, C>::P, row0, k0);
+    s.l = frag_rows<__bf16>(&X.l[0][0], SplitMat<R, C>::P, row0, k0);
+    return s;
+}
+template <int R, int C>
+__device__ __forceinline__ Split sm_cols(const SplitMat<R, C> &X, int col0, int k0) {
+    Split s;
+    s.h = cols_tr(&X.h[0][0], SplitMat<R, C>::P, col0, k0);
+    s.l = cols_tr(&X.l[0][0], SplitMat<R, C>::P, col0, k0);
+    return s;
+}
+// element (r, c) as fp32 (h + l)
+template <int R, int C>
+__device__ __forceinline__ float sm_get(const SplitMat<R, C> &X, int r, int c) {
+    return (float)X.h[r][c] + (float)X.l[r][c];
+}
+// the accumulator tile v of lane (g, c) (rows m0 + 4g .. + 3, column n0 + c) stored transposed:
+// Xt[n0 + c][m0 + 4g .. + 3], one 8-byte write per plane
+template <int R, int C>
+__device__ __forceinline__ void sm_put_t(SplitMat<R, C> &Xt, int m0, int n0, const floatx4 &v) {
     const int lane = threadIdx.x & 63;
-    const int kb = k0 + 4 * (lane >> 4);
-    const E *p = X + kb * ld + col0 + (lane & 15);
+    bf16x4 hi, lo;
+    split_bf16(v, hi, lo);
+    const int rr = n0 + (lane & 15), cc = m0 + 4 * (lane >> 4);
+    *reinterpret_cast<bf16x4 *>(&Xt.h[rr][cc]) = hi;
+    *reinterpret_cast<bf16x4 *>(&Xt.l[rr][cc]) = lo;
+}
+// rows of a split matrix (the 32 columns from column 0), each lane's row scaled by sc and split again
+template <int R, int C>
+__device__ __forceinline__ Split sm_scaled_rows(const SplitMat<R, C> &X, int row0, float sc) {
+    const Split a = sm_rows(X, row0, 0);
     Frag<float> f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        f.lo[s] = (float)p[s * ld] * sk[kb + s];
-        f.hi[s] = (float)p[(16 + s) * ld] * sk[kb + 16 + s];
+    for (int i = 0; i < 4; ++i) {
+        f.lo[i] = sc * ((float)a.h.lo[i] + (float)a.l.lo[i]);
+        f.hi[i] = sc * ((float)a.h.hi[i] + (float)a.l.hi[i]);
     }
     return split_frag(f);
 }
+// four consecutive elements of a row
+template <int R, int C>
+__device__ __forceinline__ void sm_put4(SplitMat<R, C> &X, int r, int c, const float4 &v) {
+    bf16x4 hi, lo;
+    split_bf16(floatx4{v.x, v.y, v.z, v.w}, hi, lo);
+    *reinterpret_cast<bf16x4 *>(&X.h[r][c]) = hi;
+    *reinterpret_cast<bf16x4 *>(&X.l[r][c]) = lo;
+}
+
 // a fragment slab of a record, as loaded (two 16-byte pieces per lane)
 struct Slab {
     uint4 h, l;
 };
-__device__ __forceinline__ Slab ld_slab(const uint8_t *rec, int mat, int mt, int ks) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(rec + mat * kMatBytes + (mt * kSlices + ks) * kSlabBytes +
-                                                     (threadIdx.x & 63) * 32);
+__device__ __forceinline__ Slab ld_slab(const uint8_t *rec, int off, int mt, int ks) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(rec + off + (mt * kSlices + ks) * kSlabBytes + (threadIdx.x & 63) * 32);
     Slab s;
     s.h = p[0];
     s.l = p[1];
@@ -222,10 +291,35 @@ __device__ __forceinline__ Split slab_split(const Slab &s) {
     return r;
 }
 
-// sum of x over the 16 lanes of a lane group (the columns of a tile row)
+// no instruction is moved across this point by the compiler's scheduler: keeps a phase's loads
+// from being hoisted all at once (which costs more registers than the latency it hides)
+__device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0); }
+
+// The address of an LDS object, hidden from the optimizer (it is uniform and stays in a scalar
+// register): addresses derived from it are then formed where they are used instead of being
+// hoisted out of a loop and kept live across it, which with a large LDS layout (offsets beyond
+// the 64 KiB the instructions' immediates reach) costs a vector register per access pattern.
+typedef __attribute__((address_space(3))) char lds_char;
+template <typename T>
+__device__ __forceinline__ T *lds_opaque(T *p) {
+    uint32_t off = (uint32_t)(uintptr_t)(lds_char *)(char *)p;
+    asm volatile("" : "+s"(off));
+    return reinterpret_cast<T *>((char *)(lds_char *)(uintptr_t)off);
+}
+
+// x moved between the lanes of each 16-lane row by the DPP control CTRL (a VALU operation)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// sum of x over the 16 lanes of a lane group (the columns of a tile row): swaps within quads
+// (quad_perm [1,0,3,2], [2,3,0,1]), then the row rotated by 4 and by 8 lanes; every lane ends
+// with the sum (in the same order on every run)
 __device__ __forceinline__ float row16(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x128>(x);
     return x;
 }
 // sum of x over the 4 lane groups (the rows 4g + r of a tile column, for fixed r)
@@ -237,17 +331,20 @@ __device__ __forceinline__ float col4(float x) {
 
 // The rows of one chunk of an E-typed [token][stride] matrix, W elements from the row start, as
 // 16-byte pieces shared out over NT threads: issued into registers, then stored into LDS (rows
-// past the chunk end read the chunk's first row and are stored as zeros).
+// past the chunk end read the chunk's first row and are stored as zeros). Every thread issues the
+// same number of loads (a thread past the last piece reads one again and does not store it), so
+// that the compiler can count the loads in flight exactly instead of waiting for all of them.
 template <typename E, int W, int NT>
 struct Rows {
     static constexpr int EPP = 16 / (int)sizeof(E), PR = W / EPP, N = CB * PR, PT = (N + NT - 1) / NT;
     uint4 p[PT];
     __device__ __forceinline__ void issue(const E *src, int64_t stride, const Seq &sq, int64_t c, int n, int tid) {
+        const E *base = src + sq.low(c, n) * stride;
 #pragma unroll
         for (int e = 0; e < PT; ++e) {
-            const int i = tid + e * NT, rr = i / PR, pc = i % PR;
-            p[e] = make_uint4(0, 0, 0, 0);
-            if (i < N) p[e] = *reinterpret_cast<const uint4 *>(src + sq.token(c * CB + (rr < n ? rr : 0)) * stride + pc * EPP);
+            const int i = (tid + e * NT) % N, rr = i / PR, pc = i % PR;
+            const uint32_t o = (uint32_t)(sq.off(rr < n ? rr : 0, n) * (int)stride + pc * EPP);
+            p[e] = *reinterpret_cast<const uint4 *>(base + o);
         }
     }
     __device__ __forceinline__ void store(E *dst, int pitch, int n, int tid) const {
@@ -327,6 +424,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
         sm.r[lane] = pre ? x - sm.la[lane] : x;
     }
     __syncthreads();
+    uint8_t *rec = a.rec + (head * a.nslots + slot) * Rec<DK>::kBytes;
     // the lower tiles of G (tasks 0-9) and Pm (10-19), five per wave, into registers: Pm is
     // stored over Q, so every product must be done before any tile is stored
     constexpr int kPer = 20 / (kPrepThreads / 64);
@@ -373,7 +471,6 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
     // T, T^T and Pm^T as A-operand fragments: lane (g, c) of slab (mt, ks) holds row 16 mt + c,
     // columns 32 ks + 4g + s and 32 ks + 16 + 4g + s (s = 0..3)
-    uint8_t *rec = a.rec + (head * a.nslots + slot) * kBwdRecBytes;
     for (int it = tid; it < 3 * NMT * kSlices * 64; it += kPrepThreads) {
         const int mat = it / (NMT * kSlices * 64), sl = (it / 64) % (NMT * kSlices), ln = it % 64;
         const int mt = sl / kSlices, ks = sl % kSlices;
@@ -382,7 +479,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int k = kb0 + (s < 4 ? s : 12 + s);
-            const float x = mat == kRecT ? sm.T[row * SP + k] : mat == kRecTt ? sm.T[k * SP + row] : sm.u.P[k][row];
+            const float x = mat == 0 ? sm.T[row * SP + k] : mat == 1 ? sm.T[k * SP + row] : sm.u.P[k][row];
             if (s < 4) f.lo[s] = x;
             else f.hi[s - 4] = x;
         }
@@ -392,7 +489,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
         dst[1] = __builtin_bit_cast(uint4, sp.l);
     }
     if (tid < CB) {
-        float *rb = reinterpret_cast<float *>(rec + 3 * kMatBytes);
+        float *rb = reinterpret_cast<float *>(rec + Rec<DK>::kGates);
         rb[tid] = sm.b[tid];
         rb[CB + tid] = sm.r[tid];
     }
@@ -400,37 +497,77 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- 2. sweeps
 
+// The sweeps keep the running state (H, or its adjoint D) in the MFMA accumulators of the waves
+// that update it, each wave its own 16x16 tiles, in fp32 for the whole unit. What the products read
+// is held in LDS split and transposed, so that every B operand is a row fragment: Ht[col][d]
+// (the state slice), Rt, wUt, dUt, bRt [col][token].
 template <typename E, int DK>
 struct FwdSmem {
     static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
-    E K[CB][KP];
+    float b[2][CB], beta[2][CB];
+    SplitMat<TV, CB> Rt, wUt;
+    SplitMat<TV, DK> Ht;
     E V[CB][VP];
-    float H[DK][FP], R[CB][FP], wU[CB][FP];
-    float b[CB], beta[CB];
+    E K[2][CB][KP];  // this chunk's k and the next chunk's
 };
 template <typename E, int DK>
 struct AdjSmem {
     static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
-    E K[CB][KP], Q[CB][KP];
-    E dO[CB][VP];
-    float D[DK][FP], dU[CB][FP], bR[CB][FP];
-    float b[CB], er[CB], beta[CB];
+    // the next chunk's k, q and dout go into a second buffer with bf16 inputs; fp32 ones leave no
+    // room for it and are stored after an extra barrier
+    static constexpr int NB = sizeof(E) == 2 ? 2 : 1;
+    float b[2][CB], er[2][CB], beta[2][CB];
+    SplitMat<TV, CB> dUt, bRt, eOt;  // eOt: diag(e^r) dO, transposed
+    SplitMat<TV, DK> Dt;
+    E dO[NB][CB][VP];
+    E K[NB][CB][KP], Q[NB][CB][KP];
 };
 template <typename E, int DK>
 constexpr size_t sweep_smem_bytes() {
     return sizeof(FwdSmem<E, DK>) > sizeof(AdjSmem<E, DK>) ? sizeof(FwdSmem<E, DK>) : sizeof(AdjSmem<E, DK>);
 }
 
-// A thread's part of a DK x TV state slice: SR rows of 4 consecutive columns.
+// The state tiles of a wave: tile s is (row tile (wave + 8 s) / 2 of d_k, column tile (wave + 8 s) % 2).
 template <int DK>
-struct SliceMap {
-    static constexpr int SR = DK * TV / (kThreads * 4);
-    int r0, c0;
-    __device__ __forceinline__ SliceMap(int tid) : r0((tid / (TV / 4)) * SR), c0((tid % (TV / 4)) * 4) {}
+struct StateTiles {
+    static constexpr int N = (DK / 16) * (TV / 16) / kWaves;
+    static_assert(N * kWaves == (DK / 16) * (TV / 16), "whole state tiles per wave");
+    floatx4 v[N];
+    __device__ __forceinline__ static int hm(int wave, int s) { return (wave + kWaves * s) / (TV / 16); }
+    __device__ __forceinline__ static int hn(int wave, int s) { return (wave + kWaves * s) % (TV / 16); }
+    // from / to a [dk][dv] state in global memory (the slice starting at column col0 of row p)
+    __device__ __forceinline__ void load(const float *p, int64_t dvf, int wave) {
+        const int lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+#pragma unroll
+        for (int s = 0; s < N; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[s][r] = p ? p[(int64_t)(16 * hm(wave, s) + 4 * g + r) * dvf + 16 * hn(wave, s) + cc] : 0.f;
+    }
+    __device__ __forceinline__ void save(float *p, int64_t dvf, int wave) const {
+        const int lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+#pragma unroll
+        for (int s = 0; s < N; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[(int64_t)(16 * hm(wave, s) + 4 * g + r) * dvf + 16 * hn(wave, s) + cc] = v[s][r];
+    }
+    // to a transposed TV x DK slice in the workspace: lane (g, c) holds 4 consecutive d of column c
+    __device__ __forceinline__ void save_t(float *p, int wave) const {
+        const int lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+#pragma unroll
+        for (int s = 0; s < N; ++s)
+            *reinterpret_cast<floatx4 *>(p + (16 * hn(wave, s) + cc) * DK + 16 * hm(wave, s) + 4 * g) = v[s];
+    }
+    __device__ __forceinline__ void put(SplitMat<TV, DK> &Xt, int wave) const {
+#pragma unroll
+        for (int s = 0; s < N; ++s) sm_put_t(Xt, 16 * hm(wave, s), 16 * hn(wave, s), v[s]);
+    }
 };
 
 // Forward sweep of one (sequence, value head, column slice): per chunk, the entry state to the
-// workspace, X = K H, R, U = T R (U to the workspace) and H' = gamma_last H + K^T diag(w) U.
+// workspace, X = K H, R = diag(beta) (V - diag(gamma) X), U = T R (U to the workspace) and
+// H' = gamma_last H + K^T diag(w) U. The next chunk's k, v and gates are read while the state
+// is updated and stored into the other buffer, so a chunk takes three barriers.
 template <typename E, int DK>
 __device__ __forceinline__ void fwd_sweep(const BwdArgs &a, int64_t unit, int tile, char *smraw) {
     typedef FwdSmem<E, DK> SM;
@@ -447,110 +584,112 @@ __device__ __forceinline__ void fwd_sweep(const BwdArgs &a, int64_t unit, int ti
     const E *kb = reinterpret_cast<const E *>(a.k) + (L.row * a.Hk + kh) * a.T * DK;
     const E *vb = reinterpret_cast<const E *>(a.v) + (L.row * a.Hv + head) * a.T * dvf + col0;
     const float *beb = a.beta + (L.row * a.Hv + head) * a.T;
-    float *ub = a.us + (L.row * a.Hv + head) * a.T * dvf + col0;
+    float *ub = a.us + (head * a.nslots + L.slot0) * CB * dvf + col0;
     constexpr int64_t kSlice = (int64_t)DK * TV;
     float *hs = a.hs + ((head * a.nslots + L.slot0) * a.ntiles + tile) * kSlice;
     const int64_t hstride = a.ntiles * kSlice;
-    const uint8_t *rec0 = a.rec + (head * a.nslots + L.slot0) * kBwdRecBytes;
-    const SliceMap<DK> sl(tid);
-    constexpr int SR = SliceMap<DK>::SR;
-    const int64_t sbase = (seq * a.Hv + head) * DK * dvf + col0;
-#pragma unroll
-    for (int u = 0; u < SR; ++u)
-        *reinterpret_cast<float4 *>(&sm.H[sl.r0 + u][sl.c0]) =
-            a.h0 ? *reinterpret_cast<const float4 *>(a.h0 + sbase + (int64_t)(sl.r0 + u) * dvf + sl.c0) : make_float4(0.f, 0.f, 0.f, 0.f);
-
+    const uint8_t *rec0 = a.rec + (head * a.nslots + L.slot0) * Rec<DK>::kBytes;
+    StateTiles<DK> H;
+    H.load(a.h0 ? a.h0 + (seq * a.Hv + head) * DK * dvf + col0 : nullptr, dvf, wave);
+    H.put(sm.Ht, wave);
     // this wave's output tile of X, R and U
     const int mt = wave >> 1, nt = wave & 1;
     Rows<E, DK, kThreads> kp;
     Rows<E, TV, kThreads> vp;
     float bv = 0.f, betav = 0.f;
-    Slab tr[kSlices];
+    // (every thread issues the same loads; only the first CB threads keep the gates)
     auto issue = [&](int64_t c) __attribute__((always_inline)) {
         const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
         kp.issue(kb, DK, L.sq, c, n, tid);
         vp.issue(vb, dvf, L.sq, c, n, tid);
+        const int gr = tid & (CB - 1);
+        bv = reinterpret_cast<const float *>(rec0 + c * Rec<DK>::kBytes + Rec<DK>::kGates)[gr];
+        betav = (beb + L.sq.low(c, n))[(uint32_t)L.sq.off(gr < n ? gr : 0, n)];
+    };
+    auto store = [&](int64_t c, int buf) __attribute__((always_inline)) {
+        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
+        kp.store(&sm.K[buf][0][0], SM::KP, n, tid);
+        vp.store(&sm.V[0][0], SM::VP, n, tid);
         if (tid < CB) {
-            bv = reinterpret_cast<const float *>(rec0 + c * kBwdRecBytes + 3 * kMatBytes)[tid];
-            betav = tid < n ? beb[L.sq.token(c * CB + tid)] : 0.f;
+            sm.b[buf][tid] = bv;
+            sm.beta[buf][tid] = tid < n ? betav : 0.f;
         }
     };
-    // T's rows 16 mt .. 16 mt + 15 are zero past column 16 mt + 15
+    // T's rows 16 mt .. 16 mt + 15 are zero past column 16 mt + 15 (the zero slab is read too:
+    // the same loads in every wave); a chunk's slabs are read during the previous chunk
+    Slab tr[kSlices];
     auto issue_t = [&](int64_t c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < kSlices; ++ks)
-            if (32 * ks <= 16 * mt + 15) tr[ks] = ld_slab(rec0 + c * kBwdRecBytes, kRecT, mt, ks);
+        for (int ks = 0; ks < kSlices; ++ks) tr[ks] = ld_slab(rec0 + c * Rec<DK>::kBytes, kRecT, mt, ks);
     };
     if (nch > 0) {
         issue(0);
         issue_t(0);
+        store(0, 0);
     }
     __syncthreads();
     for (int64_t c = 0; c < nch; ++c) {
-        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
-#pragma unroll
-        for (int u = 0; u < SR; ++u)
-            *reinterpret_cast<float4 *>(hs + c * hstride + (sl.r0 + u) * TV + sl.c0) =
-                *reinterpret_cast<const float4 *>(&sm.H[sl.r0 + u][sl.c0]);
-        kp.store(&sm.K[0][0], SM::KP, n, tid);
-        vp.store(&sm.V[0][0], SM::VP, n, tid);
-        if (tid < CB) {
-            sm.b[tid] = bv;
-            sm.beta[tid] = betav;
-        }
-        if (c + 1 < nch) issue(c + 1);
-        __syncthreads();
+        SM &sm = *lds_opaque(reinterpret_cast<SM *>(smraw));
+        const int cur = (int)(c & 1);
+        const E *Kc = &sm.K[cur][0][0];
+        const float *bc = sm.b[cur];
+        H.save_t(hs + c * hstride, wave);
         // X = K H, R = diag(beta) (V - diag(gamma) X)
         {
             floatx4 x = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                x = mms<kX, false>(x, ldr<E>(&sm.K[0][0], SM::KP, 16 * mt, 32 * ks), ldc<float>(&sm.H[0][0], FP, 16 * nt, 32 * ks));
+                x = mms<kX, false>(x, ldr<E>(Kc, SM::KP, 16 * mt, 32 * ks), sm_rows(sm.Ht, 16 * nt, 32 * ks));
+            floatx4 rv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                sm.R[i][j] = sm.beta[i] * ((float)sm.V[i][j] - __expf(sm.b[i]) * x[r]);
+                rv[r] = sm.beta[cur][i] * ((float)sm.V[i][j] - __expf(bc[i]) * x[r]);
             }
+            sm_put_t(sm.Rt, 16 * mt, 16 * nt, rv);
         }
         __syncthreads();
+        issue(c + 1 < nch ? c + 1 : c);
         // U = T R (to the workspace), diag(w) U
         {
             floatx4 u = zero4();
 #pragma unroll
             for (int ks = 0; ks < kSlices; ++ks)
-                if (32 * ks <= 16 * mt + 15) u = mms<false, false>(u, slab_split(tr[ks]), ldc<float>(&sm.R[0][0], FP, 16 * nt, 32 * ks));
-            const float blast = sm.b[CB - 1];
+                if (32 * ks <= 16 * mt + 15) u = mms<false, false>(u, slab_split(tr[ks]), sm_rows(sm.Rt, 16 * nt, 32 * ks));
+            const float blast = bc[CB - 1];
+            floatx4 wu;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                if (i < n) ub[L.sq.token(c * CB + i) * dvf + j] = u[r];
-                sm.wU[i][j] = __expf(fminf(blast - sm.b[i], 0.f)) * u[r];
+                ub[(c * CB + i) * dvf + j] = u[r];
+                wu[r] = __expf(fminf(blast - bc[i], 0.f)) * u[r];
             }
+            sm_put_t(sm.wUt, 16 * mt, 16 * nt, wu);
         }
-        if (c + 1 < nch) issue_t(c + 1);
+        issue_t(c + 1 < nch ? c + 1 : c);
         __syncthreads();
-        // H' = gamma_last H + K^T diag(w) U, each wave on its own tiles of H
+        // H' = gamma_last H + K^T diag(w) U, each wave on its own tiles
         {
-            const float glast = __expf(sm.b[CB - 1]);
-            for (int t = wave; t < (DK / 16) * (TV / 16); t += kWaves) {
-                const int hm = t / (TV / 16), hn = t % (TV / 16);
-                floatx4 h;
+            const float glast = __expf(bc[CB - 1]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) h[r] = glast * sm.H[16 * hm + 4 * g + r][16 * hn + cc];
+            for (int s = 0; s < StateTiles<DK>::N; ++s) {
+                const int hm = StateTiles<DK>::hm(wave, s), hn = StateTiles<DK>::hn(wave, s);
+                floatx4 h = glast * H.v[s];
 #pragma unroll
                 for (int ks = 0; ks < kSlices; ++ks)
-                    h = mms<kX, false>(h, ldc<E>(&sm.K[0][0], SM::KP, 16 * hm, 32 * ks), ldc<float>(&sm.wU[0][0], FP, 16 * hn, 32 * ks));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sm.H[16 * hm + 4 * g + r][16 * hn + cc] = h[r];
+                    h = mms<kX, false>(h, ldc<E>(Kc, SM::KP, 16 * hm, 32 * ks), sm_rows(sm.wUt, 16 * hn, 32 * ks));
+                H.v[s] = h;
             }
+            H.put(sm.Ht, wave);
         }
+        if (c + 1 < nch) store(c + 1, cur ^ 1);
         __syncthreads();
     }
 }
 
 // Adjoint sweep of one (sequence, value head, column slice), from the last chunk: per chunk, the
-// exit adjoint D to the workspace, dU = diag(w) K D + Pm^T dO, dR = T^T dU (to the workspace;
-// dV = diag(beta) dR) and D <- gamma_last D + Q^T diag(e^r) dO - K^T diag(beta gamma) dR.
+// exit adjoint D to the workspace, dU = diag(w) K D + Pm^T dO, dR = T^T dU (to the workspace)
+// and D <- gamma_last D + Q^T diag(e^r) dO - K^T diag(beta gamma) dR.
 template <typename E, int DK>
 __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int tile, char *smraw) {
     typedef AdjSmem<E, DK> SM;
@@ -568,130 +707,132 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
     const E *qb = reinterpret_cast<const E *>(a.q) + (L.row * a.Hk + kh) * a.T * DK;
     const E *ob = reinterpret_cast<const E *>(a.dout) + (L.row * a.Hv + head) * a.T * dvf + col0;
     const float *beb = a.beta + (L.row * a.Hv + head) * a.T;
-    float *drb = a.drs + (L.row * a.Hv + head) * a.T * dvf + col0;
-    float *dvb = a.dv + (L.row * a.Hv + head) * a.T * dvf + col0;
+    float *drb = a.drs + (head * a.nslots + L.slot0) * CB * dvf + col0;
     constexpr int64_t kSlice = (int64_t)DK * TV;
     float *ds = a.ds + ((head * a.nslots + L.slot0) * a.ntiles + tile) * kSlice;
     const int64_t dstride = a.ntiles * kSlice;
-    const uint8_t *rec0 = a.rec + (head * a.nslots + L.slot0) * kBwdRecBytes;
-    const SliceMap<DK> sl(tid);
-    constexpr int SR = SliceMap<DK>::SR;
+    const uint8_t *rec0 = a.rec + (head * a.nslots + L.slot0) * Rec<DK>::kBytes;
     const int64_t sbase = (seq * a.Hv + head) * DK * dvf + col0;
-#pragma unroll
-    for (int u = 0; u < SR; ++u)
-        *reinterpret_cast<float4 *>(&sm.D[sl.r0 + u][sl.c0]) =
-            a.dhT ? *reinterpret_cast<const float4 *>(a.dhT + sbase + (int64_t)(sl.r0 + u) * dvf + sl.c0) : make_float4(0.f, 0.f, 0.f, 0.f);
-
+    StateTiles<DK> D;
+    D.load(a.dhT ? a.dhT + sbase : nullptr, dvf, wave);
+    D.put(sm.Dt, wave);
     const int mt = wave >> 1, nt = wave & 1;
     Rows<E, DK, kThreads> kp, qp;
     Rows<E, TV, kThreads> op;
     float bv = 0.f, rv = 0.f, betav = 0.f;
-    // T^T and Pm^T: rows 16 mt .. 16 mt + 15 are zero before column 16 mt
-    Slab tt[kSlices], pt[kSlices];
     auto issue = [&](int64_t c) __attribute__((always_inline)) {
         const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
         kp.issue(kb, DK, L.sq, c, n, tid);
         qp.issue(qb, DK, L.sq, c, n, tid);
         op.issue(ob, dvf, L.sq, c, n, tid);
+        const int gr = tid & (CB - 1);
+        const float *rb = reinterpret_cast<const float *>(rec0 + c * Rec<DK>::kBytes + Rec<DK>::kGates);
+        bv = rb[gr];
+        rv = rb[CB + gr];
+        betav = (beb + L.sq.low(c, n))[(uint32_t)L.sq.off(gr < n ? gr : 0, n)];
+    };
+    auto store = [&](int64_t c, int buf) __attribute__((always_inline)) {
+        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
+        const int ib = SM::NB == 2 ? buf : 0;
+        kp.store(&sm.K[ib][0][0], SM::KP, n, tid);
+        qp.store(&sm.Q[ib][0][0], SM::KP, n, tid);
+        op.store(&sm.dO[ib][0][0], SM::VP, n, tid);
         if (tid < CB) {
-            const float *rb = reinterpret_cast<const float *>(rec0 + c * kBwdRecBytes + 3 * kMatBytes);
-            bv = rb[tid];
-            rv = rb[CB + tid];
-            betav = tid < n ? beb[L.sq.token(c * CB + tid)] : 0.f;
+            sm.b[buf][tid] = bv;
+            sm.er[buf][tid] = __expf(rv);
+            sm.beta[buf][tid] = tid < n ? betav : 0.f;
         }
     };
+    // T^T and Pm^T (rows 16 mt .. 16 mt + 15 are zero before column 16 mt; the zero slabs are read
+    // too), read during the previous chunk
+    Slab tt[kSlices], pt[kSlices];
+    constexpr int NDT = StateTiles<DK>::N;
     auto issue_f = [&](int64_t c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < kSlices; ++ks)
-            if (32 * ks + 31 >= 16 * mt) {
-                tt[ks] = ld_slab(rec0 + c * kBwdRecBytes, kRecTt, mt, ks);
-                pt[ks] = ld_slab(rec0 + c * kBwdRecBytes, kRecPt, mt, ks);
-            }
+        for (int ks = 0; ks < kSlices; ++ks) {
+            pt[ks] = ld_slab(rec0 + c * Rec<DK>::kBytes, kRecPt, mt, ks);
+            tt[ks] = ld_slab(rec0 + c * Rec<DK>::kBytes, kRecTt, mt, ks);
+        }
     };
     if (nch > 0) {
         issue(nch - 1);
         issue_f(nch - 1);
+        store(nch - 1, 0);
     }
     __syncthreads();
     for (int64_t c = nch - 1; c >= 0; --c) {
-        const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
-#pragma unroll
-        for (int u = 0; u < SR; ++u)
-            *reinterpret_cast<float4 *>(ds + c * dstride + (sl.r0 + u) * TV + sl.c0) =
-                *reinterpret_cast<const float4 *>(&sm.D[sl.r0 + u][sl.c0]);
-        kp.store(&sm.K[0][0], SM::KP, n, tid);
-        qp.store(&sm.Q[0][0], SM::KP, n, tid);
-        op.store(&sm.dO[0][0], SM::VP, n, tid);
-        if (tid < CB) {
-            sm.b[tid] = bv;
-            sm.er[tid] = __expf(rv);
-            sm.beta[tid] = betav;
-        }
-        if (c > 0) issue(c - 1);
-        __syncthreads();
+        SM &sm = *lds_opaque(reinterpret_cast<SM *>(smraw));
+        const int cur = (int)((nch - 1 - c) & 1), ib = SM::NB == 2 ? cur : 0;
+        const E *Kc = &sm.K[ib][0][0];
+        const E *Qc = &sm.Q[ib][0][0];
+        const E *Oc = &sm.dO[ib][0][0];
+        const float *bc = sm.b[cur];
+        D.save_t(ds + c * dstride, wave);
         // dU = diag(w) K D + Pm^T dO
         {
             floatx4 y = zero4(), p = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                y = mms<kX, false>(y, ldr<E>(&sm.K[0][0], SM::KP, 16 * mt, 32 * ks), ldc<float>(&sm.D[0][0], FP, 16 * nt, 32 * ks));
+                y = mms<kX, false>(y, ldr<E>(Kc, SM::KP, 16 * mt, 32 * ks), sm_rows(sm.Dt, 16 * nt, 32 * ks));
 #pragma unroll
             for (int ks = 0; ks < kSlices; ++ks)
-                if (32 * ks + 31 >= 16 * mt) p = mms<false, kX>(p, slab_split(pt[ks]), ldc<E>(&sm.dO[0][0], SM::VP, 16 * nt, 32 * ks));
-            const float blast = sm.b[CB - 1];
+                if (32 * ks + 31 >= 16 * mt) p = mms<false, kX>(p, slab_split(pt[ks]), ldc<E>(Oc, SM::VP, 16 * nt, 32 * ks));
+            const float blast = bc[CB - 1];
+            floatx4 du, eo;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                sm.dU[i][j] = __expf(fminf(blast - sm.b[i], 0.f)) * y[r] + p[r];
+                const int i = 16 * mt + 4 * g + r;
+                du[r] = __expf(fminf(blast - bc[i], 0.f)) * y[r] + p[r];
+                eo[r] = sm.er[cur][i] * (float)Oc[i * SM::VP + 16 * nt + cc];
             }
+            sm_put_t(sm.dUt, 16 * mt, 16 * nt, du);
+            sm_put_t(sm.eOt, 16 * mt, 16 * nt, eo);
         }
         __syncthreads();
-        // dR = T^T dU (to the workspace), dV = diag(beta) dR, -diag(beta gamma) dR
+        issue(c > 0 ? c - 1 : 0);
+        // dR = T^T dU (to the workspace), -diag(beta gamma) dR
         {
             floatx4 d = zero4();
 #pragma unroll
             for (int ks = 0; ks < kSlices; ++ks)
-                if (32 * ks + 31 >= 16 * mt) d = mms<false, false>(d, slab_split(tt[ks]), ldc<float>(&sm.dU[0][0], FP, 16 * nt, 32 * ks));
+                if (32 * ks + 31 >= 16 * mt) d = mms<false, false>(d, slab_split(tt[ks]), sm_rows(sm.dUt, 16 * nt, 32 * ks));
+            floatx4 br;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                const float be = sm.beta[i];
-                if (i < n) {
-                    const int64_t t = L.sq.token(c * CB + i);
-                    drb[t * dvf + j] = d[r];
-                    dvb[t * dvf + j] = be * d[r];
-                }
-                sm.bR[i][j] = -be * __expf(sm.b[i]) * d[r];
+                drb[(c * CB + i) * dvf + j] = d[r];
+                br[r] = -sm.beta[cur][i] * __expf(bc[i]) * d[r];
             }
+            sm_put_t(sm.bRt, 16 * mt, 16 * nt, br);
         }
-        if (c > 0) issue_f(c - 1);
         __syncthreads();
-        // D <- gamma_last D + (diag(e^r) Q)^T dO + K^T bR, each wave on its own tiles of D
+        // D <- gamma_last D + Q^T diag(e^r) dO + K^T bR, each wave on its own tiles
         {
-            const float glast = __expf(sm.b[CB - 1]);
-            for (int t = wave; t < (DK / 16) * (TV / 16); t += kWaves) {
-                const int hm = t / (TV / 16), hn = t % (TV / 16);
-                floatx4 h;
+            const float glast = __expf(bc[CB - 1]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) h[r] = glast * sm.D[16 * hm + 4 * g + r][16 * hn + cc];
+            for (int s = 0; s < NDT; ++s) {
+                const int hm = StateTiles<DK>::hm(wave, s), hn = StateTiles<DK>::hn(wave, s);
+                floatx4 h = glast * D.v[s];
 #pragma unroll
                 for (int ks = 0; ks < kSlices; ++ks) {
-                    h = mms<false, kX>(h, ldc_kscaled<E>(&sm.Q[0][0], SM::KP, 16 * hm, 32 * ks, sm.er),
-                                       ldc<E>(&sm.dO[0][0], SM::VP, 16 * hn, 32 * ks));
-                    h = mms<kX, false>(h, ldc<E>(&sm.K[0][0], SM::KP, 16 * hm, 32 * ks), ldc<float>(&sm.bR[0][0], FP, 16 * hn, 32 * ks));
+                    h = mms<kX, false>(h, ldc<E>(Qc, SM::KP, 16 * hm, 32 * ks), sm_rows(sm.eOt, 16 * hn, 32 * ks));
+                    h = mms<kX, false>(h, ldc<E>(Kc, SM::KP, 16 * hm, 32 * ks), sm_rows(sm.bRt, 16 * hn, 32 * ks));
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sm.D[16 * hm + 4 * g + r][16 * hn + cc] = h[r];
+                D.v[s] = h;
             }
+            D.put(sm.Dt, wave);
         }
-        __syncthreads();
+        issue_f(c > 0 ? c - 1 : 0);
+        if constexpr (SM::NB == 2) {
+            if (c > 0) store(c - 1, cur ^ 1);
+            __syncthreads();
+        } else {
+            __syncthreads();
+            if (c > 0) store(c - 1, cur ^ 1);
+            __syncthreads();
+        }
     }
-    if (a.dh0) {
-#pragma unroll
-        for (int u = 0; u < SR; ++u)
-            *reinterpret_cast<float4 *>(a.dh0 + sbase + (int64_t)(sl.r0 + u) * dvf + sl.c0) =
-                *reinterpret_cast<const float4 *>(&sm.D[sl.r0 + u][sl.c0]);
-    }
+    if (a.dh0) D.save(a.dh0 + sbase, dvf, wave);
 }
 
 // Both sweeps in one launch: workgroups [0, n) run the forward sweep, [n, 2n) the adjoint sweep
@@ -713,19 +854,9 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdArgs a) {
 
 template <typename E, int DK>
 struct GradSmem {
-    static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
-    E K[CB][KP], Q[CB][KP];
-    union {
-        struct {
-            float H[DK][FP], D[DK][FP];  // a column slice of the entry state and the exit adjoint
-        } t;
-        struct {
-            float M[CB][SP], N[CB][SP];  // once every slice is done
-        } m;
-    } u;
-    float U[CB][FP], dR[CB][FP];
-    E dO[CB][VP], V[CB][VP];
-    float b[CB], r[CB], beta[CB];
+    // (ordered so that the arrays indexed in many different ways lie in the first 64 KiB, within
+    // reach of the LDS instructions' immediate offsets)
+    static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>(), HP = DK + 4;
     // Per-row partial sums, one slot per contributing tile, added in a fixed order:
     //   sx, sb, sw: dR . X, dR . (V - gamma X) and (K D) . U over the two 16-column halves
     //   pr, ar, gr: row sums of dP Pm, dA A and dA G per column tile; pc, ac: their column sums
@@ -734,12 +865,32 @@ struct GradSmem {
     float pr[NMT][CB], pc[NMT][CB], ar[NMT][CB], ac[NMT][CB], gr[NMT][CB];
     float rq[DK / 16][CB];
     float hd[kWaves];
+    float b[CB], r[CB], beta[CB];
+    // a column slice of U and dR (token-major) and, with bf16 inputs, of diag(w) U and
+    // -diag(beta gamma) dR, the A operands of the dK terms (with fp32 inputs they are scaled at
+    // each read, to stay within the LDS)
+    static constexpr bool kPre = sizeof(E) == 2;
+    SplitMat<CB, TV> U, dR;
+    SplitMat<kPre ? CB : 1, kPre ? TV : 8> wU, bR;
+    union {
+        struct {
+            // a column slice of the entry state and the exit adjoint, transposed
+            SplitMat<TV, DK> Ht, Dt;
+        } t;
+        struct {
+            // M and diag(beta) N, transposed and split, once every slice is done
+            SplitMat<CB, CB> Mt, Nt;
+        } m;
+    } u;
+    E dO[CB][VP], V[CB][VP];
+    E K[CB][KP], Q[CB][KP];
 };
 
 template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
     typedef GradSmem<E, DK> SM;
-    __shared__ SM sm;
+    __shared__ SM smem;
+    SM &sm = smem;
     constexpr bool kX = std::is_same<E, __bf16>::value;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -763,9 +914,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
         qp.store(&sm.Q[0][0], SM::KP, n, tid);
     }
     // staged inputs of one (value head, column slice) step
-    const SliceMap<DK> sl(tid);
-    constexpr int SR = SliceMap<DK>::SR;
-    float4 hpre[SR], dpre[SR], upre, rpre;
+    // this thread's part of a transposed TV x DK state slice: NF4 runs of 4 floats of one row
+    constexpr int NF4 = DK * TV / (kThreads * 4), TPR = DK / (4 * NF4);
+    const int tcol = tid / TPR, td0 = (tid % TPR) * 4 * NF4;
+    float4 hpre[NF4], dpre[NF4], upre, rpre;
     Rows<E, TV, kThreads> op, vp;
     float gb = 0.f, gr_ = 0.f, gbeta = 0.f;
     const int ur = tid / (TV / 4), uc = (tid % (TV / 4)) * 4;  // the thread's 4 elements of U and dR
@@ -774,23 +926,25 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
         const int64_t head = kh * grp + it / a.ntiles;
         const int tile = (int)(it % a.ntiles);
         const int64_t sidx = ((head * a.nslots + slot) * a.ntiles + tile) * kSlice;
+        const float *hsb = a.hs + sidx, *dsb = a.ds + sidx;
 #pragma unroll
-        for (int u = 0; u < SR; ++u) {
-            hpre[u] = *reinterpret_cast<const float4 *>(a.hs + sidx + (sl.r0 + u) * TV + sl.c0);
-            dpre[u] = *reinterpret_cast<const float4 *>(a.ds + sidx + (sl.r0 + u) * TV + sl.c0);
+        for (int u = 0; u < NF4; ++u) {
+            const uint32_t o = (uint32_t)(tcol * DK + td0 + 4 * u);
+            hpre[u] = *reinterpret_cast<const float4 *>(hsb + o);
+            dpre[u] = *reinterpret_cast<const float4 *>(dsb + o);
         }
         const int64_t vbase = (L.row * a.Hv + head) * a.T * dvf + tile * TV;
-        const int64_t tu = L.sq.token(c * CB + (ur < n ? ur : 0));
-        upre = *reinterpret_cast<const float4 *>(a.us + vbase + tu * dvf + uc);
-        rpre = *reinterpret_cast<const float4 *>(a.drs + vbase + tu * dvf + uc);
+        const int64_t cbase = (head * a.nslots + slot) * CB * dvf + tile * TV;
+        const uint32_t uo = (uint32_t)(ur * (int)dvf + uc);
+        upre = *reinterpret_cast<const float4 *>(a.us + cbase + uo);
+        rpre = *reinterpret_cast<const float4 *>(a.drs + cbase + uo);
         op.issue(reinterpret_cast<const E *>(a.dout) + vbase, dvf, L.sq, c, n, tid);
         vp.issue(reinterpret_cast<const E *>(a.v) + vbase, dvf, L.sq, c, n, tid);
-        if (tid < CB) {
-            const float *rb = reinterpret_cast<const float *>(a.rec + (head * a.nslots + slot) * kBwdRecBytes + 3 * kMatBytes);
-            gb = rb[tid];
-            gr_ = rb[CB + tid];
-            gbeta = tid < n ? a.beta[(L.row * a.Hv + head) * a.T + L.sq.token(c * CB + tid)] : 0.f;
-        }
+        const int gi = tid & (CB - 1);
+        const float *rb = reinterpret_cast<const float *>(a.rec + (head * a.nslots + slot) * Rec<DK>::kBytes + Rec<DK>::kGates);
+        gb = rb[gi];
+        gr_ = rb[CB + gi];
+        gbeta = (a.beta + (L.row * a.Hv + head) * a.T + L.sq.low(c, n))[(uint32_t)L.sq.off(gi < n ? gi : 0, n)];
     };
 
     // tile assignments: X and K D: tile (xm, xn) of the CB x TV slice; dP, dA: lower tiles
@@ -809,24 +963,42 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
 
     if (nit > 0) issue(0);
     for (int64_t it = 0; it < nit; ++it) {
+        SM &sm = *lds_opaque(&smem);
         const int64_t v = it / a.ntiles;
         const int tile = (int)(it % a.ntiles);
         __syncthreads();
+        if (tile == 0) hsum = 0.f;
 #pragma unroll
-        for (int u = 0; u < SR; ++u) {
-            *reinterpret_cast<float4 *>(&sm.u.t.H[sl.r0 + u][sl.c0]) = hpre[u];
-            *reinterpret_cast<float4 *>(&sm.u.t.D[sl.r0 + u][sl.c0]) = dpre[u];
+        for (int u = 0; u < NF4; ++u) {
+            const float4 h = hpre[u], d = dpre[u];
+            sm_put4(sm.u.t.Ht, tcol, td0 + 4 * u, h);
+            sm_put4(sm.u.t.Dt, tcol, td0 + 4 * u, d);
+            hsum += h.x * d.x + h.y * d.y + h.z * d.z + h.w * d.w;
         }
-        const bool urow = ur < n;
-        *reinterpret_cast<float4 *>(&sm.U[ur][uc]) = urow ? upre : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4 *>(&sm.dR[ur][uc]) = urow ? rpre : make_float4(0.f, 0.f, 0.f, 0.f);
+        // (rows past the chunk end hold zeros in U and dR); lane l of every wave holds the gates
+        // of row l of this step's value head
+        sm_put4(sm.U, ur, uc, upre);
+        sm_put4(sm.dR, ur, uc, rpre);
+        const float be = __shfl(gbeta, ur, 64);
+        if constexpr (SM::kPre) {
+            const float bu = __shfl(gb, ur, 64), bl = __shfl(gb, CB - 1, 64);
+            const float wr = __expf(fminf(bl - bu, 0.f)), br = -be * __expf(bu);
+            sm_put4(sm.wU, ur, uc, make_float4(wr * upre.x, wr * upre.y, wr * upre.z, wr * upre.w));
+            sm_put4(sm.bR, ur, uc, make_float4(br * rpre.x, br * rpre.y, br * rpre.z, br * rpre.w));
+        }
+        // dV = diag(beta) dR
+        if (ur < n) {
+            const int64_t head = kh * grp + v;
+            *reinterpret_cast<float4 *>(a.dv + ((L.row * a.Hv + head) * a.T + L.sq.token(c * CB + ur)) * dvf + tile * TV + uc) =
+                make_float4(be * rpre.x, be * rpre.y, be * rpre.z, be * rpre.w);
+        }
         op.store(&sm.dO[0][0], SM::VP, n, tid);
         vp.store(&sm.V[0][0], SM::VP, n, tid);
         if (tile == 0) {
             if (tid < CB) {
                 sm.b[tid] = gb;
                 sm.r[tid] = gr_;
-                sm.beta[tid] = gbeta;
+                sm.beta[tid] = tid < n ? gbeta : 0.f;
             }
 #pragma unroll
             for (int s = 0; s < NQT; ++s) dQH[s] = zero4();
@@ -834,9 +1006,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
             for (int s = 0; s < 3; ++s) pa[s] = zero4();
 #pragma unroll
             for (int r = 0; r < 4; ++r) ax[r] = bx[r] = wy[r] = 0.f;
-            hsum = 0.f;
         }
-        if (it + 1 < nit) issue(it + 1);
+        // the next slice of this value head is read during this one's products; the first slice
+        // of the next value head after this one's gate gradients
+        if (tile + 1 < a.ntiles) issue(it + 1);
         __syncthreads();
         const float blast = sm.b[CB - 1];
         // X = K H and Y = K D on this wave's tile: dR . X, dR . (V - gamma X), Y . U per row
@@ -845,22 +1018,19 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 const Split ka = ldr<E>(&sm.K[0][0], SM::KP, 16 * xm, 32 * ks);
-                x = mms<kX, false>(x, ka, ldc<float>(&sm.u.t.H[0][0], FP, 16 * xn, 32 * ks));
-                y = mms<kX, false>(y, ka, ldc<float>(&sm.u.t.D[0][0], FP, 16 * xn, 32 * ks));
+                x = mms<kX, false>(x, ka, sm_rows(sm.u.t.Ht, 16 * xn, 32 * ks));
+                y = mms<kX, false>(y, ka, sm_rows(sm.u.t.Dt, 16 * xn, 32 * ks));
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * xm + 4 * g + r, j = 16 * xn + cc;
-                const float dr = sm.dR[i][j];
+                const float dr = sm_get(sm.dR, i, j);
                 ax[r] += dr * x[r];
                 bx[r] += dr * ((float)sm.V[i][j] - __expf(sm.b[i]) * x[r]);
-                wy[r] += y[r] * sm.U[i][j];
+                wy[r] += y[r] * sm_get(sm.U, i, j);
             }
         }
-#pragma unroll
-        for (int u = 0; u < SR; ++u)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) hsum += sm.u.t.D[sl.r0 + u][sl.c0 + q] * sm.u.t.H[sl.r0 + u][sl.c0 + q];
+        fence_sched();
         // dP = dO U^T and -dA = dR U^T on the lower tiles
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
@@ -868,23 +1038,31 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
             if (task < 20) {
                 int pm, pn;
                 lower_tile(task % 10, pm, pn);
-                const Split ub = ldr<float>(&sm.U[0][0], FP, 16 * pn, 0);
-                if (task >= 10) pa[s] = mms<false, false>(pa[s], ldr<float>(&sm.dR[0][0], FP, 16 * pm, 0), ub);
+                const Split ub = sm_rows(sm.U, 16 * pn, 0);
+                if (task >= 10) pa[s] = mms<false, false>(pa[s], sm_rows(sm.dR, 16 * pm, 0), ub);
                 else pa[s] = mms<kX, false>(pa[s], ldr<E>(&sm.dO[0][0], SM::VP, 16 * pm, 0), ub);
             }
         }
+        fence_sched();
         // dO H^T, and diag(w) U dH'^T - diag(beta gamma) dR H^T into dK
         {
-            const Split hB = ldr<float>(&sm.u.t.H[0][0], FP, 16 * qn, 0);
-            const Split dB = ldr<float>(&sm.u.t.D[0][0], FP, 16 * qn, 0);
+            const Split hB = sm_cols(sm.u.t.Ht, 16 * qn, 0);
+            const Split dB = sm_cols(sm.u.t.Dt, 16 * qn, 0);
 #pragma unroll
             for (int s = 0; s < NQT; ++s) {
-                const int m = qm(s), row = 16 * m + cc;
+                const int m = qm(s);
                 dQH[s] = mms<kX, false>(dQH[s], ldr<E>(&sm.dO[0][0], SM::VP, 16 * m, 0), hB);
-                const float wr = __expf(fminf(blast - sm.b[row], 0.f));
-                const float br = -sm.beta[row] * __expf(sm.b[row]);
-                dK[s] = mms<false, false>(dK[s], ldr_scaled(&sm.U[0][0], FP, 16 * m, 0, wr), dB);
-                dK[s] = mms<false, false>(dK[s], ldr_scaled(&sm.dR[0][0], FP, 16 * m, 0, br), hB);
+                if constexpr (SM::kPre) {
+                    dK[s] = mms<false, false>(dK[s], sm_rows(sm.wU, 16 * m, 0), dB);
+                    dK[s] = mms<false, false>(dK[s], sm_rows(sm.bR, 16 * m, 0), hB);
+                } else {
+                    const int row = 16 * m + cc;
+                    const float wr = __expf(fminf(blast - sm.b[row], 0.f));
+                    const float br = -sm.beta[row] * __expf(sm.b[row]);
+                    dK[s] = mms<false, false>(dK[s], sm_scaled_rows(sm.U, 16 * m, wr), dB);
+                    dK[s] = mms<false, false>(dK[s], sm_scaled_rows(sm.dR, 16 * m, br), hB);
+                }
+                fence_sched();
             }
         }
         if (tile + 1 < a.ntiles) continue;
@@ -906,7 +1084,21 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) h += __shfl_xor(h, off, 64);
             if (lane == 0) sm.hd[wave] = h;
+            // dQ += diag(e^r) dO H^T, and the read's exponent gradient e^r (dO H^T) . q
+#pragma unroll
+            for (int s = 0; s < NQT; ++s) {
+                const int m = qm(s);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * m + 4 * g + r;
+                    const float qh = __expf(sm.r[i]) * dQH[s][r];
+                    const float rqv = row16(qh * (float)sm.Q[i][16 * qn + cc]);
+                    if (cc == 0) sm.rq[qn][i] = rqv;
+                    dQ[s][r] += qh;
+                }
+            }
         }
+        fence_sched();
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             const int task = wave + kWaves * s;
@@ -921,6 +1113,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
                 gv = mms<kX, kX>(gv, ldr<E>(isa ? &sm.K[0][0] : &sm.Q[0][0], SM::KP, 16 * pm, 32 * ks),
                                  ldr<E>(&sm.K[0][0], SM::KP, 16 * pn, 32 * ks));
             float csum = 0.f;
+            floatx4 mv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * pm + 4 * g + r, j = 16 * pn + cc;
@@ -929,13 +1122,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
                     const bool keep = pre ? j < i : j <= i;
                     const float e = __expf(fminf(sm.r[i] - sm.b[j], 0.f));
                     const float dp = pa[s][r];
-                    sm.u.m.M[i][j] = keep ? dp * e : 0.f;
+                    mv[r] = keep ? dp * e : 0.f;
                     rs = keep ? dp * gv[r] * e : 0.f;  // dP_ij Pm_ij
                 } else {
                     const bool keep = j < i;
                     const float e = __expf(fminf(sm.b[i] - sm.b[j], 0.f));
                     const float da = -pa[s][r], gij = keep ? gv[r] * e : 0.f;
-                    sm.u.m.N[i][j] = keep ? sm.beta[i] * da * e : 0.f;
+                    mv[r] = keep ? sm.beta[i] * da * e : 0.f;
                     rs = da * sm.beta[i] * gij;  // dA_ij A_ij
                     rb = da * gij;               // dA_ij G_ij
                 }
@@ -950,44 +1143,36 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
                 } else if (cc == 0) {
                     sm.pr[pn][i] = rsum;
                 }
-                if (pm > pn) {
-                    const int i2 = 16 * pn + 4 * g + r, j2 = 16 * pm + cc;
-                    if (isa) sm.u.m.N[i2][j2] = 0.f;
-                    else sm.u.m.M[i2][j2] = 0.f;
-                }
             }
+            // the tile of M (or N), and the zero tile mirrored above the diagonal
+            SplitMat<CB, CB> &Xt = isa ? sm.u.m.Nt : sm.u.m.Mt;
+            sm_put_t(Xt, 16 * pm, 16 * pn, mv);
+            if (pm > pn) sm_put_t(Xt, 16 * pn, 16 * pm, zero4());
             // column sums over the tile's 16 rows enter d b_j with a minus sign
             csum = col4(csum);
             if (g == 0) {
                 if (isa) sm.ac[pm][16 * pn + cc] = -csum;
                 else sm.pc[pm][16 * pn + cc] = -csum;
             }
+            fence_sched();
         }
         __syncthreads();
-        // dQ += diag(e^r) dO H^T + M K;  dK += M^T Q + N K + N^T K (N holds diag(beta) N)
+        // dQ += M K;  dK += M^T Q + N K + N^T K (N holds diag(beta) N)
 #pragma unroll
         for (int s = 0; s < NQT; ++s) {
             const int m = qm(s);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * m + 4 * g + r;
-                const float qh = __expf(sm.r[i]) * dQH[s][r];
-                const float rqv = row16(qh * (float)sm.Q[i][16 * qn + cc]);
-                if (cc == 0) sm.rq[qn][i] = rqv;
-                dQ[s][r] += qh;
-            }
-#pragma unroll
             for (int ks = 0; ks < kSlices; ++ks) {
                 const Split kB = ldc<E>(&sm.K[0][0], SM::KP, 16 * qn, 32 * ks);
                 if (32 * ks <= 16 * m + 15) {  // rows of M and N: zero past column 16 m + 15
-                    dQ[s] = mms<false, kX>(dQ[s], ldr<float>(&sm.u.m.M[0][0], SP, 16 * m, 32 * ks), kB);
-                    dK[s] = mms<false, kX>(dK[s], ldr<float>(&sm.u.m.N[0][0], SP, 16 * m, 32 * ks), kB);
+                    dQ[s] = mms<false, kX>(dQ[s], sm_cols(sm.u.m.Mt, 16 * m, 32 * ks), kB);
+                    dK[s] = mms<false, kX>(dK[s], sm_cols(sm.u.m.Nt, 16 * m, 32 * ks), kB);
                 }
                 if (32 * ks + 31 >= 16 * m) {  // columns of M and N: zero above row 16 m
-                    dK[s] = mms<false, kX>(dK[s], ldc<float>(&sm.u.m.M[0][0], SP, 16 * m, 32 * ks),
-                                           ldc<E>(&sm.Q[0][0], SM::KP, 16 * qn, 32 * ks));
-                    dK[s] = mms<false, kX>(dK[s], ldc<float>(&sm.u.m.N[0][0], SP, 16 * m, 32 * ks), kB);
+                    dK[s] = mms<false, kX>(dK[s], sm_rows(sm.u.m.Mt, 16 * m, 32 * ks), ldc<E>(&sm.Q[0][0], SM::KP, 16 * qn, 32 * ks));
+                    dK[s] = mms<false, kX>(dK[s], sm_rows(sm.u.m.Nt, 16 * m, 32 * ks), kB);
                 }
+                fence_sched();
             }
         }
         __syncthreads();
@@ -1036,6 +1221,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
                 a.dbeta[t] = dbeta;
             }
         }
+        if (it + 1 < nit) issue(it + 1);
     }
     // dq, dk of the key head: the sum over its value heads, in order
     const int64_t qbase = (L.row * a.Hk + kh) * a.T * DK;

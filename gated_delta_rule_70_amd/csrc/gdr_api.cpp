@@ -469,9 +469,9 @@ int64_t bwd_slots(const gdr_chunk_dims_t &d, bool packed) {
 }
 
 // Workspace of the backward, in this order: a record per (value head, slot) (the chunk's
-// triangular inverse and read matrix as matrix-core operands, and its gate cumsums); the entry
-// state and the exit-state adjoint of every chunk (dk x dv fp32 each); U and dR of every token
-// ([B][Hv][T][dv] fp32 each).
+// triangular inverse and read matrix as matrix-core operands, and its gate cumsums); the
+// entry state and the exit-state adjoint of every chunk (dk x dv fp32 each); U and dR of every
+// chunk (64 x dv fp32 each, rows past a segment's end included).
 struct BwdLayout {
     int64_t rec, states, tokens, total;
 };
@@ -480,7 +480,7 @@ BwdLayout bwd_layout(const gdr_chunk_dims_t &d, bool packed) {
     const int64_t slots = bwd_slots(d, packed);
     l.rec = prod({d.Hv, slots, gdr::kBwdRecBytes});
     l.states = prod({d.Hv, slots, d.dk, d.dv, 4});
-    l.tokens = prod({d.B, d.Hv, d.T, d.dv, 4});
+    l.tokens = prod({d.Hv, slots, gdr::kBwdBlock, d.dv, 4});
     l.total = (l.rec < 0 || l.states < 0 || l.tokens < 0) ? -1 : l.rec + 2 * l.states + 2 * l.tokens;
     return l;
 }

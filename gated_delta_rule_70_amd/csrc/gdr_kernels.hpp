@@ -75,10 +75,11 @@ struct Gdn2DecodeArgs {
 // Backward of the scalar rule. Gradient buffers are fp32: dq, dk [B][Hk][T][dk] (summed over the
 // value heads of a key head), dv [B][Hv][T][dv], dlog_alpha, dbeta [B][Hv][T], dh0 like h0.
 // The workspace holds, per chunk slot of every value head (nslots per head, kBwdBlock tokens per
-// chunk): a record of kBwdRecBytes (the chunk's inverse and read matrix as matrix-core operands,
-// and its gate cumsums), the entry state hs and the exit-state adjoint ds of the chunk (per
-// kBwdCols-column slice, dk x kBwdCols fp32 each); and us, drs [B][Hv][T][dv] fp32, the chunk
-// form's U and dR of every token.
+// chunk): a record of kBwdRecBytes (the chunk's inverse and read matrix as matrix-core
+// operands, and its gate cumsums), the entry state hs and the exit-state adjoint ds
+// of the chunk (per kBwdCols-column slice, kBwdCols x dk fp32 each, transposed); and us, drs
+// [Hv][nslots][kBwdBlock][dv] fp32, the chunk form's U and dR of every chunk (rows past a
+// segment's end hold zeros).
 constexpr int kBwdBlock = 64;
 constexpr int kBwdCols = 32;  // value columns per workgroup of the state sweeps
 constexpr int64_t kBwdRecBytes = 3 * 16384 + 2 * kBwdBlock * 4;

@@ -302,18 +302,18 @@ def test_backward_rejects():
     st, msg = call(dq=FAKE + 64)
     assert st == "GDR_ERR_ALIAS" and "dq overlaps q" in msg, msg
     dims = binding.ChunkDims(4, 4096, 16, 16, 128, 128, 0, 1, 0)
-    # 16 value heads x (4 sequences x 64 chunks of 64 tokens): a 49,664-byte record per chunk
-    # (three 64 x 64 operand matrices as split bf16, 16 KiB each, and 2 x 64 gate cumsums), the
-    # entry state and the exit adjoint (64 KiB each); then U and dR of every token (fp32 [4][16][4096][128])
+    # 16 value heads x (4 sequences x 64 chunks of 64 tokens): a record per chunk (three 64 x 64
+    # operand matrices as split bf16, 4 bytes an element, and 2 x 64 gate cumsums), the entry state
+    # and the exit adjoint (64 KiB each); then U and dR of every chunk (fp32 64 x 128 each)
     slots = 16 * 4 * 64
     rec = slots * (3 * 16384 + 2 * 64 * 4)
     states = 2 * slots * 128 * 128 * 4
-    tokens = 2 * 4 * 16 * 4096 * 128 * 4
+    tokens = 2 * slots * 64 * 128 * 4
     assert lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(dims), 0) == rec + states + tokens
     # packed: slots for every 64 tokens of the total plus one per segment and one spare
     pdims = binding.ChunkDims(1, 1000, 2, 4, 64, 64, 3, 1, 0)
     pslots = 4 * (1000 // 64 + 3 + 1)
-    want = pslots * (3 * 16384 + 2 * 64 * 4) + 2 * pslots * 64 * 64 * 4 + 2 * 4 * 1000 * 64 * 4
+    want = pslots * (3 * 16384 + 2 * 64 * 4) + 2 * pslots * 64 * 64 * 4 + 2 * pslots * 64 * 64 * 4
     assert lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(pdims), 1) == want
 
 
