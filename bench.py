@@ -594,9 +594,11 @@ def main():
             "gdr-backward-bf16-B4-H16-T4096-d128": {
                 "tokens_per_s": bwr["tokens"] / (bwr["ms"] / 1e3), "ms": bwr["ms"],
                 "hbm_frac": bwr["bytes"] / (bwr["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                "workspace_bytes": bwr["ws_bytes"], "kernel": "bwd_kernel<bf16, 128>",
-                "note": "chunk-form adjoint (32-token chunks), one workgroup of 8 waves per sequence-head "
-                        "and 32 value columns; products as split-bf16 matrix-core products"},
+                "workspace_bytes": bwr["ws_bytes"],
+                "kernel": "bwd_prep_kernel + bwd_sweep_kernel + bwd_grad_kernel <bf16, 128>",
+                "note": "chunk-form adjoint over 64-token chunks: chunk-parallel prep, forward and adjoint "
+                        "state sweeps in one launch, chunk-parallel gradients; products as split-bf16 "
+                        "matrix-core products"},
             "gdn2-decode-bf16-N256-Hk16-Hv32-d128": {
                 "state_GB_per_s": g2d["state_bytes"] / (g2d["ms"] / 1e3) / 1e9, "us_per_step": g2d["ms"] * 1e3,
                 "roofline": {"bound": "hbm",

@@ -213,15 +213,17 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v,
  * dk must be 64 or 128, dv a multiple of 32 up to 256. Every output is fully written. Outputs
  * and workspace must not overlap inputs or each other (GDR_ERR_ALIAS).
  * Errors as gdr_chunk_fwd, plus GDR_ERR_DIMS when workspace_bytes is too small.
- * The backward runs the chunk form (32-token chunks) forward once, keeping each chunk's entry
- * state in the workspace (one fp32 state per chunk of every sequence-head), then walks the chunks
- * back, recomputing each chunk's quantities from its entry state. Its products run on the bf16
+ * The backward runs the chunk form over 64-token chunks as three kernels on `stream`: a
+ * chunk-parallel pass forms each chunk's gate cumsums, read matrix and triangular inverse; two
+ * sweeps (one launch) carry the state forward and its adjoint backward through the chunks,
+ * keeping every chunk's entry state, exit-state adjoint, U and dR in the workspace (each a
+ * dk x dv or 64 x dv fp32 block per chunk and value head, plus a 49,664-byte record); a second
+ * chunk-parallel pass forms every gradient of a chunk from those. Its products run on the bf16
  * matrix cores with each fp32 operand split in two bf16 parts (hi*hi + hi*lo + lo*hi, fp32
  * accumulation): a relative error near 2^-16 per product.
- * Deterministic: the same inputs give the same bits on every call. Each 32-column slice of dv
- * writes its share of dq, dk, dlog_alpha and dbeta into the workspace (4 * (2 * dk + 2) bytes per
- * token, value head and slice, beside the chunk-start states), and a second kernel on the same
- * stream adds the shares in a fixed order; no float atomics are used.
+ * Deterministic: the same inputs give the same bits on every call. Every gradient element is
+ * written once, by one workgroup, which adds the contributions of the column slices (and, for
+ * dq and dk, of the value heads of a key head) in a fixed order; no float atomics are used.
  */
 int64_t gdr_chunk_bwd_workspace_bytes(const gdr_chunk_dims_t *dims, int32_t packed);
 gdr_status_t gdr_chunk_bwd(const void *q, const void *k, const void *v,
