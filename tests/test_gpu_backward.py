@@ -147,3 +147,38 @@ def test_deterministic(gdr, shape):
     torch.cuda.synchronize()
     for n, x, y in zip(NAMES, first, second):
         assert torch.equal(x, y), "%s differs between two calls" % n
+
+
+EDGE = [
+    dict(B=1, T=130, Hk=1, Hv=1, dk=64, dv=256, dtype=torch.bfloat16),   # the widest dv: 8 column slices
+    dict(B=1, T=70, Hk=1, Hv=2, dk=128, dv=256, dtype=torch.float32),    # GQA at d_k 128, d_v 256
+    dict(B=3, T=64, Hk=2, Hv=2, dk=64, dv=32, dtype=torch.bfloat16),     # one whole chunk, one slice
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=_ids)
+def test_edge_shapes(gdr, cfg):
+    _say("backward edge shape %s" % _ids(cfg))
+    c = inputs.chunk_case(**cfg, seed=51, h0_std=0.5, regime="slow")
+    dout, dhT = _upstream(c, 52, cfg["B"])
+    _run_and_check(gdr, c, dout, dhT, "post", False, "edge")
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_no_tokens(gdr, packed):
+    # no token at all (T = 0, or packed segments that are all empty): nothing but dh0 is written,
+    # and the adjoint of h0 is dhT itself
+    _say("backward with no tokens, packed=%s" % packed)
+    if packed:
+        c = inputs.chunk_case(Hk=1, Hv=2, dk=64, dv=64, dtype=torch.bfloat16, seed=61, h0_std=0.5, lengths=[0, 0, 0])
+        S = 3
+    else:
+        c = inputs.chunk_case(B=2, T=0, Hk=1, Hv=2, dk=64, dv=64, dtype=torch.bfloat16, seed=61, h0_std=0.5)
+        S = 2
+    dout, dhT = _upstream(c, 62, S)
+    d = lambda t: None if t is None else t.cuda()
+    got = gdr.chunk_bwd(d(c.q), d(c.k), d(c.v), d(c.log_alpha), d(c.beta), d(dout), d(c.h0), d(c.cu_seqlens), d(dhT))
+    torch.cuda.synchronize()
+    for n, x in zip(NAMES[:5], got[:5]):
+        assert x.numel() == 0, "%s has %d elements" % (n, x.numel())
+    assert torch.equal(got[5].cpu(), dhT), "dh0 differs from dhT"
