@@ -69,7 +69,6 @@ constexpr int NMT = CB / 16;   // 16-row tiles of a chunk
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
 constexpr int kPrepThreads = 256;
 static_assert(CB == 64 && TV == 32, "the tile assignments are written for 64-token chunks and 32-column slices");
-constexpr int FP = TV + 4;  // pitch of fp32 [rows][TV] matrices
 constexpr int SP = CB + 4;  // pitch of fp32 [CB][CB] matrices
 template <typename E>
 constexpr int pad_of() { return 16 / (int)sizeof(E); }  // one 16-byte piece of padding per row
@@ -251,6 +250,29 @@ __device__ __forceinline__ void sm_put_t(SplitMat<R, C> &Xt, int m0, int n0, con
     const int rr = n0 + (lane & 15), cc = m0 + 4 * (lane >> 4);
     *reinterpret_cast<bf16x4 *>(&Xt.h[rr][cc]) = hi;
     *reinterpret_cast<bf16x4 *>(&Xt.l[rr][cc]) = lo;
+}
+// columns of a row-major E-typed matrix in LDS (as frag_cols), row k scaled by sk[k], split
+template <typename E>
+__device__ __forceinline__ Split cols_kscaled(const E *X, int ld, int col0, int k0, const float *sk) {
+    const int lane = threadIdx.x & 63;
+    const int kb = k0 + 4 * (lane >> 4);
+    Frag<float> f;
+    if constexpr (std::is_same<E, __bf16>::value) {
+        const Frag<__bf16> x = cols_tr(X, ld, col0, k0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            f.lo[s] = (float)x.lo[s] * sk[kb + s];
+            f.hi[s] = (float)x.hi[s] * sk[kb + 16 + s];
+        }
+    } else {
+        const Frag<float> x = frag_cols<float>(X, ld, col0, k0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            f.lo[s] = x.lo[s] * sk[kb + s];
+            f.hi[s] = x.hi[s] * sk[kb + 16 + s];
+        }
+    }
+    return split_frag(f);
 }
 // rows of a split matrix (the 32 columns from column 0), each lane's row scaled by sc and split again
 template <int R, int C>
@@ -513,14 +535,14 @@ struct FwdSmem {
 template <typename E, int DK>
 struct AdjSmem {
     static constexpr int KP = DK + pad_of<E>(), VP = TV + pad_of<E>();
-    // the next chunk's k, q and dout go into a second buffer with bf16 inputs; fp32 ones leave no
-    // room for it and are stored after an extra barrier
-    static constexpr int NB = sizeof(E) == 2 ? 2 : 1;
-    float b[2][CB], er[2][CB], beta[2][CB];
-    SplitMat<TV, CB> dUt, bRt, eOt;  // eOt: diag(e^r) dO, transposed
+    // one buffer of k, q and dout: the next chunk's are stored after an extra barrier, which
+    // keeps a workgroup under 80 KB of LDS (with bf16 inputs), so that a forward and an adjoint
+    // workgroup share a compute unit
+    float b[CB], er[CB], beta[CB];
+    SplitMat<TV, CB> dUt, bRt;
     SplitMat<TV, DK> Dt;
-    E dO[NB][CB][VP];
-    E K[NB][CB][KP], Q[NB][CB][KP];
+    E dO[CB][VP];
+    E K[CB][KP], Q[CB][KP];
 };
 template <typename E, int DK>
 constexpr size_t sweep_smem_bytes() {
@@ -657,11 +679,12 @@ __device__ __forceinline__ void fwd_sweep(const BwdArgs &a, int64_t unit, int ti
             for (int ks = 0; ks < kSlices; ++ks)
                 if (32 * ks <= 16 * mt + 15) u = mms<false, false>(u, slab_split(tr[ks]), sm_rows(sm.Rt, 16 * nt, 32 * ks));
             const float blast = bc[CB - 1];
+            float *ubc = ub + c * CB * dvf;  // (a uniform base and a 32-bit lane offset)
             floatx4 wu;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                ub[(c * CB + i) * dvf + j] = u[r];
+                ubc[(uint32_t)(i * (int)dvf + j)] = u[r];
                 wu[r] = __expf(fminf(blast - bc[i], 0.f)) * u[r];
             }
             sm_put_t(sm.wUt, 16 * mt, 16 * nt, wu);
@@ -731,16 +754,15 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
         rv = rb[CB + gr];
         betav = (beb + L.sq.low(c, n))[(uint32_t)L.sq.off(gr < n ? gr : 0, n)];
     };
-    auto store = [&](int64_t c, int buf) __attribute__((always_inline)) {
+    auto store = [&](int64_t c) __attribute__((always_inline)) {
         const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
-        const int ib = SM::NB == 2 ? buf : 0;
-        kp.store(&sm.K[ib][0][0], SM::KP, n, tid);
-        qp.store(&sm.Q[ib][0][0], SM::KP, n, tid);
-        op.store(&sm.dO[ib][0][0], SM::VP, n, tid);
+        kp.store(&sm.K[0][0], SM::KP, n, tid);
+        qp.store(&sm.Q[0][0], SM::KP, n, tid);
+        op.store(&sm.dO[0][0], SM::VP, n, tid);
         if (tid < CB) {
-            sm.b[buf][tid] = bv;
-            sm.er[buf][tid] = __expf(rv);
-            sm.beta[buf][tid] = tid < n ? betav : 0.f;
+            sm.b[tid] = bv;
+            sm.er[tid] = __expf(rv);
+            sm.beta[tid] = tid < n ? betav : 0.f;
         }
     };
     // T^T and Pm^T (rows 16 mt .. 16 mt + 15 are zero before column 16 mt; the zero slabs are read
@@ -757,16 +779,15 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
     if (nch > 0) {
         issue(nch - 1);
         issue_f(nch - 1);
-        store(nch - 1, 0);
+        store(nch - 1);
     }
     __syncthreads();
     for (int64_t c = nch - 1; c >= 0; --c) {
         SM &sm = *lds_opaque(reinterpret_cast<SM *>(smraw));
-        const int cur = (int)((nch - 1 - c) & 1), ib = SM::NB == 2 ? cur : 0;
-        const E *Kc = &sm.K[ib][0][0];
-        const E *Qc = &sm.Q[ib][0][0];
-        const E *Oc = &sm.dO[ib][0][0];
-        const float *bc = sm.b[cur];
+        const E *Kc = &sm.K[0][0];
+        const E *Qc = &sm.Q[0][0];
+        const E *Oc = &sm.dO[0][0];
+        const float *bc = sm.b;
         D.save_t(ds + c * dstride, wave);
         // dU = diag(w) K D + Pm^T dO
         {
@@ -778,15 +799,10 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
             for (int ks = 0; ks < kSlices; ++ks)
                 if (32 * ks + 31 >= 16 * mt) p = mms<false, kX>(p, slab_split(pt[ks]), ldc<E>(Oc, SM::VP, 16 * nt, 32 * ks));
             const float blast = bc[CB - 1];
-            floatx4 du, eo;
+            floatx4 du;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * g + r;
-                du[r] = __expf(fminf(blast - bc[i], 0.f)) * y[r] + p[r];
-                eo[r] = sm.er[cur][i] * (float)Oc[i * SM::VP + 16 * nt + cc];
-            }
+            for (int r = 0; r < 4; ++r) du[r] = __expf(fminf(blast - bc[16 * mt + 4 * g + r], 0.f)) * y[r] + p[r];
             sm_put_t(sm.dUt, 16 * mt, 16 * nt, du);
-            sm_put_t(sm.eOt, 16 * mt, 16 * nt, eo);
         }
         __syncthreads();
         issue(c > 0 ? c - 1 : 0);
@@ -796,12 +812,13 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
 #pragma unroll
             for (int ks = 0; ks < kSlices; ++ks)
                 if (32 * ks + 31 >= 16 * mt) d = mms<false, false>(d, slab_split(tt[ks]), sm_rows(sm.dUt, 16 * nt, 32 * ks));
+            float *drc = drb + c * CB * dvf;
             floatx4 br;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-                drb[(c * CB + i) * dvf + j] = d[r];
-                br[r] = -sm.beta[cur][i] * __expf(bc[i]) * d[r];
+                drc[(uint32_t)(i * (int)dvf + j)] = d[r];
+                br[r] = -sm.beta[i] * __expf(bc[i]) * d[r];
             }
             sm_put_t(sm.bRt, 16 * mt, 16 * nt, br);
         }
@@ -815,7 +832,7 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
                 floatx4 h = glast * D.v[s];
 #pragma unroll
                 for (int ks = 0; ks < kSlices; ++ks) {
-                    h = mms<kX, false>(h, ldc<E>(Qc, SM::KP, 16 * hm, 32 * ks), sm_rows(sm.eOt, 16 * hn, 32 * ks));
+                    h = mms<false, kX>(h, cols_kscaled<E>(Qc, SM::KP, 16 * hm, 32 * ks, sm.er), ldc<E>(Oc, SM::VP, 16 * hn, 32 * ks));
                     h = mms<kX, false>(h, ldc<E>(Kc, SM::KP, 16 * hm, 32 * ks), sm_rows(sm.bRt, 16 * hn, 32 * ks));
                 }
                 D.v[s] = h;
@@ -823,31 +840,36 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
             D.put(sm.Dt, wave);
         }
         issue_f(c > 0 ? c - 1 : 0);
-        if constexpr (SM::NB == 2) {
-            if (c > 0) store(c - 1, cur ^ 1);
-            __syncthreads();
-        } else {
-            __syncthreads();
-            if (c > 0) store(c - 1, cur ^ 1);
-            __syncthreads();
-        }
+        __syncthreads();
+        if (c > 0) store(c - 1);
+        __syncthreads();
     }
     if (a.dh0) D.save(a.dh0 + sbase, dvf, wave);
 }
 
 // Both sweeps in one launch: workgroups [0, n) run the forward sweep, [n, 2n) the adjoint sweep
-// (n = units x column slices). Workgroup ids are spread so that the column slices of a unit
-// run on the same XCD (workgroups go to the XCDs round robin) and share its L2.
+// (n = units x column slices), so that as the first n fill one slot of every compute unit the
+// second n pair each forward workgroup with an adjoint one. Within each half the ids are spread
+// so that the column slices of a unit run on the same XCD (workgroups go to the XCDs round
+// robin) and share its L2.
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdArgs a) {
+__device__ __forceinline__ void sweep_body(const BwdArgs &a) {
     __shared__ __attribute__((aligned(16))) char smraw[sweep_smem_bytes<E, DK>()];
-    const int64_t n = a.units * a.ntiles, nb = 2 * n;
-    int64_t id = blockIdx.x;
-    if (nb % 8 == 0) id = (id % 8) * (nb / 8) + id / 8;
-    const bool adjoint = id >= n;
-    const int64_t w = adjoint ? id - n : id;
+    const int64_t n = a.units * a.ntiles;
+    const bool adjoint = blockIdx.x >= n;
+    int64_t w = adjoint ? blockIdx.x - n : blockIdx.x;
+    if (n % 8 == 0) w = (w % 8) * (n / 8) + w / 8;
     if (adjoint) adj_sweep<E, DK>(a, w / a.ntiles, (int)(w % a.ntiles), smraw);
     else fwd_sweep<E, DK>(a, w / a.ntiles, (int)(w % a.ntiles), smraw);
+}
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdArgs a) {
+    sweep_body<E, DK>(a);
+}
+// bf16: at most 128 registers, so that two workgroups (8 waves each) fit on a compute unit
+template <int DK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_sweep_kernel_bf16(BwdArgs a) {
+    sweep_body<__bf16, DK>(a);
 }
 
 // ---------------------------------------------------------------- 3. gradients
@@ -1249,7 +1271,10 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (nsw > 0) {
-        hipLaunchKernelGGL((bwd_sweep_kernel<E, DK>), dim3((unsigned)nsw), dim3(kThreads), 0, s, a);
+        if constexpr (std::is_same<E, __bf16>::value)
+            hipLaunchKernelGGL((bwd_sweep_kernel_bf16<DK>), dim3((unsigned)nsw), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_sweep_kernel<E, DK>), dim3((unsigned)nsw), dim3(kThreads), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
