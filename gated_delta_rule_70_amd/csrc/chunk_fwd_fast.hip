@@ -23,10 +23,12 @@
 //   wave 3      off-diagonal tiles of K K^T (-> -A_ij) for chunk c+1, and the write-back of
 //               the output of chunk c-1 from its staging tile.
 //   waves 5, 7  the ten lower tiles of Q K^T with their decay factors (P) for chunk c+1.
-//   waves 4, 6  copies for chunk c+2 (K; Q, V and gates); they issue little.
+//   waves 4, 6  copies for chunk c+2 (K; Q, V and gates) and L2 touches of chunk c+3; they
+//               issue little.
 // Raw q/k/v of a chunk are copied once per workgroup, global -> LDS directly (16 bytes per
 // lane, no registers), into a ring of three buffers: while the chain reads chunk c and the
-// prep waves read chunk c+1, the loads for chunk c+2 are in flight. In K and Q the 16-byte
+// prep waves read chunk c+1, the loads for chunk c+2 are in flight, and chunk c+3 is being
+// brought into L2 so that those loads hit there. In K and Q the 16-byte
 // pieces of a row are XOR-swizzled by a function of the row (row_swz) so that the
 // row-fragment reads and the transposed K reads spread over the banks. The products the prep waves hand
 // to the chain go through a second, double-buffered area. One barrier per chunk.
@@ -90,7 +92,14 @@ constexpr int kSortMax = 128;  // packed segments ranked by length (beyond, the 
 // with accumulation, the output's previous values of a chunk, copied in like the V slice
 constexpr int kOffPrev = kOffStage + 2 * kStageBytes;
 constexpr int kPrevBytes = 4096;
-constexpr int kSmemBytes = kOffPrev + 2 * kPrevBytes;
+// a word per lane that the L2 prefetch touches land in; nothing reads it
+constexpr int kOffTouch = kOffPrev + 2 * kPrevBytes;
+constexpr int kSmemBytes = kOffTouch + 256;
+// L2 prefetch: how many steps ahead of its copies a chunk is touched, and the bytes one
+// touch brings in (the L2 fills a miss by 32-byte sectors)
+constexpr int kPfDist = 1;
+constexpr int kPfSector = 32;
+constexpr int kTouchPerQuarter = 4096 / kPfSector / 64;  // per quarter of a 16 KB K or Q chunk
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 static_assert((kSortMax + 2) * 4 <= kRawBytes, "segment offsets fit in a raw slot");
 
@@ -240,7 +249,80 @@ __device__ __forceinline__ void copy_gates(char *raw, u32x4 ra, u32x4 rb, const 
     dma_b32(lds_addr(raw + kRawLa), ra, co.gate_la, soff_la);
     dma_b32(lds_addr(raw + kRawBeta), rb, co.gate, soff);
 }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// L2 prefetch of a later chunk. The ring holds three chunks, so a chunk's copies are issued
+// one step before the step that needs them, and a step is shorter than a global-memory miss
+// under full load. Touches issued kPfDist steps before the copies bring the chunk into L2,
+// where its copies then hit. A touch is a one-dword load per lane into a scratch word of
+// LDS: it has no destination register, and vector loads complete in issue order, so a wave
+// waits for its copies with the count of touches issued after them still outstanding.
+// The value tiles of a unit read the same K and Q chunk; tile t touches the quarters t,
+// t + ntiles, ... of it (a tile takes nq quarter slots; slots past the fourth quarter read
+// nothing). The chunk offset is clamped so that the touched range ends inside the slab.
+struct TouchOffsets {
+    int kq[4][kTouchPerQuarter], v[2], gate;
+    __device__ __forceinline__ void init(int tile, int ntiles, int64_t dv) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = tile + j * ntiles;
+#pragma unroll
+            for (int i = 0; i < kTouchPerQuarter; ++i) {
+                kq[j][i] = q < 4 ? q * 4096 + (i * 64 + lane) * kPfSector : 0x40000000;
+                asm volatile("" : "+v"(kq[j][i]));
+            }
+        }
+        // V: the tile's 64-byte slice of row `lane`; gates: eight sectors of 32 bytes
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            v[i] = lane * (int)(dv * 2) + i * 32;
+            asm volatile("" : "+v"(v[i]));
+        }
+        gate = lane < 8 ? lane * 32 : 0x40000000;
+        asm volatile("" : "+v"(gate));
+    }
+};
+// quarter slots per tile: every quarter of K and Q is taken by one tile
+__device__ __forceinline__ int touch_slots(int ntiles) { return ntiles >= 4 ? 1 : ntiles == 1 ? 4 : 2; }
+// the chunk's byte offset in a slab, clamped so that [soff, soff + span) ends inside it
+__device__ __forceinline__ int touch_soff(int64_t off, int64_t span, int64_t slab) {
+    int64_t hi = slab - span;
+    if (hi < 0) hi = 0;
+    return __builtin_amdgcn_readfirstlane((int)(off < hi ? off : hi));
+}
+// lds: the scratch word's LDS address
+__device__ __forceinline__ void touch_kq(unsigned lds, u32x4 rsrc, const TouchOffsets &to, int nq, int64_t row0, int64_t slab) {
+    const int soff = touch_soff(row0 * 256, 16384, slab);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < nq) {
+#pragma unroll
+            for (int i = 0; i < kTouchPerQuarter; ++i) dma_b32(lds, rsrc, to.kq[j][i], soff);
+        }
+    }
+}
+__device__ __forceinline__ void touch_v(unsigned lds, u32x4 rsrc, const TouchOffsets &to, int64_t row0, int64_t dv, int64_t slab) {
+    const int soff = touch_soff(row0 * dv * 2, 64 * dv * 2, slab);
+    dma_b32(lds, rsrc, to.v[0], soff);
+    dma_b32(lds, rsrc, to.v[1], soff);
+}
+__device__ __forceinline__ void touch_gate(unsigned lds, u32x4 rsrc, const TouchOffsets &to, int64_t row0, int64_t slab) {
+    dma_b32(lds, rsrc, to.gate, touch_soff(row0 * 4, 256, slab));
+}
+// Waits until at most N vector loads of the wave are outstanding: with loads completing in
+// issue order, all but the last N issued have landed.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// the same with N = Base + PerSlot * nq, nq one of the quarter slot counts 1, 2, 4
+template <int Base, int PerSlot>
+__device__ __forceinline__ void vm_wait_slots(int nq) {
+    if (nq >= 4) vm_wait<Base + 4 * PerSlot>();
+    else if (nq >= 2) vm_wait<Base + 2 * PerSlot>();
+    else vm_wait<Base + PerSlot>();
+}
 // Workgroup barrier that orders LDS only: this wave's LDS accesses complete, then s_barrier.
 // (The plain __syncthreads() would also wait for outstanding global stores, which nobody
 // in the workgroup reads; global->LDS copies are waited for explicitly before it.)
@@ -829,6 +911,27 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 cfull.init(full, a.dv, sh);
                 clast.init(chunk_rows(t0, len, fwd, nchunks - 1), a.dv, sh);
             }
+            TouchOffsets to;
+            const int nq = touch_slots((int)a.ntiles);
+            const unsigned tl = lds_addr(smem + kOffTouch);
+            if constexpr (kCopies) to.init(tile, (int)a.ntiles, a.dv);
+            // L2 touches of chunk ch by this copy wave: kTouchBase + kTouchSlot * nq loads
+            constexpr int kTouchBase = R == kKW ? 0 : 4;
+            constexpr int kTouchSlot = (R == kKW ? (kPro ? 2 : 1) : (kPro ? 0 : 1)) * kTouchPerQuarter;
+            // loads of one chunk's copies (K, Q, V slice, two gate rows)
+            constexpr int kIssued = R == kKW ? (kPro ? 32 : 16) : (kPro ? 6 : 22);
+            auto touch = [&](int64_t ch) __attribute__((always_inline)) {
+                const int64_t lo = chunk_rows(t0, len, fwd, ch).lo;
+                if constexpr (R == kKW) {
+                    touch_kq(tl, rsrc0, to, nq, lo, Ts * kDK * 2);
+                    if constexpr (kPro) touch_kq(tl, rsrc1, to, nq, lo >> sh, a.T * kDK * 2);
+                } else {
+                    if constexpr (!kPro) touch_kq(tl, rsrc0, to, nq, lo >> sh, a.T * kDK * 2);
+                    touch_v(tl, rsrc1, to, lo, a.dv, Ts * a.dv * 2 - dcol0 * 2);
+                    touch_gate(tl, rsrc2, to, lo >> sh, ((t0 + len) >> sh) * 4);
+                    touch_gate(tl, rsrc3, to, lo, (t0 + len) * 4);
+                }
+            };
             // two explicit paths, so that each copy addresses with one of the fixed sets
             auto issue = [&](int64_t ch, const CopyOffsets &co) __attribute__((always_inline)) {
                 char *rawn = smem + kOffRaw + (int)(ch % 3) * kRawBytes;
@@ -903,25 +1006,44 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_fast_kernel(ChunkArgs a) {
                 if constexpr (R == kWaveStore) {
                     if (ch >= 1) store(ch - 1);
                 }
+                // touches go after every copy that this step's wait must see land
+                const bool touched = ch + 2 + kPfDist < nchunks;
+                if constexpr (kCopies) {
+                    if (touched) touch(ch + 2 + kPfDist);
+                }
                 if (ch + 1 < nchunks) prep(ch + 1);
-                wait_vmem();
+                // the copy waves wait for their copies; the store wave's streaming stores
+                // are not waited for (nothing reads them), and no other wave loads
+                if constexpr (kCopies) {
+                    if (touched) vm_wait_slots<kTouchBase, kTouchSlot>(nq);
+                    else vm_wait<0>();
+                }
                 if (ch + 2 < nchunks) tables(ch + 2);
                 lds_barrier();
             };
+            // The first two chunks are copied together (ring slot 1 is not read before the
+            // second barrier), then the touches of the next kPfDist chunks are issued.
+            const bool touched = nchunks >= 2 + kPfDist;
             if constexpr (kCopies) {
                 if (nchunks == 1) issue(0, clast);
                 else issue(0, cfull);
-            }
-            wait_vmem();
-            tables(0);
-            lds_barrier();
-            if constexpr (kCopies) {
                 if (nchunks == 2) issue(1, clast);
                 else if (nchunks > 2) issue(1, cfull);
+                if (touched) {
+                    for (int c2 = 2; c2 < 2 + kPfDist; ++c2) touch(c2);
+                    vm_wait_slots<kIssued + kPfDist * kTouchBase, kPfDist * kTouchSlot>(nq);
+                } else {
+                    vm_wait<0>();
+                }
             }
+            tables(0);
+            lds_barrier();
             qstage(0);
             prep(0);
-            wait_vmem();
+            if constexpr (kCopies) {
+                if (touched) vm_wait_slots<kPfDist * kTouchBase, kPfDist * kTouchSlot>(nq);
+                else vm_wait<0>();
+            }
             if (nchunks > 1) tables(1);
             lds_barrier();
             // The loop that copies full chunks and the tail that copies the last chunk are
