@@ -316,12 +316,14 @@ __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// the same with N = Base + PerSlot * nq, nq one of the quarter slot counts 1, 2, 4
+// the same with N = Base + PerSlot * nq, nq one of the quarter slot counts 1, 2, 4 (a count
+// past the counter's range is cut to its maximum, which only waits for more)
+constexpr int vm_cap(int n) { return n < 63 ? n : 63; }
 template <int Base, int PerSlot>
 __device__ __forceinline__ void vm_wait_slots(int nq) {
-    if (nq >= 4) vm_wait<Base + 4 * PerSlot>();
-    else if (nq >= 2) vm_wait<Base + 2 * PerSlot>();
-    else vm_wait<Base + PerSlot>();
+    if (nq >= 4) vm_wait<vm_cap(Base + 4 * PerSlot)>();
+    else if (nq >= 2) vm_wait<vm_cap(Base + 2 * PerSlot)>();
+    else vm_wait<vm_cap(Base + PerSlot)>();
 }
 // Workgroup barrier that orders LDS only: this wave's LDS accesses complete, then s_barrier.
 // (The plain __syncthreads() would also wait for outstanding global stores, which nobody
