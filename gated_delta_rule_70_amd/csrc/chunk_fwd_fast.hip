@@ -257,8 +257,10 @@ __device__ __forceinline__ void copy_gates(char *raw, u32x4 ra, u32x4 rb, const 
 // LDS: it has no destination register, and vector loads complete in issue order, so a wave
 // waits for its copies with the count of touches issued after them still outstanding.
 // The value tiles of a unit read the same K and Q chunk; tile t touches the quarters t,
-// t + ntiles, ... of it (a tile takes nq quarter slots; slots past the fourth quarter read
-// nothing). The chunk offset is clamped so that the touched range ends inside the slab.
+// t + ntiles, ... of it (a tile takes nq quarter slots; a slot past the fourth quarter touches
+// quarter slot mod 4 again). The chunk offset is clamped so that the touched range ends inside
+// the slab; every lane addresses inside that range, so no touch depends on the buffer's range
+// check (which a slab shorter than the range still gets).
 struct TouchOffsets {
     int kq[4][kTouchPerQuarter], v[2], gate;
     __device__ __forceinline__ void init(int tile, int ntiles, int64_t dv) {
@@ -268,17 +270,18 @@ struct TouchOffsets {
             const int q = tile + j * ntiles;
 #pragma unroll
             for (int i = 0; i < kTouchPerQuarter; ++i) {
-                kq[j][i] = q < 4 ? q * 4096 + (i * 64 + lane) * kPfSector : 0x40000000;
+                kq[j][i] = (q & 3) * 4096 + (i * 64 + lane) * kPfSector;
                 asm volatile("" : "+v"(kq[j][i]));
             }
         }
-        // V: the tile's 64-byte slice of row `lane`; gates: eight sectors of 32 bytes
+        // V: the tile's 64-byte slice of row `lane`; gates: the eight sectors of 32 bytes of
+        // a chunk's 64 rows, each taken by eight lanes
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             v[i] = lane * (int)(dv * 2) + i * 32;
             asm volatile("" : "+v"(v[i]));
         }
-        gate = lane < 8 ? lane * 32 : 0x40000000;
+        gate = (lane & 7) * 32;
         asm volatile("" : "+v"(gate));
     }
 };
