@@ -1029,9 +1029,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) ax[r] = bx[r] = wy[r] = 0.f;
         }
-        // the next slice of this value head is read during this one's products; the first slice
-        // of the next value head after this one's gate gradients
-        if (tile + 1 < a.ntiles) issue(it + 1);
         __syncthreads();
         const float blast = sm.b[CB - 1];
         // X = K H and Y = K D on this wave's tile: dR . X, dR . (V - gamma X), Y . U per row
@@ -1052,6 +1049,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
                 wy[r] += y[r] * sm_get(sm.U, i, j);
             }
         }
+        // The next slice of this value head is read during this one's products (the first slice
+        // of the next value head after this one's gate gradients). Its loads are issued here,
+        // after the first products, not before the barrier: the ~56 KB of every wave's loads
+        // queue in the vector memory path for 1-2k cycles, which before the barrier every wave
+        // waited out.
+        if (tile + 1 < a.ntiles) issue(it + 1);
         fence_sched();
         // dP = dO U^T and -dA = dR U^T on the lower tiles
 #pragma unroll
