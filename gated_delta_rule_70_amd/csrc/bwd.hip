@@ -754,15 +754,24 @@ __device__ __forceinline__ void adj_sweep(const BwdArgs &a, int64_t unit, int ti
         rv = rb[CB + gr];
         betav = (beb + L.sq.low(c, n))[(uint32_t)L.sq.off(gr < n ? gr : 0, n)];
     };
+    // The store addresses are formed at each call from a thread index the compiler cannot
+    // hoist (the lane from v_mbcnt in volatile asm) and a laundered LDS base. Kept across the
+    // loop, they were spilled under the 128-register cap, and the reloads, which share the
+    // vector-memory counter with global loads, each waited for the T^T and Pm^T slab loads
+    // issued just before.
     auto store = [&](int64_t c) __attribute__((always_inline)) {
         const int n = (int)min((int64_t)CB, L.sq.len - c * CB);
-        kp.store(&sm.K[0][0], SM::KP, n, tid);
-        qp.store(&sm.Q[0][0], SM::KP, n, tid);
-        op.store(&sm.dO[0][0], SM::VP, n, tid);
-        if (tid < CB) {
-            sm.b[tid] = bv;
-            sm.er[tid] = __expf(rv);
-            sm.beta[tid] = tid < n ? betav : 0.f;
+        int t;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(t));
+        t += wave << 6;
+        SM &sl = *lds_opaque(reinterpret_cast<SM *>(smraw));
+        kp.store(&sl.K[0][0], SM::KP, n, t);
+        qp.store(&sl.Q[0][0], SM::KP, n, t);
+        op.store(&sl.dO[0][0], SM::VP, n, t);
+        if (t < CB) {
+            sl.b[t] = bv;
+            sl.er[t] = __expf(rv);
+            sl.beta[t] = t < n ? betav : 0.f;
         }
     };
     // T^T and Pm^T (rows 16 mt .. 16 mt + 15 are zero before column 16 mt; the zero slabs are read
