@@ -689,8 +689,9 @@ __device__ __forceinline__ void fwd_sweep(const BwdArgs &a, int64_t unit, int ti
             }
             sm_put_t(sm.wUt, 16 * mt, 16 * nt, wu);
         }
-        issue_t(c + 1 < nch ? c + 1 : c);
         __syncthreads();
+        // the next chunk's T slabs (T is done with once U is formed) queue while the update runs
+        issue_t(c + 1 < nch ? c + 1 : c);
         // H' = gamma_last H + K^T diag(w) U, each wave on its own tiles
         {
             const float glast = __expf(bc[CB - 1]);
