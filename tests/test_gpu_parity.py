@@ -149,6 +149,12 @@ SMALL = [
     (torch.bfloat16, 128, 64, 2, 2, 1, 129, 64),
     (torch.bfloat16, 128, 256, 1, 1, 1, 100, 64),
     (torch.bfloat16, 128, 96, 1, 1, 1, 77, 64),
+    # long enough (five chunks and more) for the fast kernel's L2 touches, with one, three and
+    # eight column tiles: each K/Q quarter touched by one tile, by wrapped quarter slots, or by
+    # the first four tiles only
+    (torch.bfloat16, 128, 32, 2, 2, 1, 333, 64),
+    (torch.bfloat16, 128, 96, 1, 1, 2, 400, 64),
+    (torch.bfloat16, 128, 256, 1, 2, 1, 390, 64),
 ]
 
 
