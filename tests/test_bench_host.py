@@ -55,3 +55,31 @@ def test_executed_mfma_count_matches_the_counter_summary():
     ex = bench.chunk_flops_executed(4, 16, 4096, 128)
     assert abs(ex - 1.132e8 * 512) / ex < 0.01
     assert ex > bench.chunk_flops(4, 16, 4096, 128, 128)
+
+
+def test_rotation_sets_leave_the_cache_behind(monkeypatch):
+    """Each call's copy is revisited only after the other copies, which hold at least twice the
+    256 MB last-level cache; --cache-warm times one copy."""
+    made = []
+
+    def make():
+        i = len(made)
+        made.append(i)
+        return lambda: calls.append(i)
+
+    calls = []
+    monkeypatch.setattr(bench, "CACHE_WARM", False)
+    for set_bytes in (278921216, 1 << 30, 64 << 20):
+        made.clear()
+        calls.clear()
+        fn, k = bench.rotation(make, set_bytes)
+        assert k == len(made) >= 2
+        assert (k - 1) * set_bytes >= 2 * bench.CACHE_BYTES
+        assert (k - 2) * set_bytes < 2 * bench.CACHE_BYTES or k == 2
+        for _ in range(2 * k + 1):
+            fn()
+        assert calls == [i % k for i in range(2 * k + 1)]
+    monkeypatch.setattr(bench, "CACHE_WARM", True)
+    made.clear()
+    fn, k = bench.rotation(make, 278921216)
+    assert k == 1 and len(made) == 1
