@@ -762,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void gdn2_prep_kernel(Gdn2Args a) {
     __syncthreads();
     gram_tiles<E, C, DK>(sm, pre);
     __syncthreads();
-    if (wave == 0) solve_unit_lower_inverse<E, C>(sm);
+    if (wave == 0) solve_unit_lower_inverse<E, C, SM, true>(sm);
 
     char *kb = reinterpret_cast<char *>(a.ws) + (ws_slot<C>(a, seq, c) * a.Hk + kh) * WK::kBytes;
     // chunk-relative operands in place (while wave 0 solves): LA and LP times e^{G_ref} of their

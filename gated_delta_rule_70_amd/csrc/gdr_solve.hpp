@@ -14,7 +14,10 @@ namespace gdr {
 // T_10 = -T_11 A_10 T_00 (and T_32 for C = 64), then the lower-left 32x32 block
 // T_BA = -T_BB A_BA T_AA (C = 64). Writes the lower triangle of sm.T; its strictly upper
 // blocks must be zero (they are never written).
-template <typename E, int C, typename SM>
+// kHoist: the block's rows of A (the same for the sixteen lanes of a group) are all read into
+// registers before the substitution starts, so that its chain of multiply-adds does not wait on
+// LDS row by row; it takes about 30 more registers, for kernels whose occupancy the LDS sets.
+template <typename E, int C, typename SM, bool kHoist = false>
 __device__ __forceinline__ void solve_unit_lower_inverse(SM &sm) {
     constexpr int NT = C / 16;
     const int lane = threadIdx.x & 63;
@@ -22,13 +25,30 @@ __device__ __forceinline__ void solve_unit_lower_inverse(SM &sm) {
     if (g < NT) {
         const int base = 16 * g;
         float t[16];
+        if constexpr (kHoist) {
+            static_assert(SM::AP % 4 == 0, "16-byte rows of A");
+            float4 ar[16][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == cc) ? 1.f : 0.f;
-            const float *arow = sm.A + (base + i) * SM::AP + base;
+            for (int i = 1; i < 16; ++i)
 #pragma unroll
-            for (int j = 0; j < i; ++j) s -= arow[j] * t[j];
-            t[i] = s;
+                for (int q = 0; q < (i + 3) / 4; ++q)
+                    ar[i][q] = *reinterpret_cast<const float4 *>(sm.A + (base + i) * SM::AP + base + 4 * q);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) s -= ar[i][j / 4][j % 4] * t[j];
+                t[i] = s;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == cc) ? 1.f : 0.f;
+                const float *arow = sm.A + (base + i) * SM::AP + base;
+#pragma unroll
+                for (int j = 0; j < i; ++j) s -= arow[j] * t[j];
+                t[i] = s;
+            }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sm.T[(base + i) * SM::TP + base + cc] = static_cast<E>(t[i]);
