@@ -334,16 +334,16 @@ def bench_bidir(binding, inputs, steps):
         out = torch.empty_like(v)
 
         def fn():
-            binding.chunk_fwd(q, k, v, la, b, None, cu, chunk=64, read="pre", out=out, want_state=False)
-            binding.chunk_fwd(q, k, v, la2, b2, None, cu, chunk=64, read="pre", reverse=True, out=out,
-                              accumulate=True, want_state=False)
+            binding.chunk_fwd_bidir(q, k, v, la, b, la2, b2, None, None, cu, chunk=64, read="pre", out=out,
+                                    want_state=False)
 
         return fn
 
     H, T, dk, dv = case.q.shape[1], case.q.shape[2], case.q.shape[3], case.v.shape[3]
-    fn, sets = rotation(make, chunk_bytes(1, H, T, dk, dv, 2, 0, gates=4, state=False))
+    nbytes = chunk_bytes(1, H, T, dk, dv, 2, 0, gates=4, state=False)
+    fn, sets = rotation(make, nbytes)
     ms, _, _ = timed(fn, steps, 20, torch.cuda.current_stream(dev))
-    return dict(ms=ms, tokens=T, sets=sets)
+    return dict(ms=ms, tokens=T, sets=sets, bytes=nbytes)
 
 
 def gdn2_bytes(B, Hk, Hv, T, dk, dv, es, nseq):
@@ -561,9 +561,9 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / GEMM peaks")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
                     help="untimed GPU time before the warm-up of each workload (0 for counter runs)")
-    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "dp", "all"], default="all",
-                    help="gdn2, bwd, dp: only the GDN-2 workloads, the backward or DeltaProduct (for "
-                         "profiling them)")
+    ap.add_argument("--only", choices=["chunk", "decode", "gdn2", "bwd", "dp", "bidir", "all"], default="all",
+                    help="gdn2, bwd, dp, bidir: only the GDN-2 workloads, the backward, DeltaProduct or the "
+                         "bidirectional call (for profiling them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--cache-warm", action="store_true",
@@ -588,6 +588,10 @@ def main():
     if args.only == "bwd":
         r = bench_backward(binding, inputs, args.steps)
         print(json.dumps({"bwd_ms": r["ms"], "steps": args.steps, "workspace_bytes": r["ws_bytes"]}), flush=True)
+        return
+    if args.only == "bidir":
+        r = bench_bidir(binding, inputs, args.steps)
+        print(json.dumps({"bidir_ms": r["ms"], "bytes": r["bytes"], "steps": args.steps}), flush=True)
         return
     if args.only == "dp":
         r = bench_delta_product(binding, inputs, args.steps)
@@ -685,7 +689,11 @@ def main():
                 "tokens_per_s": fu["tokens"] / (fu["ms"] / 1e3), "ms": fu["ms"],
                 "prologue": "q/k rows normalised and gates formed from raw inputs in the kernel"},
             inputs.WORKLOADS[4]: {"tokens_per_s": bd["tokens"] / (bd["ms"] / 1e3), "ms": bd["ms"],
-                                  "calls": 2},
+                                  "hbm_frac": bd["bytes"] / (bd["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                  "entry": "gdr_chunk_fwd_bidir: the forward scan, then the reverse scan "
+                                           "accumulating into out (two launches of the chunk kernel)",
+                                  "bytes_note": "hbm_frac on the bytes of one read of q, k, v and both gate "
+                                                "sets and one write of out"},
             "gdn2-chunk-fwd-bf16-B4-H16-T4096-d128-c32": {
                 "tokens_per_s": g2["tokens"] / (g2["ms"] / 1e3), "ms": g2["ms"],
                 "one_pass_ms": g2["fused_ms"], "workspace_bytes": g2["ws_bytes"],

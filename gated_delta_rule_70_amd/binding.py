@@ -24,7 +24,7 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
           9: "GDR_ERR_HIP"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_bidir", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
            "gdr_gdn2_chunk_fwd", "gdr_gdn2_chunk_fwd_noalloc", "gdr_gdn2_chunk_fwd_workspace_bytes",
            "gdr_gdn2_decode_step",
            "gdr_delta_product_fwd",
@@ -61,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd_gated.argtypes = [p, p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
     lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_bidir.argtypes = [p] * 10 + [i32, p, p, p, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_chunk_fwd_bidir.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step_gated.argtypes = [p, p, p, p, p, p, p, p, p, p, ctypes.POINTER(DecodeDims), p]
@@ -159,6 +161,52 @@ def chunk_fwd_gated(q, k, v, a, b, A_log, dt_bias, h0=None, cu_seqlens=None, *, 
     [B, Hv, T] fp32 raw inputs, A_log, dt_bias [Hv] fp32; the rest as ``chunk_fwd``."""
     return _chunk(q, k, v, a, b, A_log, dt_bias, h0, cu_seqlens, chunk, read, reverse, out,
                   accumulate, hT, want_state, l2norm)
+
+
+def chunk_fwd_bidir(q, k, v, log_alpha_fwd, beta_fwd, log_alpha_rev, beta_rev, h0_fwd=None, h0_rev=None,
+                    cu_seqlens=None, *, chunk: int = 64, read: str = "pre", out=None, accumulate: bool = False,
+                    want_state: bool = True, l2norm: bool = False):
+    """Both scans of a bidirectional layer, summed per token (``gdr_chunk_fwd_bidir``): the
+    forward scan and the in-segment reversed scan, each with its own gates [B, Hv, T] fp32 (indexed
+    by token) and initial state [S, Hv, dk, dv] fp32 or None, the same ``read`` for both. Returns
+    (out [B, Hv, T, dv], hT_fwd, hT_rev), the final states None without ``want_state``."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    _need(k, "k", dt, (B, Hk, T, dk), dev)
+    _need(v, "v", dt, (B, Hv, T, dv), dev)
+    for t, n in ((log_alpha_fwd, "log_alpha_fwd"), (beta_fwd, "beta_fwd"), (log_alpha_rev, "log_alpha_rev"),
+                 (beta_rev, "beta_rev")):
+        _need(t, n, torch.float32, (B, Hv, T), dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    for t, n in ((h0_fwd, "h0_fwd"), (h0_rev, "h0_rev")):
+        if t is not None:
+            _need(t, n, torch.float32, (S, Hv, dk, dv), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, Hv, T, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, Hv, T, dv), dev)
+    hT_f = hT_r = None
+    if want_state:
+        hT_f = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+        hT_r = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_ACCUMULATE if accumulate else 0) | \
+        (GDR_QK_L2NORM if l2norm else 0)
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    _check(lib().gdr_chunk_fwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha_fwd), _ptr(beta_fwd),
+                                     _ptr(log_alpha_rev), _ptr(beta_rev), _ptr(h0_fwd), _ptr(h0_rev),
+                                     _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT_f), _ptr(hT_r),
+                                     ctypes.byref(dims), _stream(q)))
+    return out, hT_f, hT_r
 
 
 def _chunk(q, k, v, ga, gb, A_log, dt_bias, h0, cu_seqlens, chunk, read, reverse, out, accumulate,

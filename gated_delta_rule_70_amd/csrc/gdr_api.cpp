@@ -56,10 +56,25 @@ struct GateNames {
     const char *a, *b;
 };
 
+// A validated chunked-forward launch: everything the kernel needs, checked on the host.
+struct ChunkCall {
+    gdr::ChunkArgs a;
+    int32_t dtype, chunk, dk;
+};
+
+gdr_status_t chunk_prepare(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                           const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
+                           const gdr_chunk_dims_t *dims, int32_t n_sub, ChunkCall *call);
+gdr_status_t chunk_launch(const ChunkCall &call, void *stream);
 gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                         const float *beta, const float *A_log, const float *dt_bias, bool gated,
                         const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
                         const gdr_chunk_dims_t *dims, void *stream, int32_t n_sub = 1);
+gdr_status_t bidir_impl(const void *q, const void *k, const void *v, const float *la_f, const float *beta_f,
+                        const float *la_r, const float *beta_r, const float *h0_f, const float *h0_r,
+                        const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT_f, float *hT_r,
+                        const gdr_chunk_dims_t *dims, void *stream);
 gdr_status_t decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                          const float *beta, const float *A_log, const float *dt_bias, bool gated,
                          const float *state_in, float *state_out, void *out, const gdr_decode_dims_t *dims,
@@ -104,6 +119,15 @@ gdr_status_t gdr_chunk_fwd_gated(const void *q, const void *k, const void *v, co
     return chunk_impl(q, k, v, a, b, A_log, dt_bias, true, h0, cu_seqlens, chunk, out, hT, dims, stream);
 }
 
+gdr_status_t gdr_chunk_fwd_bidir(const void *q, const void *k, const void *v, const float *log_alpha_fwd,
+                                 const float *beta_fwd, const float *log_alpha_rev, const float *beta_rev,
+                                 const float *h0_fwd, const float *h0_rev, const int32_t *cu_seqlens, int32_t chunk,
+                                 void *out, float *hT_fwd, float *hT_rev, const gdr_chunk_dims_t *dims,
+                                 void *stream) {
+    return bidir_impl(q, k, v, log_alpha_fwd, beta_fwd, log_alpha_rev, beta_rev, h0_fwd, h0_rev, cu_seqlens, chunk,
+                      out, hT_fwd, hT_rev, dims, stream);
+}
+
 gdr_status_t gdr_delta_product_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                                    const float *beta, const float *h0, const int32_t *cu_seqlens, int32_t n_delta,
                                    int32_t chunk, void *out, float *hT, const gdr_chunk_dims_t *dims, void *stream) {
@@ -127,11 +151,10 @@ gdr_status_t gdr_decode_step_gated(const void *q, const void *k, const void *v, 
 
 namespace {
 
-gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
-                        const float *beta, const float *A_log, const float *dt_bias, bool gated,
-                        const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
-                        const gdr_chunk_dims_t *dims, void *stream, int32_t n_sub) {
-    g_last_error[0] = '\0';
+gdr_status_t chunk_prepare(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                           const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
+                           const gdr_chunk_dims_t *dims, int32_t n_sub, ChunkCall *call) {
     const GateNames gn = gated ? GateNames{"a", "b"} : GateNames{"log_alpha", "beta"};
     if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
     const gdr_chunk_dims_t d = *dims;
@@ -201,9 +224,70 @@ gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float
     a.n_sub = n_sub;
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
     if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
-    const hipError_t e = gdr::launch_chunk_fwd(a, d.dtype, chunk, (int)d.dk, reinterpret_cast<hipStream_t>(stream));
+    call->a = a;
+    call->dtype = d.dtype;
+    call->chunk = chunk;
+    call->dk = (int32_t)d.dk;
+    return GDR_OK;
+}
+
+gdr_status_t chunk_launch(const ChunkCall &c, void *stream) {
+    const hipError_t e = gdr::launch_chunk_fwd(c.a, c.dtype, c.chunk, c.dk, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch: %s", hipGetErrorString(e));
     return GDR_OK;
+}
+
+gdr_status_t chunk_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, const float *A_log, const float *dt_bias, bool gated,
+                        const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT,
+                        const gdr_chunk_dims_t *dims, void *stream, int32_t n_sub) {
+    g_last_error[0] = '\0';
+    ChunkCall call;
+    const gdr_status_t s = chunk_prepare(q, k, v, log_alpha, beta, A_log, dt_bias, gated, h0, cu_seqlens, chunk,
+                                         out, hT, dims, n_sub, &call);
+    return s != GDR_OK ? s : chunk_launch(call, stream);
+}
+
+// Both scans of a bidirectional layer: the forward scan writes (or accumulates into) out, then
+// the reverse scan accumulates into it. Both are validated before either is enqueued.
+gdr_status_t bidir_impl(const void *q, const void *k, const void *v, const float *la_f, const float *beta_f,
+                        const float *la_r, const float *beta_r, const float *h0_f, const float *h0_r,
+                        const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT_f, float *hT_r,
+                        const gdr_chunk_dims_t *dims, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    if (dims->flags & GDR_REVERSE)
+        return fail(GDR_ERR_FLAGS, "GDR_REVERSE is not a flag of the bidirectional call (it runs both directions)");
+    gdr_chunk_dims_t df = *dims, dr = *dims;
+    dr.flags |= GDR_REVERSE | GDR_ACCUMULATE;
+    ChunkCall cf, cr;
+    char msg[sizeof(g_last_error)];
+    gdr_status_t s = chunk_prepare(q, k, v, la_f, beta_f, nullptr, nullptr, false, h0_f, cu_seqlens, chunk, out,
+                                   hT_f, &df, 1, &cf);
+    if (s != GDR_OK) {
+        snprintf(msg, sizeof(msg), "forward scan: %s", g_last_error);
+        return fail(s, "%s", msg);
+    }
+    s = chunk_prepare(q, k, v, la_r, beta_r, nullptr, nullptr, false, h0_r, cu_seqlens, chunk, out, hT_r, &dr, 1,
+                      &cr);
+    if (s != GDR_OK) {
+        snprintf(msg, sizeof(msg), "reverse scan: %s", g_last_error);
+        return fail(s, "%s", msg);
+    }
+    // the forward scan's final state is written before the reverse scan reads its inputs, and the
+    // reverse scan's final state after the forward scan has read its own: no final state may
+    // overlap an input of the other direction, nor the other final state
+    const int64_t ns = prod({cf.a.units, dims->dk, dims->dv}) * 4, ng = prod({dims->B, dims->Hv, dims->T}) * 4;
+    const Range rhf = rng("hT_fwd", hT_f, ns), rhr = rng("hT_rev", hT_r, ns);
+    const Range others_f[] = {rng("log_alpha_rev", la_r, ng), rng("beta_rev", beta_r, ng), rng("h0_rev", h0_r, ns),
+                              rhr};
+    const Range others_r[] = {rng("log_alpha_fwd", la_f, ng), rng("beta_fwd", beta_f, ng), rng("h0_fwd", h0_f, ns)};
+    for (const Range &r : others_f)
+        if (overlap(rhf, r)) return fail(GDR_ERR_ALIAS, "hT_fwd overlaps %s", r.name);
+    for (const Range &r : others_r)
+        if (overlap(rhr, r)) return fail(GDR_ERR_ALIAS, "hT_rev overlaps %s", r.name);
+    s = chunk_launch(cf, stream);
+    return s != GDR_OK ? s : chunk_launch(cr, stream);
 }
 
 gdr_status_t decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,

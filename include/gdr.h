@@ -134,6 +134,43 @@ gdr_status_t gdr_chunk_fwd(const void *q, const void *k, const void *v,
                            const gdr_chunk_dims_t *dims, void *stream);
 
 /*
+ * gdr_chunk_fwd_bidir - both scans of a bidirectional layer over shared q, k, v, summed per
+ * token: the forward scan of every sequence or packed segment, plus the scan of each segment
+ * run from its last token to its first, each with its own gate set, initial and final state,
+ * and the same read (GDR_READ_PRE for the pre-write read both scans of the bidirectional
+ * layer on the "tiny_gdn/fugue.py" page use: `BidirectionalGatedDeltaNet2.scan` reverses each
+ * segment in place, and its `forward` adds the two directions). The page scales the sum by
+ * 1/2; that factor belongs to the caller (fold it into v, or scale out).
+ *
+ *   out[t] = o_fwd[t] + o_rev[t]   (out += both with GDR_ACCUMULATE)
+ *
+ *   q, k, v, cu_seqlens, chunk, out, dims, stream: as gdr_chunk_fwd; dims->flags may hold
+ *       GDR_READ_PRE, GDR_ACCUMULATE and GDR_QK_L2NORM (the latter for both scans).
+ *   log_alpha_fwd, beta_fwd  [B][Hv][T] fp32 gates of the forward scan
+ *   log_alpha_rev, beta_rev  [B][Hv][T] fp32 gates of the reverse scan, indexed by token as
+ *       the forward ones (not by scan position)
+ *   h0_fwd, h0_rev           [S][Hv][dk][dv] fp32 initial states, or NULL for zeros. For the
+ *       reverse scan this is the state before the segment's last token is read.
+ *   hT_fwd, hT_rev           [S][Hv][dk][dv] fp32 final states, or NULL; each may be exactly its
+ *       own direction's h0 (in place). A final state may not overlap any input of the other
+ *       direction or the other final state (GDR_ERR_ALIAS).
+ *
+ * The two scans are enqueued one after the other on the stream (the forward scan writes out,
+ * the reverse scan adds to it); both are validated before either is enqueued. No single
+ * sweep can produce the sum with one read of q, k, v: the reverse read at token t depends on
+ * every later token of the segment. The second read of q, k, v comes one scan after the first.
+ *
+ * Errors: as gdr_chunk_fwd, the message naming the scan; GDR_ERR_FLAGS for GDR_REVERSE.
+ */
+gdr_status_t gdr_chunk_fwd_bidir(const void *q, const void *k, const void *v,
+                                 const float *log_alpha_fwd, const float *beta_fwd,
+                                 const float *log_alpha_rev, const float *beta_rev,
+                                 const float *h0_fwd, const float *h0_rev,
+                                 const int32_t *cu_seqlens, int32_t chunk, void *out,
+                                 float *hT_fwd, float *hT_rev,
+                                 const gdr_chunk_dims_t *dims, void *stream);
+
+/*
  * gdr_chunk_fwd_gated - gdr_chunk_fwd with the gates formed from their raw inputs in the
  * kernel (see the fused prologue above), typically together with GDR_QK_L2NORM:
  *

@@ -81,6 +81,43 @@ def test_chunk_fwd_rejects(over, status, text):
     assert st == status and text in msg, (st, msg)
 
 
+def _bidir(lib, **over):
+    d = dict(B=1, T=128, Hk=2, Hv=2, dk=64, dv=64, num_seqs=0, dtype=1, flags=1)
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, la_f=FAKE * 4, b_f=FAKE * 5, la_r=FAKE * 10, b_r=FAKE * 11,
+               h0_f=None, h0_r=None, cu=None, out=FAKE * 6, hT_f=FAKE * 12, hT_r=FAKE * 13, chunk=64)
+    for k_, v_ in over.items():
+        (d if k_ in d else ptr)[k_] = v_
+    dims = binding.ChunkDims(d["B"], d["T"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["num_seqs"],
+                             d["dtype"], d["flags"])
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_chunk_fwd_bidir(*[vp(ptr[n]) for n in ("q", "k", "v", "la_f", "b_f", "la_r", "b_r", "h0_f",
+                                                        "h0_r", "cu")],
+                                 ptr["chunk"], vp(ptr["out"]), vp(ptr["hT_f"]), vp(ptr["hT_r"]),
+                                 ctypes.byref(dims), None)
+    return binding.STATUS[st], lib.gdr_last_error().decode()
+
+
+BIDIR_REJECTS = [
+    (dict(flags=3), "GDR_ERR_FLAGS", "GDR_REVERSE"),
+    (dict(la_f=None), "GDR_ERR_NULL", "forward scan"),
+    (dict(b_r=None), "GDR_ERR_NULL", "reverse scan"),
+    (dict(chunk=48), "GDR_ERR_CHUNK", "forward scan"),
+    (dict(out=FAKE * 10), "GDR_ERR_ALIAS", "reverse scan: out overlaps log_alpha"),
+    (dict(h0_r=FAKE * 12), "GDR_ERR_ALIAS", "hT_fwd overlaps h0_rev"),
+    (dict(hT_r=FAKE * 12 + 4096), "GDR_ERR_ALIAS", "hT_fwd overlaps hT_rev"),
+    (dict(hT_f=FAKE * 11), "GDR_ERR_ALIAS", "hT_fwd overlaps beta_rev"),
+    (dict(hT_r=FAKE * 4), "GDR_ERR_ALIAS", "hT_rev overlaps log_alpha_fwd"),
+    (dict(h0_r=FAKE * 20, hT_r=FAKE * 20 + 256), "GDR_ERR_ALIAS", "partially overlaps h0"),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status,text", BIDIR_REJECTS, ids=[c[1] + ":" + c[2] for c in BIDIR_REJECTS])
+def test_chunk_fwd_bidir_rejects(over, status, text):
+    st, msg = _bidir(binding.load(), **over)
+    assert st == status and text in msg, (st, msg)
+
+
 @needs_lib
 def test_null_dims_and_status_strings():
     lib = binding.load()

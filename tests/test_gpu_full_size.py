@@ -85,14 +85,13 @@ def test_workload2_every_segment(gdr, regime):
 @pytest.mark.parametrize("regime", REGIMES)
 def test_workload4_every_segment(gdr, regime):
     """4 x 4096 packed, H16 d128 bf16: forward pre-write scan plus the in-segment reversed
-    pre-write scan with its own gates, summed per token (two calls, the second accumulating)."""
+    pre-write scan with its own gates, summed per token (the bidirectional entry point)."""
     case = inputs.workload4(regime=regime)
     _say("workload4 every segment, regime=%s" % regime)
     q, k, v, la, b, _, cu = _dev(case)
     la_b, b_b = case.extra["log_alpha_bwd"].cuda(), case.extra["beta_bwd"].cuda()
-    out, _ = gdr.chunk_fwd(q, k, v, la, b, None, cu, chunk=64, read="pre", want_state=False)
-    gdr.chunk_fwd(q, k, v, la_b, b_b, None, cu, chunk=64, read="pre", reverse=True, out=out,
-                  accumulate=True, want_state=False)
+    out, _, _ = gdr.chunk_fwd_bidir(q, k, v, la, b, la_b, b_b, None, None, cu, chunk=64, read="pre",
+                                    want_state=False)
     torch.cuda.synchronize()
     o = gpu_np(out)
     rf, _ = oracle.scan(case.q, case.k, case.v, case.log_alpha, case.beta, None, case.cu_seqlens,
