@@ -29,7 +29,7 @@
 //
 // Only two of these quantities are carried from chunk to chunk: the state H (forward) and its
 // adjoint dH (backward). Everything else is local to a chunk once H and dH' are known. So the
-// backward runs as four kernels on one stream, 64-token chunks:
+// backward runs as three kernels on one stream, 64-token chunks:
 //
 //   1. prep, one workgroup per (value head, chunk): the gate cumsums b and r, G, Pm and
 //      T = (I + A)^{-1}; T, T^T and Pm^T go to the workspace as ready matrix-core operands.
