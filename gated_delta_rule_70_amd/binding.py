@@ -25,7 +25,7 @@ STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_DIMS", 3: "GDR_ERR_DTYPE",
 
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_bidir", "gdr_chunk_fwd_gated", "gdr_decode_step", "gdr_decode_step_gated",
-           "gdr_gdn2_chunk_fwd", "gdr_gdn2_chunk_fwd_noalloc", "gdr_gdn2_chunk_fwd_workspace_bytes",
+           "gdr_gdn2_chunk_fwd", "gdr_gdn2_chunk_fwd_bidir", "gdr_gdn2_chunk_fwd_noalloc", "gdr_gdn2_chunk_fwd_workspace_bytes",
            "gdr_gdn2_decode_step",
            "gdr_delta_product_fwd",
            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_bytes",
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_gdn2_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, p, ctypes.c_int64,
                                        ctypes.POINTER(ChunkDims), p]
     lib.gdr_gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_gdn2_chunk_fwd_bidir.argtypes = [p] * 11 + [p, i32, p, p, p, p, ctypes.c_int64, ctypes.POINTER(ChunkDims), p]
+    lib.gdr_gdn2_chunk_fwd_bidir.restype = ctypes.c_int
     lib.gdr_gdn2_chunk_fwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, ctypes.POINTER(ChunkDims), p]
     lib.gdr_gdn2_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_gdn2_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDims), i32, i32]
@@ -461,6 +463,63 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, h0=None, cu_seqlens=None, *, chunk: int = 6
                                     _ptr(cu_seqlens), int(chunk), _ptr(out), _ptr(hT), ws_ptr, ws_bytes,
                                     ctypes.byref(dims), _stream(q)))
     return out, hT
+
+
+def gdn2_chunk_fwd_bidir(q, k, v, fwd_gates, rev_gates, h0_fwd=None, h0_rev=None, cu_seqlens=None, *,
+                         chunk: int = 64, read: str = "pre", out=None, accumulate: bool = False,
+                         want_state: bool = True, l2norm: bool = False, workspace=None, fused: bool = False):
+    """Both GDN-2 scans of a bidirectional layer, summed per token (``gdr_gdn2_chunk_fwd_bidir``):
+    ``fwd_gates`` and ``rev_gates`` are (g, b, w) triples in ``gdn2_chunk_fwd``'s layouts; the rest
+    as ``chunk_fwd_bidir`` and ``gdn2_chunk_fwd`` (one workspace serves both passes). Returns
+    (out, hT_fwd, hT_rev)."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    _need(k, "k", dt, (B, Hk, T, dk), dev)
+    _need(v, "v", dt, (B, Hv, T, dv), dev)
+    for name, (g, b, w) in (("fwd", fwd_gates), ("rev", rev_gates)):
+        _need(g, "g_" + name, torch.float32, (B, Hk, T, dk), dev)
+        _need(b, "b_" + name, dt, (B, Hk, T, dk), dev)
+        _need(w, "w_" + name, dt, (B, Hv, T, dv), dev)
+    S = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        S = cu_seqlens.shape[0] - 1
+    for t, n in ((h0_fwd, "h0_fwd"), (h0_rev, "h0_rev")):
+        if t is not None:
+            _need(t, n, torch.float32, (S, Hv, dk, dv), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, Hv, T, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, Hv, T, dv), dev)
+    hT_f = hT_r = None
+    if want_state:
+        hT_f = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+        hT_r = torch.empty((S, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if read not in ("pre", "post"):
+        raise ValueError("read must be 'pre' or 'post'")
+    flags = (GDR_READ_PRE if read == "pre" else 0) | (GDR_ACCUMULATE if accumulate else 0) | \
+        (GDR_QK_L2NORM if l2norm else 0)
+    dims = ChunkDims(B, T, Hk, Hv, dk, dv, S if cu_seqlens is not None else 0, code, flags)
+    ws_ptr, ws_bytes = None, 0
+    if not fused:
+        need = lib().gdr_gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), int(chunk), int(cu_seqlens is not None))
+        if need < 0:
+            raise ValueError("invalid sizes for the GDN-2 workspace")
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, None, dev)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    (gf, bf, wf), (gr, br, wr) = fwd_gates, rev_gates
+    _check(lib().gdr_gdn2_chunk_fwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(gf), _ptr(bf), _ptr(wf), _ptr(gr),
+                                          _ptr(br), _ptr(wr), _ptr(h0_fwd), _ptr(h0_rev), _ptr(cu_seqlens), int(chunk),
+                                          _ptr(out), _ptr(hT_f), _ptr(hT_r), ws_ptr, ws_bytes, ctypes.byref(dims),
+                                          _stream(q)))
+    return out, hT_f, hT_r
 
 
 def gdn2_chunk_fwd_noalloc(q, k, v, g, b, w, h0, cu_seqlens, out, hT, *, chunk: int = 64, read: str = "post",

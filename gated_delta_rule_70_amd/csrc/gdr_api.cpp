@@ -368,11 +368,16 @@ int64_t gdn2_ws_bytes(const gdr_chunk_dims_t &d, int32_t chunk, bool packed) {
     return prod({slots, d.Hk, gdr::gdn2_ws_key_bytes(dt, chunk, (int)d.dk)});
 }
 
-gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
-                             const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out,
-                             float *hT, void *workspace, int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
-                             void *stream) {
-    g_last_error[0] = '\0';
+// A validated GDN-2 chunked-forward launch.
+struct Gdn2Call {
+    gdr::Gdn2Args a;
+    int dtype, chunk, dk;
+};
+
+gdr_status_t gdn2_prepare(const void *q, const void *k, const void *v, const float *g, const void *b,
+                          const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out,
+                          float *hT, void *workspace, int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
+                          Gdn2Call *call) {
     if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
     const gdr_chunk_dims_t d = *dims;
     if (d.dtype != GDR_F32 && d.dtype != GDR_BF16) return fail(GDR_ERR_DTYPE, "dtype %d is not GDR_F32 or GDR_BF16", d.dtype);
@@ -444,10 +449,75 @@ gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const 
     a.nslots = nslots;
     const int64_t blocks = (a.units + 7) / 8 * 8 * a.ntiles;
     if (blocks > INT32_MAX) return fail(GDR_ERR_DIMS, "too many (sequence, head) units: %lld", (long long)a.units);
-    const hipError_t e = gdr::launch_gdn2_chunk_fwd(a, d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32, chunk,
-                                                    (int)d.dk, reinterpret_cast<hipStream_t>(stream));
+    call->a = a;
+    call->dtype = d.dtype == GDR_BF16 ? gdr::kDtypeBf16 : gdr::kDtypeF32;
+    call->chunk = chunk;
+    call->dk = (int)d.dk;
+    return GDR_OK;
+}
+
+gdr_status_t gdn2_launch(const Gdn2Call &c, void *stream) {
+    const hipError_t e = gdr::launch_gdn2_chunk_fwd(c.a, c.dtype, c.chunk, c.dk, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "GDN-2 chunk forward launch: %s", hipGetErrorString(e));
     return GDR_OK;
+}
+
+gdr_status_t gdn2_chunk_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
+                             const void *w, const float *h0, const int32_t *cu_seqlens, int32_t chunk, void *out,
+                             float *hT, void *workspace, int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
+                             void *stream) {
+    g_last_error[0] = '\0';
+    Gdn2Call call;
+    const gdr_status_t s = gdn2_prepare(q, k, v, g, b, w, h0, cu_seqlens, chunk, out, hT, workspace, workspace_bytes,
+                                        dims, &call);
+    return s != GDR_OK ? s : gdn2_launch(call, stream);
+}
+
+// Both GDN-2 scans of a bidirectional layer: the forward scan writes (or accumulates into) out,
+// then the reverse scan accumulates into it; both are validated before either is enqueued, and the
+// two passes share the workspace one after the other.
+gdr_status_t gdn2_bidir_impl(const void *q, const void *k, const void *v, const float *g_f, const void *b_f,
+                             const void *w_f, const float *g_r, const void *b_r, const void *w_r, const float *h0_f,
+                             const float *h0_r, const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT_f,
+                             float *hT_r, void *workspace, int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
+                             void *stream) {
+    g_last_error[0] = '\0';
+    if (!dims) return fail(GDR_ERR_NULL, "dims is NULL");
+    if (dims->flags & GDR_REVERSE)
+        return fail(GDR_ERR_FLAGS, "GDR_REVERSE is not a flag of the bidirectional call (it runs both directions)");
+    gdr_chunk_dims_t df = *dims, dr = *dims;
+    dr.flags |= GDR_REVERSE | GDR_ACCUMULATE;
+    Gdn2Call cf, cr;
+    char msg[sizeof(g_last_error)];
+    gdr_status_t s = gdn2_prepare(q, k, v, g_f, b_f, w_f, h0_f, cu_seqlens, chunk, out, hT_f, workspace,
+                                  workspace_bytes, &df, &cf);
+    if (s != GDR_OK) {
+        snprintf(msg, sizeof(msg), "forward scan: %s", g_last_error);
+        return fail(s, "%s", msg);
+    }
+    s = gdn2_prepare(q, k, v, g_r, b_r, w_r, h0_r, cu_seqlens, chunk, out, hT_r, workspace, workspace_bytes, &dr,
+                     &cr);
+    if (s != GDR_OK) {
+        snprintf(msg, sizeof(msg), "reverse scan: %s", g_last_error);
+        return fail(s, "%s", msg);
+    }
+    // the forward scan's final state must not overlap an input of the other direction, nor the
+    // other final state (each scan's own check already keeps the workspace off its inputs)
+    const gdr_chunk_dims_t &d = *dims;
+    const int64_t es = elem_size(d.dtype);
+    const int64_t nk = prod({d.B, d.Hk, d.T, d.dk}), nvv = prod({d.B, d.Hv, d.T, d.dv});
+    const int64_t ns = prod({cf.a.units, d.dk, d.dv}) * 4;
+    const Range rhf = rng("hT_fwd", hT_f, ns), rhr = rng("hT_rev", hT_r, ns);
+    const Range ins_r[] = {rng("g_rev", g_r, nk * 4), rng("b_rev", b_r, nk * es), rng("w_rev", w_r, nvv * es),
+                           rng("h0_rev", h0_r, ns), rhr};
+    const Range ins_f[] = {rng("g_fwd", g_f, nk * 4), rng("b_fwd", b_f, nk * es), rng("w_fwd", w_f, nvv * es),
+                           rng("h0_fwd", h0_f, ns)};
+    for (const Range &r : ins_r)
+        if (overlap(rhf, r)) return fail(GDR_ERR_ALIAS, "hT_fwd overlaps %s", r.name);
+    for (const Range &r : ins_f)
+        if (overlap(rhr, r)) return fail(GDR_ERR_ALIAS, "hT_rev overlaps %s", r.name);
+    s = gdn2_launch(cf, stream);
+    return s != GDR_OK ? s : gdn2_launch(cr, stream);
 }
 
 gdr_status_t gdn2_decode_impl(const void *q, const void *k, const void *v, const float *g, const void *b,
@@ -508,6 +578,16 @@ gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v, con
                                 const gdr_chunk_dims_t *dims, void *stream) {
     return gdn2_chunk_impl(q, k, v, g, b, w, h0, cu_seqlens, chunk, out, hT, workspace, workspace_bytes, dims,
                            stream);
+}
+
+gdr_status_t gdr_gdn2_chunk_fwd_bidir(const void *q, const void *k, const void *v, const float *g_fwd,
+                                      const void *b_fwd, const void *w_fwd, const float *g_rev, const void *b_rev,
+                                      const void *w_rev, const float *h0_fwd, const float *h0_rev,
+                                      const int32_t *cu_seqlens, int32_t chunk, void *out, float *hT_fwd, float *hT_rev,
+                                      void *workspace, int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
+                                      void *stream) {
+    return gdn2_bidir_impl(q, k, v, g_fwd, b_fwd, w_fwd, g_rev, b_rev, w_rev, h0_fwd, h0_rev, cu_seqlens, chunk, out,
+                           hT_fwd, hT_rev, workspace, workspace_bytes, dims, stream);
 }
 
 gdr_status_t gdr_gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g, const void *b,

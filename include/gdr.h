@@ -352,6 +352,34 @@ gdr_status_t gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                                 const gdr_chunk_dims_t *dims, void *stream);
 
 /*
+ * gdr_gdn2_chunk_fwd_bidir - both GDN-2 scans of the bidirectional layer on the "tiny_gdn/fugue.py"
+ * page (`BidirectionalGatedDeltaNet2`: `scan` runs each packed segment forward and reversed in
+ * place, each direction with its own decay and gates; `forward` adds the two), over shared q, k,
+ * v, summed per token into out (out += both with GDR_ACCUMULATE). The page scales the sum by 1/2
+ * and reads before the write on its reverse scan; the scale is the caller's, and dims->flags
+ * (GDR_READ_PRE, GDR_ACCUMULATE, GDR_QK_L2NORM) apply to both scans.
+ *
+ *   q, k, v, cu_seqlens, chunk, out, workspace, workspace_bytes, dims, stream: as
+ *       gdr_gdn2_chunk_fwd; the two passes use the workspace one after the other, so one of
+ *       gdr_gdn2_chunk_fwd_workspace_bytes bytes serves both (NULL: the one-pass kernel).
+ *   g_fwd, b_fwd, w_fwd / g_rev, b_rev, w_rev   the forward and the reverse scan's log decay,
+ *       erase and write gates, in gdr_gdn2_chunk_fwd's layouts, indexed by token
+ *   h0_fwd, h0_rev, hT_fwd, hT_rev   per direction, as in gdr_chunk_fwd_bidir
+ *
+ * Both scans are validated before either is enqueued. Errors: as gdr_gdn2_chunk_fwd, the message
+ * naming the scan; GDR_ERR_FLAGS for GDR_REVERSE; GDR_ERR_ALIAS when a final state or the
+ * workspace overlaps an input of the other direction, or the two final states overlap.
+ */
+gdr_status_t gdr_gdn2_chunk_fwd_bidir(const void *q, const void *k, const void *v,
+                                      const float *g_fwd, const void *b_fwd, const void *w_fwd,
+                                      const float *g_rev, const void *b_rev, const void *w_rev,
+                                      const float *h0_fwd, const float *h0_rev,
+                                      const int32_t *cu_seqlens, int32_t chunk, void *out,
+                                      float *hT_fwd, float *hT_rev, void *workspace,
+                                      int64_t workspace_bytes, const gdr_chunk_dims_t *dims,
+                                      void *stream);
+
+/*
  * gdr_gdn2_chunk_fwd_noalloc - gdr_gdn2_chunk_fwd in its two-pass form without a caller
  * workspace and without allocating: for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -118,6 +118,43 @@ def test_chunk_fwd_bidir_rejects(over, status, text):
     assert st == status and text in msg, (st, msg)
 
 
+def _gdn2_bidir(lib, **over):
+    d = dict(B=1, T=128, Hk=2, Hv=2, dk=64, dv=64, num_seqs=0, dtype=1, flags=1)
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g_f=FAKE * 4, b_f=FAKE * 5, w_f=FAKE * 6, g_r=FAKE * 7,
+               b_r=FAKE * 8, w_r=FAKE * 9, h0_f=None, h0_r=None, cu=None, out=FAKE * 10, hT_f=FAKE * 11,
+               hT_r=FAKE * 12, ws=FAKE * 32, ws_bytes=1 << 24, chunk=32)
+    for k_, v_ in over.items():
+        (d if k_ in d else ptr)[k_] = v_
+    dims = binding.ChunkDims(d["B"], d["T"], d["Hk"], d["Hv"], d["dk"], d["dv"], d["num_seqs"],
+                             d["dtype"], d["flags"])
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_gdn2_chunk_fwd_bidir(*[vp(ptr[n]) for n in ("q", "k", "v", "g_f", "b_f", "w_f", "g_r", "b_r", "w_r",
+                                                             "h0_f", "h0_r", "cu")],
+                                      ptr["chunk"], vp(ptr["out"]), vp(ptr["hT_f"]), vp(ptr["hT_r"]), vp(ptr["ws"]),
+                                      ptr["ws_bytes"], ctypes.byref(dims), None)
+    return binding.STATUS[st], lib.gdr_last_error().decode()
+
+
+GDN2_BIDIR_REJECTS = [
+    (dict(flags=3), "GDR_ERR_FLAGS", "GDR_REVERSE"),
+    (dict(g_f=None), "GDR_ERR_NULL", "forward scan"),
+    (dict(w_r=None), "GDR_ERR_NULL", "reverse scan"),
+    (dict(ws_bytes=64), "GDR_ERR_DIMS", "forward scan: workspace_bytes"),
+    (dict(hT_f=FAKE * 7), "GDR_ERR_ALIAS", "hT_fwd overlaps g_rev"),
+    (dict(hT_r=FAKE * 6), "GDR_ERR_ALIAS", "hT_rev overlaps w_fwd"),
+    (dict(hT_r=FAKE * 11 + 4096), "GDR_ERR_ALIAS", "hT_fwd overlaps hT_rev"),
+    (dict(ws=FAKE * 8 - 4096), "GDR_ERR_ALIAS", "reverse scan: workspace overlaps b"),
+    (dict(ws=FAKE * 5 - 4096), "GDR_ERR_ALIAS", "forward scan: workspace overlaps b"),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status,text", GDN2_BIDIR_REJECTS, ids=[c[1] + ":" + c[2] for c in GDN2_BIDIR_REJECTS])
+def test_gdn2_chunk_fwd_bidir_rejects(over, status, text):
+    st, msg = _gdn2_bidir(binding.load(), **over)
+    assert st == status and text in msg, (st, msg)
+
+
 @needs_lib
 def test_null_dims_and_status_strings():
     lib = binding.load()
