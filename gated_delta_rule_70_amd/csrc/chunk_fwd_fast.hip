@@ -437,18 +437,10 @@ __device__ __forceinline__ void grams(floatx4 (&acc)[N], const uint4 (*x)[4], co
 __device__ __forceinline__ uint2 pack4(floatx4 v) { return __builtin_bit_cast(uint2, cvt4<__bf16>(v)); }
 
 // ------------------------------------------------------------------ gate scalars
-// Every prep wave starts from the chunk's gates in the raw buffer (lane = token row).
+// The chunk's gates per token row (lane = row).
 struct Gates {
     float la2, beta, b2;  // log2-scaled log alpha, beta, inclusive log2 cumsum
 };
-__device__ __forceinline__ Gates read_gates(const char *raw) {
-    const int lane = threadIdx.x & 63;
-    Gates gt;
-    gt.la2 = reinterpret_cast<const float *>(raw + kRawLa)[lane] * kLog2e;
-    gt.beta = reinterpret_cast<const float *>(raw + kRawBeta)[lane];
-    gt.b2 = wave_cumsum(gt.la2);
-    return gt;
-}
 
 // ------------------------------------------------------------------ diagonal prep
 // kL2: the k rows are scaled to unit length (their scales are in the chunk's table)
