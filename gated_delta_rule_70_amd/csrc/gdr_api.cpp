@@ -274,9 +274,10 @@ gdr_status_t bidir_impl(const void *q, const void *k, const void *v, const float
         snprintf(msg, sizeof(msg), "reverse scan: %s", g_last_error);
         return fail(s, "%s", msg);
     }
-    // the forward scan's final state is written before the reverse scan reads its inputs, and the
-    // reverse scan's final state after the forward scan has read its own: no final state may
-    // overlap an input of the other direction, nor the other final state
+    // the forward scan's final state is written before the reverse scan reads its inputs, so it
+    // must not overlap them; the reverse scan's final state is held to the same rule against the
+    // forward scan's inputs (stream order alone would allow that overlap), and the two final
+    // states must not overlap each other
     const int64_t ns = prod({cf.a.units, dims->dk, dims->dv}) * 4, ng = prod({dims->B, dims->Hv, dims->T}) * 4;
     const Range rhf = rng("hT_fwd", hT_f, ns), rhr = rng("hT_rev", hT_r, ns);
     const Range others_f[] = {rng("log_alpha_rev", la_r, ng), rng("beta_rev", beta_r, ng), rng("h0_rev", h0_r, ns),
@@ -501,8 +502,10 @@ gdr_status_t gdn2_bidir_impl(const void *q, const void *k, const void *v, const 
         snprintf(msg, sizeof(msg), "reverse scan: %s", g_last_error);
         return fail(s, "%s", msg);
     }
-    // the forward scan's final state must not overlap an input of the other direction, nor the
-    // other final state (each scan's own check already keeps the workspace off its inputs)
+    // the forward scan's final state must not overlap an input of the reverse scan, which reads
+    // them after it is written; the reverse scan's final state is held to the same rule against
+    // the forward scan's inputs, and the two final states must not overlap each other (each
+    // scan's own check already keeps the workspace off its inputs)
     const gdr_chunk_dims_t &d = *dims;
     const int64_t es = elem_size(d.dtype);
     const int64_t nk = prod({d.B, d.Hk, d.T, d.dk}), nvv = prod({d.B, d.Hv, d.T, d.dv});
