@@ -394,19 +394,48 @@ __device__ __forceinline__ float wave_scan(float x) {
 template <typename E, int DK>
 struct PrepSmem {
     static constexpr int KP = DK + pad_of<E>(), AP = SP, TP = SP;
-    E K[CB][KP];
+    // Once the products that read K and Q are done, T (zeroed, then written by the solve) takes
+    // the place of K and A that of Q (Pm never enters the LDS). With bf16 inputs four workgroups
+    // fit on a compute unit.
+    union {
+        E K[CB][KP];
+        float T[CB * SP];  // flat: the shared triangular inverse reads T and A so
+    };
     union {
         E Q[CB][KP];
-        float P[CB][SP];  // Pm, once the products that read Q are done
-    } u;
-    float A[CB * SP], T[CB * SP];  // flat: the shared triangular inverse reads them so
+        float A[CB * SP];
+    };
     float la[CB], beta[CB], b[CB], r[CB];
 };
+static_assert(sizeof(PrepSmem<__bf16, 128>) * 4 <= 160 * 1024, "four prep workgroups per compute unit");
+
+// The prep's products: five 16x16 tiles per wave, the ten lower tiles of G and the ten of Pm.
+// A Pm^T operand slab (mt, ks) of the record holds Pm tiles (2 ks, mt) and (2 ks + 1, mt) in the
+// same lanes (lo and hi halves of the fragment), so the Pm tiles are dealt in those pairs and each
+// slab is written from the registers of one wave; a slab whose (2 ks, mt) tile lies above the
+// diagonal has only its hi tile. Wave 0, which solves, takes G tiles only. A job is 12 bits,
+// kind | tm << 4 | tn << 8 for tile (tm, tn); five per wave.
+enum : int { kJobG = 0, kJobPLo = 1, kJobPHi = 2, kJobPOnly = 3 };
+constexpr uint64_t prep_job(int kind, int tm, int tn) { return (uint64_t)(kind | tm << 4 | tn << 8); }
+constexpr uint64_t prep_jobs(uint64_t j0, uint64_t j1, uint64_t j2, uint64_t j3, uint64_t j4) {
+    return j0 | j1 << 12 | j2 << 24 | j3 << 36 | j4 << 48;
+}
+constexpr uint64_t kPrepJobs[4] = {
+    prep_jobs(prep_job(kJobG, 0, 0), prep_job(kJobG, 1, 0), prep_job(kJobG, 1, 1), prep_job(kJobG, 2, 0),
+              prep_job(kJobG, 2, 1)),
+    prep_jobs(prep_job(kJobPLo, 0, 0), prep_job(kJobPHi, 1, 0), prep_job(kJobPLo, 2, 0), prep_job(kJobPHi, 3, 0),
+              prep_job(kJobG, 2, 2)),
+    prep_jobs(prep_job(kJobPLo, 2, 1), prep_job(kJobPHi, 3, 1), prep_job(kJobPLo, 2, 2), prep_job(kJobPHi, 3, 2),
+              prep_job(kJobG, 3, 0)),
+    prep_jobs(prep_job(kJobPOnly, 1, 1), prep_job(kJobPOnly, 3, 3), prep_job(kJobG, 3, 1), prep_job(kJobG, 3, 2),
+              prep_job(kJobG, 3, 3)),
+};
+// Pm^T slabs with no lower tile, written as zeros by wave 0: (mt, ks) = (2, 0) and (3, 0)
 
 template <typename E, int DK>
-__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
+__device__ __forceinline__ void prep_body(const BwdArgs &a) {
     typedef PrepSmem<E, DK> SM;
-    __shared__ SM sm;
+    __shared__ __align__(16) SM sm;
     constexpr bool kX = std::is_same<E, __bf16>::value;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -433,7 +462,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
             bv = beb[t];
         }
         kp.store(&sm.K[0][0], SM::KP, n, tid);
-        qp.store(&sm.u.Q[0][0], SM::KP, n, tid);
+        qp.store(&sm.Q[0][0], SM::KP, n, tid);
         if (tid < CB) {
             sm.la[tid] = lv;
             sm.beta[tid] = bv;
@@ -447,53 +476,79 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
     uint8_t *rec = a.rec + (head * a.nslots + slot) * Rec<DK>::kBytes;
-    // the lower tiles of G (tasks 0-9) and Pm (10-19), five per wave, into registers: Pm is
-    // stored over Q, so every product must be done before any tile is stored
-    constexpr int kPer = 20 / (kPrepThreads / 64);
-    floatx4 acc[kPer];
+    static_assert(kPrepThreads == 256 && NMT == 4 && kSlices == 2, "the job table is written for 4 waves and 64-token chunks");
+    const uint64_t jobs = wave == 0 ? kPrepJobs[0] : wave == 1 ? kPrepJobs[1] : wave == 2 ? kPrepJobs[2] : kPrepJobs[3];
+    auto job = [&](int s, int &kind, int &tm, int &tn) __attribute__((always_inline)) {
+        const int j = (int)((jobs >> (12 * s)) & 0xfff);
+        kind = j & 15;
+        tm = (j >> 4) & 15;
+        tn = j >> 8;
+    };
+    floatx4 acc[5];
 #pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-        const int task = wave + (kPrepThreads / 64) * s;
-        const bool isp = task >= 10;
-        int mt, nt;
-        lower_tile(task % 10, mt, nt);
+    for (int s = 0; s < 5; ++s) {
+        int kind, tm, tn;
+        job(s, kind, tm, tn);
         acc[s] = zero4();
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
-            acc[s] = mms<kX, kX>(acc[s], ldr<E>(isp ? &sm.u.Q[0][0] : &sm.K[0][0], SM::KP, 16 * mt, 32 * ks),
-                                 ldr<E>(&sm.K[0][0], SM::KP, 16 * nt, 32 * ks));
+            acc[s] = mms<kX, kX>(acc[s], ldr<E>(kind == kJobG ? &sm.K[0][0] : &sm.Q[0][0], SM::KP, 16 * tm, 32 * ks),
+                                 ldr<E>(&sm.K[0][0], SM::KP, 16 * tn, 32 * ks));
+    }
+    // Pm^T slab (mt, ks) from its tiles' registers: Pm_ij = (Q K^T)_ij e^{r_i - b_j} on the kept
+    // entries (j <= i, or j < i for the pre-write read)
+    auto put_pt = [&](int mt, int ks, const floatx4 &lo, const floatx4 &hi) __attribute__((always_inline)) {
+        Frag<float> f;
+        f.lo = lo;
+        f.hi = hi;
+        const Split sp = split_frag(f);
+        uint4 *dst = reinterpret_cast<uint4 *>(rec + kRecPt + (mt * kSlices + ks) * kSlabBytes + lane * 32);
+        dst[0] = __builtin_bit_cast(uint4, sp.h);
+        dst[1] = __builtin_bit_cast(uint4, sp.l);
+    };
+    {
+        floatx4 plo = zero4();
+#pragma unroll
+        for (int s = 0; s < 5; ++s) {
+            int kind, tm, tn;
+            job(s, kind, tm, tn);
+            if (kind == kJobG) continue;
+            floatx4 pv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * tm + 4 * g + r, j = 16 * tn + cc;
+                const bool keep = pre ? j < i : j <= i;
+                pv[r] = keep ? acc[s][r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
+            }
+            if (kind == kJobPLo) plo = pv;
+            else put_pt(tn, tm >> 1, kind == kJobPHi ? plo : zero4(), pv);
+        }
+        if (wave == 0) {
+            put_pt(2, 0, zero4(), zero4());
+            put_pt(3, 0, zero4(), zero4());
+        }
     }
     __syncthreads();
     for (int i = tid; i < CB * SP; i += kPrepThreads) sm.T[i] = 0.f;
+    // the G tiles into A (over Q), each with its mirrored upper tile of zeros
 #pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-        const int task = wave + (kPrepThreads / 64) * s;
-        const bool isp = task >= 10;
-        int mt, nt;
-        lower_tile(task % 10, mt, nt);
+    for (int s = 0; s < 5; ++s) {
+        int kind, tm, tn;
+        job(s, kind, tm, tn);
+        if (kind != kJobG) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 16 * mt + 4 * g + r, j = 16 * nt + cc;
-            if (isp) {
-                const bool keep = pre ? j < i : j <= i;
-                sm.u.P[i][j] = keep ? acc[s][r] * __expf(fminf(sm.r[i] - sm.b[j], 0.f)) : 0.f;
-            } else {
-                sm.A[i * SP + j] = j < i ? sm.beta[i] * acc[s][r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
-            }
-            // the mirrored upper tile is zero
-            if (mt > nt) {
-                const int i2 = 16 * nt + 4 * g + r, j2 = 16 * mt + cc;
-                if (isp) sm.u.P[i2][j2] = 0.f;
-                else sm.A[i2 * SP + j2] = 0.f;
-            }
+            const int i = 16 * tm + 4 * g + r, j = 16 * tn + cc;
+            sm.A[i * SP + j] = j < i ? sm.beta[i] * acc[s][r] * __expf(fminf(sm.b[i] - sm.b[j], 0.f)) : 0.f;
+            if (tm > tn) sm.A[(16 * tn + 4 * g + r) * SP + 16 * tm + cc] = 0.f;
         }
     }
     __syncthreads();
     if (wave == 0) solve_unit_lower_inverse<float, CB>(sm);
     __syncthreads();
-    // T, T^T and Pm^T as A-operand fragments: lane (g, c) of slab (mt, ks) holds row 16 mt + c,
+    // T and T^T as A-operand fragments: lane (g, c) of slab (mt, ks) holds row 16 mt + c,
     // columns 32 ks + 4g + s and 32 ks + 16 + 4g + s (s = 0..3)
-    for (int it = tid; it < 3 * NMT * kSlices * 64; it += kPrepThreads) {
+    for (int it = tid; it < 2 * NMT * kSlices * 64; it += kPrepThreads) {
         const int mat = it / (NMT * kSlices * 64), sl = (it / 64) % (NMT * kSlices), ln = it % 64;
         const int mt = sl / kSlices, ks = sl % kSlices;
         const int row = 16 * mt + (ln & 15), kb0 = 32 * ks + 4 * (ln >> 4);
@@ -501,7 +556,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int k = kb0 + (s < 4 ? s : 12 + s);
-            const float x = mat == 0 ? sm.T[row * SP + k] : mat == 1 ? sm.T[k * SP + row] : sm.u.P[k][row];
+            const float x = mat == 0 ? sm.T[row * SP + k] : sm.T[k * SP + row];
             if (s < 4) f.lo[s] = x;
             else f.hi[s - 4] = x;
         }
@@ -515,6 +570,16 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
         rb[tid] = sm.b[tid];
         rb[CB + tid] = sm.r[tid];
     }
+}
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
+    prep_body<E, DK>(a);
+}
+// bf16: at most 128 registers, so that four workgroups (4 waves each) fit on a compute unit
+template <int DK>
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_prep_kernel_bf16(BwdArgs a) {
+    prep_body<__bf16, DK>(a);
 }
 
 // ---------------------------------------------------------------- 2. sweeps
@@ -1279,7 +1344,10 @@ template <typename E, int DK>
 hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
     const int64_t np = a.Hv * a.nslots, nsw = 2 * a.units * a.ntiles, ng = a.Hk * a.nslots;
     if (np > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<E, DK>), dim3((unsigned)np), dim3(kPrepThreads), 0, s, a);
+        if constexpr (std::is_same<E, __bf16>::value)
+            hipLaunchKernelGGL((bwd_prep_kernel_bf16<DK>), dim3((unsigned)np), dim3(kPrepThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_prep_kernel<E, DK>), dim3((unsigned)np), dim3(kPrepThreads), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
